@@ -1,0 +1,470 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Nothing here compares the oracle with itself: each check uses an independent
+route (numpy's binary16 rounding, exact rational arithmetic, brute force over
+all code levels, integer Hadamard sums, closed forms, library softmax).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from synth import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+rng = np.random.default_rng(1234)
+
+
+def h16(x):
+    return np.asarray(x, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def fr16(h):
+    """Exact rational value of an fp16 bit pattern."""
+    return Fraction(float(np.uint16(h).view(np.float16)))
+
+
+# ---------------------------------------------------------------- binary16 rounding
+def test_f16_rounding_matches_numpy_random_f32():
+    bits = rng.integers(0, 2**32, size=1 << 21, dtype=np.uint64).astype(np.uint32)
+    x = bits.view(np.float32)
+    x = x[np.isfinite(x)]
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    got = O.f32_to_f16(x)
+    nan = np.isnan(x)
+    assert np.array_equal(got[~nan], ref[~nan])
+
+
+def test_f16_rounding_ties_and_boundaries():
+    # every fp16 value, the exact midpoints to both neighbours, and 1 ulp (f64) around them
+    h = np.arange(0, 0x7C00, dtype=np.uint16)
+    v = h.view(np.float16).astype(np.float64)
+    nxt = np.append(v[1:], 65536.0)
+    mids = (v + nxt) / 2
+    cand = np.concatenate([v, -v, mids, -mids, np.nextafter(mids, 0), np.nextafter(mids, np.inf),
+                           [65504.0, 65519.99, 65520.0, 2.0**-25, 2.0**-26, 3 * 2.0**-26]])
+    with np.errstate(over="ignore"):
+        ref = cand.astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.f64_to_f16(cand), ref)
+    # the same through binary32 inputs
+    c32 = cand.astype(np.float32)
+    with np.errstate(over="ignore"):
+        ref32 = c32.astype(np.float16).view(np.uint16)
+    assert np.array_equal(O.f32_to_f16(c32), ref32)
+
+
+def test_f16_widening_exact():
+    h = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = (h & 0x7C00) != 0x7C00
+    lib = O.lib()
+    got = np.array([lib.oq_f16_to_f64(int(x)) for x in h[finite][::7]])
+    assert np.array_equal(got, h[finite][::7].view(np.float16).astype(np.float64))
+
+
+# ---------------------------------------------------------------- uniform quantizers
+def _groups(n, count):
+    out = []
+    for i in range(count):
+        kind = i % 6
+        if kind == 0:
+            x = rng.standard_normal(n)
+        elif kind == 1:
+            x = rng.standard_t(3, n) * 5
+        elif kind == 2:
+            x = rng.uniform(-1e-4, 1e-4, n)      # subnormal-range scales
+        elif kind == 3:
+            x = np.full(n, rng.standard_normal())  # constant group
+        elif kind == 4:
+            x = rng.uniform(-60000, 60000, n)    # near the fp16 edge
+        else:
+            x = rng.integers(-3, 4, n).astype(np.float64)
+        out.append(h16(x))
+    return out
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_asym_round_trip_bound(bits):
+    Q = (1 << bits) - 1
+    for g in _groups(32, 300):
+        codes, (s, z) = O.quant_asym(g, bits)
+        x = g.view(np.float16).astype(np.float64)
+        sv, zv = float(np.uint16(s).view(np.float16)), float(np.uint16(z).view(np.float16))
+        assert zv == x.min()
+        assert codes.max() <= Q
+        xh = codes * sv + zv
+        err = np.abs(x - xh)
+        slack = abs(zv) * 2.0**-52 + 1e-300
+        if sv >= 2.0**-14:
+            # normal fp16 scale: every value within half a step
+            assert np.all(err <= sv / 2 * (1 + 2.0**-10) + slack)
+        else:
+            # subnormal scale: fp16 keeps few significant bits, so Q*s may fall short
+            # of the range and the top values clamp to code Q
+            over = max(0.0, (x.max() - x.min()) - Q * sv)
+            assert np.all(err <= max(sv / 2 * (1 + 2.0**-10), over) + slack)
+        if x.max() > x.min():
+            assert codes[np.argmin(x)] == 0 and s != 0
+            if sv >= 2.0**-14:
+                assert codes[np.argmax(x)] == Q
+        else:
+            assert s == 0 and not codes.any()
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_asym_codes_are_nearest_level_bruteforce(bits):
+    Q = (1 << bits) - 1
+    for g in _groups(6, 240):
+        codes, (s, z) = O.quant_asym(g, bits)
+        if s == 0:
+            continue
+        S, Z = fr16(s), fr16(z)
+        for h, c in zip(g, codes):
+            X = fr16(h)
+            d = [abs(X - (k * S + Z)) for k in range(Q + 1)]
+            best = min(d)
+            # the chosen level is the nearest one (ties within fp32 rounding allowed)
+            assert d[c] - best <= S * Fraction(1, 1 << 20), (bits, h, c, d.index(best))
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_sym_bruteforce_and_bound(bits):
+    Qs = (1 << (bits - 1)) - 1
+    mid = 1 << (bits - 1)
+    for g in _groups(8, 240):
+        codes, (s, z) = O.quant_sym(g, bits)
+        assert s & 0x8000 and z == 0
+        sm = s & 0x7FFF
+        x = g.view(np.float16).astype(np.float64)
+        if np.abs(x).max() == 0:
+            assert sm == 0 and not codes.any()
+            continue
+        S = fr16(sm)
+        assert codes.min() >= 1 and codes.max() <= 2 * Qs + 1
+        for h, c in zip(g, codes):
+            X = fr16(h)
+            d = {k: abs(X - (k - mid) * S) for k in range(mid - Qs, mid + Qs + 1)}
+            best = min(d.values())
+            assert d[int(c)] - best <= S * Fraction(1, 1 << 20)
+            bound = S / 2 * (1 + Fraction(1, 1024))
+            if sm < 0x0400:   # subnormal scale: values beyond Qs*s clamp
+                bound = max(bound, Fraction(float(np.abs(x).max())) - Qs * S)
+            assert abs(X - (int(c) - mid) * S) <= bound
+        # dequant helper agrees with the sign-bit convention
+        assert O.dequant(codes[0], s, 0, bits) == float((int(codes[0]) - mid) * S)
+
+
+def test_hybrid_decision_exact_rational():
+    def ref(g):
+        X = [fr16(h) for h in g]
+        rng_ = max(X) - min(X)
+        mean = sum(X) / len(X)
+        if rng_ == 0:
+            return mean == 0
+        return abs(mean) / rng_ <= Fraction(1, 10)
+    for g in _groups(64, 300):
+        assert O.hybrid_is_sym(g) == ref(g)
+    # adversarial: |mean|/range exactly 0.1 (sym) and just above (asym)
+    base = np.ones(64)
+    base[0], base[1] = -5.0, 5.0
+    base[2] = base[3] = 2.0          # sum = -5 + 5 + 2 + 2 + 60 = 64 -> mean 1, range 10
+    g = h16(base)
+    assert ref(g) and O.hybrid_is_sym(g)
+    base[4] = 1.0 + 2.0**-10 * 64    # sum slightly above 64
+    g = h16(base)
+    assert not ref(g) and not O.hybrid_is_sym(g)
+    assert O.hybrid_is_sym(h16(np.zeros(64)))
+    assert not O.hybrid_is_sym(h16(np.full(64, 0.5)))
+
+
+def test_golden_small_quantizer_examples():
+    with open(os.path.join(GOLDEN, "quantizer_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        g = h16(c["x"])
+        if c["kind"] == "asym":
+            codes, meta = O.quant_asym(g, c["bits"])
+        elif c["kind"] == "sym":
+            codes, meta = O.quant_sym(g, c["bits"])
+        else:
+            codes, meta = O.quant_nuq(g, h16(c["levels"]))
+        assert codes.tolist() == c["codes"], c["name"]
+        assert [int(m) for m in meta] == [int(v, 16) for v in c["meta_hex"]], c["name"]
+
+
+# ---------------------------------------------------------------- non-uniform
+def _levels(draws):
+    return np.sort(h16(np.concatenate([[0.0], draws, [1.0]])).view(np.float16)).view(np.uint16)
+
+
+def test_nuq_nearest_level_bruteforce():
+    for trial in range(200):
+        lv = _levels(rng.uniform(0, 1, 6))
+        if len(set(lv.tolist())) < 8:
+            continue
+        g = _groups(6, 6)[trial % 6]
+        codes, (s, z) = O.quant_nuq(g, lv)
+        if s == 0:
+            assert not codes.any()
+            continue
+        if s == 0x7BFF:      # range beyond fp16: scale saturates, top values clamp
+            x = g.view(np.float16).astype(np.float64)
+            assert x.max() - x.min() >= 65504 and codes[np.argmax(x)] == 7
+            continue
+        S, Z = fr16(s), fr16(z)
+        L = [fr16(v) for v in lv]
+        for h, c in zip(g, codes):
+            X = fr16(h)
+            d = [abs(X - (L[j] * S + Z)) for j in range(8)]
+            assert d[c] - min(d) <= S * Fraction(1, 1 << 18)
+
+
+def test_nuq_uniform_levels_match_3bit_uniform():
+    lv = h16(np.arange(8) / 7.0)
+    for g in _groups(32, 120):
+        c_n, (s_n, z_n) = O.quant_nuq(g, lv)
+        c_u, (s_u, z_u) = O.quant_asym(g, 3)
+        assert z_n == z_u
+        if s_n == 0 or s_n == 0x7BFF:
+            continue
+        x = g.view(np.float16).astype(np.float64)
+        t = (x - x.min()) / (x.max() - x.min()) * 7
+        near_mid = np.abs(t - np.floor(t) - 0.5) < 2e-3
+        assert np.array_equal(c_n[~near_mid], c_u[~near_mid])
+
+
+def test_nuq_round_trip_bound():
+    for trial in range(100):
+        lv = _levels(rng.uniform(0, 1, 6))
+        gap = np.diff(lv.view(np.float16).astype(np.float64)).max()
+        for g in _groups(32, 6):
+            codes, (s, z) = O.quant_nuq(g, lv)
+            x = g.view(np.float16).astype(np.float64)
+            sv, zv = float(np.uint16(s).view(np.float16)), float(np.uint16(z).view(np.float16))
+            xh = lv.view(np.float16).astype(np.float64)[codes] * sv + zv
+            if s == 0x7BFF:
+                continue
+            # rounding of the range to fp16 adds at most one half-ulp of the range
+            assert np.all(np.abs(x - xh) <= sv * gap / 2 + (x.max() - x.min()) * 2.0**-10 + 1e-300)
+
+
+# ---------------------------------------------------------------- outliers
+def test_topk_against_sort():
+    for _ in range(300):
+        row = h16(rng.standard_t(3, 128))
+        k = int(rng.integers(1, 5))
+        mags = np.abs(row.view(np.float16).astype(np.float64))
+        order = sorted(range(128), key=lambda i: (-mags[i], i))[:k]
+        assert O.topk(row, k).tolist() == sorted(order)
+
+
+def test_topk_ties():
+    row = h16(np.full(128, 2.0))
+    assert O.topk(row, 2).tolist() == [0, 1]
+    r = np.ones(128)
+    r[[5, 9, 70]] = [-3.0, 3.0, -3.0]
+    assert O.topk(h16(r), 2).tolist() == [5, 9]
+
+
+# ---------------------------------------------------------------- Hadamard
+def test_hadamard_fp16_exact_against_integer_sums():
+    D = 128
+    c = 1.0 / math.sqrt(128.0)
+    for trial in range(60):
+        v = h16(rng.standard_normal(D) * (10.0 ** rng.integers(-3, 4)))
+        ints = [int(Fraction(fr16(h)) * (1 << 24)) for h in v]
+        S = []
+        for i in range(D):
+            acc = 0
+            for j in range(D):
+                acc += -ints[j] if bin(i & j).count("1") & 1 else ints[j]
+            S.append(acc)
+        ref = np.array([float(s) / (1 << 24) * c for s in S]).astype(np.float16).view(np.uint16)
+        assert np.array_equal(O.hadamard_fp16(v), ref)
+
+
+def test_golden_hadamard_order4():
+    with open(os.path.join(GOLDEN, "hadamard_examples.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        got = O.hadamard_fp16(h16(c["v"])).view(np.float16).astype(np.float64)
+        assert got.tolist() == c["out"], c["name"]
+
+
+def test_hadamard_orthogonal_involution():
+    D = 128
+    M = np.stack([O.hadamard_f64(np.eye(D)[j]) for j in range(D)], axis=1)
+    Hint = M * math.sqrt(D)
+    assert np.array_equal(np.abs(np.round(Hint)), np.ones((D, D)))
+    assert np.allclose(Hint, np.round(Hint), atol=1e-12)
+    Hr = np.round(Hint)
+    assert np.array_equal(Hr @ Hr.T, D * np.eye(D))
+    assert np.array_equal(Hr, Hr.T) and np.all(Hr[0] == 1) and np.all(Hr[:, 0] == 1)
+    assert np.allclose(M @ M, np.eye(D), atol=1e-15)
+
+
+def test_rotate_attend_unrotate_equals_plain_attention():
+    D, n, G = 128, 300, 4
+    q = rng.standard_normal((G, D))
+    K = rng.standard_normal((n, D))
+    V = rng.standard_normal((n, D))
+    Vr = np.stack([O.hadamard_f64(v) for v in V])
+    a = O.attention(q, K, Vr, unrotate=True)
+    b = O.attention(q, K, V, unrotate=False)
+    assert np.max(np.abs(a - b)) < 1e-12
+
+
+# ---------------------------------------------------------------- attention
+def _softmax_attention(q, K, V):
+    from scipy.special import softmax
+    s = (q @ K.T) / math.sqrt(q.shape[1])
+    return softmax(s, axis=1) @ V
+
+
+def test_attention_uniform_scores_give_mean():
+    D, n = 128, 257
+    K = rng.standard_normal((n, D))
+    V = rng.standard_normal((n, D))
+    out = O.attention(np.zeros((3, D)), K, V)
+    assert np.max(np.abs(out - V.mean(axis=0))) < 1e-12
+    Vr = np.stack([O.hadamard_f64(v) for v in V])
+    out = O.attention(np.zeros((1, D)), K, Vr, unrotate=True)
+    assert np.max(np.abs(out[0] - V.mean(axis=0))) < 1e-12
+
+
+def test_attention_bruteforce_tiny():
+    for n in range(1, 9):
+        q = rng.standard_normal((2, 128)) * 3
+        K = rng.standard_normal((n, 128))
+        V = rng.standard_normal((n, 128))
+        assert np.allclose(O.attention(q, K, V), _softmax_attention(q, K, V), rtol=0, atol=1e-13)
+
+
+def test_split_lse_equals_one_pass():
+    n, D = 37, 128
+    q = rng.standard_normal((2, D)) * 2
+    K = rng.standard_normal((n, D))
+    V = rng.standard_normal((n, D))
+    ref = O.attention(q, K, V)
+    for ns in range(1, n + 3):
+        assert np.max(np.abs(O.attention_split(q, K, V, ns) - ref)) < 1e-12
+
+
+# ---------------------------------------------------------------- cache state machine
+def test_state_machine_closed_forms():
+    assert O.state_prefill(512, 0, 32, 32) == (0, 480, 32)            # C1
+    s, nb, r = O.state_prefill(32768, 4, 128, 32)                      # C2
+    assert (s, nb, r) == (4, 32608, 156)
+    n, flushes = 32768, []
+    for step in range(1, 65):
+        n, nb, r, f = O.state_append(n, nb, r, 128, 32)
+        if f:
+            flushes.append(step)
+        assert 128 <= r < 160
+    assert flushes == [4, 36] and (nb, r) == (32672, 156)
+    s, nb, r = O.state_prefill(8192, 0, 0, 32)                         # C3
+    flushes = []
+    n = 8192
+    for step in range(1, 65):
+        n, nb, r, f = O.state_append(n, nb, r, 0, 32)
+        flushes += [step] if f else []
+    assert flushes == [32, 64] and r == 0 and nb == 8256
+    s, nb, r = O.state_prefill(16384, 0, 0, 1)                         # C5: every token quantized
+    assert (nb, r) == (16384, 0)
+    assert O.state_append(16384, 16384, 0, 0, 1) == (16385, 16385, 0, True)
+    assert O.state_prefill(3, 4, 128, 32) == (3, 0, 0)                 # short prompt: all sinks
+    with open(os.path.join(GOLDEN, "state_examples.json")) as f:
+        for c in json.load(f)["cases"]:
+            got = O.state_prefill(c["n"], c["S"], c["W"], c["F"])
+            assert list(got) == c["s_nb_r"], c["name"]
+
+
+# ---------------------------------------------------------------- unit level
+def _unit(wl, n, nb, s_eff):
+    K, V = O.unit_inputs(wl, 0, 0, 0, n)
+    sc = O.scheme_for(wl, 0)
+    enc = O.encode_unit(sc, K, V, n, s_eff, nb)
+    return sc, K, V, enc
+
+
+def test_all_fp16_cache_is_plain_attention():
+    wl = W.C1.with_(T=40)                     # n <= W + S: nothing quantized
+    s, nb, r = O.state_prefill(40, 0, 32, 32)
+    assert nb == 0
+    sc, K, V, enc = _unit(wl, 40, 0, 0)
+    Kh, Vh = O.dequant_unit(sc, K, enc, 40, 0, 0)
+    q = wl.q(0, 0).reshape(1, 128).double().numpy()
+    ref = _softmax_attention(q, K.view(np.float16).astype(np.float64), V.view(np.float16).astype(np.float64))
+    assert np.max(np.abs(O.attention(q, Kh, Vh) - ref)) < 1e-12
+
+
+def test_more_bits_converge_to_fp16_attention():
+    wl = W.C1
+    K, V = O.unit_inputs(wl, 0, 0, 0, 512)
+    q = wl.q(0, 0).reshape(1, 128).double().numpy()
+    ref = _softmax_attention(q, K.view(np.float16).astype(np.float64), V.view(np.float16).astype(np.float64))
+    errs = []
+    for b in (2, 3, 4, 8):
+        sc = O.make_scheme(k_bits=b, v_bits=b)
+        enc = O.encode_unit(sc, K, V, 512, 0, 480)
+        Kh, Vh = O.dequant_unit(sc, K, enc, 512, 0, 480)
+        out = O.attention(q, Kh, Vh)
+        errs.append(np.max(np.abs(out - ref)) / np.max(np.abs(ref)))
+    assert errs == sorted(errs, reverse=True), errs
+    assert errs[-1] <= 1e-2, errs
+
+
+def test_rope_matches_complex_rotation():
+    wl = W.C4.with_(T=64, window=64)           # keep everything fp16 so only RoPE acts
+    K, V = O.unit_inputs(wl, 0, 0, 0, 64)
+    sc = O.scheme_for(wl, 0)
+    enc = O.encode_unit(sc, K, V, 64, 0, 0)
+    Kh, _ = O.dequant_unit(sc, K, enc, 64, 0, 0)
+    k = K.view(np.float16).astype(np.float64)
+    i = np.arange(64)
+    for t in (0, 1, 17, 63):
+        z = (k[t, :64] + 1j * k[t, 64:]) * np.exp(1j * t * 10000.0 ** (-2.0 * i / 128))
+        assert np.allclose(Kh[t, :64], z.real, atol=1e-12) and np.allclose(Kh[t, 64:], z.imag, atol=1e-12)
+    assert np.allclose(np.linalg.norm(Kh, axis=1), np.linalg.norm(k, axis=1), rtol=1e-13)
+
+
+def test_outliers_overwrite_and_are_excluded_from_stats():
+    wl = W.C4.with_(T=96)
+    n, nb = 96, 96
+    K, V = O.unit_inputs(wl, 0, 0, 0, n)
+    sc = O.scheme_for(wl, 0)
+    sc.pre_rope = 0                             # look at keys before RoPE
+    enc = O.encode_unit(sc, K, V, n, 0, nb)
+    Kh, Vh = O.dequant_unit(sc, K, enc, n, 0, nb)
+    k16 = K.view(np.float16).astype(np.float64)
+    for t in range(nb):
+        mags = np.abs(k16[t])
+        top = sorted(sorted(range(128), key=lambda c: (-mags[c], c))[:2])
+        assert enc["kocol"][t].tolist() == top
+        assert np.array_equal(Kh[t, top], k16[t, top])            # exact overwrite
+        assert np.array_equal(Vh[t, enc["vocol"][t]], V.view(np.float16).astype(np.float64)[t, enc["vocol"][t]])
+    # per-channel key groups: zero point is the min over non-outlier members
+    mask = np.zeros((nb, 128), bool)
+    for t in range(nb):
+        mask[t, enc["kocol"][t]] = True
+    for blk in range(nb // 32):
+        for c in range(128):
+            rows = slice(blk * 32, blk * 32 + 32)
+            members = k16[rows, c][~mask[rows, c]]
+            z = float(np.uint16(enc["kmeta"][blk, c, 1]).view(np.float16))
+            if members.size:
+                assert z == members.min()
+            else:
+                assert enc["kmeta"][blk, c].tolist() == [0, 0]
+
+
+def test_average_bits_objective():
+    with open(os.path.join(GOLDEN, "average_bits.json")) as f:
+        for c in json.load(f)["cases"]:
+            pairs = [W.PAIR_SET[i] for i in c["pair_index"]]
+            fm = sum(kb + vb for kb, vb in pairs) / (2 * len(pairs))
+            assert fm == c["f_m"], c["name"]
