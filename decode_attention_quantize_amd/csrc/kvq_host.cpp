@@ -1,0 +1,382 @@
+// kvq_host.cpp -- the C ABI: validation, buffer sizing, the sink / body /
+// window token accounting of each layer, and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+hipError_t launch_decode_generic(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
+hipError_t launch_decode_fast(const LayerDesc& L, const DecodeJob& job, hipStream_t s, bool* used);
+}  // namespace kvq
+
+using kvq::LayerDesc;
+
+namespace {
+
+constexpr int kD = kvq::kHeadDim;
+constexpr int kMaxSplits = 256;
+
+struct Layer {
+  LayerDesc d{};
+  bool bound = false;
+  bool filled = false;  // prefilled at least once since binding
+  int32_t n = 0, s_eff = 0, nb = 0, r = 0;
+};
+
+int32_t align_up(int64_t x, int64_t a) { return static_cast<int32_t>((x + a - 1) / a * a); }
+
+bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1)) == 0; }
+
+}  // namespace
+
+struct kvq_cache {
+  kvq_config cfg{};
+  int32_t G = 1, units = 1, F = 32, win_cap = 0, nblk_cap = 0;
+  std::vector<Layer> layers;
+};
+
+namespace {
+
+kvq_status fill_layout(const kvq_cache& c, int kb, int vb, const uint16_t* cb, LayerDesc& d) {
+  const kvq_config& g = c.cfg;
+  d = LayerDesc{};
+  d.B = g.batch;
+  d.Hq = g.n_q_heads;
+  d.Hkv = g.n_kv_heads;
+  d.G = c.G;
+  d.units = c.units;
+  d.kb = kb;
+  d.vb = vb;
+  d.k_inner = g.k_mode == KVQ_K_INNER;
+  d.k_group = g.k_group;
+  d.v_group = g.v_group;
+  d.k_hybrid = g.k_hybrid != 0;
+  d.ratio_num = g.sym_ratio_num;
+  d.ratio_den = g.sym_ratio_den;
+  d.nuq = g.nuq != 0;
+  d.outk = g.outliers_per_vector;
+  d.v_had = g.v_mode == KVQ_V_HADAMARD;
+  d.pre_rope = g.k_pre_rope != 0;
+  d.rope_base = g.rope_base;
+  if (cb) {
+    std::memcpy(d.lev_k, cb, 16);
+    std::memcpy(d.lev_v, cb + 8, 16);
+  }
+  d.had_scale = 1.0 / std::sqrt(static_cast<double>(kD));
+  d.k_row_bytes = kD * kb / 8;
+  int64_t off = 0;
+  d.off_kc = 0;
+  off = align_up(off + static_cast<int64_t>(kvq::kBlockTokens) * d.k_row_bytes, 16);
+  d.off_km = static_cast<int32_t>(off);
+  off = align_up(off + (d.k_inner ? kvq::kBlockTokens * (kD / d.k_group) * 4 : 2 * kD * 2), 16);
+  d.off_vc = static_cast<int32_t>(off);
+  off = align_up(off + kvq::kBlockTokens * kD * vb / 8, 16);
+  d.off_vm = static_cast<int32_t>(off);
+  off = align_up(off + 2 * (kD / d.v_group) * kvq::kBlockTokens * 2, 16);
+  d.off_ko = static_cast<int32_t>(off);
+  off = align_up(off + kvq::kBlockTokens * d.outk * 4, 16);
+  d.off_vo = static_cast<int32_t>(off);
+  off = align_up(off + kvq::kBlockTokens * d.outk * 4, 16);
+  d.rec_bytes = align_up(off, 128);
+  d.nblk_cap = c.nblk_cap;
+  d.sinks_cap = g.sink_tokens;
+  d.win_cap = c.win_cap;
+  return KVQ_OK;
+}
+
+bool valid_layer(const kvq_cache* c, int32_t layer) {
+  return c && layer >= 0 && layer < static_cast<int32_t>(c->layers.size());
+}
+
+int nsplit_for(const kvq_cache& c, int nblk, int* bps) {
+  if (nblk <= 0) {
+    *bps = 1;
+    return 0;
+  }
+  // aim for about 2048 workgroups in flight, at least 4 blocks per split
+  int want = std::max(1, 2048 / std::max(1, c.units));
+  want = std::min({want, kMaxSplits, std::max(1, nblk / 4)});
+  *bps = (nblk + want - 1) / want;
+  return (nblk + *bps - 1) / *bps;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_status_str(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_ARG: return "invalid argument";
+    case KVQ_ERR_CAPACITY: return "capacity exceeded";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_STATE: return "invalid call order";
+    case KVQ_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, const uint16_t* codebooks,
+                      kvq_cache** out) {
+  if (!cfg || !layer_bits || !out) return KVQ_ERR_ARG;
+  *out = nullptr;
+  const kvq_config& g = *cfg;
+  if (g.batch < 1 || g.n_kv_heads < 1 || g.n_q_heads < 1 || g.n_layers < 1 || g.max_tokens < 1 ||
+      g.sink_tokens < 0 || g.recent_window < 0 || g.head_dim < 1)
+    return KVQ_ERR_ARG;
+  if (g.n_q_heads % g.n_kv_heads) return KVQ_ERR_ARG;
+  if (g.max_tokens > (1 << 24) || g.sink_tokens > g.max_tokens || g.recent_window > (1 << 20))
+    return KVQ_ERR_ARG;
+  if (g.k_mode != KVQ_K_PER_CHANNEL && g.k_mode != KVQ_K_INNER) return KVQ_ERR_ARG;
+  if (g.v_mode != KVQ_V_PER_TOKEN && g.v_mode != KVQ_V_HADAMARD) return KVQ_ERR_ARG;
+  if (g.outliers_per_vector < 0 || g.outliers_per_vector > kvq::kMaxOutliers) return KVQ_ERR_ARG;
+  if (g.k_hybrid && (g.sym_ratio_num < 0 || g.sym_ratio_den <= 0)) return KVQ_ERR_ARG;
+  if (g.k_pre_rope && !(g.rope_base > 0.f)) return KVQ_ERR_ARG;
+  if (g.nuq && !codebooks) return KVQ_ERR_ARG;
+  const int G = g.n_q_heads / g.n_kv_heads;
+  if (g.head_dim != kD) return KVQ_ERR_UNSUPPORTED;
+  if (!pow2_in(G, 1, kvq::kMaxGroupRows)) return KVQ_ERR_UNSUPPORTED;
+  if (g.k_mode == KVQ_K_PER_CHANNEL && g.k_group != kvq::kBlockTokens) return KVQ_ERR_UNSUPPORTED;
+  if (g.k_mode == KVQ_K_INNER && !pow2_in(g.k_group, 16, 64)) return KVQ_ERR_UNSUPPORTED;
+  if (!pow2_in(g.v_group, 16, 64)) return KVQ_ERR_UNSUPPORTED;
+  if (g.nuq && g.k_hybrid) return KVQ_ERR_UNSUPPORTED;
+  for (int l = 0; l < g.n_layers; ++l) {
+    const int kb = layer_bits[l].k_bits, vb = layer_bits[l].v_bits;
+    if (g.nuq) {
+      if (kb != 3 || vb != 3) return KVQ_ERR_UNSUPPORTED;
+      for (int t = 0; t < 2; ++t) {
+        const uint16_t* lv = codebooks + (l * 2 + t) * 8;
+        for (int i = 0; i < 8; ++i)
+          if ((lv[i] & 0x7c00) == 0x7c00) return KVQ_ERR_ARG;  // inf / NaN level
+      }
+    } else {
+      auto ok = [](int b) { return b == 2 || b == 3 || b == 4 || b == 8; };
+      if (!ok(kb) || !ok(vb)) return KVQ_ERR_UNSUPPORTED;
+    }
+    if (g.k_hybrid && kb < 2) return KVQ_ERR_UNSUPPORTED;
+  }
+  kvq_cache* c = new (std::nothrow) kvq_cache();
+  if (!c) return KVQ_ERR_ARG;
+  c->cfg = g;
+  c->G = G;
+  c->units = g.batch * g.n_kv_heads;
+  c->F = g.k_mode == KVQ_K_PER_CHANNEL ? kvq::kBlockTokens : 1;
+  c->win_cap = (g.recent_window + c->F + c->F - 1) / c->F * c->F;
+  c->nblk_cap = (g.max_tokens + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
+  c->layers.resize(g.n_layers);
+  for (int l = 0; l < g.n_layers; ++l)
+    fill_layout(*c, layer_bits[l].k_bits, layer_bits[l].v_bits,
+                g.nuq ? codebooks + l * 16 : nullptr, c->layers[l].d);
+  *out = c;
+  return KVQ_OK;
+}
+
+kvq_status kvq_destroy(kvq_cache* c) {
+  delete c;
+  return KVQ_OK;
+}
+
+kvq_status kvq_layer_buffer_sizes(const kvq_cache* c, int32_t layer, size_t sizes[KVQ_NBUF]) {
+  if (!valid_layer(c, layer) || !sizes) return KVQ_ERR_ARG;
+  const LayerDesc& d = c->layers[layer].d;
+  sizes[KVQ_BUF_BODY] = static_cast<size_t>(c->units) * c->nblk_cap * d.rec_bytes;
+  sizes[KVQ_BUF_FP16] =
+      static_cast<size_t>(c->units) * 2 * (c->cfg.sink_tokens + c->win_cap) * kD * sizeof(uint16_t);
+  return KVQ_OK;
+}
+
+kvq_status kvq_block_layout(const kvq_cache* c, int32_t layer, kvq_block_layout_t* o) {
+  if (!valid_layer(c, layer) || !o) return KVQ_ERR_ARG;
+  const LayerDesc& d = c->layers[layer].d;
+  o->record_bytes = d.rec_bytes;
+  o->k_codes = d.off_kc;
+  o->k_meta = d.off_km;
+  o->v_codes = d.off_vc;
+  o->v_meta = d.off_vm;
+  o->k_out = d.off_ko;
+  o->v_out = d.off_vo;
+  o->k_row_bytes = d.k_row_bytes;
+  o->window_cap = c->win_cap;
+  o->flush_tokens = c->F;
+  return KVQ_OK;
+}
+
+kvq_status kvq_bind_layer(kvq_cache* c, int32_t layer, void* const bufs[KVQ_NBUF]) {
+  if (!valid_layer(c, layer) || !bufs) return KVQ_ERR_ARG;
+  for (int i = 0; i < KVQ_NBUF; ++i)
+    if (!bufs[i] || (reinterpret_cast<uintptr_t>(bufs[i]) & 255)) return KVQ_ERR_ARG;
+  Layer& L = c->layers[layer];
+  L.d.body = static_cast<uint8_t*>(bufs[KVQ_BUF_BODY]);
+  L.d.fp16 = static_cast<uint16_t*>(bufs[KVQ_BUF_FP16]);
+  L.bound = true;
+  L.filled = false;
+  L.n = L.s_eff = L.nb = L.r = 0;
+  return KVQ_OK;
+}
+
+kvq_status kvq_workspace_size(const kvq_cache* c, size_t* bytes) {
+  if (!c || !bytes) return KVQ_ERR_ARG;
+  const size_t parts = static_cast<size_t>(c->units) * (std::min(kMaxSplits, c->nblk_cap) + 1) *
+                       c->G * (kD + 2) * sizeof(float);
+  *bytes = (parts + 255) / 256 * 256 + static_cast<size_t>(c->units) * sizeof(uint32_t);
+  return KVQ_OK;
+}
+
+kvq_status kvq_layer_state(const kvq_cache* c, int32_t layer, int32_t* n, int32_t* sinks,
+                           int32_t* body, int32_t* window) {
+  if (!valid_layer(c, layer)) return KVQ_ERR_ARG;
+  const Layer& L = c->layers[layer];
+  if (n) *n = L.n;
+  if (sinks) *sinks = L.s_eff;
+  if (body) *body = L.nb;
+  if (window) *window = L.r;
+  return KVQ_OK;
+}
+
+kvq_status kvq_quantize_prefill(kvq_cache* c, int32_t layer, const void* k, const void* v, int32_t T,
+                                void* /*workspace*/, void* stream) {
+  if (!valid_layer(c, layer) || T < 0) return KVQ_ERR_ARG;
+  Layer& L = c->layers[layer];
+  if (!L.bound) return KVQ_ERR_STATE;
+  if (T > 0 && (!k || !v)) return KVQ_ERR_ARG;
+  if (T > c->cfg.max_tokens) return KVQ_ERR_CAPACITY;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int S = c->cfg.sink_tokens, W = c->cfg.recent_window, F = c->F;
+  const int s_eff = std::min(S, T);
+  const int avail = T - s_eff - W;
+  const int nb = avail > 0 ? avail / F * F : 0;
+  const int r = T - s_eff - nb;
+  const auto* ks = static_cast<const uint16_t*>(k);
+  const auto* vs = static_cast<const uint16_t*>(v);
+  if (nb > 0) {
+    kvq::QuantJob j{};
+    j.k_src = ks;
+    j.v_src = vs;
+    j.src_unit_stride = static_cast<int64_t>(T) * kD;
+    j.src_t0 = s_eff;
+    j.blk0 = 0;
+    j.nblocks = (nb + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
+    j.tok0 = 0;
+    j.cnt = kvq::kBlockTokens;
+    j.last_cnt = nb - kvq::kBlockTokens * (j.nblocks - 1);
+    j.rotate_v = L.d.v_had;
+    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  }
+  kvq::CopyJob cj{};
+  cj.k_src = ks;
+  cj.v_src = vs;
+  cj.src_unit_stride = static_cast<int64_t>(T) * kD;
+  cj.s_eff = s_eff;
+  cj.rotate_v = L.d.v_had;
+  if (s_eff > 0) {
+    cj.src_t0 = 0;
+    cj.count = s_eff;
+    cj.pos0 = 0;
+    if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  }
+  if (r > 0) {
+    cj.src_t0 = s_eff + nb;
+    cj.count = r;
+    cj.pos0 = s_eff + nb;
+    if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  }
+  L.filled = true;
+  L.n = T;
+  L.s_eff = s_eff;
+  L.nb = nb;
+  L.r = r;
+  return KVQ_OK;
+}
+
+kvq_status kvq_append_token(kvq_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                            void* stream) {
+  if (!valid_layer(c, layer) || !k_new || !v_new) return KVQ_ERR_ARG;
+  Layer& L = c->layers[layer];
+  if (!L.bound || !L.filled) return KVQ_ERR_STATE;
+  if (L.n + 1 > c->cfg.max_tokens) return KVQ_ERR_CAPACITY;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int W = c->cfg.recent_window, F = c->F;
+  const auto* ks = static_cast<const uint16_t*>(k_new);
+  const auto* vs = static_cast<const uint16_t*>(v_new);
+  if (F == 1 && W == 0) {
+    // every token goes straight into the body
+    kvq::QuantJob j{};
+    j.k_src = ks;
+    j.v_src = vs;
+    j.src_unit_stride = kD;
+    j.src_t0 = 0;
+    j.blk0 = L.nb / kvq::kBlockTokens;
+    j.nblocks = 1;
+    j.tok0 = L.nb % kvq::kBlockTokens;
+    j.cnt = j.last_cnt = 1;
+    j.rotate_v = L.d.v_had;
+    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    L.nb += 1;
+    L.n += 1;
+    return KVQ_OK;
+  }
+  kvq::CopyJob cj{};
+  cj.k_src = ks;
+  cj.v_src = vs;
+  cj.src_unit_stride = kD;
+  cj.src_t0 = 0;
+  cj.count = 1;
+  cj.pos0 = L.n;
+  cj.s_eff = L.s_eff;
+  cj.rotate_v = L.d.v_had;
+  if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  int nb = L.nb, r = L.r + 1;
+  if (r == W + F) {
+    // flush the oldest F window tokens (contiguous ring slots) into the body
+    const int slots = c->cfg.sink_tokens + c->win_cap;
+    kvq::QuantJob j{};
+    j.k_src = L.d.fp16 + static_cast<int64_t>(c->cfg.sink_tokens) * kD;
+    j.v_src = j.k_src + static_cast<int64_t>(slots) * kD;
+    j.src_unit_stride = static_cast<int64_t>(2) * slots * kD;
+    j.src_t0 = nb % c->win_cap;
+    j.blk0 = nb / kvq::kBlockTokens;
+    j.nblocks = 1;
+    j.tok0 = nb % kvq::kBlockTokens;
+    j.cnt = j.last_cnt = F;
+    j.rotate_v = 0;  // ring values are stored rotated already
+    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    nb += F;
+    r -= F;
+  }
+  L.nb = nb;
+  L.r = r;
+  L.n += 1;
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* out, void* workspace,
+                           void* stream) {
+  if (!valid_layer(c, layer) || !q || !out || !workspace) return KVQ_ERR_ARG;
+  Layer& L = c->layers[layer];
+  if (!L.bound || !L.filled || L.n == 0) return KVQ_ERR_STATE;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  kvq::DecodeJob j{};
+  j.q = static_cast<const uint16_t*>(q);
+  j.out = out;
+  j.partials = static_cast<float*>(workspace);
+  const size_t parts = static_cast<size_t>(c->units) * (std::min(kMaxSplits, c->nblk_cap) + 1) *
+                       c->G * (kD + 2) * sizeof(float);
+  j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + (parts + 255) / 256 * 256);
+  j.st = kvq::TokenState{L.n, L.s_eff, L.nb, L.r};
+  const int nblk = (L.nb + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
+  j.nsplit_body = nsplit_for(*c, nblk, &j.blocks_per_split);
+  j.fp16_split = (L.s_eff + L.r) > 0 ? 1 : 0;
+  bool used = false;
+  hipError_t e = kvq::launch_decode_fast(L.d, j, s, &used);
+  if (!used) e = kvq::launch_decode_generic(L.d, j, s);
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// kvq_internal.h -- descriptors shared by the host entry points and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace kvq {
+
+constexpr int kBlockTokens = 32;  // tokens per body block (= per-channel key group)
+constexpr int kHeadDim = 128;
+constexpr int kMaxGroupRows = 16;  // query heads per kv head
+constexpr int kMaxOutliers = 8;
+
+// Everything a kernel needs to read or write one layer, passed by value.
+struct LayerDesc {
+  // shapes
+  int32_t B, Hq, Hkv, G;  // G = Hq / Hkv
+  int32_t units;          // B * Hkv
+  // scheme
+  int32_t kb, vb;
+  int32_t k_inner, k_group, v_group;
+  int32_t k_hybrid, ratio_num, ratio_den;
+  int32_t nuq, outk, v_had, pre_rope;
+  float rope_base;
+  uint16_t lev_k[8], lev_v[8];
+  double had_scale;  // fl64(1/sqrt(D)), computed on the host
+  // record layout
+  int32_t rec_bytes, k_row_bytes;
+  int32_t off_kc, off_km, off_vc, off_vm, off_ko, off_vo;
+  int32_t nblk_cap;  // blocks per unit
+  // fp16 area
+  int32_t sinks_cap, win_cap;  // slots per unit: S, Wcap
+  // buffers
+  uint8_t* body;     // [units][nblk_cap][rec_bytes]
+  uint16_t* fp16;    // [units][2][sinks_cap + win_cap][D]
+};
+
+// Token state of a layer at a decode call.
+struct TokenState {
+  int32_t n, s_eff, nb, r;
+};
+
+// ---------------------------------------------------------------- launchers
+// Quantize tokens into body blocks.  For each unit u and each of nblocks
+// blocks: block index blk0 + i, slots [tok0, tok0 + cnt) (cnt tokens, all in
+// the same block when nblocks == 1, else cnt == 32 for every block but the
+// last, which holds last_cnt).  Source token j of block i of unit u is at
+// src + u * src_unit_stride + (src_t0 + 32*i + j) * D (fp16 elements); the
+// value source is rotated first when rotate_v.
+struct QuantJob {
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t src_unit_stride;  // elements
+  int32_t src_t0;
+  int32_t blk0, nblocks, tok0, cnt, last_cnt;
+  int32_t rotate_v;
+};
+hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t s);
+
+// Copy fp16 tokens into the sink/window area: for each unit, tokens
+// [src_t0, src_t0 + count) of the source go to slots slot_of(t) where sink
+// positions p < s_eff use slot p and window positions use
+// sinks_cap + ((p - s_eff) mod win_cap); positions are src_pos0 + j.
+struct CopyJob {
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t src_unit_stride;
+  int32_t src_t0, count, pos0, s_eff;
+  int32_t rotate_v;
+};
+hipError_t launch_copy_fp16(const LayerDesc& L, const CopyJob& job, hipStream_t s);
+
+// Decode attention.  partials: [units][nsplit_total][G][D + 2] fp32;
+// counters: [units] uint32 (zero on entry, zero on exit).
+struct DecodeJob {
+  const uint16_t* q;  // [B][Hq][D]
+  float* out;         // [B][Hq][D]
+  float* partials;
+  uint32_t* counters;
+  TokenState st;
+  int32_t nsplit_body;    // splits over body blocks
+  int32_t blocks_per_split;
+  int32_t fp16_split;     // 1 when sinks/window tokens exist (one extra split)
+};
+hipError_t launch_decode(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
+
+}  // namespace kvq

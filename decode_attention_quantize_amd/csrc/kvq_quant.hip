@@ -1,0 +1,449 @@
+// kvq_quant.hip -- quantize/pack kernels (prefill blocks, window flushes,
+// per-token appends) and the fp16 sink/window copy.
+//
+// Arithmetic per group (no contraction, IEEE division, round-half-even):
+//   asymmetric (KVTuner review obs. 2; RateQuant sec. 3; InnerQ method 2):
+//     s = fp16(fp32(max-min)/Q), z = min, code = clamp(rne(fp32(x-z)/s), 0, Q)
+//   symmetric (InnerQ method 2): s = fp16(fp32(max|x|)/(2^(b-1)-1)),
+//     code = clamp(rne(x/s), -Qs, Qs) + 2^(b-1), sign bit of s set
+//   hybrid choice: symmetric iff den*|sum x| <= num*g*(max-min), on exact
+//     int64 sums of fp16 values in units of 2^-24
+//   codebook (KVQuant iii): s = fp16(max-min), z = min, code = number of level
+//     midpoints strictly below fp32(x-z)/s
+//   sparse outliers (KVQuant iv): top-k |x| of each token row, lower column
+//     first on ties, excluded from the group statistics
+//   Hadamard values (aitrends.kr page): v' = fp16(fl64(H v) * 1/sqrt(D)) with
+//     exact binary64 butterflies
+#include <hip/hip_runtime.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+constexpr int D = kHeadDim;
+
+// 48 KiB: the fp64 Hadamard rows are dead before codes and masks are written.
+struct QuantSmem {
+  uint16_t k[kBlockTokens][D];
+  uint16_t v[kBlockTokens][D];
+  union {
+    double had[kBlockTokens][D];
+    struct {
+      uint8_t ck[kBlockTokens][D];
+      uint8_t cv[kBlockTokens][D];
+      uint8_t exk[kBlockTokens][D];
+      uint8_t exv[kBlockTokens][D];
+    };
+  };
+};
+
+__device__ __forceinline__ void asym_params(float mn, float mx, bool any, int Q, uint16_t& s,
+                                            uint16_t& z) {
+  if (!any) {
+    s = 0;
+    z = 0;
+    return;
+  }
+  const float range = __fsub_rn(mx, mn);
+  s = f2h(__fdiv_rn(range, static_cast<float>(Q)));
+  if (mx > mn && s == 0) s = 1;
+  z = f2h(mn);
+}
+
+__device__ __forceinline__ int asym_code(float x, float mn, uint16_t s, int Q) {
+  if (s == 0) return 0;
+  const float t = __fdiv_rn(__fsub_rn(x, mn), h2f(s));
+  const float r = fminf(fmaxf(rintf(t), 0.f), static_cast<float>(Q));
+  return static_cast<int>(r);
+}
+
+__device__ __forceinline__ uint16_t sym_scale(float a, int bits) {
+  const int Qs = (1 << (bits - 1)) - 1;
+  uint16_t s = f2h(__fdiv_rn(a, static_cast<float>(Qs)));
+  if (a > 0.f && s == 0) s = 1;
+  return s;
+}
+
+__device__ __forceinline__ int sym_code(float x, uint16_t s, int bits) {
+  if (s == 0) return 0;
+  const int Qs = (1 << (bits - 1)) - 1;
+  const float r = fminf(fmaxf(rintf(__fdiv_rn(x, h2f(s))), static_cast<float>(-Qs)),
+                        static_cast<float>(Qs));
+  return static_cast<int>(r) + (1 << (bits - 1));
+}
+
+__device__ __forceinline__ void nuq_params(float mn, float mx, bool any, uint16_t& s, uint16_t& z) {
+  if (!any) {
+    s = 0;
+    z = 0;
+    return;
+  }
+  s = f2h(__fsub_rn(mx, mn));
+  if (s == 0x7c00) s = 0x7bff;
+  if (mx > mn && s == 0) s = 1;
+  z = f2h(mn);
+}
+
+__device__ __forceinline__ int nuq_code(float x, float mn, uint16_t s, const uint16_t* lev) {
+  if (s == 0) return 0;
+  const float u = __fdiv_rn(__fsub_rn(x, mn), h2f(s));
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const float mid = __fmul_rn(__fadd_rn(h2f(lev[j]), h2f(lev[j + 1])), 0.5f);
+    c += u > mid ? 1 : 0;
+  }
+  return c;
+}
+
+// Exact fp64 fast Walsh-Hadamard transform of `rows` rows held in had[][],
+// then v' = fp16(fl64(S * c)).  All 128 threads cooperate.
+__device__ void hadamard_rows(QuantSmem& sm, uint16_t (*vrows)[D], int rows, double c) {
+  const int t = threadIdx.x;
+  for (int j = 0; j < rows; ++j) sm.had[j][t] = static_cast<double>(h2f(vrows[j][t]));
+  __syncthreads();
+  for (int h = 1; h < D; h <<= 1) {
+    // rows*D/2 butterflies, 128 threads
+    for (int i = t; i < rows * (D / 2); i += blockDim.x) {
+      const int j = i / (D / 2);
+      const int p = i % (D / 2);
+      const int lo = ((p / h) * 2 * h) + (p % h);
+      const double a = sm.had[j][lo];
+      const double b = sm.had[j][lo + h];
+      sm.had[j][lo] = a + b;
+      sm.had[j][lo + h] = a - b;
+    }
+    __syncthreads();
+  }
+  for (int j = 0; j < rows; ++j) vrows[j][t] = d2h(sm.had[j][t] * c);
+  __syncthreads();
+}
+
+// top-k columns of each row by |x|, lower column first on equal magnitude.
+__device__ void mark_outliers(const uint16_t (*rows)[D], uint8_t (*ex)[D], int nrows, int k,
+                              uint8_t* out_base, int slot0) {
+  const int t = threadIdx.x;
+  for (int j = 0; j < nrows; ++j) ex[j][t] = 0;
+  __syncthreads();
+  if (t < nrows) {
+    int chosen[kMaxOutliers];
+    for (int i = 0; i < k; ++i) {
+      int best = -1;
+      uint16_t bm = 0;
+      for (int c = 0; c < D; ++c) {
+        if (ex[t][c]) continue;
+        const uint16_t m = rows[t][c] & 0x7fff;
+        if (best < 0 || m > bm) {
+          best = c;
+          bm = m;
+        }
+      }
+      ex[t][best] = 1;
+      chosen[i] = best;
+    }
+    // ascending column order
+    for (int a = 1; a < k; ++a)
+      for (int b = a; b > 0 && chosen[b] < chosen[b - 1]; --b) {
+        const int tmp = chosen[b];
+        chosen[b] = chosen[b - 1];
+        chosen[b - 1] = tmp;
+      }
+    uint32_t* rec = reinterpret_cast<uint32_t*>(out_base) + (slot0 + t) * k;
+    for (int i = 0; i < k; ++i)
+      rec[i] = static_cast<uint32_t>(chosen[i]) | (static_cast<uint32_t>(rows[t][chosen[i]]) << 16);
+  }
+  __syncthreads();
+}
+
+// Quantize one token's per-token group (v_group or inner key group) with the
+// lanes of the group cooperating through xor shuffles.
+template <int W>
+__device__ __forceinline__ void token_group(uint16_t xh, bool excluded, int bits, bool nuq,
+                                            const uint16_t* lev, bool hybrid, int rnum, int rden,
+                                            int& code, uint16_t& s, uint16_t& z) {
+  const float x = h2f(xh);
+  float mn = excluded ? __int_as_float(0x7f800000) : x;
+  float mx = excluded ? __int_as_float(0xff800000) : x;
+  group_minmax<W>(mn, mx);
+  const bool any = mn <= mx;
+  bool sym = false;
+  if (hybrid) {
+    const int64_t fx = h2fixed(xh);
+    const int64_t sum = group_sum64<W>(fx);
+    int64_t fmn = fx, fmx = fx;
+    // exact integer extremes
+    {
+      float a = x, b = x;
+      group_minmax<W>(a, b);
+      fmn = h2fixed(f2h(a));
+      fmx = h2fixed(f2h(b));
+    }
+    const int64_t lhs = static_cast<int64_t>(rden) * (sum < 0 ? -sum : sum);
+    const int64_t rhs = static_cast<int64_t>(rnum) * W * (fmx - fmn);
+    sym = lhs <= rhs;
+  }
+  if (sym) {
+    const float a = group_max<W>(fabsf(x));
+    const uint16_t sv = sym_scale(a, bits);
+    code = sym_code(x, sv, bits);
+    s = sv | 0x8000;
+    z = 0;
+  } else if (nuq) {
+    nuq_params(mn, mx, any, s, z);
+    code = nuq_code(x, mn, s, lev);
+  } else {
+    asym_params(mn, mx, any, (1 << bits) - 1, s, z);
+    code = asym_code(x, mn, s, (1 << bits) - 1);
+  }
+}
+
+template <int W>
+__device__ void quant_token_groups(const uint16_t (*rows)[D], const uint8_t (*ex)[D],
+                                   uint8_t (*codes)[D], int nrows, int bits, bool nuq,
+                                   const uint16_t* lev, bool hybrid, int rnum, int rden,
+                                   uint8_t* meta_base, int meta_kind, int slot0) {
+  // meta_kind 0: inner keys [32][D/W] (s,z) pairs; 1: values s[D/W][32], z[D/W][32]
+  const int t = threadIdx.x;
+  const int g = t / W;
+  const int ng = D / W;
+  uint16_t* m16 = reinterpret_cast<uint16_t*>(meta_base);
+  for (int j = 0; j < nrows; ++j) {
+    int code;
+    uint16_t s, z;
+    token_group<W>(rows[j][t], ex ? ex[j][t] != 0 : false, bits, nuq, lev, hybrid, rnum, rden,
+                   code, s, z);
+    codes[j][t] = static_cast<uint8_t>(code);
+    if ((t % W) == 0) {
+      const int slot = slot0 + j;
+      if (meta_kind == 0) {
+        m16[(slot * ng + g) * 2 + 0] = s;
+        m16[(slot * ng + g) * 2 + 1] = z;
+      } else {
+        m16[g * kBlockTokens + slot] = s;
+        m16[ng * kBlockTokens + g * kBlockTokens + slot] = z;
+      }
+    }
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void quant_token_groups_dispatch(int w, const uint16_t (*rows)[D],
+                                                            const uint8_t (*ex)[D],
+                                                            uint8_t (*codes)[D], int nrows,
+                                                            int bits, bool nuq,
+                                                            const uint16_t* lev, bool hybrid,
+                                                            int rnum, int rden, uint8_t* meta,
+                                                            int kind, int slot0) {
+  quant_token_groups<W>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta, kind,
+                        slot0);
+}
+
+__device__ void quant_groups_any(int w, const uint16_t (*rows)[D], const uint8_t (*ex)[D],
+                                 uint8_t (*codes)[D], int nrows, int bits, bool nuq,
+                                 const uint16_t* lev, bool hybrid, int rnum, int rden,
+                                 uint8_t* meta, int kind, int slot0) {
+  switch (w) {
+    case 16:
+      quant_token_groups<16>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta,
+                             kind, slot0);
+      break;
+    case 32:
+      quant_token_groups<32>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta,
+                             kind, slot0);
+      break;
+    default:
+      quant_token_groups<64>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta,
+                             kind, slot0);
+      break;
+  }
+}
+
+// Pack token-major rows (keys, 3-bit values) for slots [slot0, slot0+nrows).
+__device__ void pack_rows(const uint8_t (*codes)[D], int nrows, int bits, uint8_t* dst, int row_bytes,
+                          int slot0) {
+  const int wpr = row_bytes / 4;
+  for (int i = threadIdx.x; i < nrows * wpr; i += blockDim.x) {
+    const int j = i / wpr;
+    const int w = i % wpr;
+    uint32_t word = 0;
+    if (bits == 8) {
+      for (int e = 0; e < 4; ++e) word |= static_cast<uint32_t>(codes[j][4 * w + e]) << (8 * e);
+    } else if (bits == 3) {
+      const int g = w / 3, p = w % 3;
+      for (int e = 0; e < 32; ++e) word |= static_cast<uint32_t>((codes[j][32 * g + e] >> p) & 1) << e;
+    } else {
+      const int n = 32 / bits;
+      for (int e = 0; e < n; ++e)
+        word |= static_cast<uint32_t>(codes[j][n * w + e]) << pair_split_pos(bits, e);
+    }
+    reinterpret_cast<uint32_t*>(dst + (slot0 + j) * row_bytes)[w] = word;
+  }
+}
+
+// Pack values into the lane-chunk layout.  A fresh block (slot0 == 0) is
+// written whole (slots >= nrows get code 0); otherwise only the bits of slots
+// [slot0, slot0+nrows) are replaced.
+__device__ void pack_vchunks(const uint8_t (*codes)[D], int nrows, int bits, uint8_t* dst,
+                             int slot0) {
+  const int words = 64 * 2 * bits;
+  const int n = bits == 8 ? 4 : 32 / bits;
+  const uint32_t fmask = (1u << bits) - 1;
+  for (int i = threadIdx.x; i < words; i += blockDim.x) {
+    const int lane = i / (2 * bits);
+    const int wi = i % (2 * bits);
+    uint32_t word = 0, keep = 0xffffffffu;
+    for (int e = 0; e < n; ++e) {
+      const int idx = wi * n + e;
+      const int j = 8 * (lane >> 4) + (idx & 7);  // token slot
+      const int c = 16 * (idx >> 3) + (lane & 15);
+      const int pos = bits == 8 ? 8 * e : pair_split_pos(bits, e);
+      if (j >= slot0 && j < slot0 + nrows) {
+        word |= static_cast<uint32_t>(codes[j - slot0][c]) << pos;
+        keep &= ~(fmask << pos);
+      }
+    }
+    uint32_t* wp = reinterpret_cast<uint32_t*>(dst) + i;
+    if (slot0 == 0)
+      *wp = word;
+    else if (keep != 0xffffffffu)
+      *wp = (*wp & keep) | word;
+  }
+}
+
+__global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  QuantSmem& sm = *reinterpret_cast<QuantSmem*>(smem_raw);
+  const int t = threadIdx.x;
+  const int u = blockIdx.y;
+  const int bi = blockIdx.x;
+  const int blk = J.blk0 + bi;
+  const int nrows = (bi == J.nblocks - 1) ? J.last_cnt : J.cnt;
+  const int slot0 = J.tok0;
+  uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + blk) * L.rec_bytes;
+
+  const int64_t base = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + kBlockTokens * bi) * D;
+  for (int j = 0; j < kBlockTokens; ++j) {
+    sm.k[j][t] = j < nrows ? J.k_src[base + j * D + t] : 0;
+    sm.v[j][t] = j < nrows ? J.v_src[base + j * D + t] : 0;
+  }
+  __syncthreads();
+  if (J.rotate_v) hadamard_rows(sm, sm.v, nrows, L.had_scale);
+
+  const bool out = L.outk > 0;
+  if (out) {
+    mark_outliers(sm.k, sm.exk, nrows, L.outk, rec + L.off_ko, slot0);
+    mark_outliers(sm.v, sm.exv, nrows, L.outk, rec + L.off_vo, slot0);
+  }
+
+  // ---- keys
+  if (!L.k_inner) {
+    // one group per channel over the block's tokens: thread t owns channel t
+    bool any = false;
+    float mn = 0.f, mx = 0.f;
+    for (int j = 0; j < nrows; ++j) {
+      if (out && sm.exk[j][t]) continue;
+      const float x = h2f(sm.k[j][t]);
+      if (!any) {
+        mn = mx = x;
+        any = true;
+      } else {
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+    }
+    uint16_t s, z;
+    bool sym = false;
+    if (L.k_hybrid) {
+      int64_t sum = 0, fmn = 0, fmx = 0;
+      for (int j = 0; j < nrows; ++j) {
+        const int64_t f = h2fixed(sm.k[j][t]);
+        sum += f;
+        if (j == 0 || f < fmn) fmn = f;
+        if (j == 0 || f > fmx) fmx = f;
+      }
+      sym = static_cast<int64_t>(L.ratio_den) * (sum < 0 ? -sum : sum) <=
+            static_cast<int64_t>(L.ratio_num) * nrows * (fmx - fmn);
+    }
+    if (sym) {
+      float a = 0.f;
+      for (int j = 0; j < nrows; ++j) a = fmaxf(a, fabsf(h2f(sm.k[j][t])));
+      const uint16_t sv = sym_scale(a, L.kb);
+      for (int j = 0; j < nrows; ++j) sm.ck[j][t] = static_cast<uint8_t>(sym_code(h2f(sm.k[j][t]), sv, L.kb));
+      s = sv | 0x8000;
+      z = 0;
+    } else if (L.nuq) {
+      nuq_params(mn, mx, any, s, z);
+      for (int j = 0; j < nrows; ++j)
+        sm.ck[j][t] = static_cast<uint8_t>(nuq_code(h2f(sm.k[j][t]), mn, s, L.lev_k));
+    } else {
+      asym_params(mn, mx, any, (1 << L.kb) - 1, s, z);
+      for (int j = 0; j < nrows; ++j)
+        sm.ck[j][t] = static_cast<uint8_t>(asym_code(h2f(sm.k[j][t]), mn, s, (1 << L.kb) - 1));
+    }
+    for (int j = nrows; j < kBlockTokens; ++j) sm.ck[j][t] = 0;
+    uint16_t* km = reinterpret_cast<uint16_t*>(rec + L.off_km);
+    km[t] = s;
+    km[D + t] = z;
+  } else {
+    quant_groups_any(L.k_group, sm.k, out ? sm.exk : nullptr, sm.ck, nrows, L.kb, L.nuq != 0,
+                     L.lev_k, L.k_hybrid != 0, L.ratio_num, L.ratio_den, rec + L.off_km, 0, slot0);
+  }
+  // ---- values: per-token groups
+  quant_groups_any(L.v_group, sm.v, out ? sm.exv : nullptr, sm.cv, nrows, L.vb, L.nuq != 0,
+                   L.lev_v, false, 1, 1, rec + L.off_vm, 1, slot0);
+  __syncthreads();
+
+  pack_rows(sm.ck, nrows, L.kb, rec + L.off_kc, L.k_row_bytes, slot0);
+  if (L.vb == 3)
+    pack_rows(sm.cv, nrows, 3, rec + L.off_vc, 48, slot0);
+  else
+    pack_vchunks(sm.cv, nrows, L.vb, rec + L.off_vc, slot0);
+}
+
+__global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) {
+  extern __shared__ __align__(16) uint8_t smem_raw[];
+  QuantSmem& sm = *reinterpret_cast<QuantSmem*>(smem_raw);
+  const int t = threadIdx.x;
+  const int u = blockIdx.y;
+  const int j0 = blockIdx.x * kBlockTokens;
+  const int rows = min(kBlockTokens, J.count - j0);
+  const int64_t base = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + j0) * D;
+  for (int j = 0; j < rows; ++j) {
+    sm.k[j][t] = J.k_src[base + j * D + t];
+    sm.v[j][t] = J.v_src[base + j * D + t];
+  }
+  __syncthreads();
+  if (J.rotate_v) hadamard_rows(sm, sm.v, rows, L.had_scale);
+  const int slots = L.sinks_cap + L.win_cap;
+  uint16_t* kdst = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
+  uint16_t* vdst = kdst + static_cast<int64_t>(slots) * D;
+  for (int j = 0; j < rows; ++j) {
+    const int p = J.pos0 + j0 + j;
+    const int slot = p < J.s_eff ? p : L.sinks_cap + (p - J.s_eff) % L.win_cap;
+    kdst[slot * D + t] = sm.k[j][t];
+    vdst[slot * D + t] = sm.v[j][t];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t s) {
+  if (job.nblocks <= 0) return hipSuccess;
+  const size_t smem = sizeof(QuantSmem);
+  hipLaunchKernelGGL(quantize_kernel, dim3(job.nblocks, L.units), dim3(128), smem, s, L, job);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_fp16(const LayerDesc& L, const CopyJob& job, hipStream_t s) {
+  if (job.count <= 0) return hipSuccess;
+  const size_t smem = sizeof(QuantSmem);
+  const int grid = (job.count + kBlockTokens - 1) / kBlockTokens;
+  hipLaunchKernelGGL(copy_fp16_kernel, dim3(grid, L.units), dim3(128), smem, s, L, job);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

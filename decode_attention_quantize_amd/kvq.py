@@ -1,0 +1,255 @@
+"""ctypes binding of libkvq.so (include/kvq.h), same entry-point names.
+
+Argument marshalling only: every step of quantization and decode runs in the
+HIP kernels of libkvq.so.  ``KVQCache`` adds torch plumbing (device buffers,
+the current stream) around the raw calls.  There is no fallback: without the
+built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_CAPACITY, KVQ_ERR_UNSUPPORTED, KVQ_ERR_STATE, KVQ_ERR_DEVICE = range(6)
+KVQ_K_PER_CHANNEL, KVQ_K_INNER = 0, 1
+KVQ_V_PER_TOKEN, KVQ_V_HADAMARD = 0, 1
+KVQ_NBUF = 2
+KVQ_BUF_BODY, KVQ_BUF_FP16 = 0, 1
+
+EXPORTS = ("kvq_create", "kvq_destroy", "kvq_layer_buffer_sizes", "kvq_block_layout",
+           "kvq_bind_layer", "kvq_workspace_size", "kvq_quantize_prefill", "kvq_append_token",
+           "kvq_decode_attn", "kvq_layer_state", "kvq_status_str")
+
+
+class kvq_config(C.Structure):
+    _fields_ = [
+        ("batch", C.c_int32), ("n_q_heads", C.c_int32), ("n_kv_heads", C.c_int32),
+        ("head_dim", C.c_int32), ("n_layers", C.c_int32), ("max_tokens", C.c_int32),
+        ("sink_tokens", C.c_int32), ("recent_window", C.c_int32),
+        ("k_mode", C.c_int32), ("k_group", C.c_int32), ("v_mode", C.c_int32), ("v_group", C.c_int32),
+        ("k_hybrid", C.c_int32), ("sym_ratio_num", C.c_int32), ("sym_ratio_den", C.c_int32),
+        ("k_pre_rope", C.c_int32), ("rope_base", C.c_float), ("nuq", C.c_int32),
+        ("outliers_per_vector", C.c_int32),
+    ]
+
+
+class kvq_bitpair(C.Structure):
+    _fields_ = [("k_bits", C.c_uint8), ("v_bits", C.c_uint8)]
+
+
+class kvq_block_layout_t(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in (
+        "record_bytes", "k_codes", "k_meta", "v_codes", "v_meta", "k_out", "v_out",
+        "k_row_bytes", "window_cap", "flush_tokens")]
+
+
+class KVQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    """Load libkvq.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -c 'import __graft_entry__ as g; g.build()'`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, pcache = C.c_void_p, C.c_int32, C.c_void_p
+        L.kvq_status_str.restype = C.c_char_p
+        L.kvq_status_str.argtypes = [C.c_int]
+        L.kvq_create.argtypes = [C.POINTER(kvq_config), C.POINTER(kvq_bitpair), C.POINTER(C.c_uint16),
+                                 C.POINTER(C.c_void_p)]
+        L.kvq_destroy.argtypes = [pcache]
+        L.kvq_layer_buffer_sizes.argtypes = [pcache, i32, C.POINTER(C.c_size_t)]
+        L.kvq_block_layout.argtypes = [pcache, i32, C.POINTER(kvq_block_layout_t)]
+        L.kvq_bind_layer.argtypes = [pcache, i32, C.POINTER(C.c_void_p)]
+        L.kvq_workspace_size.argtypes = [pcache, C.POINTER(C.c_size_t)]
+        L.kvq_quantize_prefill.argtypes = [pcache, i32, vp, vp, i32, vp, vp]
+        L.kvq_append_token.argtypes = [pcache, i32, vp, vp, vp]
+        L.kvq_decode_attn.argtypes = [pcache, i32, vp, vp, vp, vp]
+        L.kvq_layer_state.argtypes = [pcache, i32] + [C.POINTER(C.c_int32)] * 4
+        for name in EXPORTS:
+            if name != "kvq_status_str":
+                getattr(L, name).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_str(status: int) -> str:
+    return lib().kvq_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != KVQ_OK:
+        raise KVQError(status, where)
+
+
+# ---------------------------------------------------------------- raw entry points
+def kvq_create(cfg: kvq_config, layer_bits, codebooks=None) -> int:
+    pairs = (kvq_bitpair * len(layer_bits))(*[kvq_bitpair(kb, vb) for kb, vb in layer_bits])
+    cb = None
+    if codebooks is not None:
+        import numpy as np
+        arr = np.ascontiguousarray(codebooks, dtype=np.uint16).ravel()
+        cb = (C.c_uint16 * arr.size)(*arr.tolist())
+    h = C.c_void_p()
+    _check(lib().kvq_create(C.byref(cfg), pairs, cb, C.byref(h)), "kvq_create")
+    return h.value
+
+
+def kvq_destroy(handle: int):
+    _check(lib().kvq_destroy(handle), "kvq_destroy")
+
+
+def kvq_layer_buffer_sizes(handle: int, layer: int):
+    sizes = (C.c_size_t * KVQ_NBUF)()
+    _check(lib().kvq_layer_buffer_sizes(handle, layer, sizes), "kvq_layer_buffer_sizes")
+    return list(sizes)
+
+
+def kvq_block_layout(handle: int, layer: int) -> dict:
+    o = kvq_block_layout_t()
+    _check(lib().kvq_block_layout(handle, layer, C.byref(o)), "kvq_block_layout")
+    return {n: getattr(o, n) for n, _ in kvq_block_layout_t._fields_}
+
+
+def kvq_bind_layer(handle: int, layer: int, ptrs):
+    arr = (C.c_void_p * KVQ_NBUF)(*ptrs)
+    _check(lib().kvq_bind_layer(handle, layer, arr), "kvq_bind_layer")
+
+
+def kvq_workspace_size(handle: int) -> int:
+    n = C.c_size_t()
+    _check(lib().kvq_workspace_size(handle, C.byref(n)), "kvq_workspace_size")
+    return n.value
+
+
+def kvq_quantize_prefill(handle, layer, k_ptr, v_ptr, T, ws_ptr, stream):
+    _check(lib().kvq_quantize_prefill(handle, layer, k_ptr, v_ptr, T, ws_ptr, stream),
+           "kvq_quantize_prefill")
+
+
+def kvq_append_token(handle, layer, k_ptr, v_ptr, stream):
+    _check(lib().kvq_append_token(handle, layer, k_ptr, v_ptr, stream), "kvq_append_token")
+
+
+def kvq_decode_attn(handle, layer, q_ptr, out_ptr, ws_ptr, stream):
+    _check(lib().kvq_decode_attn(handle, layer, q_ptr, out_ptr, ws_ptr, stream), "kvq_decode_attn")
+
+
+def kvq_layer_state(handle, layer):
+    v = [C.c_int32() for _ in range(4)]
+    _check(lib().kvq_layer_state(handle, layer, *[C.byref(x) for x in v]), "kvq_layer_state")
+    return tuple(x.value for x in v)
+
+
+# ---------------------------------------------------------------- configuration helpers
+def make_config(B, Hq, Hkv, L, max_tokens, D=128, sinks=0, window=0, k_mode=KVQ_K_PER_CHANNEL,
+                k_group=32, v_mode=KVQ_V_PER_TOKEN, v_group=32, k_hybrid=0, sym_ratio=(1, 10),
+                k_pre_rope=0, rope_base=10000.0, nuq=0, outliers=0) -> kvq_config:
+    c = kvq_config()
+    c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim = B, Hq, Hkv, D
+    c.n_layers, c.max_tokens, c.sink_tokens, c.recent_window = L, max_tokens, sinks, window
+    c.k_mode, c.k_group, c.v_mode, c.v_group = k_mode, k_group, v_mode, v_group
+    c.k_hybrid, c.sym_ratio_num, c.sym_ratio_den = k_hybrid, sym_ratio[0], sym_ratio[1]
+    c.k_pre_rope, c.rope_base, c.nuq, c.outliers_per_vector = k_pre_rope, rope_base, nuq, outliers
+    return c
+
+
+def config_from_workload(wl, max_tokens=None) -> kvq_config:
+    from fractions import Fraction
+    f = Fraction(wl.sym_ratio).limit_denominator(1000)
+    return make_config(
+        wl.B, wl.Hq, wl.Hkv, wl.L,
+        max_tokens if max_tokens is not None else wl.T + (wl.steps if wl.append else 0),
+        D=wl.D, sinks=wl.sinks, window=wl.window,
+        k_mode=KVQ_K_PER_CHANNEL if wl.k_mode == "channel" else KVQ_K_INNER, k_group=wl.k_group,
+        v_mode=KVQ_V_HADAMARD if wl.v_hadamard else KVQ_V_PER_TOKEN, v_group=wl.v_group,
+        k_hybrid=int(wl.k_hybrid), sym_ratio=(f.numerator, f.denominator),
+        k_pre_rope=int(wl.pre_rope), rope_base=wl.rope_base, nuq=int(wl.nuq), outliers=wl.outliers)
+
+
+# ---------------------------------------------------------------- torch plumbing
+class KVQCache:
+    """A libkvq cache whose device buffers are torch tensors on one GPU."""
+
+    def __init__(self, cfg: kvq_config, layer_bits, codebooks=None, device="cuda", layers=None):
+        import torch
+        self.torch = torch
+        self.device = torch.device(device)
+        self.cfg = cfg
+        self.handle = kvq_create(cfg, layer_bits, codebooks)
+        self.buffers = {}
+        for l in (range(cfg.n_layers) if layers is None else layers):
+            self.bind(l)
+        ws = kvq_workspace_size(self.handle)
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device=self.device)
+
+    def bind(self, layer):
+        torch = self.torch
+        sizes = kvq_layer_buffer_sizes(self.handle, layer)
+        bufs = [torch.zeros(max(s, 256) + 256, dtype=torch.uint8, device=self.device) for s in sizes]
+        ptrs = []
+        for b in bufs:
+            p = b.data_ptr()
+            ptrs.append(p + (-p) % 256)
+        kvq_bind_layer(self.handle, layer, ptrs)
+        self.buffers[layer] = (bufs, ptrs, sizes)
+
+    def unbind(self, layer):
+        self.buffers.pop(layer, None)
+
+    def layout(self, layer):
+        return kvq_block_layout(self.handle, layer)
+
+    def raw(self, layer, which):
+        """uint8 view of a bound buffer (exact size, aligned)."""
+        bufs, ptrs, sizes = self.buffers[layer]
+        b = bufs[which]
+        off = ptrs[which] - b.data_ptr()
+        return b[off:off + sizes[which]]
+
+    def _stream(self):
+        return self.torch.cuda.current_stream(self.device).cuda_stream
+
+    def prefill(self, layer, k, v):
+        assert k.is_contiguous() and v.is_contiguous() and k.dtype == self.torch.float16
+        T = k.shape[2]
+        kvq_quantize_prefill(self.handle, layer, k.data_ptr(), v.data_ptr(), T,
+                             self.workspace.data_ptr(), self._stream())
+
+    def append(self, layer, k, v):
+        assert k.is_contiguous() and v.is_contiguous() and k.dtype == self.torch.float16
+        kvq_append_token(self.handle, layer, k.data_ptr(), v.data_ptr(), self._stream())
+
+    def decode(self, layer, q, out=None):
+        torch = self.torch
+        assert q.is_contiguous() and q.dtype == torch.float16
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+        kvq_decode_attn(self.handle, layer, q.data_ptr(), out.data_ptr(), self.workspace.data_ptr(),
+                        self._stream())
+        return out
+
+    def state(self, layer):
+        return kvq_layer_state(self.handle, layer)
+
+    def close(self):
+        if self.handle:
+            kvq_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

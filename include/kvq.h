@@ -1,0 +1,196 @@
+/* kvq.h -- packed KV-cache quantization and fused dequantize-attend decode
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The library keeps an LLM key/value cache as packed 2/3/4/8-bit codes with
+ * per-group fp16 parameters, and computes decode attention directly over it.
+ * Three calls make the path, in the order the Hadamard 2-bit values page
+ * (aitrends.kr, "practical advice") says quantized caches must be exercised:
+ * quantize the prompt into the cache, then decode token by token through it.
+ *
+ *   kvq_quantize_prefill  quantize a prompt's keys/values into one layer's cache
+ *   kvq_append_token      add one decoded token (quantizing a flush block when due)
+ *   kvq_decode_attn       attention of one query step over the whole cache
+ *
+ * Schemes (pages as titled):
+ *   keys per channel, asymmetric, groups of 32 tokens  -- KVTuner review,
+ *       observation 2; KVQuant abstract item (i)
+ *   values per token, asymmetric, groups of v_group channels -- RateQuant,
+ *       section 3 (KIVI layout); Hadamard page, KIVI int4 glossary entry
+ *   keys in inner-dimension groups of k_group channels with a per-group
+ *       symmetric/asymmetric choice -- InnerQ, methodology 1 and 2
+ *   pre-RoPE keys with RoPE applied after dequantization -- KVQuant (ii)
+ *   3-bit per-layer non-uniform codebooks -- KVQuant (iii)
+ *   per-vector sparse fp16 outliers (top-k by magnitude) -- KVQuant (iv)
+ *   values rotated by a normalised Hadamard matrix before 2-bit quantization,
+ *       rotation undone after the attention sum -- Hadamard page, TL;DR
+ *   fp16 sink tokens and recent window -- InnerQ, methodology 4
+ *   per-layer (k_bits, v_bits) pair chosen offline from
+ *       {KV8, K8V4, KV4, K4V2, KV2} -- KVTuner review, method steps 1 and 4
+ *
+ * Ownership.  The library allocates no device memory.  The caller sizes the
+ * per-layer buffers with kvq_layer_buffer_sizes(), allocates them (any
+ * allocator, 256-byte aligned), binds them with kvq_bind_layer(), and owns
+ * them.  The handle holds host metadata only (token counts per layer).
+ *
+ * Streams.  Every device call is asynchronous on the caller's HIP stream
+ * (passed as void*; NULL is the null stream).  Calls on one cache must be
+ * stream-ordered; the handle has no internal locking.
+ *
+ * Errors.  Argument, state and capacity checks run on the host before any
+ * launch; a failing call returns its status and leaves host state and device
+ * buffers untouched.  A failed launch returns KVQ_ERR_DEVICE (the host state
+ * of that call is rolled back).  No C++ exception crosses this interface.
+ *
+ * Data types: fp16 = IEEE binary16 bit patterns in uint16 storage.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvq_cache kvq_cache;
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_ERR_ARG = 1,          /* null pointer, out-of-range layer, bad size or config field */
+  KVQ_ERR_CAPACITY = 2,     /* the call would hold more than max_tokens tokens */
+  KVQ_ERR_UNSUPPORTED = 3,  /* valid but not implemented (bit width, head_dim, group) */
+  KVQ_ERR_STATE = 4,        /* wrong call order: unbound layer, append/decode before prefill */
+  KVQ_ERR_DEVICE = 5        /* a HIP runtime call or kernel launch failed */
+} kvq_status;
+
+enum { KVQ_K_PER_CHANNEL = 0, KVQ_K_INNER = 1 };
+enum { KVQ_V_PER_TOKEN = 0, KVQ_V_HADAMARD = 1 };
+
+/* (k_bits, v_bits) of one layer: 2, 3, 4 or 8 each (3 only with nuq). */
+typedef struct {
+  uint8_t k_bits, v_bits;
+} kvq_bitpair;
+
+typedef struct {
+  int32_t batch;          /* B  >= 1 */
+  int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads; Hq/Hkv <= 16 */
+  int32_t n_kv_heads;     /* Hkv >= 1 */
+  int32_t head_dim;       /* D; must be 128 */
+  int32_t n_layers;       /* L >= 1 */
+  int32_t max_tokens;     /* capacity per (layer, batch, kv head) */
+  int32_t sink_tokens;    /* S: first S positions kept fp16 */
+  int32_t recent_window;  /* W: most recent W..W+F-1 positions kept fp16 */
+  int32_t k_mode;         /* KVQ_K_PER_CHANNEL (k_group must be 32) | KVQ_K_INNER */
+  int32_t k_group;        /* tokens per key group (per channel) or channels (inner: 32|64|128) */
+  int32_t v_mode;         /* KVQ_V_PER_TOKEN | KVQ_V_HADAMARD */
+  int32_t v_group;        /* channels per value group: 16, 32 or 64 */
+  int32_t k_hybrid;       /* inner groups: symmetric iff |mean|/range <= num/den */
+  int32_t sym_ratio_num, sym_ratio_den;  /* e.g. 1/10 */
+  int32_t k_pre_rope;     /* keys are stored pre-RoPE; RoPE applied at decode */
+  float rope_base;        /* e.g. 10000 (rotate-half pairs (i, i+D/2)) */
+  int32_t nuq;            /* 1: 3-bit codebook quantizer for keys and values */
+  int32_t outliers_per_vector; /* 0, or k sparse fp16 entries per token row (k <= 8) */
+} kvq_config;
+
+/* Per-layer device buffers (caller-owned). */
+#define KVQ_NBUF 2
+enum {
+  KVQ_BUF_BODY = 0,   /* packed blocks: [B*Hkv][ceil(max_tokens/32)][record] */
+  KVQ_BUF_FP16 = 1    /* fp16 sinks and window ring: [B*Hkv][2 (K,V)][S + Wcap][D] */
+};
+
+/* Byte layout of one body block record (32 consecutive quantized tokens of one
+ * (batch, kv head) unit), as reported by kvq_block_layout().  Every section
+ * starts 16-byte aligned.
+ *
+ *  k_codes  token-major rows of D codes, row_bytes = D*k_bits/8.
+ *           2/4 bits: each 32-bit word holds n = 32/bits consecutive channels
+ *             e_0..e_(n-1) with e_(2j) at bit bits*j and e_(2j+1) at bit
+ *             16 + bits*j ("pair-split" word).
+ *           8 bits: one byte per channel.
+ *           3 bits: per 32 channels three 32-bit bit-planes; bit i of plane p
+ *             is bit p of channel i's code.
+ *  k_meta   per-channel keys: s[D] fp16 then z[D] fp16 (one group per channel
+ *           per block).  Inner keys: [32 tokens][D/k_group] pairs (s, z).
+ *           A set sign bit on s marks a symmetric group: value = (code-2^(b-1))*|s|;
+ *           otherwise value = code*s + z; codebook mode: value = L[code]*s + z.
+ *  v_codes  2/4/8 bits: 64 lane chunks of 8*v_bits bytes; chunk l covers
+ *           tokens 8*(l/16)..+7 and channels 16*t + l%16 (t = 0..7); its
+ *           element sequence is e_(8t+j) = code(token 8*(l/16)+j, channel
+ *           16t + l%16), packed in pair-split words (2/4 bits) or bytes (8).
+ *           3 bits: token-major bit-plane rows as for keys.
+ *  v_meta   s[D/v_group][32 tokens] fp16 then z[D/v_group][32 tokens] fp16.
+ *  k_out,   outliers_per_vector entries per token: {uint16 column, fp16
+ *  v_out    value}, columns ascending; the fp16 value replaces the dequantized
+ *           element.
+ */
+typedef struct {
+  int32_t record_bytes;
+  int32_t k_codes, k_meta, v_codes, v_meta, k_out, v_out;  /* section offsets */
+  int32_t k_row_bytes;
+  int32_t window_cap;     /* Wcap: window ring slots per unit */
+  int32_t flush_tokens;   /* F: 32 for per-channel keys, 1 for inner keys */
+} kvq_block_layout_t;
+
+/* Create a cache handle.  layer_bits[n_layers]; codebooks: NULL or
+ * [n_layers][2 (K,V)][8] fp16 levels sorted ascending (required when nuq).
+ * The inputs are copied.  Errors: KVQ_ERR_ARG, KVQ_ERR_UNSUPPORTED. */
+kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits,
+                      const uint16_t* codebooks, kvq_cache** out);
+
+/* Release the handle (not the caller's buffers). NULL is accepted. */
+kvq_status kvq_destroy(kvq_cache* cache);
+
+/* Bytes needed for each KVQ_BUF_* buffer of a layer. */
+kvq_status kvq_layer_buffer_sizes(const kvq_cache* cache, int32_t layer, size_t sizes[KVQ_NBUF]);
+
+/* Record layout of a layer's body blocks. */
+kvq_status kvq_block_layout(const kvq_cache* cache, int32_t layer, kvq_block_layout_t* out);
+
+/* Attach caller-owned device buffers to a layer (re-binding resets the layer). */
+kvq_status kvq_bind_layer(kvq_cache* cache, int32_t layer, void* const bufs[KVQ_NBUF]);
+
+/* Bytes of device workspace kvq_decode_attn needs.  The workspace must be
+ * zero-filled once before its first use; each decode call leaves its
+ * completion counters at zero again.  One workspace serves one stream. */
+kvq_status kvq_workspace_size(const kvq_cache* cache, size_t* bytes);
+
+/* Quantize a prompt of T tokens into a layer, replacing its contents.
+ * k, v: device fp16 [B][Hkv][T][D] (keys pre-RoPE when k_pre_rope).
+ * Positions [0,S') become fp16 sinks (S' = min(S,T)); then the largest whole
+ * number of flush blocks is quantized; the remaining tokens form the fp16
+ * window.  workspace is unused (may be NULL).
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (unbound), KVQ_ERR_CAPACITY (T > max_tokens). */
+kvq_status kvq_quantize_prefill(kvq_cache* cache, int32_t layer, const void* k, const void* v,
+                                int32_t T, void* workspace, void* stream);
+
+/* Append one token per unit.  k_new, v_new: device fp16 [B][Hkv][D].  The
+ * token enters the fp16 window; when the window reaches W+F tokens its
+ * oldest F tokens are quantized into the next body block (keys and values
+ * together).  With inner keys and W = 0 the token is quantized at once.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (before prefill), KVQ_ERR_CAPACITY. */
+kvq_status kvq_append_token(kvq_cache* cache, int32_t layer, const void* k_new,
+                            const void* v_new, void* stream);
+
+/* Decode attention over every token currently in the layer (append first).
+ * q: device fp16 [B][Hq][D], already position-encoded; q head h reads kv
+ * head h / (Hq/Hkv).  out: device fp32 [B][Hq][D] =
+ * softmax(q.K^T / sqrt(D)) V, with keys/values dequantized (outliers merged,
+ * RoPE applied to pre-RoPE keys, Hadamard rotation undone).
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (empty cache / unbound), KVQ_ERR_DEVICE. */
+kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, float* out,
+                           void* workspace, void* stream);
+
+/* Host-side token accounting of a layer: total tokens n, sink tokens,
+ * quantized body tokens and fp16 window tokens (n = sinks + body + window). */
+kvq_status kvq_layer_state(const kvq_cache* cache, int32_t layer, int32_t* n, int32_t* sinks,
+                           int32_t* body, int32_t* window);
+
+/* Static text for a status code. */
+const char* kvq_status_str(kvq_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

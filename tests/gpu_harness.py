@@ -1,0 +1,107 @@
+"""Drive a workload through the GPU library and compare with the oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from decode_attention_quantize_amd import KVQCache, config_from_workload
+from kvq_unpack import unpack_unit
+
+TOL = 2e-3   # row-max-normalised error bound on attention outputs
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(wl, layers=None, steps=None, keep_units=None, device="cuda"):
+    """Prefill every layer, then per step: per layer append (when the workload
+    appends) and decode.  Returns outputs [layer][step] -> cpu fp32 [B][Hq][D]
+    (only for the kept units when keep_units is given) and raw unit bodies."""
+    dev = torch.device(device)
+    layers = list(range(wl.L)) if layers is None else layers
+    steps = wl.steps if steps is None else steps
+    cache = KVQCache(config_from_workload(wl), wl.bit_pairs(), wl.codebooks(), device=dev,
+                     layers=layers)
+    B, Hkv, Hq, T = wl.B, wl.Hkv, wl.Hq, wl.T
+    for l in layers:
+        k = wl.k(l, 0, B, 0, Hkv, 0, T, device=dev).contiguous()
+        v = wl.v(l, 0, B, 0, Hkv, 0, T, device=dev).contiguous()
+        cache.prefill(l, k, v)
+        del k, v
+    outs = {l: {} for l in layers}
+    for i in range(steps):
+        for l in layers:
+            if wl.append:
+                kt = wl.k(l, 0, B, 0, Hkv, T + i, T + i + 1, device=dev).reshape(B, Hkv, wl.D).contiguous()
+                vt = wl.v(l, 0, B, 0, Hkv, T + i, T + i + 1, device=dev).reshape(B, Hkv, wl.D).contiguous()
+                cache.append(l, kt, vt)
+            q = wl.q(l, i, device=dev).contiguous()
+            o = cache.decode(l, q)
+            if keep_units is None:
+                outs[l][i] = o.cpu()
+            else:
+                outs[l][i] = {u: o[u // Hkv, (u % Hkv) * wl.gq:(u % Hkv + 1) * wl.gq].cpu()
+                              for u in keep_units}
+    torch.cuda.synchronize()
+    return cache, outs
+
+
+def unit_body(cache, layer, u):
+    lay = cache.layout(layer)
+    raw = cache.raw(layer, 0)
+    per_unit = raw.numel() // (cache.cfg.batch * cache.cfg.n_kv_heads)
+    return raw[u * per_unit:(u + 1) * per_unit].cpu().numpy(), lay
+
+
+def unit_fp16(cache, layer, u, wcap):
+    slots = cache.cfg.sink_tokens + wcap
+    per = 2 * slots * 128 * 2
+    raw = cache.raw(layer, 1)[u * per:(u + 1) * per].cpu().numpy()
+    return raw.view(np.uint16).reshape(2, slots, 128)
+
+
+def rel_err(got, ref):
+    got = np.asarray(got, np.float64)
+    den = np.max(np.abs(ref), axis=-1)
+    return np.max(np.abs(got - ref), axis=-1) / np.where(den == 0, 1.0, den)
+
+
+def check_unit(wl, cache, outs, layer, u, steps=None, check_steps=None, label=""):
+    """Bit-exact codes/params/outliers/fp16 area and per-step outputs of one unit."""
+    b, h = divmod(u, wl.Hkv)
+    ref = O.run_unit(wl, layer, b, h, steps=steps, only_steps=check_steps)
+    enc, nb = ref["enc"], ref["nb_final"]
+    body, lay = unit_body(cache, layer, u)
+    kb, vb = wl.bit_pairs()[layer]
+    got = unpack_unit(body, lay, kb, vb, nb, wl.k_mode == "inner", wl.k_group, wl.v_group, wl.outliers)
+    for key in ("kcodes", "kmeta", "vcodes", "vmeta"):
+        g, r = got[key], enc[key]
+        assert g.shape == r.shape, (label, key, g.shape, r.shape)
+        bad = np.argwhere(g != r)
+        assert bad.size == 0, (label, key, "mismatches", bad.shape[0], bad[:5].tolist(),
+                               g[tuple(bad[0])], r[tuple(bad[0])])
+    if wl.outliers:
+        for key in ("kocol", "koval", "vocol", "voval"):
+            assert np.array_equal(got[key], enc[key]), (label, key)
+    # fp16 sinks + window ring hold the exact (rotated, for values) tokens
+    n, s_eff, nbody, r = cache.state(layer)
+    assert (n, nbody) == (ref["n_final"], nb)
+    wcap = lay["window_cap"]
+    fp = unit_fp16(cache, layer, u, wcap)
+    for p in list(range(s_eff)) + list(range(s_eff + nb, n)):
+        slot = p if p < s_eff else wl.sinks + (p - s_eff) % wcap
+        assert np.array_equal(fp[0, slot], ref["K"][p]), (label, "fp16 K", p)
+        assert np.array_equal(fp[1, slot], enc["vrot"][p]), (label, "fp16 V", p)
+    worst = 0.0
+    for i, o_ref in ref["out"].items():
+        o = outs[layer][i]
+        o = o[u] if isinstance(o, dict) else o[b, h * wl.gq:(h + 1) * wl.gq]
+        e = rel_err(o.double().numpy(), o_ref)
+        worst = max(worst, float(e.max()))
+        assert e.max() <= TOL, (label, "step", i, e.max())
+    return worst

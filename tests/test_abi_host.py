@@ -1,0 +1,181 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library is loaded and every symbol include/kvq.h declares must be
+exported; configuration validation, buffer sizing and the call-order / capacity
+errors are all decided on the host before any launch, so they run here with
+dummy (never dereferenced) aligned pointers.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_attention_quantize_amd import build as kb
+from decode_attention_quantize_amd import kvq as K
+from synth import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built():
+    if kb.is_stale():
+        kb.build()
+    K.lib()
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|const char\*)\s+(kvq_\w+)\s*\(", txt, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) == 11, names
+    L = C.CDLL(K.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(K.EXPORTS)
+
+
+def test_status_strings():
+    for s in range(6):
+        assert K.status_str(s)
+    assert K.status_str(99) == "unknown status"
+
+
+def _cfg(**kw):
+    base = dict(B=1, Hq=4, Hkv=2, L=2, max_tokens=1000)
+    base.update(kw)
+    return K.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), K.KVQ_ERR_ARG),
+    (dict(Hq=3, Hkv=2), K.KVQ_ERR_ARG),
+    (dict(max_tokens=0), K.KVQ_ERR_ARG),
+    (dict(D=64), K.KVQ_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=2), K.KVQ_ERR_UNSUPPORTED),       # 3 q heads per kv head
+    (dict(Hq=64, Hkv=2), K.KVQ_ERR_UNSUPPORTED),      # 32 rows per kv head
+    (dict(k_group=16), K.KVQ_ERR_UNSUPPORTED),        # per-channel groups must be 32 tokens
+    (dict(k_mode=1, k_group=128), K.KVQ_ERR_UNSUPPORTED),
+    (dict(v_group=128), K.KVQ_ERR_UNSUPPORTED),
+    (dict(k_mode=7), K.KVQ_ERR_ARG),
+    (dict(outliers=9), K.KVQ_ERR_ARG),
+    (dict(k_pre_rope=1, rope_base=0.0), K.KVQ_ERR_ARG),
+])
+def test_create_rejects(kw, status):
+    with pytest.raises(K.KVQError) as e:
+        K.kvq_create(_cfg(**kw), [(4, 4), (4, 2)])
+    assert e.value.status == status
+
+
+def test_create_rejects_bits_and_codebooks():
+    with pytest.raises(K.KVQError) as e:
+        K.kvq_create(_cfg(), [(4, 5), (4, 2)])
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+    with pytest.raises(K.KVQError) as e:
+        K.kvq_create(_cfg(nuq=1), [(3, 3), (3, 3)])      # codebooks missing
+    assert e.value.status == K.KVQ_ERR_ARG
+    cb = np.zeros((2, 2, 8), np.uint16)
+    with pytest.raises(K.KVQError) as e:
+        K.kvq_create(_cfg(nuq=1), [(4, 4), (3, 3)], cb)  # codebook mode is 3-bit
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+    cb[1, 0, 3] = 0x7C00
+    with pytest.raises(K.KVQError) as e:
+        K.kvq_create(_cfg(nuq=1), [(3, 3), (3, 3)], cb)  # infinite level
+    assert e.value.status == K.KVQ_ERR_ARG
+    rc = K.lib().kvq_create(None, None, None, None)
+    assert rc == K.KVQ_ERR_ARG
+
+
+def _expected_record(kb_, vb, k_inner=False, kg=32, vg=32, outk=0):
+    a16 = lambda x: (x + 15) // 16 * 16
+    kc = 32 * 128 * kb_ // 8
+    km = 32 * (128 // kg) * 4 if k_inner else 512
+    vc = 32 * 128 * vb // 8
+    vm = 2 * (128 // vg) * 32 * 2
+    ko = 32 * outk * 4
+    off = [0]
+    for sz in (kc, km, vc, vm, ko, ko):
+        off.append(a16(off[-1] + sz))
+    return off[:6], (off[6] + 127) // 128 * 128
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+def test_layout_and_sizes_follow_the_spec(name):
+    wl = W.ALL[name]
+    h = K.kvq_create(K.config_from_workload(wl), wl.bit_pairs(), wl.codebooks())
+    try:
+        pairs = wl.bit_pairs()
+        units = wl.B * wl.Hkv
+        max_tokens = wl.T + (wl.steps if wl.append else 0)
+        for l in range(min(wl.L, 6)):
+            kb_, vb = pairs[l]
+            lay = K.kvq_block_layout(h, l)
+            offs, rec = _expected_record(kb_, vb, wl.k_mode == "inner", wl.k_group, wl.v_group, wl.outliers)
+            assert [lay[k] for k in ("k_codes", "k_meta", "v_codes", "v_meta", "k_out", "v_out")] == offs
+            assert lay["record_bytes"] == rec
+            assert lay["k_row_bytes"] == 128 * kb_ // 8
+            F = 32 if wl.k_mode == "channel" else 1
+            assert lay["flush_tokens"] == F
+            wcap = -(-(wl.window + F) // F) * F
+            assert lay["window_cap"] == wcap
+            sizes = K.kvq_layer_buffer_sizes(h, l)
+            assert sizes[0] == units * (-(-max_tokens // 32)) * rec
+            assert sizes[1] == units * 2 * (wl.sinks + wcap) * 128 * 2
+        assert K.kvq_workspace_size(h) > 0
+    finally:
+        K.kvq_destroy(h)
+
+
+def test_average_bits_from_code_bytes():
+    """f_m(P) = sum(P)/2L (KVTuner review, method step 0) equals the mean bit
+    width implied by the packed code bytes of each layer's records."""
+    wl = W.C3
+    h = K.kvq_create(K.config_from_workload(wl), wl.bit_pairs())
+    try:
+        bits = []
+        for l in range(wl.L):
+            lay = K.kvq_block_layout(h, l)
+            k_bits = (lay["k_meta"] - lay["k_codes"]) * 8 / (32 * 128)
+            v_bits = (lay["v_meta"] - lay["v_codes"]) * 8 / (32 * 128)
+            bits += [k_bits, v_bits]
+        pairs = wl.bit_pairs()
+        f_m = sum(kb_ + vb for kb_, vb in pairs) / (2 * wl.L)
+        assert np.mean(bits) == f_m
+        assert set(pairs) <= set(W.PAIR_SET) and len(set(pairs)) == 5
+    finally:
+        K.kvq_destroy(h)
+
+
+def test_call_order_and_capacity_errors_on_host():
+    cfg = _cfg(max_tokens=100, window=8)
+    h = K.kvq_create(cfg, [(4, 4), (4, 2)])
+    fake = 1 << 20                      # aligned, never dereferenced: every call fails first
+    stream = None
+    try:
+        def st(fn, *a):
+            return fn(*a)
+        L = K.lib()
+        assert L.kvq_quantize_prefill(h, 0, fake, fake, 10, None, stream) == K.KVQ_ERR_STATE   # unbound
+        assert L.kvq_decode_attn(h, 0, fake, fake, fake, stream) == K.KVQ_ERR_STATE
+        assert L.kvq_append_token(h, 0, fake, fake, stream) == K.KVQ_ERR_STATE
+        assert L.kvq_quantize_prefill(h, 5, fake, fake, 10, None, stream) == K.KVQ_ERR_ARG     # layer
+        arr = (C.c_void_p * 2)(fake, fake + 1)                                                # misaligned
+        assert L.kvq_bind_layer(h, 0, arr) == K.KVQ_ERR_ARG
+        arr = (C.c_void_p * 2)(fake, fake)
+        assert L.kvq_bind_layer(h, 0, arr) == K.KVQ_OK
+        assert L.kvq_quantize_prefill(h, 0, fake, fake, 101, None, stream) == K.KVQ_ERR_CAPACITY
+        assert L.kvq_quantize_prefill(h, 0, fake, fake, -1, None, stream) == K.KVQ_ERR_ARG
+        assert L.kvq_quantize_prefill(h, 0, None, fake, 4, None, stream) == K.KVQ_ERR_ARG
+        assert L.kvq_append_token(h, 0, fake, fake, stream) == K.KVQ_ERR_STATE               # before prefill
+        assert L.kvq_decode_attn(h, 0, fake, fake, fake, stream) == K.KVQ_ERR_STATE
+        assert L.kvq_decode_attn(h, 0, None, fake, fake, stream) == K.KVQ_ERR_ARG
+        assert K.kvq_layer_state(h, 0) == (0, 0, 0, 0)
+        assert L.kvq_layer_state(h, 9, None, None, None, None) == K.KVQ_ERR_ARG
+    finally:
+        K.kvq_destroy(h)
+    assert K.lib().kvq_destroy(None) == K.KVQ_OK

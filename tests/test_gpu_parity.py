@@ -1,0 +1,124 @@
+"""GPU path vs the CPU oracle: codes, parameters, outliers and fp16 windows
+bit-exact; attention outputs within 2e-3 (row-max-normalised) at every decode
+step, always through the compressed cache (prefill, then token by token)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_harness import TOL, check_unit, run_gpu, say
+from synth import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    "C1": W.C1,
+    "C2r": W.C2.with_(Hq=4, Hkv=4, T=1024),                       # flushes at steps 4 and 36
+    "C2r-peaky": W.C2.with_(Hq=2, Hkv=2, T=1024, steps=8, q_scale=4.0),
+    "C3r": W.C3.with_(L=5, B=2, Hq=8, Hkv=2, T=512, steps=40, fixed_pairs=W.PAIR_SET),
+    "C4r": W.C4.with_(Hq=2, Hkv=2, T=1024, steps=33),             # one flush at step 32
+    "C5r": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4),          # ragged last block
+}
+
+EDGE = {
+    "short-prompt-all-sinks": W.C2.with_(Hq=2, Hkv=2, T=3, steps=5),
+    "window-only": W.C1.with_(T=40),
+    "one-block": W.C1.with_(T=64),
+    "inner-single-token": W.C5.with_(B=1, Hq=8, Hkv=1, T=1, steps=3),
+    "uniform-3bit": W.C2.with_(Hq=2, Hkv=2, T=300, steps=3, fixed_pairs=((3, 3),)),
+    "gqa2-kv8": W.C3.with_(L=1, B=1, Hq=4, Hkv=2, T=200, steps=2, fixed_pairs=((8, 8),)),
+    "gqa16": W.C3.with_(L=1, B=1, Hq=16, Hkv=1, T=300, steps=2, fixed_pairs=((4, 2),)),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_all(name, wl):
+    say(f"[parity] {name}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} L={wl.L} T={wl.T} steps={wl.steps}")
+    cache, outs = run_gpu(wl)
+    worst = 0.0
+    for l in range(wl.L):
+        for u in range(wl.units):
+            worst = max(worst, check_unit(wl, cache, outs, l, u, label=f"{name} l{l} u{u}"))
+    say(f"[parity] {name}: worst row error {worst:.3e}")
+    cache.close()
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_reduced_configs(name):
+    _check_all(name, REDUCED[name])
+
+
+@pytest.mark.parametrize("name", list(EDGE))
+def test_edge_cases(name):
+    _check_all(name, EDGE[name])
+
+
+def test_generator_matches_cpu():
+    wl = W.C4
+    a = wl.k(0, 0, 1, 3, 5, 1000, 1100, device="cuda").cpu()
+    b = wl.k(0, 0, 1, 3, 5, 1000, 1100)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    a = W.C5.v(0, 1, 2, 0, 8, 0, 40, device="cuda").cpu()
+    b = W.C5.v(0, 1, 2, 0, 8, 0, 40)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_capacity_and_state_errors_on_device_cache():
+    from decode_attention_quantize_amd import KVQCache, KVQError, config_from_workload
+    wl = W.C1.with_(T=64)
+    cache = KVQCache(config_from_workload(wl, max_tokens=64), wl.bit_pairs(), device="cuda")
+    q = wl.q(0, 0, device="cuda")
+    with pytest.raises(KVQError):
+        cache.decode(0, q)                                   # before prefill
+    k = wl.k(0, 0, 1, 0, 1, 0, 64, device="cuda").contiguous()
+    v = wl.v(0, 0, 1, 0, 1, 0, 64, device="cuda").contiguous()
+    cache.prefill(0, k, v)
+    with pytest.raises(KVQError) as e:
+        cache.append(0, k[:, :, 0].contiguous(), v[:, :, 0].contiguous())
+    assert e.value.status == 2                               # capacity
+    assert cache.state(0) == (64, 0, 32, 32)
+    out = cache.decode(0, q)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    cache.prefill(0, k[:, :, :0].contiguous(), v[:, :, :0].contiguous())   # T = 0
+    with pytest.raises(KVQError) as e:
+        cache.decode(0, q)
+    assert e.value.status == 4
+    cache.close()
+
+
+# ---------------------------------------------------------------- full sizes, sampled units
+def _full(wl, samples, check_steps=None):
+    units = sorted({u for _, u in samples})
+    layers = sorted({l for l, _ in samples})
+    say(f"[parity-full] {wl.name}: units {units} layers {layers}")
+    cache, outs = run_gpu(wl, keep_units=units)
+    for l, u in samples:
+        w = check_unit(wl, cache, outs, l, u, check_steps=check_steps, label=f"{wl.name} l{l} u{u}")
+        say(f"[parity-full] {wl.name} layer {l} unit {u}: worst row error {w:.3e}")
+    cache.close()
+
+
+def test_full_c2_sampled():
+    _full(W.C2, [(0, 0), (0, 17), (0, 31)])
+
+
+def test_full_c3_sampled():
+    pairs = W.C3.bit_pairs()
+    first = {}
+    for l, p in enumerate(pairs):
+        first.setdefault(p, l)
+    samples = [(l, (7 * i + 3) % W.C3.units) for i, l in enumerate(sorted(first.values()))]
+    _full(W.C3, samples, check_steps={0, 31, 32, 63})
+
+
+def test_full_c4_sampled():
+    _full(W.C4, [(0, 0), (0, 29)], check_steps={0, 30, 31})
+
+
+def test_full_c5_sampled():
+    _full(W.C5, [(0, 0), (0, 255), (0, 511)])
