@@ -1,0 +1,279 @@
+"""Benchmark: fused dequant decode attention over the packed KV cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2|C3|C4|C5]
+
+A step is one pass of the hot path for every layer in the stack: append one
+token (quantizing a flush block when due) and decode attention of one query
+per head over the whole packed cache.  The default workload is the Llama-7B
+shaped MHA layer (32 heads, d=128, 32768-token context, keys 4-bit per
+channel, values 2-bit per token, 4 sink + 128 recent fp16 tokens), run as a
+stack of 8 independent layer caches so that consecutive decodes read HBM
+rather than the 256 MB Infinity Cache.
+
+The JSON line reports effective KV GB/s (algorithmic bytes of the decode,
+whole-job over the timed steps), decode tokens/s per layer, the decode
+kernel's roofline fraction (bytes per launch / event-timed launch duration,
+against 8 TB/s HBM) and the CPU oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "fused dequant decode-attn: effective KV GB/s (% HBM peak), tokens/s per layer"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=64)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--workload", default="C2")
+    p.add_argument("--layers", type=int, default=None, help="layer caches in the stack")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--copy-calib", type=int, default=0,
+                   help="only run a plain device copy of this many bytes (counter calibration)")
+    return p.parse_args()
+
+
+def workload(name, layers):
+    from synth import workloads as W
+    wl = W.ALL[name]
+    if name == "C2":
+        wl = wl.with_(L=layers or 8, fixed_pairs=((4, 2),) * (layers or 8))
+    elif layers:
+        pairs = wl.bit_pairs()
+        wl = wl.with_(L=layers, fixed_pairs=tuple(pairs[:layers]) if len(pairs) >= layers else ())
+    return wl
+
+
+def decode_bytes(wl, layer, n, s_eff, nb, r):
+    """Algorithmic bytes one decode must move (codes, per-group fp16 params,
+    sparse outliers, fp16 sinks/window, q in, out)."""
+    kb, vb = wl.bit_pairs()[layer]
+    D = wl.D
+    per_unit = nb * D * (kb + vb) / 8
+    if wl.k_mode == "channel":
+        per_unit += (nb // 32) * D * 4 + (nb % 32 > 0) * D * 4
+    else:
+        per_unit += nb * (D // wl.k_group) * 4
+    per_unit += nb * (D // wl.v_group) * 4
+    per_unit += nb * wl.outliers * 4 * 2
+    per_unit += (s_eff + r) * D * 2 * 2
+    total = per_unit * wl.units + wl.B * wl.Hq * D * (2 + 4)
+    if wl.nuq:
+        total += 32
+    return total
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "decode_attention_quantize_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.startswith("kvq_decode") or f.endswith(".h"):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(name):
+    path = os.path.join(ROOT, "profiles", f"decode_{name.lower()}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, seconds):
+    """The oracle (as it stands) decoding sampled units of one step on this host."""
+    import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
+    import oracle as O
+
+    layer = 0
+    sc = O.scheme_for(wl, layer)
+    F = wl.flush
+    s_eff, nb, r = O.state_prefill(wl.T, wl.sinks, wl.window, F)
+    n = wl.T
+    cores = max(1, min(os.cpu_count() or 1, 16))
+    units = list(range(min(wl.units, 2 * cores)))
+    prepared = []
+    for u in units:
+        b, h = divmod(u, wl.Hkv)
+        K, V = O.unit_inputs(wl, layer, b, h, n)
+        enc = O.encode_unit(sc, K, V, n, s_eff, nb)
+        q = wl.q(layer, 0, b0=b, b1=b + 1, h0=h * wl.gq, h1=(h + 1) * wl.gq).reshape(wl.gq, wl.D)
+        prepared.append((K, enc, q.double().numpy()))
+
+    def one(item):
+        K, enc, q = item
+        Kh, Vh = O.dequant_unit(sc, K, enc, n, s_eff, nb)
+        return O.attention(q, Kh, Vh, unrotate=bool(wl.v_hadamard))
+
+    per_unit_bytes = (decode_bytes(wl, layer, n, s_eff, nb, r) - wl.B * wl.Hq * wl.D * 6) / wl.units \
+        + wl.gq * wl.D * 6
+    done, t0 = 0, time.perf_counter()
+    with ThreadPoolExecutor(cores) as ex:
+        while True:
+            list(ex.map(one, prepared))
+            done += len(prepared)
+            if time.perf_counter() - t0 >= seconds:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": round(per_unit_bytes * done / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{done} (batch, kv-head) unit decodes of step 0 of {wl.name} "
+                      f"(dequantize {n} tokens in binary64 + attention), {cores} threads, {dt:.1f} s"}
+
+
+def copy_calibration(nbytes):
+    import torch
+    x = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "launches": 5}))
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the path has no multi-GPU "
+              "component in this build", file=sys.stderr)
+        sys.exit(2)
+    if a.copy_calib:
+        copy_calibration(a.copy_calib)
+        return
+    import torch
+    from decode_attention_quantize_amd import build as kb
+    if not os.path.exists(kb.OUT):
+        kb.build()
+    from decode_attention_quantize_amd import KVQCache, config_from_workload
+
+    wl = workload(a.workload, a.layers)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    total_steps = a.warmup + a.steps
+    if wl.append:
+        wl = wl.with_(steps=total_steps)
+    cfg = config_from_workload(wl, max_tokens=wl.T + total_steps)
+    cache = KVQCache(cfg, wl.bit_pairs(), wl.codebooks(), device=dev)
+    B, Hkv, T, D = wl.B, wl.Hkv, wl.T, wl.D
+    for l in range(wl.L):
+        k = wl.k(l, 0, B, 0, Hkv, 0, T, device=dev).contiguous()
+        v = wl.v(l, 0, B, 0, Hkv, 0, T, device=dev).contiguous()
+        cache.prefill(l, k, v)
+        del k, v
+    torch.cuda.synchronize()
+    # per-step inputs, generated before timing
+    steps_in = []
+    for i in range(total_steps):
+        row = []
+        for l in range(wl.L):
+            kt = wl.k(l, 0, B, 0, Hkv, T + i, T + i + 1, device=dev).reshape(B, Hkv, D).contiguous()
+            vt = wl.v(l, 0, B, 0, Hkv, T + i, T + i + 1, device=dev).reshape(B, Hkv, D).contiguous()
+            q = wl.q(l, i, device=dev).contiguous()
+            row.append((kt, vt, q))
+        steps_in.append(row)
+    outs = [torch.empty(B, wl.Hq, D, dtype=torch.float32, device=dev) for _ in range(wl.L)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, events=None, nbytes=None):
+        for l in range(wl.L):
+            kt, vt, q = steps_in[i][l]
+            if wl.append:
+                cache.append(l, kt, vt)
+            if nbytes is not None:
+                n, s_eff, nb, r = cache.state(l)
+                nbytes.append(decode_bytes(wl, l, n, s_eff, nb, r))
+            if events is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                cache.decode(l, q, outs[l])
+                e1.record(stream)
+                events.append((e0, e1))
+            else:
+                cache.decode(l, q, outs[l])
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events, nbytes = [], []
+    t0 = time.perf_counter()
+    for i in range(a.warmup, total_steps):
+        step(i, events, nbytes)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kern_ms = [e0.elapsed_time(e1) for e0, e1 in events]
+    assert all(torch.isfinite(o).all() for o in outs)
+
+    total_bytes = sum(nbytes)
+    value = total_bytes / dt / 1e9
+    launches = len(kern_ms)
+    avg_kernel_s = sum(kern_ms) / launches / 1e3
+    bytes_per_launch = total_bytes / launches
+    achieved = bytes_per_launch / avg_kernel_s / 1e9
+    tokens_per_s_layer = a.steps * wl.L * B / dt
+    traffic = traffic_record(a.workload)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(dt / a.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: B={B} Hq={wl.Hq} Hkv={Hkv} D={D} context={T}+steps, "
+                        f"pairs={sorted(set(wl.bit_pairs()))}, sinks={wl.sinks}, window={wl.window}, "
+                        f"stack of {wl.L} layer caches; step = per layer append + decode",
+            "layers": wl.L,
+            "batch": B,
+            "context": T,
+        },
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s_per_layer": round(tokens_per_s_layer, 1),
+        "decode_kernel_us": round(avg_kernel_s * 1e6, 2),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": round(bytes_per_launch),
+            "kernel": "decode (split + in-kernel LSE merge)",
+        },
+    }
+    if not a.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(W_for_cpu(a.workload), a.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+    cache.close()
+
+
+def W_for_cpu(name):
+    from synth import workloads as W
+    return W.ALL[name]
+
+
+if __name__ == "__main__":
+    main()
