@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -38,6 +39,7 @@ bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1))
 
 struct kvq_cache {
   kvq_config cfg{};
+  bool force_generic = false;  // KVQ_DECODE_KERNEL=generic: always use the LDS-staged decode
   int32_t G = 1, units = 1, F = 32, win_cap = 0, nblk_cap = 0;
   std::vector<Layer> layers;
 };
@@ -165,6 +167,7 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
   kvq_cache* c = new (std::nothrow) kvq_cache();
   if (!c) return KVQ_ERR_ARG;
   c->cfg = g;
+  if (const char* e = std::getenv("KVQ_DECODE_KERNEL")) c->force_generic = std::strcmp(e, "generic") == 0;
   c->G = G;
   c->units = g.batch * g.n_kv_heads;
   c->F = g.k_mode == KVQ_K_PER_CHANNEL ? kvq::kBlockTokens : 1;
@@ -374,7 +377,8 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   j.nsplit_body = nsplit_for(*c, nblk, &j.blocks_per_split);
   j.fp16_split = (L.s_eff + L.r) > 0 ? 1 : 0;
   bool used = false;
-  hipError_t e = kvq::launch_decode_fast(L.d, j, s, &used);
+  hipError_t e = hipSuccess;
+  if (!c->force_generic) e = kvq::launch_decode_fast(L.d, j, s, &used);
   if (!used) e = kvq::launch_decode_generic(L.d, j, s);
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }

@@ -57,6 +57,14 @@ def test_edge_cases(name):
     _check_all(name, EDGE[name])
 
 
+@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C5r"])
+def test_reduced_configs_general_kernel(name, monkeypatch):
+    """The same workloads through the LDS-staged decode kernel (the path every
+    scheme the matrix-core kernel does not cover takes)."""
+    monkeypatch.setenv("KVQ_DECODE_KERNEL", "generic")
+    _check_all(name + "/general", REDUCED[name])
+
+
 def test_generator_matches_cpu():
     wl = W.C4
     a = wl.k(0, 0, 1, 3, 5, 1000, 1100, device="cuda").cpu()
