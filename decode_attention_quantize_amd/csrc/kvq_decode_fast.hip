@@ -16,6 +16,9 @@
 //   last wavefront of each unit; Hadamard-rotated values unrotated there.
 // Only the first G rows of the 16-row MFMA tiles carry queries (the GQA group
 // of a kv head); keys of one block are read once for all of them.
+// Block records stream HBM -> LDS with global_load_lds_dwordx4 into a ring of
+// NBUF slots, NBUF-1 blocks ahead of the one being computed, so memory
+// latency hides behind the MFMA/VALU work without holding data in VGPRs.
 #include <hip/hip_runtime.h>
 
 #include "kvq_device.h"
@@ -33,12 +36,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int D = kHeadDim;
 constexpr int PW = D + 2;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kWaves = 4;
-
-struct WaveSmem {
-  _Float16 p[16][32];
-  float row[16];
-};
 
 __device__ __forceinline__ f32x4 mfma(half8 a, half8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -124,22 +121,72 @@ __device__ __forceinline__ int kchan(int g4, int j, int kk) {
   return 32 * g4 + 8 * j + kk;
 }
 
-template <int KB, int VB, int G, bool INNER>
-__global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, DecodeJob J) {
-  __shared__ WaveSmem smem[kWaves];
-  const int wave = threadIdx.x >> 6;
-  const int l = threadIdx.x & 63;
+
+// Compile-time record layout of a block (D = 128, value groups of 32, no
+// sparse outliers); the launcher checks it against the layer's layout.
+template <int KB, int VB, bool INNER>
+struct Rec {
+  static constexpr int kc = 32 * 16 * KB;
+  static constexpr int km = INNER ? 32 * 2 * 4 : 2 * D * 2;
+  static constexpr int vc = 32 * 16 * VB;
+  static constexpr int vm = 2 * 4 * 32 * 2;
+  static constexpr int off_km = kc;
+  static constexpr int off_vc = off_km + km;
+  static constexpr int off_vm = off_vc + vc;
+  static constexpr int bytes = off_vm + vm;
+  static constexpr int loads = (bytes + 1023) / 1024;  // 1 KiB per wave-wide load
+};
+
+// Reads of the LDS ring filled by global_load_lds.  They are issued as
+// inline-asm ds_reads: the compiler's wait insertion cannot see through the
+// DMA writes precisely (it would drain every in-flight block), so the ring is
+// guarded by explicit vmcnt waits, and each batch of reads is completed by
+// lds_done(), which pins the loaded registers behind an lgkmcnt(0) wait.
+__device__ __forceinline__ uint32_t lds_off(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 dsr16(uint32_t a) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 dsr8(uint32_t a) {
+  u32x2 r;
+  asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+__device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+template <class T>
+__device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+
+// s_waitcnt vmcnt(N) leaving the other counters free
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int KB, int VB, int G, bool INNER, int NBUF>
+__global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob J) {
+  using R = Rec<KB, VB, INNER>;
+  // one LDS object per ring slot: the compiler then tells the slots apart and
+  // keeps the partial vmcnt waits instead of draining every in-flight load
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[R::loads * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[R::loads * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF == 3 ? R::loads * 1024 : 16];
+  __shared__ __attribute__((aligned(16))) _Float16 ptile[16][32];
+  __shared__ float wsplit[kMaxBodySplits + kMaxFp16Splits];
+  const int l = threadIdx.x;
   const int n16 = l & 15, g4 = l >> 4;
-  WaveSmem& sm = smem[wave];
   const int nsplit = J.nsplit_body + J.fp16_split;
-  const int sp = blockIdx.x * kWaves + wave;
-  if (sp >= nsplit) return;
+  const int sp = blockIdx.x;
   const int u = blockIdx.y;
   const int b = u / L.Hkv, h = u % L.Hkv;
   const TokenState st = J.st;
   constexpr int RI = G < 4 ? G : 4;           // output rows per lane (registers)
   const bool rows_here = 4 * g4 < G;           // lane holds real query rows
-  constexpr int ngv = D / 32;  // value groups of 32 channels
+  constexpr int ngv = D / 32;                  // value groups of 32 channels
 
   // ---- query operand (natural channel order per K-step)
   half8 qa[4];
@@ -155,8 +202,6 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
   // inner groups: per-row sums of q over each 64-channel group
   float qsum[2][RI];
   if constexpr (INNER) {
-    float part[2];
-    // full-row sums: lanes n16, n16+16, n16+32, n16+48 hold the four quarters
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
       float s = 0.f;
@@ -166,9 +211,8 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
         for (int kk = 0; kk < 8; ++kk) s += static_cast<float>(qa[2 * gg + jj][kk]);
       s += xshflf<16>(s);
       s += __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __float_as_int(s)));
-      part[gg] = s;
 #pragma unroll
-      for (int i = 0; i < RI; ++i) qsum[gg][i] = lane_bcast(part[gg], 20 * g4 + i);
+      for (int i = 0; i < RI; ++i) qsum[gg][i] = lane_bcast(s, 20 * g4 + i);
     }
   }
 
@@ -184,146 +228,9 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) oacc[nt] = {0.f, 0.f, 0.f, 0.f};
 
-  const bool fp16_part = J.fp16_split && sp == J.nsplit_body;
-  const int nblk_body = (st.nb + kBlockTokens - 1) / kBlockTokens;
-  int c_begin, c_end;
-  if (fp16_part) {
-    c_begin = 0;
-    c_end = (st.s_eff + st.r + kBlockTokens - 1) / kBlockTokens;
-  } else {
-    c_begin = sp * J.blocks_per_split;
-    c_end = min(nblk_body, c_begin + J.blocks_per_split);
-  }
-  const int slots = L.sinks_cap + L.win_cap;
-  const uint16_t* kf = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
-  const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
-
-  for (int ch = c_begin; ch < c_end; ++ch) {
-    f32x4 sacc[2];
-    int count;
-    half8 pa;
-    if (!fp16_part) {
-      const uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + ch) * L.rec_bytes;
-      count = min(kBlockTokens, st.nb - ch * kBlockTokens);
-      // ---------------- keys
-      uint32_t kw[2][KB];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const uint8_t* row = rec + L.off_kc + (16 * nt + n16) * (16 * KB);
-        if constexpr (INNER) {
-          const u32x2 a = ld8(row + 8 * g4);
-          const u32x2 c2 = ld8(row + 32 + 8 * g4);
-          kw[nt][0] = a[0]; kw[nt][1] = a[1]; kw[nt][2] = c2[0]; kw[nt][3] = c2[1];
-        } else if constexpr (KB == 4) {
-          const u32x4 a = ld16(row + 16 * g4);
-          kw[nt][0] = a[0]; kw[nt][1] = a[1]; kw[nt][2] = a[2]; kw[nt][3] = a[3];
-        } else if constexpr (KB == 2) {
-          const u32x2 a = ld8(row + 8 * g4);
-          kw[nt][0] = a[0]; kw[nt][1] = a[1];
-        } else {
-          const u32x4 a = ld16(row + 32 * g4);
-          const u32x4 c2 = ld16(row + 32 * g4 + 16);
-          kw[nt][0] = a[0]; kw[nt][1] = a[1]; kw[nt][2] = a[2]; kw[nt][3] = a[3];
-          kw[nt][4] = c2[0]; kw[nt][5] = c2[1]; kw[nt][6] = c2[2]; kw[nt][7] = c2[3];
-        }
-      }
-      if constexpr (!INNER) {
-        // A = q * s per channel as a pair hi + lo of fp16 exact to ~2^-22
-        // (lo = fma(q, s, -hi) rounds only the residual).  One MFMA chain
-        // against the block's parameters broadcast over the tile's columns
-        // gives, per query row, C_z = sum_c q_c z_c (columns 0-7) and
-        // C_s = sum_c q_c s_c (columns 8-15); the score of token t is
-        //   (sum_c A_c B_ct - base * C_s) * inv_unit + C_z.
-        const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + L.off_km);
-        half8 qh[4], ql[4];
-        f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
-        const uint16_t* zs = km + (n16 < 8 ? D : 0) + 32 * g4;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const half8 s8 = h8(ld16(km + 32 * g4 + 8 * j));
-          qh[j] = qa[j] * s8;
-          ql[j] = __builtin_elementwise_fma(qa[j], s8, -qh[j]);
-          cacc = mfma(qa[j], h8(ld16(zs + 8 * j)), cacc);
-        }
-        constexpr float base = CodeEnc<KB>::base, iu = CodeEnc<KB>::inv_unit;
-        f32x4 init;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float other = xshflf<8>(cacc[i]);
-          const float cz = n16 < 8 ? cacc[i] : other;
-          const float cs = n16 < 8 ? other : cacc[i];
-          init[i] = fmaf(cz, 1.f / iu, -base * cs);
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          sacc[nt] = init;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const half8 bk = kstep<KB>(kw[nt], j);
-            sacc[nt] = mfma(qh[j], bk, sacc[nt]);
-            sacc[nt] = mfma(ql[j], bk, sacc[nt]);
-          }
-        }
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sacc[nt][i] *= iu * kscale;
-      } else {
-        // per-token groups of 64 channels: group sums sum_c q_c B_ct, offset
-        // removed with the group sums of q, then scaled per token
-        constexpr float base = CodeEnc<KB>::base, iu = CodeEnc<KB>::inv_unit;
-        const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + L.off_km);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
-          p0 = mfma(qa[0], kstep<KB>(kw[nt], 0), p0);
-          p0 = mfma(qa[1], kstep<KB>(kw[nt], 1), p0);
-          p1 = mfma(qa[2], kstep<KB>(kw[nt], 2), p1);
-          p1 = mfma(qa[3], kstep<KB>(kw[nt], 3), p1);
-          const int tok = 16 * nt + n16;
-          const u32x2 mm = ld8(km + tok * 4);  // (s0, z0), (s1, z1)
-          float sg[2], zg[2];
-#pragma unroll
-          for (int gg = 0; gg < 2; ++gg) {
-            const uint16_t s16 = static_cast<uint16_t>(mm[gg] & 0xffff);
-            const uint16_t z16 = static_cast<uint16_t>(mm[gg] >> 16);
-            const float sv = h2f(s16 & 0x7fff);
-            const bool sym = (s16 & 0x8000) != 0;
-            sg[gg] = sv * iu;
-            zg[gg] = sym ? -static_cast<float>(1 << (KB - 1)) * sv : h2f(z16);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float sc = 0.f;
-            if (i < RI) {
-              sc = fmaf(sg[0], fmaf(-base, qsum[0][i], p0[i]), zg[0] * qsum[0][i]);
-              sc = fmaf(sg[1], fmaf(-base, qsum[1][i], p1[i]), fmaf(zg[1], qsum[1][i], sc));
-            }
-            sacc[nt][i] = sc * kscale;
-          }
-        }
-      }
-    } else {
-      // ---------------- fp16 sinks / window tokens: B = keys as stored
-      count = min(kBlockTokens, st.s_eff + st.r - ch * kBlockTokens);
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int vi = ch * kBlockTokens + 16 * nt + n16;
-        int slot = 0;
-        if (vi < count + ch * kBlockTokens) {
-          const int pos = vi < st.s_eff ? vi : st.s_eff + st.nb + (vi - st.s_eff);
-          slot = vi < st.s_eff ? vi : L.sinks_cap + (pos - st.s_eff) % L.win_cap;
-        }
-        sacc[nt] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sacc[nt] = mfma(qa[j], h8(ld16(kf + slot * D + kchan<INNER>(g4, j, 0))), sacc[nt]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[nt][i] *= kscale;
-      }
-    }
-
-    // ---------------- online softmax over the block (rows 4*g4 + i)
+  // online softmax of one 32-token tile; P (fp16) lands in ptile, the
+  // accumulators are rescaled; returns nothing, reads sacc
+  auto softmax_tile = [&](f32x4 (&sacc)[2], int count) __attribute__((always_inline)) -> half8 {
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
       if (16 * nt + n16 >= count)
@@ -335,15 +242,15 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
       const float bm = row16_max<16>(fmaxf(sacc[0][i], sacc[1][i]));
       const float mn = fmaxf(m_run[i], bm);
       alpha[i] = exp2f(m_run[i] - mn);
-      // P is used as fp16 in every product below; the denominator sums the
-      // same rounded weights so numerator and denominator stay consistent
+      // P is used as fp16 in every product; the denominator sums the same
+      // rounded weights so numerator and denominator stay consistent
       const _Float16 p0 = static_cast<_Float16>(exp2f(sacc[0][i] - mn));
       const _Float16 p1 = static_cast<_Float16>(exp2f(sacc[1][i] - mn));
       l_run[i] = fmaf(l_run[i], alpha[i], static_cast<float>(p0) + static_cast<float>(p1));
       m_run[i] = mn;
       if (rows_here) {
-        sm.p[4 * g4 + i][n16] = p0;
-        sm.p[4 * g4 + i][16 + n16] = p1;
+        ptile[4 * g4 + i][n16] = p0;
+        ptile[4 * g4 + i][16 + n16] = p1;
       }
     }
 #pragma unroll
@@ -355,52 +262,256 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    pa = n16 < G ? *reinterpret_cast<const half8*>(&sm.p[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
+    return n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
+  };
 
-    // ---------------- values
-    if (!fp16_part) {
-      const uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + ch) * L.rec_bytes;
-      const uint16_t* vm = reinterpret_cast<const uint16_t*>(rec + L.off_vm);
-      uint32_t vw[2 * VB];
-      const uint8_t* chunk = rec + L.off_vc + l * (8 * VB);
+  // one quantized block whose record sits in LDS at rec
+  auto body_block = [&](const uint8_t* rec, int count) __attribute__((always_inline)) {
+    const uint32_t r0 = lds_off(rec);
+    f32x4 sacc[2];
+    // ---------------- keys: one batch of LDS reads
+    uint32_t kw[2][KB];
+    u32x4 kmeta[8];
+    u32x2 imeta[2];
+    {
+      if constexpr (INNER) {
+        const uint32_t a = r0 + n16 * 64 + 8 * g4;
+        const u32x2 x0 = dsr8<0>(a), x1 = dsr8<32>(a), y0 = dsr8<1024>(a), y1 = dsr8<1024 + 32>(a);
+        const uint32_t am = r0 + R::off_km + 8 * n16;
+        imeta[0] = dsr8<0>(am);
+        imeta[1] = dsr8<128>(am);
+        kw[0][0] = x0[0]; kw[0][1] = x0[1]; kw[0][2] = x1[0]; kw[0][3] = x1[1];
+        kw[1][0] = y0[0]; kw[1][1] = y0[1]; kw[1][2] = y1[0]; kw[1][3] = y1[1];
+      } else {
+        constexpr int RB = 16 * KB;  // key row bytes
+        constexpr int CB = 4 * KB;   // bytes of one lane's 32-channel chunk
+        const uint32_t a = r0 + n16 * RB + CB * g4;
+        if constexpr (KB == 4) {
+          const u32x4 x = dsr16<0>(a), y = dsr16<16 * RB>(a);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { kw[0][e] = x[e]; kw[1][e] = y[e]; }
+        } else if constexpr (KB == 2) {
+          const u32x2 x = dsr8<0>(a), y = dsr8<16 * RB>(a);
+#pragma unroll
+          for (int e = 0; e < 2; ++e) { kw[0][e] = x[e]; kw[1][e] = y[e]; }
+        } else {
+          const u32x4 x0 = dsr16<0>(a), x1 = dsr16<16>(a), y0 = dsr16<16 * RB>(a), y1 = dsr16<16 * RB + 16>(a);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { kw[0][e] = x0[e]; kw[0][4 + e] = x1[e]; kw[1][e] = y0[e]; kw[1][4 + e] = y1[e]; }
+        }
+        // C-term operand (z for columns 0-7, s for 8-15) and the scale chunk
+        const uint32_t ac = r0 + R::off_km + (n16 < 8 ? 2 * D : 0) + 64 * g4;
+        const uint32_t as = r0 + R::off_km + 64 * g4;
+        kmeta[0] = dsr16<0>(ac); kmeta[1] = dsr16<16>(ac); kmeta[2] = dsr16<32>(ac); kmeta[3] = dsr16<48>(ac);
+        kmeta[4] = dsr16<0>(as); kmeta[5] = dsr16<16>(as); kmeta[6] = dsr16<32>(as); kmeta[7] = dsr16<48>(as);
+      }
+      lds_wait();
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int e = 0; e < KB; ++e) pin(kw[nt][e]);
+      if constexpr (INNER) {
+        pin(imeta[0]);
+        pin(imeta[1]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pin(kmeta[e]);
+      }
+    }
+    if constexpr (!INNER) {
+      // A = q * s per channel as a pair hi + lo of fp16 exact to ~2^-22
+      // (lo = fma(q, s, -hi) rounds only the residual).  One MFMA chain
+      // against the block's parameters broadcast over the tile's columns
+      // gives, per query row, C_z = sum_c q_c z_c (columns 0-7) and
+      // C_s = sum_c q_c s_c (columns 8-15); the score of token t is
+      //   (sum_c A_c B_ct - base * C_s) * inv_unit + C_z.
+      constexpr float base = CodeEnc<KB>::base, iu = CodeEnc<KB>::inv_unit;
+      f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cacc = mfma(qa[j], h8(kmeta[j]), cacc);
+      f32x4 init;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float other = xshflf<8>(cacc[i]);
+        const float cz = n16 < 8 ? cacc[i] : other;
+        const float cs = n16 < 8 ? other : cacc[i];
+        init[i] = fmaf(cz, 1.f / iu, -base * cs);
+      }
+      sacc[0] = init;
+      sacc[1] = init;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half8 s8 = h8(kmeta[4 + j]);
+        const half8 qh = qa[j] * s8;
+        const half8 ql = __builtin_elementwise_fma(qa[j], s8, -qh);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const half8 bk = kstep<KB>(kw[nt], j);
+          sacc[nt] = mfma(qh, bk, sacc[nt]);
+          sacc[nt] = mfma(ql, bk, sacc[nt]);
+        }
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[nt][i] *= iu * kscale;
+    } else {
+      // per-token groups of 64 channels: group sums sum_c q_c B_ct, offset
+      // removed with the group sums of q, then scaled per token
+      constexpr float base = CodeEnc<KB>::base, iu = CodeEnc<KB>::inv_unit;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+        p0 = mfma(qa[0], kstep<KB>(kw[nt], 0), p0);
+        p0 = mfma(qa[1], kstep<KB>(kw[nt], 1), p0);
+        p1 = mfma(qa[2], kstep<KB>(kw[nt], 2), p1);
+        p1 = mfma(qa[3], kstep<KB>(kw[nt], 3), p1);
+        const u32x2 mm = imeta[nt];  // (s0, z0), (s1, z1) of token 16 nt + n16
+        float sg[2], zg[2];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const uint16_t s16 = static_cast<uint16_t>(mm[gg] & 0xffff);
+          const uint16_t z16 = static_cast<uint16_t>(mm[gg] >> 16);
+          const float sv = h2f(s16 & 0x7fff);
+          const bool sym = (s16 & 0x8000) != 0;
+          sg[gg] = sv * iu;
+          zg[gg] = sym ? -static_cast<float>(1 << (KB - 1)) * sv : h2f(z16);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float sc = 0.f;
+          if (i < RI) {
+            sc = fmaf(sg[0], fmaf(-base, qsum[0][i], p0[i]), zg[0] * qsum[0][i]);
+            sc = fmaf(sg[1], fmaf(-base, qsum[1][i], p1[i]), fmaf(zg[1], qsum[1][i], sc));
+          }
+          sacc[nt][i] = sc * kscale;
+        }
+      }
+    }
+    // ---------------- values: one batch of LDS reads (issued before the softmax)
+    uint32_t vw[2 * VB];
+    u32x4 vmeta[5];
+    {
+      const uint32_t av = r0 + R::off_vc + l * (8 * VB);
+      u32x4 c[(2 * VB) / 4];
+      c[0] = dsr16<0>(av);
+      if constexpr (VB >= 4) c[1] = dsr16<16>(av);
+      if constexpr (VB == 8) { c[2] = dsr16<32>(av); c[3] = dsr16<48>(av); }
+      const uint32_t az = r0 + R::off_vm + (n16 < 4 ? 2 * ngv * kBlockTokens : 0) + 2 * ((n16 & 3) * kBlockTokens + 8 * g4);
+      const uint32_t asv = r0 + R::off_vm + 16 * g4;
+      vmeta[4] = dsr16<0>(az);
+      vmeta[0] = dsr16<0>(asv); vmeta[1] = dsr16<64>(asv); vmeta[2] = dsr16<128>(asv); vmeta[3] = dsr16<192>(asv);
+      lds_wait();
 #pragma unroll
       for (int q4 = 0; q4 < (2 * VB) / 4; ++q4) {
-        const u32x4 a = ld16(chunk + 16 * q4);
-        vw[4 * q4] = a[0]; vw[4 * q4 + 1] = a[1]; vw[4 * q4 + 2] = a[2]; vw[4 * q4 + 3] = a[3];
-      }
-      // one MFMA of P against the block's value parameters: column g < 4 holds
-      // z_g (zero points), column 4 + g holds s_g (removes the code offset)
-      {
-        const int col = n16 & 3;
-        const uint16_t* src = vm + (n16 < 4 ? ngv * kBlockTokens : 0) + col * kBlockTokens + 8 * g4;
-        const half8 bz = h8(ld16(src));
-        zacc = mfma(pa, n16 < 2 * ngv ? bz : h8(0u, 0u, 0u, 0u), zacc);
-      }
-      // weights w = p * s per (token, value group) as an exact hi + lo pair
-      half8 wh[ngv], wl[ngv];
+        pin(c[q4]);
 #pragma unroll
-      for (int g = 0; g < ngv; ++g) {
-        const half8 s8 = h8(ld16(vm + g * kBlockTokens + 8 * g4));
-        wh[g] = pa * s8;
-        wl[g] = __builtin_elementwise_fma(pa, s8, -wh[g]);
+        for (int e = 0; e < 4; ++e) vw[4 * q4 + e] = c[q4][e];
       }
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
+      for (int e = 0; e < 5; ++e) pin(vmeta[e]);
+    }
+    const half8 pa = softmax_tile(sacc, count);
+    // one MFMA of P against the block's value parameters: column g < 4 holds
+    // z_g (zero points), column 4 + g holds s_g (removes the code offset)
+    zacc = mfma(pa, n16 < 2 * ngv ? h8(vmeta[4]) : h8(0u, 0u, 0u, 0u), zacc);
+    // weights w = p * s per (token, value group) as an exact hi + lo pair
+#pragma unroll
+    for (int g = 0; g < ngv; ++g) {
+      const half8 s8 = h8(vmeta[g]);
+      const half8 wh = pa * s8;
+      const half8 wl = __builtin_elementwise_fma(pa, s8, -wh);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int nt = 2 * g + t;
         const half8 bv = vtile<VB>(vw, nt);
-        oacc[nt] = mfma(wh[nt >> 1], bv, oacc[nt]);
-        oacc[nt] = mfma(wl[nt >> 1], bv, oacc[nt]);
+        oacc[nt] = mfma(wh, bv, oacc[nt]);
+        oacc[nt] = mfma(wl, bv, oacc[nt]);
       }
-    } else {
-      // fp16 values: B[t][c] = v[t][c], gathered per lane (8 tokens of one channel)
-      const int vi0 = ch * kBlockTokens + 8 * g4;
+    }
+  };
+
+  const bool fp16_part = sp >= J.nsplit_body;
+  const int slots = L.sinks_cap + L.win_cap;
+  if (!fp16_part) {
+    const int nblk_body = (st.nb + kBlockTokens - 1) / kBlockTokens;
+    const int c_begin = sp * J.blocks_per_split;
+    const int c_end = min(nblk_body, c_begin + J.blocks_per_split);
+    const int nmy = c_end - c_begin;
+    const uint8_t* ubase = L.body + static_cast<int64_t>(u) * L.nblk_cap * L.rec_bytes;
+    auto issue = [&](int i, uint8_t* dst) __attribute__((always_inline)) {
+      const uint8_t* src = ubase + static_cast<int64_t>(c_begin + i) * L.rec_bytes;
+#pragma unroll
+      for (int k = 0; k < R::loads; ++k) {
+        const int off = k * 1024 + l * 16;
+        if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
+      }
+    };
+    // block i sits in slot i % NBUF.  Steady state: every step issues block
+    // i + NBUF - 1 and waits until only the (NBUF - 1) newer blocks are in
+    // flight, so the waits are the same on every path.  The tail drains.
+    auto step = [&](int i, uint8_t* cur, uint8_t* ahead) __attribute__((always_inline)) {
+      issue(i + NBUF - 1, ahead);
+      wait_vm<(NBUF - 1) * R::loads>();
+      const int ch = c_begin + i;
+      body_block(cur, min(kBlockTokens, st.nb - ch * kBlockTokens));
+    };
+    if (nmy > 0) issue(0, ring0);
+    if (NBUF == 3 && nmy > 1) issue(1, ring1);
+    int i = 0;
+    for (; i + 2 * NBUF - 2 < nmy; i += NBUF) {
+      if constexpr (NBUF == 3) {
+        step(i, ring0, ring2);
+        step(i + 1, ring1, ring0);
+        step(i + 2, ring2, ring1);
+      } else {
+        step(i, ring0, ring1);
+        step(i + 1, ring1, ring0);
+      }
+    }
+    for (; i < nmy; ++i) {
+      // remaining blocks: issue what is still missing, then drain in order
+      const int ahead = i + NBUF - 1;
+      if (ahead < nmy) {
+        const int s_ah = ahead % NBUF;
+        issue(ahead, s_ah == 0 ? ring0 : (s_ah == 1 ? ring1 : ring2));
+      }
+      wait_vm<0>();
+      const int s_cur = i % NBUF;
+      const int ch = c_begin + i;
+      body_block(s_cur == 0 ? ring0 : (s_cur == 1 ? ring1 : ring2),
+                 min(kBlockTokens, st.nb - ch * kBlockTokens));
+    }
+  } else {
+    // ---------------- fp16 sinks / window tokens: operands as stored
+    const uint16_t* kf = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
+    const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
+    const int nch = (st.s_eff + st.r + kBlockTokens - 1) / kBlockTokens;
+    const int f0 = (sp - J.nsplit_body) * J.fp16_chunks_per_split;
+    const int f1 = min(nch, f0 + J.fp16_chunks_per_split);
+    for (int ch = f0; ch < f1; ++ch) {
+      const int count = min(kBlockTokens, st.s_eff + st.r - ch * kBlockTokens);
+      auto slot_of = [&](int vi) __attribute__((always_inline)) {
+        if (vi - ch * kBlockTokens >= count) return 0;
+        if (vi < st.s_eff) return vi;
+        const int pos = st.s_eff + st.nb + (vi - st.s_eff);
+        return L.sinks_cap + (pos - st.s_eff) % L.win_cap;
+      };
+      f32x4 sacc[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int slot = slot_of(ch * kBlockTokens + 16 * nt + n16);
+        sacc[nt] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sacc[nt] = mfma(qa[j], h8(ld16(kf + slot * D + kchan<INNER>(g4, j, 0))), sacc[nt]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[nt][i] *= kscale;
+      }
+      const half8 pa = softmax_tile(sacc, count);
       int slot[8];
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const int vi = vi0 + kk;
-        const int pos = vi < st.s_eff ? vi : st.s_eff + st.nb + (vi - st.s_eff);
-        slot[kk] = (vi - ch * kBlockTokens) >= count ? 0
-                   : (vi < st.s_eff ? vi : L.sinks_cap + (pos - st.s_eff) % L.win_cap);
-      }
+      for (int kk = 0; kk < 8; ++kk) slot[kk] = slot_of(ch * kBlockTokens + 8 * g4 + kk);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) {
         const int c = 16 * nt + n16;
@@ -417,7 +528,8 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
   // ---------------- partial of this split
   //   o = (O_raw - base * W_g) * inv_unit + Z_g  (body splits; fp16 split: O_raw)
   constexpr float vbase = CodeEnc<VB>::base, viu = CodeEnc<VB>::inv_unit;
-  float* part = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * G * PW;
+  float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * G * D;
+  float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * G * 2;
 #pragma unroll
   for (int i = 0; i < RI; ++i) {
     const float lsum = row16_sum(l_run[i]);
@@ -427,11 +539,11 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
       const float z = lane_bcast(zacc[i], (l & 48) | (nt >> 1));
       const float w = lane_bcast(zacc[i], (l & 48) | (4 + (nt >> 1)));
       const float o = fp16_part ? oacc[nt][i] : fmaf(fmaf(-vbase, w, oacc[nt][i]), viu, z);
-      if (rows_here && row < G) part[row * PW + 16 * nt + n16] = o;
+      if (rows_here && row < G) opart[row * D + 16 * nt + n16] = o;
     }
     if (rows_here && row < G && n16 == 0) {
-      part[row * PW + D] = m_run[i];
-      part[row * PW + D + 1] = lsum;
+      mlpart[row * 2] = m_run[i];
+      mlpart[row * 2 + 1] = lsum;
     }
   }
   __threadfence();
@@ -443,24 +555,58 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
   __threadfence();
 
   // ---------------- log-sum-exp merge (this wavefront is the last of the unit)
-  const float* base = J.partials + static_cast<int64_t>(u) * nsplit * G * PW;
+  // split scalars are spread over lanes; every partial vector is requested
+  // before any is consumed, so the merge costs a few memory round trips
+  const float* obase = J.partials + static_cast<int64_t>(u) * nsplit * G * D;
+  const float* mlbase = J.partials + J.ml_off + static_cast<int64_t>(u) * nsplit * G * 2;
   for (int r = 0; r < G; ++r) {
     float M = -INFINITY;
-    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, base[(i * G + r) * PW + D]);
-    float Ls = 0.f, a0 = 0.f, a1 = 0.f;
-    for (int i = 0; i < nsplit; ++i) {
-      const float* pr = base + (i * G + r) * PW;
-      const float mi = pr[D];
-      if (mi == -INFINITY) continue;
-      const float w = exp2f(mi - M);
-      Ls = fmaf(pr[D + 1], w, Ls);
-      a0 = fmaf(pr[2 * l], w, a0);
-      a1 = fmaf(pr[2 * l + 1], w, a1);
+    for (int i = l; i < nsplit; i += 64) M = fmaxf(M, mlbase[(i * G + r) * 2]);
+    M = fmaxf(M, xshflf<1>(M));
+    M = fmaxf(M, xshflf<2>(M));
+    M = fmaxf(M, xshflf<4>(M));
+    M = fmaxf(M, xshflf<8>(M));
+    M = fmaxf(M, xshflf<16>(M));
+    M = fmaxf(M, xshflf<32>(M));
+    float Lp = 0.f;
+    for (int i = l; i < nsplit; i += 64) {
+      const float mi = mlbase[(i * G + r) * 2];
+      const float w = mi == -INFINITY ? 0.f : exp2f(mi - M);
+      Lp = fmaf(mlbase[(i * G + r) * 2 + 1], w, Lp);
+      wsplit[i] = w;
     }
-    float y0 = a0 / Ls, y1 = a1 / Ls;
+    Lp += xshflf<1>(Lp);
+    Lp += xshflf<2>(Lp);
+    Lp += xshflf<4>(Lp);
+    Lp += xshflf<8>(Lp);
+    Lp += xshflf<16>(Lp);
+    Lp += xshflf<32>(Lp);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float a0 = 0.f, a1 = 0.f;
+    int i = 0;
+    for (; i + 8 <= nsplit; i += 8) {
+      u32x2 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = ld8(obase + ((i + k) * G + r) * D + 2 * l);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float w = wsplit[i + k];
+        a0 = fmaf(__uint_as_float(v[k][0]), w, a0);
+        a1 = fmaf(__uint_as_float(v[k][1]), w, a1);
+      }
+    }
+    for (; i < nsplit; ++i) {
+      const u32x2 v = ld8(obase + (i * G + r) * D + 2 * l);
+      const float w = wsplit[i];
+      a0 = fmaf(__uint_as_float(v[0]), w, a0);
+      a1 = fmaf(__uint_as_float(v[1]), w, a1);
+    }
+    float y0 = a0 / Lp, y1 = a1 / Lp;
     if (L.v_had) {
       // c * H * o with H the Sylvester matrix; lane l holds channels 2l, 2l+1
-      float t0 = y0 + y1, t1 = y0 - y1;
+      const float t0 = y0 + y1, t1 = y0 - y1;
       y0 = t0;
       y1 = t1;
 #pragma unroll
@@ -478,24 +624,30 @@ __global__ void __launch_bounds__(64 * kWaves) decode_mfma_kernel(LayerDesc L, D
     float* op = J.out + (static_cast<int64_t>(b) * L.Hq + h * G + r) * D;
     op[2 * l] = y0;
     op[2 * l + 1] = y1;
+    __builtin_amdgcn_wave_barrier();
   }
   if (l == 0) J.counters[u] = 0;
 }
 
 template <int KB, int VB, int G, bool INNER>
-hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s) {
+hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* used) {
+  using R = Rec<KB, VB, INNER>;
+  if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm) return hipSuccess;
+  *used = true;
   const int nsplit = j.nsplit_body + j.fp16_split;
-  hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER>), dim3((nsplit + kWaves - 1) / kWaves, L.units),
-                     dim3(64 * kWaves), 0, s, L, j);
+  // ring depth: two blocks in flight when records are small, one otherwise
+  if constexpr (R::loads <= 5)
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, 3>), dim3(nsplit, L.units), dim3(64), 0, s, L, j);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, 2>), dim3(nsplit, L.units), dim3(64), 0, s, L, j);
   return hipGetLastError();
 }
 
 template <int G, bool INNER>
 hipError_t by_bits(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* used) {
-  *used = true;
   const int k = L.kb, v = L.vb;
 #define KVQ_CASE(KB, VB) \
-  if (k == KB && v == VB) return launch_t<KB, VB, G, INNER>(L, j, s);
+  if (k == KB && v == VB) return launch_t<KB, VB, G, INNER>(L, j, s, used);
   if constexpr (INNER) {
     KVQ_CASE(4, 2) KVQ_CASE(4, 4)
   } else {
@@ -504,7 +656,6 @@ hipError_t by_bits(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* 
     KVQ_CASE(8, 2) KVQ_CASE(8, 4) KVQ_CASE(8, 8)
   }
 #undef KVQ_CASE
-  *used = false;
   return hipSuccess;
 }
 

@@ -22,7 +22,7 @@ using kvq::LayerDesc;
 namespace {
 
 constexpr int kD = kvq::kHeadDim;
-constexpr int kMaxSplits = 256;
+constexpr int kMaxSplits = kvq::kMaxBodySplits + kvq::kMaxFp16Splits;
 
 struct Layer {
   LayerDesc d{};
@@ -93,20 +93,41 @@ kvq_status fill_layout(const kvq_cache& c, int kb, int vb, const uint16_t* cb, L
   return KVQ_OK;
 }
 
+int max_splits(const kvq_cache& c) {
+  return std::min(kvq::kMaxBodySplits, c.nblk_cap) + kvq::kMaxFp16Splits;
+}
+size_t partials_bytes(const kvq_cache& c) {
+  return static_cast<size_t>(c.units) * max_splits(c) * c.G * (kD + 2) * sizeof(float);
+}
+
 bool valid_layer(const kvq_cache* c, int32_t layer) {
   return c && layer >= 0 && layer < static_cast<int32_t>(c->layers.size());
 }
 
-int nsplit_for(const kvq_cache& c, int nblk, int* bps) {
-  if (nblk <= 0) {
-    *bps = 1;
-    return 0;
+// Split plan.  The matrix-core path runs one wavefront per split and aims at
+// one full round of resident wavefronts (about 2048 on 256 CUs at two waves
+// per SIMD); sink/window tokens get their own splits of up to two 32-token
+// chunks.  The LDS-staged path uses one fp16 split.
+void plan_splits(const kvq_cache& c, const kvq::TokenState& st, bool fast, kvq::DecodeJob& j) {
+  const int nblk = (st.nb + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
+  const int nch = (st.s_eff + st.r + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
+  if (fast) {
+    j.fp16_split = std::min(kvq::kMaxFp16Splits, (nch + 1) / 2);
+    j.fp16_chunks_per_split = j.fp16_split ? (nch + j.fp16_split - 1) / j.fp16_split : 1;
+  } else {
+    j.fp16_split = nch > 0 ? 1 : 0;
+    j.fp16_chunks_per_split = nch;
   }
-  // aim for about 2048 workgroups in flight, at least 4 blocks per split
-  int want = std::max(1, 2048 / std::max(1, c.units));
-  want = std::min({want, kMaxSplits, std::max(1, nblk / 4)});
-  *bps = (nblk + want - 1) / want;
-  return (nblk + *bps - 1) / *bps;
+  if (nblk <= 0) {
+    j.nsplit_body = 0;
+    j.blocks_per_split = 1;
+    return;
+  }
+  int want = fast ? std::max(1, 2048 / std::max(1, c.units) - j.fp16_split)
+                  : std::max(1, 2048 / std::max(1, c.units));
+  want = std::min({want, kvq::kMaxBodySplits, std::max(1, nblk / 4)});
+  j.blocks_per_split = (nblk + want - 1) / want;
+  j.nsplit_body = (nblk + j.blocks_per_split - 1) / j.blocks_per_split;
 }
 
 }  // namespace
@@ -226,9 +247,7 @@ kvq_status kvq_bind_layer(kvq_cache* c, int32_t layer, void* const bufs[KVQ_NBUF
 
 kvq_status kvq_workspace_size(const kvq_cache* c, size_t* bytes) {
   if (!c || !bytes) return KVQ_ERR_ARG;
-  const size_t parts = static_cast<size_t>(c->units) * (std::min(kMaxSplits, c->nblk_cap) + 1) *
-                       c->G * (kD + 2) * sizeof(float);
-  *bytes = (parts + 255) / 256 * 256 + static_cast<size_t>(c->units) * sizeof(uint32_t);
+  *bytes = (partials_bytes(*c) + 255) / 256 * 256 + static_cast<size_t>(c->units) * sizeof(uint32_t);
   return KVQ_OK;
 }
 
@@ -369,17 +388,20 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   j.q = static_cast<const uint16_t*>(q);
   j.out = out;
   j.partials = static_cast<float*>(workspace);
-  const size_t parts = static_cast<size_t>(c->units) * (std::min(kMaxSplits, c->nblk_cap) + 1) *
-                       c->G * (kD + 2) * sizeof(float);
-  j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + (parts + 255) / 256 * 256);
+  j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
+                                           (partials_bytes(*c) + 255) / 256 * 256);
+  j.ml_off = static_cast<int64_t>(c->units) * max_splits(*c) * c->G * kD;
   j.st = kvq::TokenState{L.n, L.s_eff, L.nb, L.r};
-  const int nblk = (L.nb + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
-  j.nsplit_body = nsplit_for(*c, nblk, &j.blocks_per_split);
-  j.fp16_split = (L.s_eff + L.r) > 0 ? 1 : 0;
   bool used = false;
   hipError_t e = hipSuccess;
-  if (!c->force_generic) e = kvq::launch_decode_fast(L.d, j, s, &used);
-  if (!used) e = kvq::launch_decode_generic(L.d, j, s);
+  if (!c->force_generic) {
+    plan_splits(*c, j.st, true, j);
+    e = kvq::launch_decode_fast(L.d, j, s, &used);
+  }
+  if (!used) {
+    plan_splits(*c, j.st, false, j);
+    e = kvq::launch_decode_generic(L.d, j, s);
+  }
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 

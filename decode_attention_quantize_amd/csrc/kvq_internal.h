@@ -70,8 +70,11 @@ struct CopyJob {
 };
 hipError_t launch_copy_fp16(const LayerDesc& L, const CopyJob& job, hipStream_t s);
 
-// Decode attention.  partials: [units][nsplit_total][G][D + 2] fp32;
-// counters: [units] uint32 (zero on entry, zero on exit).
+// Decode attention.  partials: LDS-staged path [units][nsplit][G][D + 2] fp32;
+// matrix-core path o [units][nsplit][G][D] then (max, sum) [units][nsplit][G][2]
+// at ml_off.  counters: [units] uint32 (zero on entry, zero on exit).
+constexpr int kMaxBodySplits = 256;
+constexpr int kMaxFp16Splits = 8;
 struct DecodeJob {
   const uint16_t* q;  // [B][Hq][D]
   float* out;         // [B][Hq][D]
@@ -80,7 +83,9 @@ struct DecodeJob {
   TokenState st;
   int32_t nsplit_body;    // splits over body blocks
   int32_t blocks_per_split;
-  int32_t fp16_split;     // 1 when sinks/window tokens exist (one extra split)
+  int32_t fp16_split;     // splits over the fp16 sink/window tokens (after the body splits)
+  int32_t fp16_chunks_per_split;  // 32-token chunks per fp16 split
+  int64_t ml_off;         // matrix-core path: float offset of the (max, sum) records
 };
 hipError_t launch_decode(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
 
