@@ -167,6 +167,14 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// device-coherent loads of split records written by other wavefronts
+__device__ __forceinline__ float ldc(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ldc2(const float* p) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int KB, int VB, int G, bool INNER, int NBUF>
 __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   using R = Rec<KB, VB, INNER>;
@@ -179,7 +187,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   __shared__ float wsplit[kMaxBodySplits + kMaxFp16Splits];
   const int l = threadIdx.x;
   const int n16 = l & 15, g4 = l >> 4;
-  const int nsplit = J.nsplit_body + J.fp16_split;
+  const int nsplit = J.nsplit;
   const int sp = blockIdx.x;
   const int u = blockIdx.y;
   const int b = u / L.Hkv, h = u % L.Hkv;
@@ -241,11 +249,12 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     for (int i = 0; i < RI; ++i) {
       const float bm = row16_max<16>(fmaxf(sacc[0][i], sacc[1][i]));
       const float mn = fmaxf(m_run[i], bm);
-      alpha[i] = exp2f(m_run[i] - mn);
+      const float mr = mn == -INFINITY ? 0.f : mn;  // nothing live yet: weights 0
+      alpha[i] = exp2f(m_run[i] - mr);
       // P is used as fp16 in every product; the denominator sums the same
       // rounded weights so numerator and denominator stay consistent
-      const _Float16 p0 = static_cast<_Float16>(exp2f(sacc[0][i] - mn));
-      const _Float16 p1 = static_cast<_Float16>(exp2f(sacc[1][i] - mn));
+      const _Float16 p0 = static_cast<_Float16>(exp2f(sacc[0][i] - mr));
+      const _Float16 p1 = static_cast<_Float16>(exp2f(sacc[1][i] - mr));
       l_run[i] = fmaf(l_run[i], alpha[i], static_cast<float>(p0) + static_cast<float>(p1));
       m_run[i] = mn;
       if (rows_here) {
@@ -431,22 +440,75 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     }
   };
 
-  const bool fp16_part = sp >= J.nsplit_body;
-  const int slots = L.sinks_cap + L.win_cap;
-  if (!fp16_part) {
-    const int nblk_body = (st.nb + kBlockTokens - 1) / kBlockTokens;
-    const int c_begin = sp * J.blocks_per_split;
-    const int c_end = min(nblk_body, c_begin + J.blocks_per_split);
-    const int nmy = c_end - c_begin;
-    const uint8_t* ubase = L.body + static_cast<int64_t>(u) * L.nblk_cap * L.rec_bytes;
-    auto issue = [&](int i, uint8_t* dst) __attribute__((always_inline)) {
-      const uint8_t* src = ubase + static_cast<int64_t>(c_begin + i) * L.rec_bytes;
+  constexpr float vbase = CodeEnc<VB>::base, viu = CodeEnc<VB>::inv_unit;
+  const int nblk_body = (st.nb + kBlockTokens - 1) / kBlockTokens;
+  const int c_begin = sp * J.blocks_per_split;
+  const int c_end = sp < J.nsplit_body ? min(nblk_body, c_begin + J.blocks_per_split) : c_begin;
+  const int nmy = c_end - c_begin;
+  const uint8_t* ubase = L.body + static_cast<int64_t>(u) * L.nblk_cap * L.rec_bytes;
+  auto issue = [&](int i, uint8_t* dst) __attribute__((always_inline)) {
+    const uint8_t* src = ubase + static_cast<int64_t>(c_begin + i) * L.rec_bytes;
 #pragma unroll
-      for (int k = 0; k < R::loads; ++k) {
-        const int off = k * 1024 + l * 16;
-        if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
+    for (int k = 0; k < R::loads; ++k) {
+      const int off = k * 1024 + l * 16;
+      if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
+    }
+  };
+  if (nmy > 0) issue(0, ring0);
+  if (NBUF == 3 && nmy > 1) issue(1, ring1);
+
+  // ---------------- sink / window tokens: fp16 operands as stored, one
+  // 32-slot chunk at a time (slots without a live token are masked).  They
+  // are accumulated at 1/inv_unit scale so that the body's final code-unit
+  // rescale (a power of two, exact) restores them.
+  {
+    const int slots = L.sinks_cap + L.win_cap;
+    const uint16_t* kf = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
+    const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
+    const int wchunks = L.win_cap / kBlockTokens;
+    const int wstart = st.nb % L.win_cap;  // ring index of the oldest window token
+    for (int c = sp; c < J.fp16_chunks; c += nsplit) {
+      const bool sinkc = c < J.sink_chunks;
+      const int slot0 = sinkc ? kBlockTokens * c
+                              : L.sinks_cap + kBlockTokens * ((J.win_chunk0 + c - J.sink_chunks) % wchunks);
+      u32x4 kv[2][4], vv[8];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kv[nt][j] = ld16(kf + (slot0 + 16 * nt + n16) * D + kchan<INNER>(g4, j, 0));
+      // lane: slots slot0 + 8*g4 .. +7 of channel 16*nt + n16 (16 contiguous bytes)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) vv[nt] = ld16(vf + (static_cast<int64_t>(slot0 / 8 + g4) * D + 16 * nt + n16) * 8);
+      f32x4 sacc[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int x = slot0 + 16 * nt + n16;
+        bool live;
+        if (sinkc) {
+          live = x < st.s_eff;
+        } else {
+          int d = x - L.sinks_cap - wstart;
+          if (d < 0) d += L.win_cap;
+          live = d < st.r;
+        }
+        sacc[nt] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sacc[nt] = mfma(qa[j], h8(kv[nt][j]), sacc[nt]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sacc[nt][i] = live ? sacc[nt][i] * kscale : -INFINITY;
       }
-    };
+      const half8 pa = softmax_tile(sacc, kBlockTokens);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[nt][i] *= 1.0f / viu;
+  }
+
+  // ---------------- quantized body blocks through the LDS ring
+  {
     // block i sits in slot i % NBUF.  Steady state: every step issues block
     // i + NBUF - 1 and waits until only the (NBUF - 1) newer blocks are in
     // flight, so the waits are the same on every path.  The tail drains.
@@ -456,8 +518,6 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       const int ch = c_begin + i;
       body_block(cur, min(kBlockTokens, st.nb - ch * kBlockTokens));
     };
-    if (nmy > 0) issue(0, ring0);
-    if (NBUF == 3 && nmy > 1) issue(1, ring1);
     int i = 0;
     for (; i + 2 * NBUF - 2 < nmy; i += NBUF) {
       if constexpr (NBUF == 3) {
@@ -482,52 +542,13 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       body_block(s_cur == 0 ? ring0 : (s_cur == 1 ? ring1 : ring2),
                  min(kBlockTokens, st.nb - ch * kBlockTokens));
     }
-  } else {
-    // ---------------- fp16 sinks / window tokens: operands as stored
-    const uint16_t* kf = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
-    const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
-    const int nch = (st.s_eff + st.r + kBlockTokens - 1) / kBlockTokens;
-    const int f0 = (sp - J.nsplit_body) * J.fp16_chunks_per_split;
-    const int f1 = min(nch, f0 + J.fp16_chunks_per_split);
-    for (int ch = f0; ch < f1; ++ch) {
-      const int count = min(kBlockTokens, st.s_eff + st.r - ch * kBlockTokens);
-      auto slot_of = [&](int vi) __attribute__((always_inline)) {
-        if (vi - ch * kBlockTokens >= count) return 0;
-        if (vi < st.s_eff) return vi;
-        const int pos = st.s_eff + st.nb + (vi - st.s_eff);
-        return L.sinks_cap + (pos - st.s_eff) % L.win_cap;
-      };
-      f32x4 sacc[2];
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int slot = slot_of(ch * kBlockTokens + 16 * nt + n16);
-        sacc[nt] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sacc[nt] = mfma(qa[j], h8(ld16(kf + slot * D + kchan<INNER>(g4, j, 0))), sacc[nt]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[nt][i] *= kscale;
-      }
-      const half8 pa = softmax_tile(sacc, count);
-      int slot[8];
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) slot[kk] = slot_of(ch * kBlockTokens + 8 * g4 + kk);
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int c = 16 * nt + n16;
-        uint32_t w[4];
-#pragma unroll
-        for (int kk = 0; kk < 8; kk += 2)
-          w[kk / 2] = static_cast<uint32_t>(vf[slot[kk] * D + c]) |
-                      (static_cast<uint32_t>(vf[slot[kk + 1] * D + c]) << 16);
-        oacc[nt] = mfma(pa, h8(w[0], w[1], w[2], w[3]), oacc[nt]);
-      }
-    }
   }
 
-  // ---------------- partial of this split
-  //   o = (O_raw - base * W_g) * inv_unit + Z_g  (body splits; fp16 split: O_raw)
-  constexpr float vbase = CodeEnc<VB>::base, viu = CodeEnc<VB>::inv_unit;
+  // ---------------- partial of this split: o = (O_raw - base * W_g) * inv_unit + Z_g
+  // The records are written with device-coherent stores, their completion
+  // is awaited, and only then is the unit's counter bumped; the wavefront
+  // that sees the last count reads them back with device-coherent loads.
+  // No cache write-back of the whole L2 is needed for this hand-over.
   float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * G * D;
   float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * G * 2;
 #pragma unroll
@@ -538,21 +559,21 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     for (int nt = 0; nt < 8; ++nt) {
       const float z = lane_bcast(zacc[i], (l & 48) | (nt >> 1));
       const float w = lane_bcast(zacc[i], (l & 48) | (4 + (nt >> 1)));
-      const float o = fp16_part ? oacc[nt][i] : fmaf(fmaf(-vbase, w, oacc[nt][i]), viu, z);
-      if (rows_here && row < G) opart[row * D + 16 * nt + n16] = o;
+      const float o = fmaf(fmaf(-vbase, w, oacc[nt][i]), viu, z);
+      if (rows_here && row < G)
+        __hip_atomic_store(opart + row * D + 16 * nt + n16, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (rows_here && row < G && n16 == 0) {
-      mlpart[row * 2] = m_run[i];
-      mlpart[row * 2 + 1] = lsum;
+      __hip_atomic_store(mlpart + row * 2, m_run[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(mlpart + row * 2 + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   uint32_t prev = 0;
-  if (l == 0)
-    prev = __hip_atomic_fetch_add(J.counters + u, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  if (l == 0) prev = __hip_atomic_fetch_add(J.counters + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   prev = __builtin_amdgcn_readfirstlane(prev);
   if (prev != static_cast<uint32_t>(nsplit - 1)) return;
-  __threadfence();
+  asm volatile("" ::: "memory");
 
   // ---------------- log-sum-exp merge (this wavefront is the last of the unit)
   // split scalars are spread over lanes; every partial vector is requested
@@ -561,7 +582,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   const float* mlbase = J.partials + J.ml_off + static_cast<int64_t>(u) * nsplit * G * 2;
   for (int r = 0; r < G; ++r) {
     float M = -INFINITY;
-    for (int i = l; i < nsplit; i += 64) M = fmaxf(M, mlbase[(i * G + r) * 2]);
+    for (int i = l; i < nsplit; i += 64) M = fmaxf(M, ldc(mlbase + (i * G + r) * 2));
     M = fmaxf(M, xshflf<1>(M));
     M = fmaxf(M, xshflf<2>(M));
     M = fmaxf(M, xshflf<4>(M));
@@ -570,9 +591,9 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     M = fmaxf(M, xshflf<32>(M));
     float Lp = 0.f;
     for (int i = l; i < nsplit; i += 64) {
-      const float mi = mlbase[(i * G + r) * 2];
+      const float mi = ldc(mlbase + (i * G + r) * 2);
       const float w = mi == -INFINITY ? 0.f : exp2f(mi - M);
-      Lp = fmaf(mlbase[(i * G + r) * 2 + 1], w, Lp);
+      Lp = fmaf(ldc(mlbase + (i * G + r) * 2 + 1), w, Lp);
       wsplit[i] = w;
     }
     Lp += xshflf<1>(Lp);
@@ -587,21 +608,21 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     float a0 = 0.f, a1 = 0.f;
     int i = 0;
     for (; i + 8 <= nsplit; i += 8) {
-      u32x2 v[8];
+      uint64_t v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = ld8(obase + ((i + k) * G + r) * D + 2 * l);
+      for (int k = 0; k < 8; ++k) v[k] = ldc2(obase + ((i + k) * G + r) * D + 2 * l);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const float w = wsplit[i + k];
-        a0 = fmaf(__uint_as_float(v[k][0]), w, a0);
-        a1 = fmaf(__uint_as_float(v[k][1]), w, a1);
+        a0 = fmaf(__uint_as_float(static_cast<uint32_t>(v[k])), w, a0);
+        a1 = fmaf(__uint_as_float(static_cast<uint32_t>(v[k] >> 32)), w, a1);
       }
     }
     for (; i < nsplit; ++i) {
-      const u32x2 v = ld8(obase + (i * G + r) * D + 2 * l);
+      const uint64_t v = ldc2(obase + (i * G + r) * D + 2 * l);
       const float w = wsplit[i];
-      a0 = fmaf(__uint_as_float(v[0]), w, a0);
-      a1 = fmaf(__uint_as_float(v[1]), w, a1);
+      a0 = fmaf(__uint_as_float(static_cast<uint32_t>(v)), w, a0);
+      a1 = fmaf(__uint_as_float(static_cast<uint32_t>(v >> 32)), w, a1);
     }
     float y0 = a0 / Lp, y1 = a1 / Lp;
     if (L.v_had) {
@@ -634,7 +655,7 @@ hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool*
   using R = Rec<KB, VB, INNER>;
   if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm) return hipSuccess;
   *used = true;
-  const int nsplit = j.nsplit_body + j.fp16_split;
+  const int nsplit = j.nsplit;
   // ring depth: two blocks in flight when records are small, one otherwise
   if constexpr (R::loads <= 5)
     hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, 3>), dim3(nsplit, L.units), dim3(64), 0, s, L, j);

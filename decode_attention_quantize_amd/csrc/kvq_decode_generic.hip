@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(LayerDesc L, Decode
   const int u = blockIdx.y;
   const int sp = blockIdx.x;
   const int b = u / L.Hkv, h = u % L.Hkv;
-  const int nsplit = J.nsplit_body + J.fp16_split;
+  const int nsplit = J.nsplit;
   const TokenState st = J.st;
   const float scale = 1.0f / sqrtf(static_cast<float>(D));
 
@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(LayerDesc L, Decode
       } else {
         int slot, pos;
         fp16_slot(L, st, ch * kBlockTokens + j, slot, pos);
-        x = h2f(vf[slot * D + t]);
+        x = h2f(vf[vslot(slot, t)]);
       }
       for (int r = 0; r < G; ++r) o[r] = fmaf(sm.p[r][j], x, o[r]);
     }
@@ -256,7 +256,7 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(LayerDesc L, Decode
 
 template <int G>
 hipError_t launch_g(const LayerDesc& L, const DecodeJob& j, hipStream_t s) {
-  const int nsplit = j.nsplit_body + j.fp16_split;
+  const int nsplit = j.nsplit;
   hipLaunchKernelGGL(decode_generic_kernel<G>, dim3(nsplit, L.units), dim3(128), 0, s, L, j);
   return hipGetLastError();
 }

@@ -40,7 +40,7 @@ bool pow2_in(int v, int lo, int hi) { return v >= lo && v <= hi && (v & (v - 1))
 struct kvq_cache {
   kvq_config cfg{};
   bool force_generic = false;  // KVQ_DECODE_KERNEL=generic: always use the LDS-staged decode
-  int32_t G = 1, units = 1, F = 32, win_cap = 0, nblk_cap = 0;
+  int32_t G = 1, units = 1, F = 32, sink_cap = 0, win_cap = 0, nblk_cap = 0;
   std::vector<Layer> layers;
 };
 
@@ -88,7 +88,7 @@ kvq_status fill_layout(const kvq_cache& c, int kb, int vb, const uint16_t* cb, L
   off = align_up(off + kvq::kBlockTokens * d.outk * 4, 16);
   d.rec_bytes = align_up(off, 128);
   d.nblk_cap = c.nblk_cap;
-  d.sinks_cap = g.sink_tokens;
+  d.sinks_cap = c.sink_cap;
   d.win_cap = c.win_cap;
   return KVQ_OK;
 }
@@ -106,28 +106,40 @@ bool valid_layer(const kvq_cache* c, int32_t layer) {
 
 // Split plan.  The matrix-core path runs one wavefront per split and aims at
 // one full round of resident wavefronts (about 2048 on 256 CUs at two waves
-// per SIMD); sink/window tokens get their own splits of up to two 32-token
-// chunks.  The LDS-staged path uses one fp16 split.
+// per SIMD); the 32-slot sink / window chunks ride along on the first splits.
+// The LDS-staged path walks the sink / window tokens in one extra split.
 void plan_splits(const kvq_cache& c, const kvq::TokenState& st, bool fast, kvq::DecodeJob& j) {
   const int nblk = (st.nb + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
-  const int nch = (st.s_eff + st.r + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
+  j.fp16_split = 0;
+  j.fp16_chunks = j.sink_chunks = j.win_chunk0 = 0;
   if (fast) {
-    j.fp16_split = std::min(kvq::kMaxFp16Splits, (nch + 1) / 2);
-    j.fp16_chunks_per_split = j.fp16_split ? (nch + j.fp16_split - 1) / j.fp16_split : 1;
+    j.sink_chunks = (st.s_eff + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
+    int wchunks = 0;
+    if (st.r > 0) {
+      const int start = st.nb % c.win_cap;  // ring index of the oldest window token
+      j.win_chunk0 = start / kvq::kBlockTokens;
+      // chunks the live ring range touches; a range that wraps back into its
+      // first chunk still visits each chunk once (the live mask covers both ends)
+      wchunks = std::min((start + st.r - 1) / kvq::kBlockTokens - j.win_chunk0 + 1,
+                         c.win_cap / kvq::kBlockTokens);
+    }
+    j.fp16_chunks = j.sink_chunks + wchunks;
   } else {
-    j.fp16_split = nch > 0 ? 1 : 0;
-    j.fp16_chunks_per_split = nch;
+    j.fp16_split = st.s_eff + st.r > 0 ? 1 : 0;
   }
   if (nblk <= 0) {
     j.nsplit_body = 0;
     j.blocks_per_split = 1;
-    return;
+  } else {
+    int want = std::max(1, 2048 / std::max(1, c.units));
+    want = std::min({want, kvq::kMaxBodySplits, std::max(1, nblk / 4)});
+    j.blocks_per_split = (nblk + want - 1) / want;
+    j.nsplit_body = (nblk + j.blocks_per_split - 1) / j.blocks_per_split;
   }
-  int want = fast ? std::max(1, 2048 / std::max(1, c.units) - j.fp16_split)
-                  : std::max(1, 2048 / std::max(1, c.units));
-  want = std::min({want, kvq::kMaxBodySplits, std::max(1, nblk / 4)});
-  j.blocks_per_split = (nblk + want - 1) / want;
-  j.nsplit_body = (nblk + j.blocks_per_split - 1) / j.blocks_per_split;
+  if (fast)
+    j.nsplit = std::max(j.nsplit_body, std::min(j.fp16_chunks, kvq::kMaxFp16Splits));
+  else
+    j.nsplit = j.nsplit_body + j.fp16_split;
 }
 
 }  // namespace
@@ -192,7 +204,10 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
   c->G = G;
   c->units = g.batch * g.n_kv_heads;
   c->F = g.k_mode == KVQ_K_PER_CHANNEL ? kvq::kBlockTokens : 1;
-  c->win_cap = (g.recent_window + c->F + c->F - 1) / c->F * c->F;
+  // fp16 slot counts are multiples of 32: whole 32-slot chunks for the decode
+  // and whole 8-slot groups for the interleaved value layout
+  c->sink_cap = align_up(g.sink_tokens, kvq::kBlockTokens);
+  c->win_cap = align_up(g.recent_window + c->F, kvq::kBlockTokens);
   c->nblk_cap = (g.max_tokens + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
   c->layers.resize(g.n_layers);
   for (int l = 0; l < g.n_layers; ++l)
@@ -212,7 +227,7 @@ kvq_status kvq_layer_buffer_sizes(const kvq_cache* c, int32_t layer, size_t size
   const LayerDesc& d = c->layers[layer].d;
   sizes[KVQ_BUF_BODY] = static_cast<size_t>(c->units) * c->nblk_cap * d.rec_bytes;
   sizes[KVQ_BUF_FP16] =
-      static_cast<size_t>(c->units) * 2 * (c->cfg.sink_tokens + c->win_cap) * kD * sizeof(uint16_t);
+      static_cast<size_t>(c->units) * 2 * (c->sink_cap + c->win_cap) * kD * sizeof(uint16_t);
   return KVQ_OK;
 }
 
@@ -227,6 +242,7 @@ kvq_status kvq_block_layout(const kvq_cache* c, int32_t layer, kvq_block_layout_
   o->k_out = d.off_ko;
   o->v_out = d.off_vo;
   o->k_row_bytes = d.k_row_bytes;
+  o->sink_cap = c->sink_cap;
   o->window_cap = c->win_cap;
   o->flush_tokens = c->F;
   return KVQ_OK;
@@ -291,6 +307,7 @@ kvq_status kvq_quantize_prefill(kvq_cache* c, int32_t layer, const void* k, cons
     j.rotate_v = L.d.v_had;
     if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return KVQ_ERR_DEVICE;
   }
+  if (kvq::launch_zero_fp16(L.d, s) != hipSuccess) return KVQ_ERR_DEVICE;
   kvq::CopyJob cj{};
   cj.k_src = ks;
   cj.v_src = vs;
@@ -357,10 +374,11 @@ kvq_status kvq_append_token(kvq_cache* c, int32_t layer, const void* k_new, cons
   int nb = L.nb, r = L.r + 1;
   if (r == W + F) {
     // flush the oldest F window tokens (contiguous ring slots) into the body
-    const int slots = c->cfg.sink_tokens + c->win_cap;
+    const int slots = c->sink_cap + c->win_cap;
     kvq::QuantJob j{};
-    j.k_src = L.d.fp16 + static_cast<int64_t>(c->cfg.sink_tokens) * kD;
-    j.v_src = j.k_src + static_cast<int64_t>(slots) * kD;
+    j.k_src = L.d.fp16 + static_cast<int64_t>(c->sink_cap) * kD;
+    j.v_src = j.k_src + static_cast<int64_t>(slots) * kD;  // sink_cap is a multiple of 8
+    j.v_interleaved = 1;
     j.src_unit_stride = static_cast<int64_t>(2) * slots * kD;
     j.src_t0 = nb % c->win_cap;
     j.blk0 = nb / kvq::kBlockTokens;

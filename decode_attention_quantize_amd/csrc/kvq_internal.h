@@ -29,11 +29,18 @@ struct LayerDesc {
   int32_t off_kc, off_km, off_vc, off_vm, off_ko, off_vo;
   int32_t nblk_cap;  // blocks per unit
   // fp16 area
-  int32_t sinks_cap, win_cap;  // slots per unit: S, Wcap
+  int32_t sinks_cap, win_cap;  // slots per unit, both multiples of 32
   // buffers
   uint8_t* body;     // [units][nblk_cap][rec_bytes]
-  uint16_t* fp16;    // [units][2][sinks_cap + win_cap][D]
+  uint16_t* fp16;    // per unit: K [slots][D], then V [slots / 8][D][8]
 };
+
+// Element offset of value (slot, channel) inside a unit's fp16 value area:
+// eight consecutive slots of one channel are adjacent, which is the operand
+// order of a matrix-core product over tokens.
+__host__ __device__ inline int64_t vslot(int slot, int c) {
+  return static_cast<int64_t>(slot >> 3) * (kHeadDim * 8) + c * 8 + (slot & 7);
+}
 
 // Token state of a layer at a decode call.
 struct TokenState {
@@ -54,6 +61,7 @@ struct QuantJob {
   int32_t src_t0;
   int32_t blk0, nblocks, tok0, cnt, last_cnt;
   int32_t rotate_v;
+  int32_t v_interleaved;
 };
 hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t s);
 
@@ -70,9 +78,14 @@ struct CopyJob {
 };
 hipError_t launch_copy_fp16(const LayerDesc& L, const CopyJob& job, hipStream_t s);
 
-// Decode attention.  partials: LDS-staged path [units][nsplit][G][D + 2] fp32;
-// matrix-core path o [units][nsplit][G][D] then (max, sum) [units][nsplit][G][2]
-// at ml_off.  counters: [units] uint32 (zero on entry, zero on exit).
+// Zero a layer's fp16 area (every unit), so that slots never written hold
+// finite values.
+hipError_t launch_zero_fp16(const LayerDesc& L, hipStream_t s);
+
+// Decode attention.  grid.x = nsplit wavefront groups per unit.
+// partials: LDS-staged path [units][nsplit][G][D + 2] fp32; matrix-core path
+// o [units][nsplit][G][D] then (max, sum) [units][nsplit][G][2] at ml_off.
+// counters: [units] uint32 (zero on entry, zero on exit).
 constexpr int kMaxBodySplits = 256;
 constexpr int kMaxFp16Splits = 8;
 struct DecodeJob {
@@ -81,10 +94,16 @@ struct DecodeJob {
   float* partials;
   uint32_t* counters;
   TokenState st;
-  int32_t nsplit_body;    // splits over body blocks
+  int32_t nsplit;
+  int32_t nsplit_body;    // the first nsplit_body splits own body blocks
   int32_t blocks_per_split;
-  int32_t fp16_split;     // splits over the fp16 sink/window tokens (after the body splits)
-  int32_t fp16_chunks_per_split;  // 32-token chunks per fp16 split
+  // sink / window tokens.  LDS-staged path: when fp16_split, split
+  // nsplit_body walks them in position order.  Matrix-core path: 32-slot
+  // chunk c < fp16_chunks goes to split c % nsplit; chunks below sink_chunks
+  // are sink slots 32c.., the others window ring chunks win_chunk0, +1, ...
+  // (mod win_cap / 32); slots holding no live token are masked.
+  int32_t fp16_split;
+  int32_t fp16_chunks, sink_chunks, win_chunk0;
   int64_t ml_off;         // matrix-core path: float offset of the (max, sum) records
 };
 hipError_t launch_decode(const LayerDesc& L, const DecodeJob& job, hipStream_t s);

@@ -16,6 +16,8 @@
 //     exact binary64 butterflies
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -325,10 +327,13 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
   const int slot0 = J.tok0;
   uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + blk) * L.rec_bytes;
 
-  const int64_t base = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + kBlockTokens * bi) * D;
+  const int tt0 = J.src_t0 + kBlockTokens * bi;
+  const int64_t base = u * J.src_unit_stride + static_cast<int64_t>(tt0) * D;
+  const uint16_t* vsrc = J.v_src + u * J.src_unit_stride;
   for (int j = 0; j < kBlockTokens; ++j) {
     sm.k[j][t] = j < nrows ? J.k_src[base + j * D + t] : 0;
-    sm.v[j][t] = j < nrows ? J.v_src[base + j * D + t] : 0;
+    const int64_t vo = J.v_interleaved ? vslot(tt0 + j, t) : static_cast<int64_t>(tt0 + j) * D + t;
+    sm.v[j][t] = j < nrows ? vsrc[vo] : 0;
   }
   __syncthreads();
   if (J.rotate_v) hadamard_rows(sm, sm.v, nrows, L.had_scale);
@@ -425,11 +430,24 @@ __global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) 
     const int p = J.pos0 + j0 + j;
     const int slot = p < J.s_eff ? p : L.sinks_cap + (p - J.s_eff) % L.win_cap;
     kdst[slot * D + t] = sm.k[j][t];
-    vdst[slot * D + t] = sm.v[j][t];
+    vdst[vslot(slot, t)] = sm.v[j][t];
   }
 }
 
+__global__ void __launch_bounds__(256) zero_kernel(uint4* p, int64_t n16) {
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n16; i += static_cast<int64_t>(gridDim.x) * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 }  // namespace
+
+hipError_t launch_zero_fp16(const LayerDesc& L, hipStream_t s) {
+  const int64_t bytes = static_cast<int64_t>(L.units) * 2 * (L.sinks_cap + L.win_cap) * D * 2;
+  const int64_t n16 = bytes / 16;  // slots are a multiple of 32, so bytes is a multiple of 16
+  const int grid = static_cast<int>(std::min<int64_t>((n16 + 255) / 256, 4096));
+  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(L.fp16), n16);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t s) {
   if (job.nblocks <= 0) return hipSuccess;

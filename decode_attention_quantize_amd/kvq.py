@@ -43,7 +43,7 @@ class kvq_bitpair(C.Structure):
 class kvq_block_layout_t(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "record_bytes", "k_codes", "k_meta", "v_codes", "v_meta", "k_out", "v_out",
-        "k_row_bytes", "window_cap", "flush_tokens")]
+        "k_row_bytes", "sink_cap", "window_cap", "flush_tokens")]
 
 
 class KVQError(RuntimeError):

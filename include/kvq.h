@@ -97,8 +97,15 @@ typedef struct {
 #define KVQ_NBUF 2
 enum {
   KVQ_BUF_BODY = 0,   /* packed blocks: [B*Hkv][ceil(max_tokens/32)][record] */
-  KVQ_BUF_FP16 = 1    /* fp16 sinks and window ring: [B*Hkv][2 (K,V)][S + Wcap][D] */
+  KVQ_BUF_FP16 = 1    /* fp16 sinks and window ring, see below */
 };
+
+/* fp16 area of one (batch, kv head) unit, units back to back: Scap + Wcap
+ * slots (Scap = S and Wcap = W + F, each rounded up to a multiple of 32).
+ * Position p < S' sits in slot p; a window position p sits in slot
+ * Scap + (p - S') mod Wcap.  Keys: [Scap + Wcap][D] token-major.  Values:
+ * [(Scap + Wcap)/8][D][8], i.e. value (slot, c) at ((slot/8)*D + c)*8 +
+ * slot%8.  Slots holding no token are zero after a prefill. */
 
 /* Byte layout of one body block record (32 consecutive quantized tokens of one
  * (batch, kv head) unit), as reported by kvq_block_layout().  Every section
@@ -129,6 +136,7 @@ typedef struct {
   int32_t record_bytes;
   int32_t k_codes, k_meta, v_codes, v_meta, k_out, v_out;  /* section offsets */
   int32_t k_row_bytes;
+  int32_t sink_cap;       /* Scap: sink slots per unit */
   int32_t window_cap;     /* Wcap: window ring slots per unit */
   int32_t flush_tokens;   /* F: 32 for per-channel keys, 1 for inner keys */
 } kvq_block_layout_t;

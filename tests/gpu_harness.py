@@ -58,11 +58,15 @@ def unit_body(cache, layer, u):
     return raw[u * per_unit:(u + 1) * per_unit].cpu().numpy(), lay
 
 
-def unit_fp16(cache, layer, u, wcap):
-    slots = cache.cfg.sink_tokens + wcap
+def unit_fp16(cache, layer, u, scap, wcap):
+    """(K, V) of one unit's fp16 area as [slots][128] arrays, from the
+    documented layout: keys token-major, values 8-slot interleaved."""
+    slots = scap + wcap
     per = 2 * slots * 128 * 2
-    raw = cache.raw(layer, 1)[u * per:(u + 1) * per].cpu().numpy()
-    return raw.view(np.uint16).reshape(2, slots, 128)
+    raw = cache.raw(layer, 1)[u * per:(u + 1) * per].cpu().numpy().view(np.uint16)
+    k = raw[:slots * 128].reshape(slots, 128)
+    v = raw[slots * 128:].reshape(slots // 8, 128, 8).transpose(0, 2, 1).reshape(slots, 128)
+    return k, v
 
 
 def rel_err(got, ref):
@@ -91,12 +95,12 @@ def check_unit(wl, cache, outs, layer, u, steps=None, check_steps=None, label=""
     # fp16 sinks + window ring hold the exact (rotated, for values) tokens
     n, s_eff, nbody, r = cache.state(layer)
     assert (n, nbody) == (ref["n_final"], nb)
-    wcap = lay["window_cap"]
-    fp = unit_fp16(cache, layer, u, wcap)
+    scap, wcap = lay["sink_cap"], lay["window_cap"]
+    fk, fv = unit_fp16(cache, layer, u, scap, wcap)
     for p in list(range(s_eff)) + list(range(s_eff + nb, n)):
-        slot = p if p < s_eff else wl.sinks + (p - s_eff) % wcap
-        assert np.array_equal(fp[0, slot], ref["K"][p]), (label, "fp16 K", p)
-        assert np.array_equal(fp[1, slot], enc["vrot"][p]), (label, "fp16 V", p)
+        slot = p if p < s_eff else scap + (p - s_eff) % wcap
+        assert np.array_equal(fk[slot], ref["K"][p]), (label, "fp16 K", p)
+        assert np.array_equal(fv[slot], enc["vrot"][p]), (label, "fp16 V", p)
     worst = 0.0
     for i, o_ref in ref["out"].items():
         o = outs[layer][i]

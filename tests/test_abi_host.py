@@ -121,11 +121,12 @@ def test_layout_and_sizes_follow_the_spec(name):
             assert lay["k_row_bytes"] == 128 * kb_ // 8
             F = 32 if wl.k_mode == "channel" else 1
             assert lay["flush_tokens"] == F
-            wcap = -(-(wl.window + F) // F) * F
-            assert lay["window_cap"] == wcap
+            wcap = -(-(wl.window + F) // 32) * 32
+            scap = -(-wl.sinks // 32) * 32
+            assert lay["window_cap"] == wcap and lay["sink_cap"] == scap
             sizes = K.kvq_layer_buffer_sizes(h, l)
             assert sizes[0] == units * (-(-max_tokens // 32)) * rec
-            assert sizes[1] == units * 2 * (wl.sinks + wcap) * 128 * 2
+            assert sizes[1] == units * 2 * (scap + wcap) * 128 * 2
         assert K.kvq_workspace_size(h) > 0
     finally:
         K.kvq_destroy(h)
