@@ -29,9 +29,17 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
+# Per-source additions.  The matrix-core decode keeps its MFMA accumulators
+# in ordinary VGPRs: it rescales and reads them on the VALU every block, and
+# accumulation registers would cost a copy each way.
+EXTRA = {
+    "kvq_decode_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -1,25 +1,31 @@
 // kvq_decode_fast.hip -- matrix-core (MFMA) split-context decode over the
 // packed cache for uniform 2/4/8-bit keys and values.
 //
-// One wavefront per split.  A 32-token block is two 16-token tiles:
-//   scores  S[r][t] = sum_c A[r][c] B[c][t] with v_mfma_f32_16x16x32_f16, where
-//           B holds the codes as fp16 subnormals (bit pattern = code, value
-//           code * 2^-24: exact in the MFMA, no offset to undo) and
-//           A = fp16(q * s) when keys have one scale per channel per block
-//           (KVTuner obs. 2 / KVQuant (i)); the zero points enter as the
-//           per-row constant sum_c q_c z_c.  For InnerQ inner-dimension groups
-//           (per-token scales) A = q and the group sums are scaled afterwards.
+// One wavefront per split; a 32-token block is two 16-token tiles.
+//   scores  S[r][t] = sum_c A[r][c] B[c][t] with v_mfma_f32_16x16x32_f16.  B
+//           holds the codes as normal fp16 values base + code / inv_unit
+//           (every product exact); with one key scale per channel per block
+//           (KVTuner obs. 2 / KVQuant (i)) A = q * s as an exact fp16 hi + lo
+//           pair, and the offset and the zero points enter through one more
+//           MFMA against the block's (z, s) columns.  For InnerQ inner-dimension
+//           groups (per-token scales) A = q and the group sums are scaled
+//           afterwards.
 //   values  O[r][c] += sum_t (p[r][t] * s[t][g]) code[t][c]: per-token value
-//           scales (RateQuant sec. 3, KIVI layout) fold into P; the zero points
-//           sum_t p z are one more MFMA against the block's z column.
-//   online softmax in the log2 domain; splits merged by log-sum-exp in the
-//   last wavefront of each unit; Hadamard-rotated values unrotated there.
-// Only the first G rows of the 16-row MFMA tiles carry queries (the GQA group
-// of a kv head); keys of one block are read once for all of them.
+//           scales (KIVI layout) fold into P as an exact hi + lo pair; the zero
+//           points and the code offset are one more MFMA against the block's
+//           (z, s) columns.
+//   online softmax in the log2 domain; P is rounded to fp16 once and the
+//   denominator sums the same rounded weights.
+// Only the first G rows of the 16-row tiles carry queries (the GQA group of a
+// kv head); the keys and values of a block are read once for all of them.
 // Block records stream HBM -> LDS with global_load_lds_dwordx4 into a ring of
-// NBUF slots, NBUF-1 blocks ahead of the one being computed, so memory
-// latency hides behind the MFMA/VALU work without holding data in VGPRs.
+// NBUF slots, NBUF-1 blocks ahead of the one being computed.  Sink / window
+// tokens (fp16) are read straight into registers.  Each split writes an
+// (o, max, sum) partial; decode_merge_kernel combines them by log-sum-exp and
+// undoes the value rotation.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -50,64 +56,85 @@ __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<c
 
 // ---- code words -> eight fp16 code values, K-order = element order.
 // 2-bit codes become 1 + c/4 and 4-bit codes 1 + c/16 (code bits placed at
-// the top of the fp16 mantissa under the exponent of 1.0: one and-or per word);
-// 8-bit codes become the integer c.  Normal fp16 operands keep every MFMA
-// product exact; the constant offset (base * sum of A) is removed afterwards.
+// the top of the fp16 mantissa under the exponent of 1.0: a shift and one
+// v_and_or_b32 per output word); 8-bit codes become 1024 + c (one byte
+// permute per output word against a register of 0x64 exponent bytes).
+// Normal fp16 operands keep every MFMA product exact; the constant offset
+// (base * sum of A) is removed afterwards.
 template <int B> struct CodeEnc;
 template <> struct CodeEnc<2> { static constexpr float base = 1.f, inv_unit = 4.f; };
 template <> struct CodeEnc<4> { static constexpr float base = 1.f, inv_unit = 16.f; };
-template <> struct CodeEnc<8> { static constexpr float base = 0.f, inv_unit = 1.f; };
+template <> struct CodeEnc<8> { static constexpr float base = 1024.f, inv_unit = 1.f; };
 
+// Loop-invariant unpack constants, held in registers (the VOP3 forms take
+// no literal operands) and made opaque once, so that the and-or pairs are
+// selected as single v_and_or_b32 and the constants are not rematerialised.
+struct Unpack {
+  uint32_t m4, m2, e8;  // VGPRs
+  uint32_t one2;        // SGPR: fp16 1.0 in both halves
+};
 __device__ __forceinline__ uint32_t andor(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
-__device__ __forceinline__ half8 ex4(uint32_t x) {
-  constexpr uint32_t M = 0x03C003C0u, O = 0x3C003C00u;
-  return h8(andor(x << 6, M, O), andor(x << 2, M, O), andor(x >> 2, M, O), andor(x >> 6, M, O));
+__device__ __forceinline__ half8 ex4(const Unpack& k, uint32_t x) {
+  return h8(andor(x << 6, k.m4, k.one2), andor(x << 2, k.m4, k.one2), andor(x >> 2, k.m4, k.one2),
+            andor(x >> 6, k.m4, k.one2));
 }
 template <int E>
-__device__ __forceinline__ half8 ex2(uint32_t x) {
-  constexpr uint32_t M = 0x03000300u, O = 0x3C003C00u;
+__device__ __forceinline__ half8 ex2(const Unpack& k, uint32_t x) {
   if constexpr (E == 0)
-    return h8(andor(x << 8, M, O), andor(x << 6, M, O), andor(x << 4, M, O), andor(x << 2, M, O));
+    return h8(andor(x << 8, k.m2, k.one2), andor(x << 6, k.m2, k.one2), andor(x << 4, k.m2, k.one2),
+              andor(x << 2, k.m2, k.one2));
   else
-    return h8(andor(x, M, O), andor(x >> 2, M, O), andor(x >> 4, M, O), andor(x >> 6, M, O));
+    return h8(andor(x, k.m2, k.one2), andor(x >> 2, k.m2, k.one2), andor(x >> 4, k.m2, k.one2),
+              andor(x >> 6, k.m2, k.one2));
 }
-__device__ __forceinline__ uint32_t u8pair(uint32_t x, int sh) {
-  const float a = static_cast<float>((x >> sh) & 0xffu);
-  const float b = static_cast<float>((x >> (sh + 8)) & 0xffu);
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+// bytes b0, b1 (sh = 0) or b2, b3 (sh = 16) of x as fp16 1024 + b
+__device__ __forceinline__ uint32_t u8pair(const Unpack& k, uint32_t x, int sh) {
+  return __builtin_amdgcn_perm(k.e8, x, sh == 0 ? 0x04010400u : 0x04030402u);
 }
-__device__ __forceinline__ half8 ex8(uint32_t x, uint32_t y) {
-  return h8(u8pair(x, 0), u8pair(x, 16), u8pair(y, 0), u8pair(y, 16));
+__device__ __forceinline__ half8 ex8(const Unpack& k, uint32_t x, uint32_t y) {
+  return h8(u8pair(k, x, 0), u8pair(k, x, 16), u8pair(k, y, 0), u8pair(k, y, 16));
 }
 
 // B operand of K-step j from a lane's key chunk (32 channels, KB bits each)
 template <int KB>
-__device__ __forceinline__ half8 kstep(const uint32_t* w, int j) {
-  if constexpr (KB == 4) return ex4(w[j]);
-  if constexpr (KB == 2) return (j & 1) ? ex2<1>(w[j >> 1]) : ex2<0>(w[j >> 1]);
-  if constexpr (KB == 8) return ex8(w[2 * j], w[2 * j + 1]);
+__device__ __forceinline__ half8 kstep(const Unpack& k, const uint32_t* w, int j) {
+  if constexpr (KB == 4) return ex4(k, w[j]);
+  if constexpr (KB == 2) return (j & 1) ? ex2<1>(k, w[j >> 1]) : ex2<0>(k, w[j >> 1]);
+  if constexpr (KB == 8) return ex8(k, w[2 * j], w[2 * j + 1]);
 }
 // B operand of value N-tile nt from a lane's value chunk
 template <int VB>
-__device__ __forceinline__ half8 vtile(const uint32_t* w, int nt) {
-  if constexpr (VB == 4) return ex4(w[nt]);
-  if constexpr (VB == 2) return (nt & 1) ? ex2<1>(w[nt >> 1]) : ex2<0>(w[nt >> 1]);
-  if constexpr (VB == 8) return ex8(w[2 * nt], w[2 * nt + 1]);
+__device__ __forceinline__ half8 vtile(const Unpack& k, const uint32_t* w, int nt) {
+  if constexpr (VB == 4) return ex4(k, w[nt]);
+  if constexpr (VB == 2) return (nt & 1) ? ex2<1>(k, w[nt >> 1]) : ex2<0>(k, w[nt >> 1]);
+  if constexpr (VB == 8) return ex8(k, w[2 * nt], w[2 * nt + 1]);
 }
 
-template <int W>
+// 2^x with the hardware approximation (v_exp_f32, about 1 ulp); inputs are
+// <= 0 here and results that would be fp32 subnormal only ever weigh tokens
+// far below fp16 resolution of the row maximum
+__device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Cross-lane steps inside rows of 16 lanes as DPP moves (VALU latency, no
+// LDS round trip): quad permutes for xor 1 / xor 2, row rotations by 4 and 8
+// (a rotation by 8 inside a 16-lane row is xor 8).
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
 __device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, xshflf<1>(v));
-  v = fmaxf(v, xshflf<2>(v));
-  v = fmaxf(v, xshflf<4>(v));
-  v = fmaxf(v, xshflf<8>(v));
+  v = fmaxf(v, dppf<kQuadXor1>(v));
+  v = fmaxf(v, dppf<kQuadXor2>(v));
+  v = fmaxf(v, dppf<kRowRor4>(v));
+  v = fmaxf(v, dppf<kRowRor8>(v));
   return v;
 }
 __device__ __forceinline__ float row16_sum(float v) {
-  v += xshflf<1>(v);
-  v += xshflf<2>(v);
-  v += xshflf<4>(v);
-  v += xshflf<8>(v);
+  v += dppf<kQuadXor1>(v);
+  v += dppf<kQuadXor2>(v);
+  v += dppf<kRowRor4>(v);
+  v += dppf<kRowRor8>(v);
   return v;
 }
 __device__ __forceinline__ float lane_bcast(float v, int src) {
@@ -142,7 +169,8 @@ struct Rec {
 // DMA writes precisely (it would drain every in-flight block), so the ring is
 // guarded by explicit vmcnt waits, and each batch of reads is completed by
 // lds_done(), which pins the loaded registers behind an lgkmcnt(0) wait.
-__device__ __forceinline__ uint32_t lds_off(const void* p) {
+typedef __attribute__((address_space(3))) uint8_t lds_u8;  // LDS byte (no generic-pointer checks)
+__device__ __forceinline__ uint32_t lds_off(const lds_u8* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 template <int OFF>
@@ -167,24 +195,24 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// device-coherent loads of split records written by other wavefronts
-__device__ __forceinline__ float ldc(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t ldc2(const float* p) {
-  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 template <int KB, int VB, int G, bool INNER, int NBUF>
 __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   using R = Rec<KB, VB, INNER>;
   // one LDS object per ring slot: the compiler then tells the slots apart and
   // keeps the partial vmcnt waits instead of draining every in-flight load
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 slots");
   __shared__ __attribute__((aligned(16))) uint8_t ring0[R::loads * 1024];
   __shared__ __attribute__((aligned(16))) uint8_t ring1[R::loads * 1024];
-  __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF == 3 ? R::loads * 1024 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF >= 3 ? R::loads * 1024 : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t ring3[NBUF >= 4 ? R::loads * 1024 : 16];
+  lds_u8* const slot0 = (lds_u8*)ring0;
+  lds_u8* const slot1 = (lds_u8*)ring1;
+  lds_u8* const slot2 = (lds_u8*)ring2;
+  lds_u8* const slot3 = (lds_u8*)ring3;
+  auto slot_at = [&](int k) __attribute__((always_inline)) {
+    return k == 0 ? slot0 : (k == 1 ? slot1 : (k == 2 ? slot2 : slot3));
+  };
   __shared__ __attribute__((aligned(16))) _Float16 ptile[16][32];
-  __shared__ float wsplit[kMaxBodySplits + kMaxFp16Splits];
   const int l = threadIdx.x;
   const int n16 = l & 15, g4 = l >> 4;
   const int nsplit = J.nsplit;
@@ -195,6 +223,11 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   constexpr int RI = G < 4 ? G : 4;           // output rows per lane (registers)
   const bool rows_here = 4 * g4 < G;           // lane holds real query rows
   constexpr int ngv = D / 32;                  // value groups of 32 channels
+  Unpack unp{0x03C003C0u, 0x03000300u, 0x64646464u, 0x3C003C00u};
+  pin(unp.m4);
+  pin(unp.m2);
+  pin(unp.e8);
+  asm volatile("" : "+s"(unp.one2));
 
   // ---- query operand (natural channel order per K-step)
   half8 qa[4];
@@ -239,22 +272,24 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   // online softmax of one 32-token tile; P (fp16) lands in ptile, the
   // accumulators are rescaled; returns nothing, reads sacc
   auto softmax_tile = [&](f32x4 (&sacc)[2], int count) __attribute__((always_inline)) -> half8 {
+    if (count < kBlockTokens) {  // wave-uniform: only a partial last block
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-      if (16 * nt + n16 >= count)
+      for (int nt = 0; nt < 2; ++nt)
+        if (16 * nt + n16 >= count)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[nt][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) sacc[nt][i] = -INFINITY;
+    }
     float alpha[RI];
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
-      const float bm = row16_max<16>(fmaxf(sacc[0][i], sacc[1][i]));
+      const float bm = row16_max(fmaxf(sacc[0][i], sacc[1][i]));
       const float mn = fmaxf(m_run[i], bm);
       const float mr = mn == -INFINITY ? 0.f : mn;  // nothing live yet: weights 0
-      alpha[i] = exp2f(m_run[i] - mr);
+      alpha[i] = fexp2(m_run[i] - mr);
       // P is used as fp16 in every product; the denominator sums the same
       // rounded weights so numerator and denominator stay consistent
-      const _Float16 p0 = static_cast<_Float16>(exp2f(sacc[0][i] - mr));
-      const _Float16 p1 = static_cast<_Float16>(exp2f(sacc[1][i] - mr));
+      const _Float16 p0 = static_cast<_Float16>(fexp2(sacc[0][i] - mr));
+      const _Float16 p1 = static_cast<_Float16>(fexp2(sacc[1][i] - mr));
       l_run[i] = fmaf(l_run[i], alpha[i], static_cast<float>(p0) + static_cast<float>(p1));
       m_run[i] = mn;
       if (rows_here) {
@@ -262,12 +297,19 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
         ptile[4 * g4 + i][16 + n16] = p1;
       }
     }
+    // the running max moves rarely once a few tiles are in: the (exact)
+    // rescale by alpha = 1 is skipped unless some row of the wave moved
+    bool moved = false;
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int i = 0; i < RI; ++i) moved |= alpha[i] != 1.f;
+    if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-      for (int i = 0; i < RI; ++i) oacc[nt][i] *= alpha[i];
+      for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-    for (int i = 0; i < RI; ++i) zacc[i] *= alpha[i];
+        for (int i = 0; i < RI; ++i) oacc[nt][i] *= alpha[i];
+#pragma unroll
+      for (int i = 0; i < RI; ++i) zacc[i] *= alpha[i];
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -275,7 +317,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   };
 
   // one quantized block whose record sits in LDS at rec
-  auto body_block = [&](const uint8_t* rec, int count) __attribute__((always_inline)) {
+  auto body_block = [&](const lds_u8* rec, int count) __attribute__((always_inline)) {
     const uint32_t r0 = lds_off(rec);
     f32x4 sacc[2];
     // ---------------- keys: one batch of LDS reads
@@ -341,7 +383,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       f32x4 init;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float other = xshflf<8>(cacc[i]);
+        const float other = dppf<kRowRor8>(cacc[i]);
         const float cz = n16 < 8 ? cacc[i] : other;
         const float cs = n16 < 8 ? other : cacc[i];
         init[i] = fmaf(cz, 1.f / iu, -base * cs);
@@ -355,7 +397,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
         const half8 ql = __builtin_elementwise_fma(qa[j], s8, -qh);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          const half8 bk = kstep<KB>(kw[nt], j);
+          const half8 bk = kstep<KB>(unp, kw[nt], j);
           sacc[nt] = mfma(qh, bk, sacc[nt]);
           sacc[nt] = mfma(ql, bk, sacc[nt]);
         }
@@ -371,10 +413,10 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
-        p0 = mfma(qa[0], kstep<KB>(kw[nt], 0), p0);
-        p0 = mfma(qa[1], kstep<KB>(kw[nt], 1), p0);
-        p1 = mfma(qa[2], kstep<KB>(kw[nt], 2), p1);
-        p1 = mfma(qa[3], kstep<KB>(kw[nt], 3), p1);
+        p0 = mfma(qa[0], kstep<KB>(unp, kw[nt], 0), p0);
+        p0 = mfma(qa[1], kstep<KB>(unp, kw[nt], 1), p0);
+        p1 = mfma(qa[2], kstep<KB>(unp, kw[nt], 2), p1);
+        p1 = mfma(qa[3], kstep<KB>(unp, kw[nt], 3), p1);
         const u32x2 mm = imeta[nt];  // (s0, z0), (s1, z1) of token 16 nt + n16
         float sg[2], zg[2];
 #pragma unroll
@@ -433,7 +475,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int nt = 2 * g + t;
-        const half8 bv = vtile<VB>(vw, nt);
+        const half8 bv = vtile<VB>(unp, vw, nt);
         oacc[nt] = mfma(wh, bv, oacc[nt]);
         oacc[nt] = mfma(wl, bv, oacc[nt]);
       }
@@ -446,7 +488,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   const int c_end = sp < J.nsplit_body ? min(nblk_body, c_begin + J.blocks_per_split) : c_begin;
   const int nmy = c_end - c_begin;
   const uint8_t* ubase = L.body + static_cast<int64_t>(u) * L.nblk_cap * L.rec_bytes;
-  auto issue = [&](int i, uint8_t* dst) __attribute__((always_inline)) {
+  auto issue = [&](int i, lds_u8* dst) __attribute__((always_inline)) {
     const uint8_t* src = ubase + static_cast<int64_t>(c_begin + i) * L.rec_bytes;
 #pragma unroll
     for (int k = 0; k < R::loads; ++k) {
@@ -454,8 +496,9 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
     }
   };
-  if (nmy > 0) issue(0, ring0);
-  if (NBUF == 3 && nmy > 1) issue(1, ring1);
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (k < nmy) issue(k, slot_at(k));
 
   // ---------------- sink / window tokens: fp16 operands as stored, one
   // 32-slot chunk at a time (slots without a live token are masked).  They
@@ -512,7 +555,23 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     // block i sits in slot i % NBUF.  Steady state: every step issues block
     // i + NBUF - 1 and waits until only the (NBUF - 1) newer blocks are in
     // flight, so the waits are the same on every path.  The tail drains.
-    auto step = [&](int i, uint8_t* cur, uint8_t* ahead) __attribute__((always_inline)) {
+    // Wavefronts sharing a SIMD are picked oldest first, so without help the
+    // last one dispatched finishes long after the others.  Each wavefront
+    // lowers its priority as it gets through its blocks: one that is ahead
+    // yields to those behind and the SIMD's wavefronts finish together.
+    int prio_q = 0;
+    auto age = [&](int i) __attribute__((always_inline)) {
+      const int q = (4 * i) / nmy;
+      if (q != prio_q) {
+        prio_q = q;
+        if (q == 1) __builtin_amdgcn_s_setprio(2);
+        else if (q == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    };
+    __builtin_amdgcn_s_setprio(3);
+    auto step = [&](int i, lds_u8* cur, lds_u8* ahead) __attribute__((always_inline)) {
+      age(i);
       issue(i + NBUF - 1, ahead);
       wait_vm<(NBUF - 1) * R::loads>();
       const int ch = c_begin + i;
@@ -520,35 +579,48 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     };
     int i = 0;
     for (; i + 2 * NBUF - 2 < nmy; i += NBUF) {
-      if constexpr (NBUF == 3) {
-        step(i, ring0, ring2);
-        step(i + 1, ring1, ring0);
-        step(i + 2, ring2, ring1);
+      if constexpr (NBUF == 4) {
+        step(i, slot0, slot3);
+        step(i + 1, slot1, slot0);
+        step(i + 2, slot2, slot1);
+        step(i + 3, slot3, slot2);
+      } else if constexpr (NBUF == 3) {
+        step(i, slot0, slot2);
+        step(i + 1, slot1, slot0);
+        step(i + 2, slot2, slot1);
       } else {
-        step(i, ring0, ring1);
-        step(i + 1, ring1, ring0);
+        step(i, slot0, slot1);
+        step(i + 1, slot1, slot0);
       }
     }
     for (; i < nmy; ++i) {
+      age(i);
       // remaining blocks: issue what is still missing, then drain in order
       const int ahead = i + NBUF - 1;
       if (ahead < nmy) {
         const int s_ah = ahead % NBUF;
-        issue(ahead, s_ah == 0 ? ring0 : (s_ah == 1 ? ring1 : ring2));
+        issue(ahead, slot_at(s_ah));
       }
-      wait_vm<0>();
+      // wait for block i only: the blocks issued after it stay in flight
+      const int newer = min(NBUF - 1, nmy - 1 - i);
+      if (NBUF >= 4 && newer >= 3)
+        wait_vm<(NBUF >= 4 ? 3 : 0) * R::loads>();
+      else if (NBUF >= 3 && newer >= 2)
+        wait_vm<(NBUF >= 3 ? 2 : 0) * R::loads>();
+      else if (newer >= 1)
+        wait_vm<R::loads>();
+      else
+        wait_vm<0>();
       const int s_cur = i % NBUF;
       const int ch = c_begin + i;
-      body_block(s_cur == 0 ? ring0 : (s_cur == 1 ? ring1 : ring2),
+      body_block(slot_at(s_cur),
                  min(kBlockTokens, st.nb - ch * kBlockTokens));
     }
   }
 
-  // ---------------- partial of this split: o = (O_raw - base * W_g) * inv_unit + Z_g
-  // The records are written with device-coherent stores, their completion
-  // is awaited, and only then is the unit's counter bumped; the wavefront
-  // that sees the last count reads them back with device-coherent loads.
-  // No cache write-back of the whole L2 is needed for this hand-over.
+  __builtin_amdgcn_s_setprio(0);
+  // ---------------- partial of this split: o = (O_raw - base * W_g) * inv_unit + Z_g,
+  // merged by decode_merge_kernel (launched next on the same stream)
   float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * G * D;
   float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * G * 2;
 #pragma unroll
@@ -560,115 +632,161 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       const float z = lane_bcast(zacc[i], (l & 48) | (nt >> 1));
       const float w = lane_bcast(zacc[i], (l & 48) | (4 + (nt >> 1)));
       const float o = fmaf(fmaf(-vbase, w, oacc[nt][i]), viu, z);
-      if (rows_here && row < G)
-        __hip_atomic_store(opart + row * D + 16 * nt + n16, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (rows_here && row < G) opart[row * D + 16 * nt + n16] = o;
     }
     if (rows_here && row < G && n16 == 0) {
-      __hip_atomic_store(mlpart + row * 2, m_run[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(mlpart + row * 2 + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      mlpart[row * 2] = m_run[i];
+      mlpart[row * 2 + 1] = lsum;
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  uint32_t prev = 0;
-  if (l == 0) prev = __hip_atomic_fetch_add(J.counters + u, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __builtin_amdgcn_readfirstlane(prev);
-  if (prev != static_cast<uint32_t>(nsplit - 1)) return;
-  asm volatile("" ::: "memory");
-
-  // ---------------- log-sum-exp merge (this wavefront is the last of the unit)
-  // split scalars are spread over lanes; every partial vector is requested
-  // before any is consumed, so the merge costs a few memory round trips
-  const float* obase = J.partials + static_cast<int64_t>(u) * nsplit * G * D;
-  const float* mlbase = J.partials + J.ml_off + static_cast<int64_t>(u) * nsplit * G * 2;
-  for (int r = 0; r < G; ++r) {
-    float M = -INFINITY;
-    for (int i = l; i < nsplit; i += 64) M = fmaxf(M, ldc(mlbase + (i * G + r) * 2));
-    M = fmaxf(M, xshflf<1>(M));
-    M = fmaxf(M, xshflf<2>(M));
-    M = fmaxf(M, xshflf<4>(M));
-    M = fmaxf(M, xshflf<8>(M));
-    M = fmaxf(M, xshflf<16>(M));
-    M = fmaxf(M, xshflf<32>(M));
-    float Lp = 0.f;
-    for (int i = l; i < nsplit; i += 64) {
-      const float mi = ldc(mlbase + (i * G + r) * 2);
-      const float w = mi == -INFINITY ? 0.f : exp2f(mi - M);
-      Lp = fmaf(ldc(mlbase + (i * G + r) * 2 + 1), w, Lp);
-      wsplit[i] = w;
-    }
-    Lp += xshflf<1>(Lp);
-    Lp += xshflf<2>(Lp);
-    Lp += xshflf<4>(Lp);
-    Lp += xshflf<8>(Lp);
-    Lp += xshflf<16>(Lp);
-    Lp += xshflf<32>(Lp);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float a0 = 0.f, a1 = 0.f;
-    int i = 0;
-    for (; i + 8 <= nsplit; i += 8) {
-      uint64_t v[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = ldc2(obase + ((i + k) * G + r) * D + 2 * l);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float w = wsplit[i + k];
-        a0 = fmaf(__uint_as_float(static_cast<uint32_t>(v[k])), w, a0);
-        a1 = fmaf(__uint_as_float(static_cast<uint32_t>(v[k] >> 32)), w, a1);
-      }
-    }
-    for (; i < nsplit; ++i) {
-      const uint64_t v = ldc2(obase + (i * G + r) * D + 2 * l);
-      const float w = wsplit[i];
-      a0 = fmaf(__uint_as_float(static_cast<uint32_t>(v)), w, a0);
-      a1 = fmaf(__uint_as_float(static_cast<uint32_t>(v >> 32)), w, a1);
-    }
-    float y0 = a0 / Lp, y1 = a1 / Lp;
-    if (L.v_had) {
-      // c * H * o with H the Sylvester matrix; lane l holds channels 2l, 2l+1
-      const float t0 = y0 + y1, t1 = y0 - y1;
-      y0 = t0;
-      y1 = t1;
-#pragma unroll
-      for (int hb = 1; hb < 64; hb <<= 1) {
-        const float o0 = __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ hb) << 2, __float_as_int(y0)));
-        const float o1 = __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ hb) << 2, __float_as_int(y1)));
-        const bool hi = (l & hb) != 0;
-        y0 = hi ? o0 - y0 : y0 + o0;
-        y1 = hi ? o1 - y1 : y1 + o1;
-      }
-      const float c = static_cast<float>(L.had_scale);
-      y0 *= c;
-      y1 *= c;
-    }
-    float* op = J.out + (static_cast<int64_t>(b) * L.Hq + h * G + r) * D;
-    op[2 * l] = y0;
-    op[2 * l + 1] = y1;
-    __builtin_amdgcn_wave_barrier();
-  }
-  if (l == 0) J.counters[u] = 0;
 }
 
+// Log-sum-exp merge of the split partials of one (unit, query row): four
+// wavefronts share the splits, every partial vector of a wavefront is
+// requested before it is consumed, and the four sums meet in LDS.  Values
+// stored Hadamard-rotated are rotated back here (c * H * o, H Sylvester).
+__global__ void __launch_bounds__(256) decode_merge_kernel(LayerDesc L, DecodeJob J) {
+  constexpr int kMaxSplits = kMaxBodySplits + kMaxFp16Splits;
+  __shared__ float wts[kMaxSplits];
+  __shared__ float red[4][D];
+  __shared__ float scal[2][4];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int u = blockIdx.x, r = blockIdx.y;
+  const int G = L.G, nsplit = J.nsplit;
+  const int b = u / L.Hkv, h = u % L.Hkv;
+  const float* obase = J.partials + static_cast<int64_t>(u) * nsplit * G * D;
+  const float* mlbase = J.partials + J.ml_off + static_cast<int64_t>(u) * nsplit * G * 2;
+
+  // this wavefront's partial vectors (splits w, w + 4, ...), first batch in flight early
+  constexpr int kBatch = 16;
+  u32x2 v[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int i = w + 4 * k;
+    v[k] = i < nsplit ? ld8(obase + (static_cast<int64_t>(i) * G + r) * D + 2 * l) : u32x2{0u, 0u};
+  }
+  // global max and weights
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
+  if (tid < nsplit) { m0 = mlbase[(tid * G + r) * 2]; l0 = mlbase[(tid * G + r) * 2 + 1]; }
+  if (tid + 256 < nsplit) { m1 = mlbase[((tid + 256) * G + r) * 2]; l1 = mlbase[((tid + 256) * G + r) * 2 + 1]; }
+  float M = fmaxf(m0, m1);
+  M = fmaxf(M, xshflf<1>(M));
+  M = fmaxf(M, xshflf<2>(M));
+  M = fmaxf(M, xshflf<4>(M));
+  M = fmaxf(M, xshflf<8>(M));
+  M = fmaxf(M, xshflf<16>(M));
+  M = fmaxf(M, xshflf<32>(M));
+  if (l == 0) scal[0][w] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(scal[0][0], scal[0][1]), fmaxf(scal[0][2], scal[0][3]));
+  const float w0 = m0 == -INFINITY ? 0.f : exp2f(m0 - M);
+  const float w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
+  if (tid < nsplit) wts[tid] = w0;
+  if (tid + 256 < nsplit) wts[tid + 256] = w1;
+  float Ls = fmaf(l0, w0, l1 * w1);
+  Ls += xshflf<1>(Ls);
+  Ls += xshflf<2>(Ls);
+  Ls += xshflf<4>(Ls);
+  Ls += xshflf<8>(Ls);
+  Ls += xshflf<16>(Ls);
+  Ls += xshflf<32>(Ls);
+  if (l == 0) scal[1][w] = Ls;
+  __syncthreads();
+  // weighted sum of this wavefront's partials
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int i = w + 4 * k;
+    const float wt = i < nsplit ? wts[i] : 0.f;
+    a0 = fmaf(__uint_as_float(v[k][0]), wt, a0);
+    a1 = fmaf(__uint_as_float(v[k][1]), wt, a1);
+  }
+  for (int i0 = 4 * kBatch; i0 < nsplit; i0 += 4 * kBatch) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + w + 4 * k;
+      v[k] = i < nsplit ? ld8(obase + (static_cast<int64_t>(i) * G + r) * D + 2 * l) : u32x2{0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int i = i0 + w + 4 * k;
+      const float wt = i < nsplit ? wts[i] : 0.f;
+      a0 = fmaf(__uint_as_float(v[k][0]), wt, a0);
+      a1 = fmaf(__uint_as_float(v[k][1]), wt, a1);
+    }
+  }
+  red[w][2 * l] = a0;
+  red[w][2 * l + 1] = a1;
+  __syncthreads();
+  if (w != 0) return;
+  const float Lt = (scal[1][0] + scal[1][1]) + (scal[1][2] + scal[1][3]);
+  float y0 = ((red[0][2 * l] + red[1][2 * l]) + (red[2][2 * l] + red[3][2 * l])) / Lt;
+  float y1 = ((red[0][2 * l + 1] + red[1][2 * l + 1]) + (red[2][2 * l + 1] + red[3][2 * l + 1])) / Lt;
+  if (L.v_had) {
+    // lane l holds channels 2l, 2l+1: the first butterfly is in-lane
+    const float t0 = y0 + y1, t1 = y0 - y1;
+    y0 = t0;
+    y1 = t1;
+#pragma unroll
+    for (int hb = 1; hb < 64; hb <<= 1) {
+      const float o0 = __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ hb) << 2, __float_as_int(y0)));
+      const float o1 = __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ hb) << 2, __float_as_int(y1)));
+      const bool hi = (l & hb) != 0;
+      y0 = hi ? o0 - y0 : y0 + o0;
+      y1 = hi ? o1 - y1 : y1 + o1;
+    }
+    const float c = static_cast<float>(L.had_scale);
+    y0 *= c;
+    y1 *= c;
+  }
+  float* op = J.out + (static_cast<int64_t>(b) * L.Hq + h * G + r) * D;
+  op[2 * l] = y0;
+  op[2 * l + 1] = y1;
+}
+
+// Ring depth and residency.  MHA layers (one query row per kv head) carry
+// the fewest registers and can run three wavefronts per SIMD, GQA layers two.
+// The ring takes as many slots (2..4) as the LDS share of that many
+// wavefronts allows: deeper rings keep more blocks in flight behind the
+// VALU / MFMA work of the block being computed.
+constexpr int kLdsPerCu = 160 * 1024;
 template <int KB, int VB, int G, bool INNER>
-hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* used) {
+constexpr int ring_slots() {
+  constexpr int waves = G == 1 ? 12 : 8;
+  constexpr int budget = kLdsPerCu / waves - 16 * 32 * 2 - 512;
+  constexpr int n = budget / (Rec<KB, VB, INNER>::loads * 1024);
+  return n < 2 ? 2 : (n > 4 ? 4 : n);
+}
+template <int KB, int VB, int G, bool INNER>
+hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
   using R = Rec<KB, VB, INNER>;
   if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm) return hipSuccess;
-  *used = true;
-  const int nsplit = j.nsplit;
-  // ring depth: two blocks in flight when records are small, one otherwise
-  if constexpr (R::loads <= 5)
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, 3>), dim3(nsplit, L.units), dim3(64), 0, s, L, j);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, 2>), dim3(nsplit, L.units), dim3(64), 0, s, L, j);
+  constexpr int NB = ring_slots<KB, VB, G, INNER>();
+  // one full round of resident wavefronts, from the runtime's occupancy of
+  // this instance (registers and LDS as compiled) and the device's CU count
+  static int resident = 0;
+  if (resident == 0) {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<KB, VB, G, INNER, NB>, 64, 0) !=
+            hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    resident = std::max(1, per_cu) * std::max(1, cus);
+  }
+  *waves = resident;
+  if (!j.q) return hipSuccess;  // query only
+  hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, NB>), dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(L.units, G), dim3(256), 0, s, L, j);
   return hipGetLastError();
 }
 
 template <int G, bool INNER>
-hipError_t by_bits(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* used) {
+hipError_t by_bits(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
   const int k = L.kb, v = L.vb;
 #define KVQ_CASE(KB, VB) \
-  if (k == KB && v == VB) return launch_t<KB, VB, G, INNER>(L, j, s, used);
+  if (k == KB && v == VB) return launch_t<KB, VB, G, INNER>(L, j, s, waves);
   if constexpr (INNER) {
     KVQ_CASE(4, 2) KVQ_CASE(4, 4)
   } else {
@@ -680,19 +798,33 @@ hipError_t by_bits(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* 
   return hipSuccess;
 }
 
-}  // namespace
-
-hipError_t launch_decode_fast(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* used) {
-  *used = false;
+hipError_t dispatch(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
+  *waves = 0;
   if (L.nuq || L.outk || L.pre_rope || (L.k_hybrid && !L.k_inner)) return hipSuccess;
   if (L.k_inner && L.k_group != 64) return hipSuccess;
   if (L.v_group != 32) return hipSuccess;
   switch (L.G) {
-    case 1: return L.k_inner ? by_bits<1, true>(L, j, s, used) : by_bits<1, false>(L, j, s, used);
-    case 4: return L.k_inner ? by_bits<4, true>(L, j, s, used) : by_bits<4, false>(L, j, s, used);
-    case 8: return L.k_inner ? by_bits<8, true>(L, j, s, used) : by_bits<8, false>(L, j, s, used);
+    case 1: return L.k_inner ? by_bits<1, true>(L, j, s, waves) : by_bits<1, false>(L, j, s, waves);
+    case 4: return L.k_inner ? by_bits<4, true>(L, j, s, waves) : by_bits<4, false>(L, j, s, waves);
+    case 8: return L.k_inner ? by_bits<8, true>(L, j, s, waves) : by_bits<8, false>(L, j, s, waves);
     default: return hipSuccess;
   }
+}
+
+}  // namespace
+
+int decode_fast_waves(const LayerDesc& L) {
+  DecodeJob none{};
+  int waves = 0;
+  dispatch(L, none, nullptr, &waves);
+  return waves;
+}
+
+hipError_t launch_decode_fast(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* used) {
+  int waves = 0;
+  const hipError_t e = dispatch(L, j, s, &waves);
+  *used = waves > 0;
+  return e;
 }
 
 }  // namespace kvq

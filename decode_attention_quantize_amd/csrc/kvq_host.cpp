@@ -15,6 +15,7 @@
 namespace kvq {
 hipError_t launch_decode_generic(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
 hipError_t launch_decode_fast(const LayerDesc& L, const DecodeJob& job, hipStream_t s, bool* used);
+int decode_fast_waves(const LayerDesc& L);  // resident wavefront target, 0 if the layer is not covered
 }  // namespace kvq
 
 using kvq::LayerDesc;
@@ -22,7 +23,6 @@ using kvq::LayerDesc;
 namespace {
 
 constexpr int kD = kvq::kHeadDim;
-constexpr int kMaxSplits = kvq::kMaxBodySplits + kvq::kMaxFp16Splits;
 
 struct Layer {
   LayerDesc d{};
@@ -105,10 +105,12 @@ bool valid_layer(const kvq_cache* c, int32_t layer) {
 }
 
 // Split plan.  The matrix-core path runs one wavefront per split and aims at
-// one full round of resident wavefronts (about 2048 on 256 CUs at two waves
-// per SIMD); the 32-slot sink / window chunks ride along on the first splits.
+// one full round of resident wavefronts (fast_waves, from the kernel's ring
+// depth and register budget); the 32-slot sink / window chunks ride along on
+// the first splits.
 // The LDS-staged path walks the sink / window tokens in one extra split.
-void plan_splits(const kvq_cache& c, const kvq::TokenState& st, bool fast, kvq::DecodeJob& j) {
+void plan_splits(const kvq_cache& c, const kvq::TokenState& st, int fast_waves, kvq::DecodeJob& j) {
+  const bool fast = fast_waves > 0;
   const int nblk = (st.nb + kvq::kBlockTokens - 1) / kvq::kBlockTokens;
   j.fp16_split = 0;
   j.fp16_chunks = j.sink_chunks = j.win_chunk0 = 0;
@@ -131,7 +133,7 @@ void plan_splits(const kvq_cache& c, const kvq::TokenState& st, bool fast, kvq::
     j.nsplit_body = 0;
     j.blocks_per_split = 1;
   } else {
-    int want = std::max(1, 2048 / std::max(1, c.units));
+    int want = std::max(1, (fast ? fast_waves : 2048) / std::max(1, c.units));
     want = std::min({want, kvq::kMaxBodySplits, std::max(1, nblk / 4)});
     j.blocks_per_split = (nblk + want - 1) / want;
     j.nsplit_body = (nblk + j.blocks_per_split - 1) / j.blocks_per_split;
@@ -412,12 +414,13 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   j.st = kvq::TokenState{L.n, L.s_eff, L.nb, L.r};
   bool used = false;
   hipError_t e = hipSuccess;
-  if (!c->force_generic) {
-    plan_splits(*c, j.st, true, j);
+  const int fast_waves = c->force_generic ? 0 : kvq::decode_fast_waves(L.d);
+  if (fast_waves > 0) {
+    plan_splits(*c, j.st, fast_waves, j);
     e = kvq::launch_decode_fast(L.d, j, s, &used);
   }
   if (!used) {
-    plan_splits(*c, j.st, false, j);
+    plan_splits(*c, j.st, 0, j);
     e = kvq::launch_decode_generic(L.d, j, s);
   }
   return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
