@@ -641,35 +641,40 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   }
 }
 
-// Log-sum-exp merge of the split partials of one (unit, query row): four
-// wavefronts share the splits, every partial vector of a wavefront is
-// requested before it is consumed, and the four sums meet in LDS.  Values
-// stored Hadamard-rotated are rotated back here (c * H * o, H Sylvester).
+// Log-sum-exp merge of the split partials of one (unit, query row).  Thread
+// t owns channels 4*(t % 32) .. +3 of splits t / 32, t / 32 + 8, ...: every
+// partial vector and every (max, sum) pair is requested at once, so the merge
+// costs about two memory round trips.  The eight per-thread sums meet in LDS.
+// Values stored Hadamard-rotated are rotated back (c * H * o, H Sylvester).
 __global__ void __launch_bounds__(256) decode_merge_kernel(LayerDesc L, DecodeJob J) {
-  constexpr int kMaxSplits = kMaxBodySplits + kMaxFp16Splits;
+  // the split plan keeps nsplit <= max(kMaxBodySplits, kMaxFp16Splits) = 256
+  constexpr int kMaxSplits = 256;
+  static_assert(kMaxBodySplits <= kMaxSplits && kMaxFp16Splits <= kMaxSplits, "one split per thread");
+  constexpr int kPer = kMaxSplits / 8;  // splits per thread
   __shared__ float wts[kMaxSplits];
-  __shared__ float red[4][D];
+  __shared__ float red[8][D];
   __shared__ float scal[2][4];
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
+  const int so = tid >> 5, cq = tid & 31;
   const int u = blockIdx.x, r = blockIdx.y;
   const int G = L.G, nsplit = J.nsplit;
   const int b = u / L.Hkv, h = u % L.Hkv;
   const float* obase = J.partials + static_cast<int64_t>(u) * nsplit * G * D;
   const float* mlbase = J.partials + J.ml_off + static_cast<int64_t>(u) * nsplit * G * 2;
 
-  // this wavefront's partial vectors (splits w, w + 4, ...), first batch in flight early
-  constexpr int kBatch = 16;
-  u32x2 v[kBatch];
+  f32x4 v[kPer];
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int i = w + 4 * k;
-    v[k] = i < nsplit ? ld8(obase + (static_cast<int64_t>(i) * G + r) * D + 2 * l) : u32x2{0u, 0u};
+  for (int k = 0; k < kPer; ++k) {
+    const int i = so + 8 * k;
+    v[k] = i < nsplit ? *reinterpret_cast<const f32x4*>(obase + (static_cast<int64_t>(i) * G + r) * D + 4 * cq)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // global max and weights
-  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f;
-  if (tid < nsplit) { m0 = mlbase[(tid * G + r) * 2]; l0 = mlbase[(tid * G + r) * 2 + 1]; }
-  if (tid + 256 < nsplit) { m1 = mlbase[((tid + 256) * G + r) * 2]; l1 = mlbase[((tid + 256) * G + r) * 2 + 1]; }
-  float M = fmaxf(m0, m1);
+  float m0 = -INFINITY, l0 = 0.f;
+  if (tid < nsplit) {
+    m0 = mlbase[(tid * G + r) * 2];
+    l0 = mlbase[(tid * G + r) * 2 + 1];
+  }
+  float M = m0;
   M = fmaxf(M, xshflf<1>(M));
   M = fmaxf(M, xshflf<2>(M));
   M = fmaxf(M, xshflf<4>(M));
@@ -680,10 +685,8 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(LayerDesc L, DecodeJo
   __syncthreads();
   M = fmaxf(fmaxf(scal[0][0], scal[0][1]), fmaxf(scal[0][2], scal[0][3]));
   const float w0 = m0 == -INFINITY ? 0.f : exp2f(m0 - M);
-  const float w1 = m1 == -INFINITY ? 0.f : exp2f(m1 - M);
   if (tid < nsplit) wts[tid] = w0;
-  if (tid + 256 < nsplit) wts[tid + 256] = w1;
-  float Ls = fmaf(l0, w0, l1 * w1);
+  float Ls = l0 * w0;
   Ls += xshflf<1>(Ls);
   Ls += xshflf<2>(Ls);
   Ls += xshflf<4>(Ls);
@@ -692,36 +695,28 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(LayerDesc L, DecodeJo
   Ls += xshflf<32>(Ls);
   if (l == 0) scal[1][w] = Ls;
   __syncthreads();
-  // weighted sum of this wavefront's partials
-  float a0 = 0.f, a1 = 0.f;
+  f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int i = w + 4 * k;
+  for (int k = 0; k < kPer; ++k) {
+    const int i = so + 8 * k;
     const float wt = i < nsplit ? wts[i] : 0.f;
-    a0 = fmaf(__uint_as_float(v[k][0]), wt, a0);
-    a1 = fmaf(__uint_as_float(v[k][1]), wt, a1);
-  }
-  for (int i0 = 4 * kBatch; i0 < nsplit; i0 += 4 * kBatch) {
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int i = i0 + w + 4 * k;
-      v[k] = i < nsplit ? ld8(obase + (static_cast<int64_t>(i) * G + r) * D + 2 * l) : u32x2{0u, 0u};
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int i = i0 + w + 4 * k;
-      const float wt = i < nsplit ? wts[i] : 0.f;
-      a0 = fmaf(__uint_as_float(v[k][0]), wt, a0);
-      a1 = fmaf(__uint_as_float(v[k][1]), wt, a1);
-    }
+    for (int e = 0; e < 4; ++e) a[e] = fmaf(v[k][e], wt, a[e]);
   }
-  red[w][2 * l] = a0;
-  red[w][2 * l + 1] = a1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) red[so][4 * cq + e] = a[e];
   __syncthreads();
   if (w != 0) return;
   const float Lt = (scal[1][0] + scal[1][1]) + (scal[1][2] + scal[1][3]);
-  float y0 = ((red[0][2 * l] + red[1][2 * l]) + (red[2][2 * l] + red[3][2 * l])) / Lt;
-  float y1 = ((red[0][2 * l + 1] + red[1][2 * l + 1]) + (red[2][2 * l + 1] + red[3][2 * l + 1])) / Lt;
+  float y[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t += red[k][2 * l + e];
+    y[e] = t / Lt;
+  }
+  float y0 = y[0], y1 = y[1];
   if (L.v_had) {
     // lane l holds channels 2l, 2l+1: the first butterfly is in-lane
     const float t0 = y0 + y1, t1 = y0 - y1;
