@@ -47,7 +47,7 @@ __device__ __forceinline__ void fp16_slot(const LayerDesc& L, const TokenState& 
 }
 
 __device__ __forceinline__ float load_k_body(const LayerDesc& L, const uint8_t* rec, int j, int c) {
-  const int code = row_code(rec + L.off_kc + j * L.k_row_bytes, L.kb, c);
+  const int code = L.kb == 3 ? k3_code(rec + L.off_kc, j, c) : row_code(rec + L.off_kc + j * L.k_row_bytes, L.kb, c);
   const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + L.off_km);
   uint16_t s, z;
   if (!L.k_inner) {

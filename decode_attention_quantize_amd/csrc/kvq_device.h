@@ -120,14 +120,31 @@ __device__ __forceinline__ int pair_split_pos(int b, int e) {
 }
 
 // Code of channel c in a token-major row (keys; 3-bit values).
+// 3-bit codes live in 64 lane chunks of 24 bytes (one little-endian bit
+// stream per chunk, element E at bits 3E..3E+2), so that a lane's operand
+// for one matrix step is a contiguous 24-bit field.
+//   keys:   chunk 16g + n, element 32*tile + 8*j + i = token n + 16*tile,
+//           channel (j < 2 ? 16g + 8j : 64 + 16g + 8(j-2)) + i
+//   values: chunk 16g + n, element 8*t + i = token 8g + i, channel 16t + n
+__device__ __forceinline__ int chunk3_code(const uint8_t* codes, int lane, int e) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(codes) + 6 * lane;
+  const int bit = 3 * e;
+  const uint64_t pair = static_cast<uint64_t>(w[bit >> 5]) |
+                        (static_cast<uint64_t>((bit >> 5) < 5 ? w[(bit >> 5) + 1] : 0u) << 32);
+  return static_cast<int>((pair >> (bit & 31)) & 7u);
+}
+__device__ __forceinline__ int k3_code(const uint8_t* codes, int j, int c) {
+  const int g = (c & 63) >> 4, jj = ((c >> 6) << 1) | ((c & 15) >> 3);
+  return chunk3_code(codes, 16 * g + (j & 15), 32 * (j >> 4) + 8 * jj + (c & 7));
+}
+__device__ __forceinline__ int v3_code(const uint8_t* codes, int j, int c) {
+  return chunk3_code(codes, 16 * (j >> 3) + (c & 15), 8 * (c >> 4) + (j & 7));
+}
+
+// Code of (token slot j, channel c) in a token-major row of 2/4/8-bit codes.
 __device__ __forceinline__ int row_code(const uint8_t* row, int bits, int c) {
   const uint32_t* w = reinterpret_cast<const uint32_t*>(row);
   if (bits == 8) return row[c];
-  if (bits == 3) {
-    const uint32_t* p = w + (c >> 5) * 3;
-    const int i = c & 31;
-    return ((p[0] >> i) & 1) | (((p[1] >> i) & 1) << 1) | (((p[2] >> i) & 1) << 2);
-  }
   const int n = 32 / bits;
   return (w[c / n] >> pair_split_pos(bits, c % n)) & ((1 << bits) - 1);
 }
@@ -147,7 +164,7 @@ __device__ __forceinline__ VLoc v_loc(int bits, int j, int c) {
 }
 
 __device__ __forceinline__ int v_code(const uint8_t* vc, int bits, int j, int c) {
-  if (bits == 3) return row_code(vc + j * 48, 3, c);
+  if (bits == 3) return v3_code(vc, j, c);
   const VLoc l = v_loc(bits, j, c);
   return (reinterpret_cast<const uint32_t*>(vc)[l.word] >> l.shift) & ((1 << bits) - 1);
 }

@@ -264,7 +264,7 @@ __device__ void quant_groups_any(int w, const uint16_t (*rows)[D], const uint8_t
   }
 }
 
-// Pack token-major rows (keys, 3-bit values) for slots [slot0, slot0+nrows).
+// Pack token-major 2/4/8-bit key rows for slots [slot0, slot0+nrows).
 __device__ void pack_rows(const uint8_t (*codes)[D], int nrows, int bits, uint8_t* dst, int row_bytes,
                           int slot0) {
   const int wpr = row_bytes / 4;
@@ -274,15 +274,62 @@ __device__ void pack_rows(const uint8_t (*codes)[D], int nrows, int bits, uint8_
     uint32_t word = 0;
     if (bits == 8) {
       for (int e = 0; e < 4; ++e) word |= static_cast<uint32_t>(codes[j][4 * w + e]) << (8 * e);
-    } else if (bits == 3) {
-      const int g = w / 3, p = w % 3;
-      for (int e = 0; e < 32; ++e) word |= static_cast<uint32_t>((codes[j][32 * g + e] >> p) & 1) << e;
     } else {
       const int n = 32 / bits;
       for (int e = 0; e < n; ++e)
         word |= static_cast<uint32_t>(codes[j][n * w + e]) << pair_split_pos(bits, e);
     }
     reinterpret_cast<uint32_t*>(dst + (slot0 + j) * row_bytes)[w] = word;
+  }
+}
+
+// 3-bit codes: 64 lane chunks of 6 words, element E at bits 3E..3E+2 of the
+// chunk's bit stream (see the decode readers for the element maps).
+// Bits of 3-bit element e that fall into 32-bit word w of a stream.
+__device__ __forceinline__ uint32_t bits3_in_word(uint32_t code, int e, int w) {
+  const int sh = 3 * e - 32 * w;
+  if (sh <= -3 || sh >= 32) return 0u;
+  return sh >= 0 ? code << sh : code >> -sh;
+}
+
+// Keys: chunk 16g + n holds tokens n (words 0..2) and n + 16 (words 3..5);
+// within a token's 96 bits element 8j + i is channel
+// (j < 2 ? 16g + 8j : 64 + 16g + 8(j-2)) + i.  A token's words hold no other
+// token's codes, so tokens [slot0, slot0 + nrows) are written without a read.
+__device__ void pack_k3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int slot0) {
+  for (int i = threadIdx.x; i < nrows * 12; i += blockDim.x) {
+    const int jr = i / 12, g = (i % 12) / 3, w = i % 3;
+    const int j = slot0 + jr;
+    uint32_t word = 0;
+    for (int e = 0; e < 32; ++e) {
+      const int jj = e >> 3;
+      const int c = (jj < 2 ? 16 * g + 8 * jj : 64 + 16 * g + 8 * (jj - 2)) + (e & 7);
+      word |= bits3_in_word(codes[jr][c], e, w);
+    }
+    reinterpret_cast<uint32_t*>(dst)[6 * (16 * g + (j & 15)) + 3 * (j >> 4) + w] = word;
+  }
+}
+
+// Values: chunk 16g + n, element 8t + i = token 8g + i of channel 16t + n.
+// A fresh block (slot0 == 0) is written whole; otherwise only the bits of
+// tokens [slot0, slot0 + nrows) are replaced.
+__device__ void pack_v3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int slot0) {
+  for (int i = threadIdx.x; i < 64 * 6; i += blockDim.x) {
+    const int lane = i / 6, w = i % 6;
+    uint32_t word = 0, keep = 0xffffffffu;
+    for (int e = (32 * w) / 3; e <= (32 * w + 31) / 3 && e < 64; ++e) {
+      const int j = 8 * (lane >> 4) + (e & 7);
+      const int c = 16 * (e >> 3) + (lane & 15);
+      if (j >= slot0 && j < slot0 + nrows) {
+        word |= bits3_in_word(codes[j - slot0][c], e, w);
+        keep &= ~bits3_in_word(7u, e, w);
+      }
+    }
+    uint32_t* wp = reinterpret_cast<uint32_t*>(dst) + i;
+    if (slot0 == 0)
+      *wp = word;
+    else if (keep != 0xffffffffu)
+      *wp = (*wp & keep) | word;
   }
 }
 
@@ -402,9 +449,12 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
                    L.lev_v, false, 1, 1, rec + L.off_vm, 1, slot0);
   __syncthreads();
 
-  pack_rows(sm.ck, nrows, L.kb, rec + L.off_kc, L.k_row_bytes, slot0);
+  if (L.kb == 3)
+    pack_k3(sm.ck, nrows, rec + L.off_kc, slot0);
+  else
+    pack_rows(sm.ck, nrows, L.kb, rec + L.off_kc, L.k_row_bytes, slot0);
   if (L.vb == 3)
-    pack_rows(sm.cv, nrows, 3, rec + L.off_vc, 48, slot0);
+    pack_v3(sm.cv, nrows, rec + L.off_vc, slot0);
   else
     pack_vchunks(sm.cv, nrows, L.vb, rec + L.off_vc, slot0);
 }

@@ -111,13 +111,15 @@ enum {
  * (batch, kv head) unit), as reported by kvq_block_layout().  Every section
  * starts 16-byte aligned.
  *
- *  k_codes  token-major rows of D codes, row_bytes = D*k_bits/8.
+ *  k_codes  2/4/8 bits: token-major rows of D codes, row_bytes = D*k_bits/8.
  *           2/4 bits: each 32-bit word holds n = 32/bits consecutive channels
  *             e_0..e_(n-1) with e_(2j) at bit bits*j and e_(2j+1) at bit
  *             16 + bits*j ("pair-split" word).
  *           8 bits: one byte per channel.
- *           3 bits: per 32 channels three 32-bit bit-planes; bit i of plane p
- *             is bit p of channel i's code.
+ *           3 bits: 64 lane chunks of 24 bytes, each a little-endian bit
+ *             stream with element E at bits 3E..3E+2.  Chunk 16g + n holds
+ *             element 32*t + 8*j + i = code(token n + 16t, channel
+ *             (j < 2 ? 16g + 8j : 64 + 16g + 8(j-2)) + i), t = 0..1, j, i < 4, 8.
  *  k_meta   per-channel keys: s[D] fp16 then z[D] fp16 (one group per channel
  *           per block).  Inner keys: [32 tokens][D/k_group] pairs (s, z).
  *           A set sign bit on s marks a symmetric group: value = (code-2^(b-1))*|s|;
@@ -126,7 +128,9 @@ enum {
  *           tokens 8*(l/16)..+7 and channels 16*t + l%16 (t = 0..7); its
  *           element sequence is e_(8t+j) = code(token 8*(l/16)+j, channel
  *           16t + l%16), packed in pair-split words (2/4 bits) or bytes (8).
- *           3 bits: token-major bit-plane rows as for keys.
+ *           3 bits: 64 lane chunks of 24 bytes (bit stream as for keys);
+ *             chunk 16g + n holds element 8t + i = code(token 8g + i,
+ *             channel 16t + n).
  *  v_meta   s[D/v_group][32 tokens] fp16 then z[D/v_group][32 tokens] fp16.
  *  k_out,   outliers_per_vector entries per token: {uint16 column, fp16
  *  v_out    value}, columns ascending; the fp16 value replaces the dequantized

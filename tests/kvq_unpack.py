@@ -1,7 +1,7 @@
 """Turn raw libkvq body records back into logical codes and parameters.
 
 Written from the byte-layout specification in include/kvq.h (pair-split
-words, lane chunks, bit planes, SoA value parameters); it shares no code with
+words, lane chunks, 3-bit lane fields, SoA value parameters); it shares no code with
 the kernels.  Used by the parity tests to compare packed GPU buffers with the
 oracle's logical arrays bit for bit.
 """
@@ -25,20 +25,48 @@ def _pair_split_fields(words: np.ndarray, bits: int) -> np.ndarray:
 
 
 def _rows(raw: np.ndarray, bits: int, nrows: int) -> np.ndarray:
-    """Token-major code rows: raw bytes [nrows * D*bits/8] -> [nrows][D]."""
+    """Token-major code rows (2/4/8 bits): raw bytes [nrows * D*bits/8] -> [nrows][D]."""
     rb = D * bits // 8
     r = raw[: nrows * rb].reshape(nrows, rb)
     if bits == 8:
         return r.copy()
-    words = r.view(np.uint32)
-    if bits == 3:
-        planes = words.reshape(nrows, D // 32, 3)
-        out = np.zeros((nrows, D // 32, 32), np.uint8)
-        for p in range(3):
-            bitsv = (planes[:, :, p:p + 1] >> np.arange(32, dtype=np.uint32)) & 1
-            out |= (bitsv << p).astype(np.uint8)
-        return out.reshape(nrows, D)
-    return _pair_split_fields(words, bits)
+    return _pair_split_fields(r.view(np.uint32), bits)
+
+
+def _chunk3_fields(raw: np.ndarray) -> np.ndarray:
+    """3-bit lane chunks: 64 chunks of 24 bytes -> [64 lanes][64 elements],
+    element E at bits 3E..3E+2 of the chunk (little-endian bit stream)."""
+    b = raw[: 64 * 24].reshape(64, 24)
+    bits = np.unpackbits(b, axis=1, bitorder="little")          # [64][192]
+    f = bits.reshape(64, 64, 3).astype(np.uint8)
+    return f[..., 0] | (f[..., 1] << 1) | (f[..., 2] << 2)
+
+
+def _kchunks3(raw: np.ndarray) -> np.ndarray:
+    """3-bit keys -> [32 tokens][D].  Chunk l = 16*g + n holds tokens n (tile 0)
+    and n + 16 (tile 1); element 32*tile + 8*j + i is channel
+    (j < 2 ? 16g + 8j : 64 + 16g + 8(j-2)) + i."""
+    el = _chunk3_fields(raw)
+    out = np.zeros((BT, D), np.uint8)
+    for lane in range(64):
+        n, g = lane % 16, lane // 16
+        for e in range(64):
+            tile, j, i = e // 32, (e // 8) % 4, e % 8
+            c = (16 * g + 8 * j if j < 2 else 64 + 16 * g + 8 * (j - 2)) + i
+            out[n + 16 * tile, c] = el[lane, e]
+    return out
+
+
+def _vchunks3(raw: np.ndarray) -> np.ndarray:
+    """3-bit values -> [32 tokens][D].  Chunk l = 16*g + n, element 8*t + i is
+    token 8g + i of channel 16t + n."""
+    el = _chunk3_fields(raw)
+    out = np.zeros((BT, D), np.uint8)
+    for lane in range(64):
+        n, g = lane % 16, lane // 16
+        for e in range(64):
+            out[8 * g + e % 8, 16 * (e // 8) + n] = el[lane, e]
+    return out
 
 
 def _vchunks(raw: np.ndarray, bits: int) -> np.ndarray:
@@ -75,9 +103,12 @@ def unpack_unit(body_unit: np.ndarray, lay: dict, kb: int, vb: int, nb: int, k_i
     for i in range(nblk):
         r = recs[i]
         cnt = min(BT, nb - BT * i)
-        kc.append(_rows(r[lay["k_codes"]:], kb, BT)[:cnt])
+        if kb == 3:
+            kc.append(_kchunks3(r[lay["k_codes"]:])[:cnt])
+        else:
+            kc.append(_rows(r[lay["k_codes"]:], kb, BT)[:cnt])
         if vb == 3:
-            vc.append(_rows(r[lay["v_codes"]:], 3, BT)[:cnt])
+            vc.append(_vchunks3(r[lay["v_codes"]:])[:cnt])
         else:
             vc.append(_vchunks(r[lay["v_codes"]:], vb)[:cnt])
         m16 = r[lay["k_meta"]:].view(np.uint16)
