@@ -1,0 +1,588 @@
+// kvq_decode_lut.hip -- split-context decode for MHA layers whose keys and
+// values are 3-bit codes with per-layer level tables (KVQuant (iii) codebooks,
+// or the uniform grid 0..7), per-vector sparse fp16 outliers (KVQuant (iv))
+// and keys cached before RoPE (KVQuant (ii)).
+//
+// One wavefront per split, one query row per kv head.  A 32-token block:
+//   keys    lane (n, g) owns tokens n and n + 16 and the 32 channels
+//           16g..16g+15, 64+16g..64+16g+15 (RoPE pairs (i, i + 64) in one
+//           lane).  Codes are decoded two at a time through a 64-entry LDS
+//           table of level pairs, dequantized in fp32 (L * s + z with one
+//           v_fma_mix) and dotted with the query rotated back to each token's
+//           position: q . R(p) k = (R(-p) q) . k.  The rotated queries move
+//           from block to block by one fixed rotation per pair (fp32), and are
+//           recomputed exactly (fp64 angle reduction) at the start of a split.
+//   scores  summed over the four lanes of a token, plus the outlier
+//           corrections (x_out - k_dense) * (R(-p) q)[col] gathered in LDS.
+//   values  O += sum_t (p_t s_tg) L[code] on v_mfma_f32_16x16x32_f16, with the
+//           level pairs from a second LDS table as the B operand, the
+//           zero points through one more MFMA, and the value outliers
+//           (x_out - v_dense) * p_t accumulated per channel in LDS.
+// Splits write (o, max, sum) partials for decode_merge_kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+#include "kvq_mfma.h"
+
+namespace kvq {
+namespace {
+
+// Record of a block with 3-bit keys and values, value groups of 32 and K
+// outliers per token vector (the host layout rules, fixed at compile time).
+template <int OUTK>
+struct Rec3 {
+  static constexpr int off_km = 1536;
+  static constexpr int off_vc = off_km + 512;
+  static constexpr int off_vm = off_vc + 1536;
+  static constexpr int off_ko = off_vm + 512;
+  static constexpr int off_vo = off_ko + (32 * OUTK * 4 + 15) / 16 * 16;
+  static constexpr int bytes = off_vo + (32 * OUTK * 4 + 15) / 16 * 16;
+  static constexpr int loads = (bytes + 1023) / 1024;
+};
+
+constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
+
+// cos/sin of an angle given in revolutions (|x| <= 256): the hardware
+// v_cos_f32 / v_sin_f32 (absolute error about 1e-6)
+__device__ __forceinline__ void cs_rev(float x, float& c, float& s) {
+  c = __builtin_amdgcn_cosf(x);
+  s = __builtin_amdgcn_sinf(x);
+}
+// cos/sin of p * theta: the angle is reduced modulo 2 pi in binary64 (error
+// ~1e-11 rad for the positions here), then evaluated as above
+__device__ __forceinline__ void rot_cs(double p, double theta, float& c, float& s) {
+  const double a = p * theta;
+  const double r = fma(-rint(a * kInvTwoPi), kTwoPi, a);
+  cs_rev(static_cast<float>(r * kInvTwoPi), c, s);
+}
+
+// 3-bit fields of a lane's chunk (six words): the six bits at bit offset
+// `bit` of the 192-bit stream, scaled by 4 (a byte offset into a table of
+// 32-bit entries).
+__device__ __forceinline__ uint32_t pair_off(const uint32_t (&w)[6], int bit) {
+  const int q = bit >> 5, r = bit & 31;
+  const uint32_t v = r <= 26 ? (w[q] >> r) : __builtin_amdgcn_alignbit(w[q + 1], w[q], r);
+  return (v << 2) & 0xFCu;
+}
+
+// 3-bit code of (token slot j, channel c) in an LDS copy of a record section
+// (the lane-chunk maps of the key and value layouts).
+__device__ __forceinline__ int chunk3_lds(const lds_u8* codes, int lane, int e) {
+  typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+  const lds_u32* w = reinterpret_cast<lds_u32*>(codes) + 6 * lane;
+  const int bit = 3 * e;
+  const uint32_t lo = w[bit >> 5];
+  const uint32_t hi = (bit >> 5) < 5 ? w[(bit >> 5) + 1] : 0u;
+  return static_cast<int>(__builtin_amdgcn_alignbit(hi, lo, bit & 31) & 7u);
+}
+__device__ __forceinline__ int k3_lds(const lds_u8* codes, int j, int c) {
+  const int g = (c & 63) >> 4, jj = ((c >> 6) << 1) | ((c & 15) >> 3);
+  return chunk3_lds(codes, 16 * g + (j & 15), 32 * (j >> 4) + 8 * jj + (c & 7));
+}
+__device__ __forceinline__ int v3_lds(const lds_u8* codes, int j, int c) {
+  return chunk3_lds(codes, 16 * (j >> 3) + (c & 15), 8 * (c >> 4) + (j & 7));
+}
+
+template <int OUTK, bool ROPE, int NBUF>
+__global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J) {
+  using R = Rec3<OUTK>;
+  static_assert(NBUF >= 2 && NBUF <= 3, "ring of 2 or 3 slots");
+  static_assert(OUTK >= 0 && OUTK <= 2, "one outlier entry per lane");
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[R::loads * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[R::loads * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF >= 3 ? R::loads * 1024 : 16];
+  __shared__ uint32_t lutk[64], lutv[64];
+  __shared__ __attribute__((aligned(16))) _Float16 ptile[16][32];
+  __shared__ float scorr[32], ocorr[D], qs[D];
+  __shared__ float2 tb[64];
+  __shared__ float thf[64];
+  lds_u8* const slot0 = (lds_u8*)ring0;
+  lds_u8* const slot1 = (lds_u8*)ring1;
+  lds_u8* const slot2 = (lds_u8*)ring2;
+  auto slot_at = [&](int k) __attribute__((always_inline)) {
+    return k == 0 ? slot0 : (k == 1 ? slot1 : slot2);
+  };
+
+  const int l = threadIdx.x;
+  const int n16 = l & 15, g4 = l >> 4;
+  const int nsplit = J.nsplit;
+  const int sp = blockIdx.x;
+  const int u = blockIdx.y;
+  const int b = u / L.Hkv, h = u % L.Hkv;
+  const TokenState st = J.st;
+  const float kscale = kLog2e / sqrtf(static_cast<float>(D));
+
+  // ---- level-pair tables, query, per-channel value corrections
+  {
+    // entry c0 + 8 c1 = (L[c0], L[c1]); levels picked with constant indices.
+    // Without codebooks the levels are the uniform grid 0..7 (fp16 bits).
+    constexpr uint16_t kGrid[8] = {0x0000, 0x3C00, 0x4000, 0x4200, 0x4400, 0x4500, 0x4600, 0x4700};
+    uint32_t k0 = 0, k1 = 0, v0 = 0, v1 = 0;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const uint32_t lk = L.nuq ? L.lev_k[c] : kGrid[c], lv = L.nuq ? L.lev_v[c] : kGrid[c];
+      if ((l & 7) == c) { k0 = lk; v0 = lv; }
+      if ((l >> 3) == c) { k1 = lk; v1 = lv; }
+    }
+    lutk[l] = k0 | (k1 << 16);
+    lutv[l] = v0 | (v1 << 16);
+  }
+  const uint16_t* qp = J.q + (static_cast<int64_t>(b) * L.Hq + h) * D;
+  const float q_lo = h2f(qp[l]), q_hi = h2f(qp[64 + l]);  // pair l: channels l, l + 64
+  qs[l] = q_lo;
+  qs[64 + l] = q_hi;
+  ocorr[l] = 0.f;
+  ocorr[64 + l] = 0.f;
+  const double theta_l = pow(static_cast<double>(L.rope_base), -2.0 * l / D);
+  thf[l] = static_cast<float>(theta_l);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // this lane's pairs p = 0..15: channels 16g + p and 64 + 16g + p
+  float qa[16], qb[16];
+  double th[16];  // RoPE frequency of each pair, binary64
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    qa[p] = qs[16 * g4 + p];
+    qb[p] = qs[64 + 16 * g4 + p];
+    th[p] = ROPE ? pow(static_cast<double>(L.rope_base), -2.0 * (16 * g4 + p) / D) : 0.0;
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[8];
+  f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) oacc[nt] = {0.f, 0.f, 0.f, 0.f};
+
+  // online softmax of the 32 scores (tokens n16, 16 + n16 in every lane);
+  // P (fp16) of the query row lands in ptile row 0
+  auto softmax_tile = [&](float s0, float s1) __attribute__((always_inline)) -> half8 {
+    const float bm = row16_max(fmaxf(s0, s1));
+    const float mn = fmaxf(m_run, bm);
+    const float mr = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fexp2(m_run - mr);
+    const _Float16 p0 = static_cast<_Float16>(fexp2(s0 - mr));
+    const _Float16 p1 = static_cast<_Float16>(fexp2(s1 - mr));
+    l_run = fmaf(l_run, alpha, static_cast<float>(p0) + static_cast<float>(p1));
+    m_run = mn;
+    if (g4 == 0) {
+      ptile[0][n16] = p0;
+      ptile[0][16 + n16] = p1;
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) oacc[nt][0] *= alpha;
+      zacc[0] *= alpha;
+      ocorr[l] *= alpha;
+      ocorr[64 + l] *= alpha;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return n16 == 0 ? *reinterpret_cast<const half8*>(&ptile[0][8 * g4]) : h8(0u, 0u, 0u, 0u);
+  };
+  // sum over the four lanes that hold one token's partial dots
+  auto lanes4_sum = [&](float v) __attribute__((always_inline)) {
+    v += xshflf<16>(v);
+    v += __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __float_as_int(v)));
+    return v;
+  };
+
+  // ---- rotated queries of this lane's two tokens, W = R(-pos) q per pair
+  // W = R(-pos) q per pair for this lane's tile-0 token; the tile-1 token
+  // (16 positions later) and the next block's tile-0 token (16 more) follow
+  // by the same fixed rotation
+  float wa[16], wb[16];
+  float rc[16], rs[16];  // rotation by 16 positions, per pair
+  float tc = 1.f, ts = 0.f, trc = 1.f, trs = 0.f;  // (cos, sin)(theta_l * block start), step
+  auto rotate_w = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const float a = wa[p], bq = wb[p];
+      wa[p] = fmaf(rc[p], a, rs[p] * bq);
+      wb[p] = fmaf(rc[p], bq, -(rs[p] * a));
+    }
+  };
+  auto init_w = [&](int pos_first) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      if constexpr (ROPE) {
+        float c, s;
+        rot_cs(static_cast<double>(pos_first + n16), th[p], c, s);
+        wa[p] = fmaf(qa[p], c, qb[p] * s);
+        wb[p] = fmaf(qb[p], c, -(qa[p] * s));
+        rot_cs(16.0, th[p], c, s);
+        rc[p] = c;
+        rs[p] = s;
+      } else {
+        wa[p] = qa[p];
+        wb[p] = qb[p];
+      }
+    }
+  };
+
+  // ================= sink / window tokens (fp16), one 32-slot chunk at a time
+  {
+    const int slots = L.sinks_cap + L.win_cap;
+    const uint16_t* kf = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
+    const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
+    const int wchunks = L.win_cap / kBlockTokens;
+    const int wstart = st.nb % L.win_cap;
+    for (int c = sp; c < J.fp16_chunks; c += nsplit) {
+      const bool sinkc = c < J.sink_chunks;
+      const int s0 = sinkc ? kBlockTokens * c
+                           : L.sinks_cap + kBlockTokens * ((J.win_chunk0 + c - J.sink_chunks) % wchunks);
+      float sc[2];
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int x = s0 + 16 * nt + n16;
+        bool live;
+        int pos;
+        if (sinkc) {
+          live = x < st.s_eff;
+          pos = x;
+        } else {
+          int d = x - L.sinks_cap - wstart;
+          if (d < 0) d += L.win_cap;
+          live = d < st.r;
+          pos = st.s_eff + st.nb + d;
+        }
+        const uint16_t* kr = kf + static_cast<int64_t>(x) * D;
+        const u32x4 ka0 = ld16(kr + 16 * g4), ka1 = ld16(kr + 16 * g4 + 8);
+        const u32x4 kb0 = ld16(kr + 64 + 16 * g4), kb1 = ld16(kr + 64 + 16 * g4 + 8);
+        const half8 ha0 = h8(ka0), ha1 = h8(ka1), hb0 = h8(kb0), hb1 = h8(kb1);
+        float acc = 0.f;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) {
+          float c1 = 1.f, s1 = 0.f;
+          if constexpr (ROPE) rot_cs(static_cast<double>(pos), th[p], c1, s1);
+          const float wa1 = fmaf(qa[p], c1, qb[p] * s1), wb1 = fmaf(qb[p], c1, -(qa[p] * s1));
+          const float ka = static_cast<float>(p < 8 ? ha0[p] : ha1[p - 8]);
+          const float kb = static_cast<float>(p < 8 ? hb0[p] : hb1[p - 8]);
+          acc = fmaf(ka, wa1, fmaf(kb, wb1, acc));
+        }
+        acc = lanes4_sum(acc);
+        sc[nt] = live ? acc * kscale : -INFINITY;
+      }
+      u32x4 vv[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) vv[nt] = ld16(vf + (static_cast<int64_t>(s0 / 8 + g4) * D + 16 * nt + n16) * 8);
+      const half8 pa = softmax_tile(sc[0], sc[1]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
+    }
+  }
+
+  // ================= quantized body blocks through the LDS ring
+  const int nblk_body = (st.nb + kBlockTokens - 1) / kBlockTokens;
+  const int c_begin = sp * J.blocks_per_split;
+  const int c_end = sp < J.nsplit_body ? min(nblk_body, c_begin + J.blocks_per_split) : c_begin;
+  const int nmy = c_end - c_begin;
+  const uint8_t* ubase = L.body + static_cast<int64_t>(u) * L.nblk_cap * L.rec_bytes;
+  auto issue = [&](int i, lds_u8* dst) __attribute__((always_inline)) {
+    const uint8_t* src = ubase + static_cast<int64_t>(c_begin + i) * L.rec_bytes;
+#pragma unroll
+    for (int k = 0; k < R::loads; ++k) {
+      const int off = k * 1024 + l * 16;
+      if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < NBUF - 1; ++k)
+    if (k < nmy) issue(k, slot_at(k));
+
+  if (nmy > 0) {
+    const int pos0 = st.s_eff + kBlockTokens * c_begin;
+    init_w(pos0);
+    if constexpr (ROPE) {
+      if constexpr (OUTK > 0) {
+        rot_cs(static_cast<double>(pos0), theta_l, tc, ts);
+        rot_cs(32.0, theta_l, trc, trs);
+      }
+    }
+  }
+
+  // one block whose record sits in LDS at rec
+  auto body_block = [&](const lds_u8* rec, int count) __attribute__((always_inline)) {
+    const uint32_t r0 = lds_off(rec);
+    const lds_u8* rb = rec;
+    typedef __attribute__((address_space(3))) const uint32_t lds_u32;
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+    uint32_t kw[6];
+    u32x4 sa[2], sb[2], za[2], zb[2];
+    {
+      const uint32_t ak = r0 + 24 * l;
+      u32x2 k0 = dsr8<0>(ak), k1 = dsr8<8>(ak), k2 = dsr8<16>(ak);
+      const uint32_t am = r0 + R::off_km + 32 * g4;
+      sa[0] = dsr16<0>(am);
+      sa[1] = dsr16<16>(am);
+      sb[0] = dsr16<128>(am);
+      sb[1] = dsr16<144>(am);
+      za[0] = dsr16<256>(am);
+      za[1] = dsr16<272>(am);
+      zb[0] = dsr16<384>(am);
+      zb[1] = dsr16<400>(am);
+      lds_wait();
+      pin(k0);
+      pin(k1);
+      pin(k2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        pin(sa[e]);
+        pin(sb[e]);
+        pin(za[e]);
+        pin(zb[e]);
+      }
+      kw[0] = k0[0]; kw[1] = k0[1]; kw[2] = k1[0]; kw[3] = k1[1]; kw[4] = k2[0]; kw[5] = k2[1];
+    }
+
+    // ---- key outliers: (x_out - k_dense) * W_t[col] into scorr[t]
+    if constexpr (OUTK > 0) {
+      if (l < 32) scorr[l] = 0.f;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int t = OUTK == 2 ? (l >> 1) : l;
+      if (t < count && (OUTK == 2 || l < 32)) {
+        const uint32_t ent = *reinterpret_cast<lds_u32*>(rb + R::off_ko + 4 * (t * OUTK + (OUTK == 2 ? (l & 1) : 0)));
+        const int col = static_cast<int>(ent & 0x7Fu);  // columns are < 128
+        const float val = h2f(static_cast<uint16_t>(ent >> 16));
+        const int code = k3_lds(rb, t, col);
+        const lds_u16* km = reinterpret_cast<lds_u16*>(rb + R::off_km);
+        const float kd = fmaf(h2f(static_cast<uint16_t>(lutk[9 * code])), h2f(km[col]), h2f(km[D + col]));
+        const int i = col & 63;
+        float w;
+        if constexpr (ROPE) {
+          const float2 base = tb[i];
+          float st_, ct_;
+          cs_rev(static_cast<float>(t) * thf[i] * static_cast<float>(kInvTwoPi), ct_, st_);
+          const float c = base.x * ct_ - base.y * st_;
+          const float s = base.y * ct_ + base.x * st_;
+          w = col < 64 ? fmaf(qs[i], c, qs[64 + i] * s) : fmaf(qs[64 + i], c, -(qs[i] * s));
+        } else {
+          w = qs[col];
+        }
+        atomicAdd(&scorr[t], (val - kd) * w);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+
+    // ---- key codes -> levels (pairs through lutk), dequantize, dot with W
+    float sc[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      uint32_t lv[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) lv[m] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lutk) + pair_off(kw, 96 * nt + 6 * m));
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        const half2v lp = __builtin_bit_cast(half2v, lv[m]);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int el = 2 * m + e;  // 0..15: channel 16g + el; 16..31: 64 + 16g + el - 16
+          const int p = el & 15;
+          const u32x4& sv = el < 16 ? sa[p >> 3] : sb[p >> 3];
+          const u32x4& zv = el < 16 ? za[p >> 3] : zb[p >> 3];
+          const half8 s8 = h8(sv), z8 = h8(zv);
+          const float kd = fmaf(static_cast<float>(lp[e]), static_cast<float>(s8[p & 7]), static_cast<float>(z8[p & 7]));
+          acc = fmaf(kd, el < 16 ? wa[p] : wb[p], acc);
+        }
+      }
+      if constexpr (ROPE) rotate_w();  // to the next token of this lane
+      acc = lanes4_sum(acc);
+      if constexpr (OUTK > 0) acc += scorr[16 * nt + n16];
+      sc[nt] = 16 * nt + n16 < count ? acc * kscale : -INFINITY;
+    }
+
+    // ---- values: level pairs through lutv as the MFMA B operand
+    uint32_t vw[6];
+    u32x4 vmeta[5];
+    {
+      const uint32_t av = r0 + R::off_vc + 24 * l;
+      u32x2 v0 = dsr8<0>(av), v1 = dsr8<8>(av), v2 = dsr8<16>(av);
+      const uint32_t az = r0 + R::off_vm + (n16 < 4 ? 2 * 4 * kBlockTokens : 0) + 2 * ((n16 & 3) * kBlockTokens + 8 * g4);
+      const uint32_t asv = r0 + R::off_vm + 16 * g4;
+      vmeta[4] = dsr16<0>(az);
+      vmeta[0] = dsr16<0>(asv);
+      vmeta[1] = dsr16<64>(asv);
+      vmeta[2] = dsr16<128>(asv);
+      vmeta[3] = dsr16<192>(asv);
+      lds_wait();
+      pin(v0);
+      pin(v1);
+      pin(v2);
+#pragma unroll
+      for (int e = 0; e < 5; ++e) pin(vmeta[e]);
+      vw[0] = v0[0]; vw[1] = v0[1]; vw[2] = v1[0]; vw[3] = v1[1]; vw[4] = v2[0]; vw[5] = v2[1];
+    }
+    const half8 pa = softmax_tile(sc[0], sc[1]);
+    zacc = mfma(pa, n16 < 8 ? h8(vmeta[4]) : h8(0u, 0u, 0u, 0u), zacc);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const half8 s8 = h8(vmeta[g]);
+      const half8 wh = pa * s8;
+      const half8 wl = __builtin_elementwise_fma(pa, s8, -wh);
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        const int nt = 2 * g + t2;
+        uint32_t vl[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          vl[m] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lutv) + pair_off(vw, 24 * nt + 6 * m));
+        const half8 bv = h8(vl[0], vl[1], vl[2], vl[3]);
+        oacc[nt] = mfma(wh, bv, oacc[nt]);
+        oacc[nt] = mfma(wl, bv, oacc[nt]);
+      }
+    }
+
+    // ---- value outliers: (x_out - v_dense) * p_t into ocorr[col]
+    if constexpr (OUTK > 0) {
+      const int t = OUTK == 2 ? (l >> 1) : l;
+      if (t < count && (OUTK == 2 || l < 32)) {
+        const uint32_t ent = *reinterpret_cast<lds_u32*>(rb + R::off_vo + 4 * (t * OUTK + (OUTK == 2 ? (l & 1) : 0)));
+        const int col = static_cast<int>(ent & 0x7Fu);  // columns are < 128
+        const float val = h2f(static_cast<uint16_t>(ent >> 16));
+        const int code = v3_lds(rb + R::off_vc, t, col);
+        const lds_u16* vm = reinterpret_cast<lds_u16*>(rb + R::off_vm);
+        const int g = col >> 5;
+        const float vd = fmaf(h2f(static_cast<uint16_t>(lutv[9 * code])), h2f(vm[g * kBlockTokens + t]),
+                              h2f(vm[4 * kBlockTokens + g * kBlockTokens + t]));
+        atomicAdd(&ocorr[col], (val - vd) * static_cast<float>(ptile[0][t]));
+      }
+    }
+
+    // ---- advance the rotated queries (and the outlier angle table) by 32 positions
+    if constexpr (ROPE) {
+      if constexpr (OUTK > 0) {
+        const float c = tc, s = ts;
+        tc = fmaf(c, trc, -(s * trs));
+        ts = fmaf(s, trc, c * trs);
+        tb[l] = make_float2(tc, ts);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  if constexpr (ROPE && OUTK > 0) {
+    tb[l] = make_float2(tc, ts);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  {
+    auto step = [&](int i, lds_u8* cur, lds_u8* ahead) __attribute__((always_inline)) {
+      issue(i + NBUF - 1, ahead);
+      wait_vm<(NBUF - 1) * R::loads>();
+      const int ch = c_begin + i;
+      body_block(cur, min(kBlockTokens, st.nb - ch * kBlockTokens));
+    };
+    int i = 0;
+    for (; i + 2 * NBUF - 2 < nmy; i += NBUF) {
+      if constexpr (NBUF == 3) {
+        step(i, slot0, slot2);
+        step(i + 1, slot1, slot0);
+        step(i + 2, slot2, slot1);
+      } else {
+        step(i, slot0, slot1);
+        step(i + 1, slot1, slot0);
+      }
+    }
+    for (; i < nmy; ++i) {
+      const int ahead = i + NBUF - 1;
+      if (ahead < nmy) issue(ahead, slot_at(ahead % NBUF));
+      const int newer = min(NBUF - 1, nmy - 1 - i);
+      if (NBUF >= 3 && newer >= 2)
+        wait_vm<(NBUF >= 3 ? 2 : 0) * R::loads>();
+      else if (newer >= 1)
+        wait_vm<R::loads>();
+      else
+        wait_vm<0>();
+      const int ch = c_begin + i;
+      body_block(slot_at(i % NBUF), min(kBlockTokens, st.nb - ch * kBlockTokens));
+    }
+  }
+
+  // ---- partial of this split (row 0): o = O_raw + Z + value-outlier corrections
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * D;
+  float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * 2;
+  const float lsum = row16_sum(l_run);
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    const float z = lane_bcast(zacc[0], (l & 48) | (nt >> 1));
+    const float o = oacc[nt][0] + z + ocorr[16 * nt + n16];
+    if (g4 == 0) opart[16 * nt + n16] = o;
+  }
+  if (l == 0) {
+    mlpart[0] = m_run;
+    mlpart[1] = lsum;
+  }
+}
+
+// Ring depth: two slots keep twelve wavefronts per CU within the LDS.
+template <int OUTK, bool ROPE>
+hipError_t launch_lut(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
+  using R = Rec3<OUTK>;
+  if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm ||
+      (OUTK > 0 && (L.off_ko != R::off_ko || L.off_vo != R::off_vo)))
+    return hipSuccess;
+  constexpr int NB = 2;
+  static int resident = 0;
+  if (resident == 0) {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_lut_kernel<OUTK, ROPE, NB>, 64, 0) !=
+            hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return hipErrorInvalidValue;
+    resident = std::max(1, per_cu) * std::max(1, cus);
+  }
+  *waves = resident;
+  if (!j.q) return hipSuccess;  // query only
+  hipLaunchKernelGGL((decode_lut_kernel<OUTK, ROPE, NB>), dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return launch_decode_merge(L, j, s);
+}
+
+hipError_t dispatch_lut(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
+  *waves = 0;
+  if (L.G != 1 || L.kb != 3 || L.vb != 3 || L.k_inner || L.k_hybrid || L.v_had || L.v_group != 32)
+    return hipSuccess;
+  const bool rope = L.pre_rope != 0;
+  switch (L.outk) {
+    case 0: return rope ? launch_lut<0, true>(L, j, s, waves) : launch_lut<0, false>(L, j, s, waves);
+    case 1: return rope ? launch_lut<1, true>(L, j, s, waves) : launch_lut<1, false>(L, j, s, waves);
+    case 2: return rope ? launch_lut<2, true>(L, j, s, waves) : launch_lut<2, false>(L, j, s, waves);
+    default: return hipSuccess;
+  }
+}
+
+}  // namespace
+
+int decode_lut_waves(const LayerDesc& L) {
+  DecodeJob none{};
+  int waves = 0;
+  dispatch_lut(L, none, nullptr, &waves);
+  return waves;
+}
+
+hipError_t launch_decode_lut(const LayerDesc& L, const DecodeJob& j, hipStream_t s, bool* used) {
+  int waves = 0;
+  const hipError_t e = dispatch_lut(L, j, s, &waves);
+  *used = waves > 0;
+  return e;
+}
+
+}  // namespace kvq

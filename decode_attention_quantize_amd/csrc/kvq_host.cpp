@@ -16,6 +16,8 @@ namespace kvq {
 hipError_t launch_decode_generic(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
 hipError_t launch_decode_fast(const LayerDesc& L, const DecodeJob& job, hipStream_t s, bool* used);
 int decode_fast_waves(const LayerDesc& L);  // resident wavefront target, 0 if the layer is not covered
+hipError_t launch_decode_lut(const LayerDesc& L, const DecodeJob& job, hipStream_t s, bool* used);
+int decode_lut_waves(const LayerDesc& L);
 }  // namespace kvq
 
 using kvq::LayerDesc;
@@ -414,10 +416,15 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   j.st = kvq::TokenState{L.n, L.s_eff, L.nb, L.r};
   bool used = false;
   hipError_t e = hipSuccess;
-  const int fast_waves = c->force_generic ? 0 : kvq::decode_fast_waves(L.d);
+  // matrix-core kernels first (uniform 2/4/8-bit; 3-bit tables with outliers
+  // and pre-RoPE keys for MHA layers), the LDS-staged kernel otherwise
+  int fast_waves = c->force_generic ? 0 : kvq::decode_fast_waves(L.d);
   if (fast_waves > 0) {
     plan_splits(*c, j.st, fast_waves, j);
     e = kvq::launch_decode_fast(L.d, j, s, &used);
+  } else if ((fast_waves = c->force_generic ? 0 : kvq::decode_lut_waves(L.d)) > 0) {
+    plan_splits(*c, j.st, fast_waves, j);
+    e = kvq::launch_decode_lut(L.d, j, s, &used);
   }
   if (!used) {
     plan_splits(*c, j.st, 0, j);

@@ -106,6 +106,8 @@ struct DecodeJob {
   int32_t fp16_chunks, sink_chunks, win_chunk0;
   int64_t ml_off;         // matrix-core path: float offset of the (max, sum) records
 };
-hipError_t launch_decode(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
+// Log-sum-exp merge of matrix-core split partials into job.out (one
+// (unit, query row) per workgroup); undoes the value rotation when set.
+hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
 
 }  // namespace kvq

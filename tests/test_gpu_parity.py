@@ -57,7 +57,7 @@ def test_edge_cases(name):
     _check_all(name, EDGE[name])
 
 
-@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C5r"])
+@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C4r", "C5r"])
 def test_reduced_configs_general_kernel(name, monkeypatch):
     """The same workloads through the LDS-staged decode kernel (the path every
     scheme the matrix-core kernel does not cover takes)."""
