@@ -98,7 +98,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
   __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF >= 3 ? R::loads * 1024 : 16];
   __shared__ uint32_t lutk[64], lutv[64];
   __shared__ __attribute__((aligned(16))) _Float16 ptile[16][32];
-  __shared__ float scorr[32], ocorr[D], qs[D];
+  __shared__ float ocorr[D], qs[D];
   __shared__ float2 tb[64];
   __shared__ float thf[64];
   lds_u8* const slot0 = (lds_u8*)ring0;
@@ -341,12 +341,10 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       kw[0] = k0[0]; kw[1] = k0[1]; kw[2] = k1[0]; kw[3] = k1[1]; kw[4] = k2[0]; kw[5] = k2[1];
     }
 
-    // ---- key outliers: (x_out - k_dense) * W_t[col] into scorr[t]
+    // ---- key outliers: lane OUTK*t + e computes (x_out - k_dense) * W_t[col]
+    // for entry e of token t; the token's sum is fetched by the score lanes
+    float kcorr = 0.f;
     if constexpr (OUTK > 0) {
-      if (l < 32) scorr[l] = 0.f;
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       const int t = OUTK == 2 ? (l >> 1) : l;
       if (t < count && (OUTK == 2 || l < 32)) {
         const uint32_t ent = *reinterpret_cast<lds_u32*>(rb + R::off_ko + 4 * (t * OUTK + (OUTK == 2 ? (l & 1) : 0)));
@@ -367,11 +365,9 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
         } else {
           w = qs[col];
         }
-        atomicAdd(&scorr[t], (val - kd) * w);
+        kcorr = (val - kd) * w;
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if constexpr (OUTK == 2) kcorr += dppf<kQuadXor1>(kcorr);
     }
 
     // ---- key codes -> levels (pairs through lutk), dequantize, dot with W
@@ -381,7 +377,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       uint32_t lv[16];
 #pragma unroll
       for (int m = 0; m < 16; ++m) lv[m] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lutk) + pair_off(kw, 96 * nt + 6 * m));
-      float acc = 0.f;
+      float acc4[4] = {0.f, 0.f, 0.f, 0.f};  // independent chains
 #pragma unroll
       for (int m = 0; m < 16; ++m) {
         const half2v lp = __builtin_bit_cast(half2v, lv[m]);
@@ -393,12 +389,13 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
           const u32x4& zv = el < 16 ? za[p >> 3] : zb[p >> 3];
           const half8 s8 = h8(sv), z8 = h8(zv);
           const float kd = fmaf(static_cast<float>(lp[e]), static_cast<float>(s8[p & 7]), static_cast<float>(z8[p & 7]));
-          acc = fmaf(kd, el < 16 ? wa[p] : wb[p], acc);
+          acc4[el & 3] = fmaf(kd, el < 16 ? wa[p] : wb[p], acc4[el & 3]);
         }
       }
       if constexpr (ROPE) rotate_w();  // to the next token of this lane
-      acc = lanes4_sum(acc);
-      if constexpr (OUTK > 0) acc += scorr[16 * nt + n16];
+      float acc = lanes4_sum((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]));
+      if constexpr (OUTK > 0)
+        acc += __int_as_float(__builtin_amdgcn_ds_bpermute((OUTK * (16 * nt + n16)) << 2, __float_as_int(kcorr)));
       sc[nt] = 16 * nt + n16 < count ? acc * kscale : -INFINITY;
     }
 
@@ -531,14 +528,15 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
   }
 }
 
-// Ring depth: two slots keep twelve wavefronts per CU within the LDS.
 template <int OUTK, bool ROPE>
 hipError_t launch_lut(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
   using R = Rec3<OUTK>;
   if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm ||
       (OUTK > 0 && (L.off_ko != R::off_ko || L.off_vo != R::off_vo)))
     return hipSuccess;
-  constexpr int NB = 2;
+  // three slots for records with outliers (LDS allows them at two
+  // wavefronts per SIMD), two otherwise
+  constexpr int NB = OUTK > 0 ? 3 : 2;
   static int resident = 0;
   if (resident == 0) {
     int per_cu = 0, dev = 0, cus = 0;
