@@ -559,102 +559,111 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   }
 }
 
-// Log-sum-exp merge of the split partials of one (unit, query row).  Thread
-// t owns channels 4*(t % 32) .. +3 of splits t / 32, t / 32 + 8, ...: every
-// partial vector and every (max, sum) pair is requested at once, so the merge
-// costs about two memory round trips.  The eight per-thread sums meet in LDS.
-// Values stored Hadamard-rotated are rotated back (c * H * o, H Sylvester).
+// Log-sum-exp merge of the split partials of one unit (all its query rows).
+// 256 threads = 8 groups of 32; thread (group, q) owns channels 4q..4q+3.
+// With G rows, 8/G groups share a row (G <= 8) and take its splits in turn;
+// each group pulls every (max, sum) pair of its row from LDS, so the row
+// maximum needs no extra pass, and requests its partial vectors eight at a
+// time.  The groups of a row meet in LDS; values stored Hadamard-rotated are
+// rotated back there (c * H * o, H Sylvester).
 __global__ void __launch_bounds__(256) decode_merge_kernel(LayerDesc L, DecodeJob J) {
   // the split plan keeps nsplit <= max(kMaxBodySplits, kMaxFp16Splits) = 256
   constexpr int kMaxSplits = 256;
-  static_assert(kMaxBodySplits <= kMaxSplits && kMaxFp16Splits <= kMaxSplits, "one split per thread");
-  constexpr int kPer = kMaxSplits / 8;  // splits per thread
-  __shared__ float wts[kMaxSplits];
+  static_assert(kMaxBodySplits <= kMaxSplits && kMaxFp16Splits <= kMaxSplits, "split bound");
+  constexpr int kMaxRows = kMaxGroupRows;
+  __shared__ float ms[kMaxSplits * kMaxRows], ls[kMaxSplits * kMaxRows];
   __shared__ float red[8][D];
-  __shared__ float scal[2][4];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int so = tid >> 5, cq = tid & 31;
-  const int u = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x, grp = tid >> 5, cq = tid & 31;
+  const int u = blockIdx.x;
   const int G = L.G, nsplit = J.nsplit;
   const int b = u / L.Hkv, h = u % L.Hkv;
   const float* obase = J.partials + static_cast<int64_t>(u) * nsplit * G * D;
   const float* mlbase = J.partials + J.ml_off + static_cast<int64_t>(u) * nsplit * G * 2;
-
-  f32x4 v[kPer];
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = so + 8 * k;
-    v[k] = i < nsplit ? *reinterpret_cast<const f32x4*>(obase + (static_cast<int64_t>(i) * G + r) * D + 4 * cq)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = tid; i < nsplit * G; i += 256) {
+    ms[i] = mlbase[2 * i];
+    ls[i] = mlbase[2 * i + 1];
   }
-  float m0 = -INFINITY, l0 = 0.f;
-  if (tid < nsplit) {
-    m0 = mlbase[(tid * G + r) * 2];
-    l0 = mlbase[(tid * G + r) * 2 + 1];
-  }
-  float M = m0;
-  M = fmaxf(M, xshflf<1>(M));
-  M = fmaxf(M, xshflf<2>(M));
-  M = fmaxf(M, xshflf<4>(M));
-  M = fmaxf(M, xshflf<8>(M));
-  M = fmaxf(M, xshflf<16>(M));
-  M = fmaxf(M, xshflf<32>(M));
-  if (l == 0) scal[0][w] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(scal[0][0], scal[0][1]), fmaxf(scal[0][2], scal[0][3]));
-  const float w0 = m0 == -INFINITY ? 0.f : exp2f(m0 - M);
-  if (tid < nsplit) wts[tid] = w0;
-  float Ls = l0 * w0;
-  Ls += xshflf<1>(Ls);
-  Ls += xshflf<2>(Ls);
-  Ls += xshflf<4>(Ls);
-  Ls += xshflf<8>(Ls);
-  Ls += xshflf<16>(Ls);
-  Ls += xshflf<32>(Ls);
-  if (l == 0) scal[1][w] = Ls;
-  __syncthreads();
-  f32x4 a = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int k = 0; k < kPer; ++k) {
-    const int i = so + 8 * k;
-    const float wt = i < nsplit ? wts[i] : 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = fmaf(v[k][e], wt, a[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) red[so][4 * cq + e] = a[e];
-  __syncthreads();
-  if (w != 0) return;
-  const float Lt = (scal[1][0] + scal[1][1]) + (scal[1][2] + scal[1][3]);
-  float y[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    float t = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) t += red[k][2 * l + e];
-    y[e] = t / Lt;
-  }
-  float y0 = y[0], y1 = y[1];
-  if (L.v_had) {
-    // lane l holds channels 2l, 2l+1: the first butterfly is in-lane
-    const float t0 = y0 + y1, t1 = y0 - y1;
-    y0 = t0;
-    y1 = t1;
-#pragma unroll
-    for (int hb = 1; hb < 64; hb <<= 1) {
-      const float o0 = __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ hb) << 2, __float_as_int(y0)));
-      const float o1 = __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ hb) << 2, __float_as_int(y1)));
-      const bool hi = (l & hb) != 0;
-      y0 = hi ? o0 - y0 : y0 + o0;
-      y1 = hi ? o1 - y1 : y1 + o1;
+  const int lpr = G >= 8 ? 1 : 8 / G;      // groups per row
+  const int so = grp % lpr;                // this group's first split
+  for (int r = grp / lpr; r < G; r += 8 / lpr) {
+    // row maximum and sum over all splits (32 lanes, then the group)
+    float M = -INFINITY;
+    for (int i = cq; i < nsplit; i += 32) M = fmaxf(M, ms[i * G + r]);
+    M = fmaxf(M, xshflf<1>(M));
+    M = fmaxf(M, xshflf<2>(M));
+    M = fmaxf(M, xshflf<4>(M));
+    M = fmaxf(M, xshflf<8>(M));
+    M = fmaxf(M, xshflf<16>(M));
+    float Ls = 0.f;
+    for (int i = cq; i < nsplit; i += 32) {
+      const float mi = ms[i * G + r];
+      Ls = fmaf(ls[i * G + r], mi == -INFINITY ? 0.f : exp2f(mi - M), Ls);
     }
-    const float c = static_cast<float>(L.had_scale);
-    y0 *= c;
-    y1 *= c;
+    Ls += xshflf<1>(Ls);
+    Ls += xshflf<2>(Ls);
+    Ls += xshflf<4>(Ls);
+    Ls += xshflf<8>(Ls);
+    Ls += xshflf<16>(Ls);
+    // weighted sum of this group's splits so, so + lpr, ...
+    constexpr int kBatch = 8;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = so; i0 < nsplit; i0 += kBatch * lpr) {
+      f32x4 v[kBatch];
+      float wt[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int i = i0 + k * lpr;
+        v[k] = i < nsplit ? *reinterpret_cast<const f32x4*>(obase + (static_cast<int64_t>(i) * G + r) * D + 4 * cq)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+        const float mi = i < nsplit ? ms[i * G + r] : -INFINITY;
+        wt[k] = mi == -INFINITY ? 0.f : exp2f(mi - M);
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[e] = fmaf(v[k][e], wt[k], a[e]);
+    }
+    if (lpr > 1) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[grp][4 * cq + e] = a[e];
+    }
+    __syncthreads();
+    if (so == 0) {
+      if (lpr > 1) {
+        for (int k = 1; k < lpr; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) a[e] += red[grp + k][4 * cq + e];
+      }
+      float y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = a[e] / Ls;
+      if (L.v_had) {
+        // channels 4q + e: butterflies over e in-lane, over q across the group
+        float t0 = y[0] + y[1], t1 = y[0] - y[1], t2 = y[2] + y[3], t3 = y[2] - y[3];
+        y[0] = t0 + t2;
+        y[1] = t1 + t3;
+        y[2] = t0 - t2;
+        y[3] = t1 - t3;
+        const int lane = tid & 63;
+#pragma unroll
+        for (int hb = 1; hb < 32; hb <<= 1) {
+          const bool hi = (cq & hb) != 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float o = __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ hb) << 2, __float_as_int(y[e])));
+            y[e] = hi ? o - y[e] : y[e] + o;
+          }
+        }
+        const float c = static_cast<float>(L.had_scale);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] *= c;
+      }
+      float* op = J.out + (static_cast<int64_t>(b) * L.Hq + h * G + r) * D + 4 * cq;
+      *reinterpret_cast<f32x4*>(op) = f32x4{y[0], y[1], y[2], y[3]};
+    }
+    __syncthreads();
   }
-  float* op = J.out + (static_cast<int64_t>(b) * L.Hq + h * G + r) * D;
-  op[2 * l] = y0;
-  op[2 * l + 1] = y1;
 }
 
 // Ring depth and residency.  MHA layers (one query row per kv head) carry
@@ -726,7 +735,9 @@ hipError_t dispatch(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* 
 }  // namespace
 
 hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& j, hipStream_t s) {
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(L.units, L.G), dim3(256), 0, s, L, j);
+  // every group of the workgroup runs the same number of row passes
+  if (L.G < 1 || L.G > kMaxGroupRows || (L.G & (L.G - 1)) != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(L.units), dim3(256), 0, s, L, j);
   return hipGetLastError();
 }
 
