@@ -29,11 +29,13 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
-# Per-source additions.  The matrix-core decode keeps its MFMA accumulators
-# in ordinary VGPRs: it rescales and reads them on the VALU every block, and
-# accumulation registers would cost a copy each way.
+# Per-source additions.  The matrix-core decodes keep their MFMA accumulators
+# in ordinary VGPRs: they rescale and read them on the VALU every block, and
+# accumulation registers would cost a copy each way (and count against the
+# same per-lane register budget that sets occupancy).
 EXTRA = {
     "kvq_decode_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "kvq_decode_lut.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
 }
 
 

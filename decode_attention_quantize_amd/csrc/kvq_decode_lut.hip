@@ -4,16 +4,19 @@
 // and keys cached before RoPE (KVQuant (ii)).
 //
 // One wavefront per split, one query row per kv head.  A 32-token block:
-//   keys    lane (n, g) owns tokens n and n + 16 and the 32 channels
-//           16g..16g+15, 64+16g..64+16g+15 (RoPE pairs (i, i + 64) in one
-//           lane).  Codes are decoded two at a time through a 64-entry LDS
-//           table of level pairs, dequantized in fp32 (L * s + z with one
-//           v_fma_mix) and dotted with the query rotated back to each token's
-//           position: q . R(p) k = (R(-p) q) . k.  The rotated queries move
-//           from block to block by one fixed rotation per pair (fp32), and are
-//           recomputed exactly (fp64 angle reduction) at the start of a split.
-//   scores  summed over the four lanes of a token, plus the outlier
-//           corrections (x_out - k_dense) * (R(-p) q)[col] gathered in LDS.
+//   keys    lane l owns RoPE pair (l, l + 64) for all 32 tokens; a token's
+//           two codes form one 6-bit field that indexes a 64-entry LDS table
+//           of level pairs.  Keys are dequantized in fp32 (L * s + z) and
+//           dotted with the query rotated back to the token's position,
+//           q . R(p) k = (R(-p) q) . k: the lane steps its pair of the
+//           rotated query one position per token (fp32 rotation by theta_l,
+//           tokens 0..15 and 16..31 as two chains), and both chains are
+//           recomputed exactly (fp64 angle reduction) at each split start.
+//   scores  the 64 lanes' partial dots of 32 tokens are summed by a
+//           transpose-reduce (permlane swaps across halves and rows, then DPP
+//           inside rows) that leaves token l/2 in lanes l; the outlier
+//           corrections (x_out - k_dense) * (R(-p) q)[col] are computed in
+//           those same lanes.
 //   values  O += sum_t (p_t s_tg) L[code] on v_mfma_f32_16x16x32_f16, with the
 //           level pairs from a second LDS table as the B operand, the
 //           zero points through one more MFMA, and the value outliers
@@ -61,13 +64,31 @@ __device__ __forceinline__ void rot_cs(double p, double theta, float& c, float& 
   cs_rev(static_cast<float>(r * kInvTwoPi), c, s);
 }
 
-// 3-bit fields of a lane's chunk (six words): the six bits at bit offset
-// `bit` of the 192-bit stream, scaled by 4 (a byte offset into a table of
-// 32-bit entries).
-__device__ __forceinline__ uint32_t pair_off(const uint32_t (&w)[6], int bit) {
+// cos/sin of a (radians) to fp32 rounding: reduction modulo 2 pi in binary64,
+// Taylor series of degree 12 at a/8 (|a/8| <= pi/8, truncation < 1e-14),
+// then three angle doublings.  For the per-lane rotation constants that are
+// applied many times in a row.
+__device__ __forceinline__ void cs_accurate(double a, float& c, float& s) {
+  const double r = fma(-rint(a * kInvTwoPi), kTwoPi, a) * 0.125;
+  const double x2 = r * r;
+  double sn = r * (1.0 + x2 * (-1.0 / 6 + x2 * (1.0 / 120 + x2 * (-1.0 / 5040 + x2 * (1.0 / 362880 + x2 * (-1.0 / 39916800))))));
+  double cs = 1.0 + x2 * (-0.5 + x2 * (1.0 / 24 + x2 * (-1.0 / 720 + x2 * (1.0 / 40320 + x2 * (-1.0 / 3628800 + x2 * (1.0 / 479001600))))));
+  for (int k = 0; k < 3; ++k) {
+    const double s2 = 2.0 * sn * cs;
+    cs = 1.0 - 2.0 * sn * sn;
+    sn = s2;
+  }
+  c = static_cast<float>(cs);
+  s = static_cast<float>(sn);
+}
+
+// Two 3-bit codes of a lane's chunk (six words) as one 6-bit field at bit
+// offset `bit` of the 192-bit stream: the LDS address of the entry it selects
+// in a table of 32-bit level pairs at `base`.
+__device__ __forceinline__ uint32_t pair_addr(const uint32_t (&w)[6], int bit, uint32_t base) {
   const int q = bit >> 5, r = bit & 31;
-  const uint32_t v = r <= 26 ? (w[q] >> r) : __builtin_amdgcn_alignbit(w[q + 1], w[q], r);
-  return (v << 2) & 0xFCu;
+  const uint32_t f = r <= 26 ? __builtin_amdgcn_ubfe(w[q], r, 6) : (__builtin_amdgcn_alignbit(w[q + 1], w[q], r) & 63u);
+  return (f << 2) + base;
 }
 
 // 3-bit code of (token slot j, channel c) in an LDS copy of a record section
@@ -81,8 +102,7 @@ __device__ __forceinline__ int chunk3_lds(const lds_u8* codes, int lane, int e) 
   return static_cast<int>(__builtin_amdgcn_alignbit(hi, lo, bit & 31) & 7u);
 }
 __device__ __forceinline__ int k3_lds(const lds_u8* codes, int j, int c) {
-  const int g = (c & 63) >> 4, jj = ((c >> 6) << 1) | ((c & 15) >> 3);
-  return chunk3_lds(codes, 16 * g + (j & 15), 32 * (j >> 4) + 8 * jj + (c & 7));
+  return chunk3_lds(codes, c & 63, 2 * j + (c >> 6));
 }
 __device__ __forceinline__ int v3_lds(const lds_u8* codes, int j, int c) {
   return chunk3_lds(codes, 16 * (j >> 3) + (c & 15), 8 * (c >> 4) + (j & 7));
@@ -93,14 +113,16 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
   using R = Rec3<OUTK>;
   static_assert(NBUF >= 2 && NBUF <= 3, "ring of 2 or 3 slots");
   static_assert(OUTK >= 0 && OUTK <= 2, "one outlier entry per lane");
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[R::loads * 1024];
-  __shared__ __attribute__((aligned(16))) uint8_t ring1[R::loads * 1024];
-  __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF >= 3 ? R::loads * 1024 : 16];
+  // a slot holds exactly one record: lanes past the record's end issue no copy
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[R::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[R::bytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF >= 3 ? R::bytes : 16];
   __shared__ uint32_t lutk[64], lutv[64];
-  __shared__ __attribute__((aligned(16))) _Float16 ptile[16][32];
+  __shared__ __attribute__((aligned(16))) _Float16 ptile[32];  // P of the query row
   __shared__ float ocorr[D], qs[D];
   __shared__ float2 tb[64];
   __shared__ float thf[64];
+  __shared__ double thd[64];
   lds_u8* const slot0 = (lds_u8*)ring0;
   lds_u8* const slot1 = (lds_u8*)ring1;
   lds_u8* const slot2 = (lds_u8*)ring2;
@@ -140,18 +162,21 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
   ocorr[64 + l] = 0.f;
   const double theta_l = pow(static_cast<double>(L.rope_base), -2.0 * l / D);
   thf[l] = static_cast<float>(theta_l);
+  thd[l] = theta_l;
+  // rotation of pair l by one and by 16 positions
+  float c1 = 1.f, s1 = 0.f, c16 = 1.f, s16 = 0.f;
+  if constexpr (ROPE) {
+    cs_accurate(theta_l, c1, s1);
+    cs_accurate(16.0 * theta_l, c16, s16);
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // this lane's pairs p = 0..15: channels 16g + p and 64 + 16g + p
-  float qa[16], qb[16];
-  double th[16];  // RoPE frequency of each pair, binary64
-#pragma unroll
-  for (int p = 0; p < 16; ++p) {
-    qa[p] = qs[16 * g4 + p];
-    qb[p] = qs[64 + 16 * g4 + p];
-    th[p] = ROPE ? pow(static_cast<double>(L.rope_base), -2.0 * (16 * g4 + p) / D) : 0.0;
-  }
+  // (query halves qs, binary64 frequencies thd: read from LDS where needed)
+  const float* qa = qs + 16 * g4;
+  const float* qb = qs + 64 + 16 * g4;
+  const double* th = thd + 16 * g4;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[8];
@@ -159,21 +184,18 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) oacc[nt] = {0.f, 0.f, 0.f, 0.f};
 
-  // online softmax of the 32 scores (tokens n16, 16 + n16 in every lane);
-  // P (fp16) of the query row lands in ptile row 0
-  auto softmax_tile = [&](float s0, float s1) __attribute__((always_inline)) -> half8 {
-    const float bm = row16_max(fmaxf(s0, s1));
+  // online softmax of the 32 scores (lanes 2t and 2t + 1 hold token t);
+  // P (fp16) of the query row lands in ptile, l_run keeps this lane's share
+  // of the row sum (even lanes)
+  auto softmax_tile = [&](float sv) __attribute__((always_inline)) -> half8 {
+    const float bm = wave_max(sv);
     const float mn = fmaxf(m_run, bm);
     const float mr = mn == -INFINITY ? 0.f : mn;
     const float alpha = fexp2(m_run - mr);
-    const _Float16 p0 = static_cast<_Float16>(fexp2(s0 - mr));
-    const _Float16 p1 = static_cast<_Float16>(fexp2(s1 - mr));
-    l_run = fmaf(l_run, alpha, static_cast<float>(p0) + static_cast<float>(p1));
+    const _Float16 pt = static_cast<_Float16>(fexp2(sv - mr));
+    l_run = fmaf(l_run, alpha, (l & 1) ? 0.f : static_cast<float>(pt));
     m_run = mn;
-    if (g4 == 0) {
-      ptile[0][n16] = p0;
-      ptile[0][16 + n16] = p1;
-    }
+    if (!(l & 1)) ptile[l >> 1] = pt;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) oacc[nt][0] *= alpha;
@@ -184,7 +206,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    return n16 == 0 ? *reinterpret_cast<const half8*>(&ptile[0][8 * g4]) : h8(0u, 0u, 0u, 0u);
+    return n16 == 0 ? *reinterpret_cast<const half8*>(&ptile[8 * g4]) : h8(0u, 0u, 0u, 0u);
   };
   // sum over the four lanes that hold one token's partial dots
   auto lanes4_sum = [&](float v) __attribute__((always_inline)) {
@@ -193,36 +215,25 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     return v;
   };
 
-  // ---- rotated queries of this lane's two tokens, W = R(-pos) q per pair
-  // W = R(-pos) q per pair for this lane's tile-0 token; the tile-1 token
-  // (16 positions later) and the next block's tile-0 token (16 more) follow
-  // by the same fixed rotation
-  float wa[16], wb[16];
-  float rc[16], rs[16];  // rotation by 16 positions, per pair
+  // ---- this lane's pair of the rotated query, W = R(-pos) q, at the
+  // block's tokens 0 (w1) and 16 (w2); each chain steps one position per token
+  float w1a = q_lo, w1b = q_hi, w2a = q_lo, w2b = q_hi;
   float tc = 1.f, ts = 0.f, trc = 1.f, trs = 0.f;  // (cos, sin)(theta_l * block start), step
-  auto rotate_w = [&]() __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const float a = wa[p], bq = wb[p];
-      wa[p] = fmaf(rc[p], a, rs[p] * bq);
-      wb[p] = fmaf(rc[p], bq, -(rs[p] * a));
-    }
+  const uint32_t lutv_at = lds_off((lds_u8*)lutv), lutk_at = lds_off((lds_u8*)lutk);
+  auto rot_by = [](float& a, float& b, float c, float s) __attribute__((always_inline)) {
+    const float a0 = a, b0 = b;
+    a = fmaf(c, a0, s * b0);
+    b = fmaf(c, b0, -(s * a0));
   };
   auto init_w = [&](int pos_first) __attribute__((always_inline)) {
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      if constexpr (ROPE) {
-        float c, s;
-        rot_cs(static_cast<double>(pos_first + n16), th[p], c, s);
-        wa[p] = fmaf(qa[p], c, qb[p] * s);
-        wb[p] = fmaf(qb[p], c, -(qa[p] * s));
-        rot_cs(16.0, th[p], c, s);
-        rc[p] = c;
-        rs[p] = s;
-      } else {
-        wa[p] = qa[p];
-        wb[p] = qb[p];
-      }
+    if constexpr (ROPE) {
+      float c, s;
+      rot_cs(static_cast<double>(pos_first), theta_l, c, s);
+      w1a = fmaf(q_lo, c, q_hi * s);
+      w1b = fmaf(q_hi, c, -(q_lo * s));
+      rot_cs(static_cast<double>(pos_first + 16), theta_l, c, s);
+      w2a = fmaf(q_lo, c, q_hi * s);
+      w2b = fmaf(q_hi, c, -(q_lo * s));
     }
   };
 
@@ -272,7 +283,9 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       u32x4 vv[8];
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) vv[nt] = ld16(vf + (static_cast<int64_t>(s0 / 8 + g4) * D + 16 * nt + n16) * 8);
-      const half8 pa = softmax_tile(sc[0], sc[1]);
+      // token l/2 of the chunk: tile (l/2)/16, lane (l/2)%16 of row 0
+      const float sa0 = lane_bcast(sc[0], (l >> 1) & 15), sa1 = lane_bcast(sc[1], (l >> 1) & 15);
+      const half8 pa = softmax_tile(l < 32 ? sa0 : sa1);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
     }
@@ -313,45 +326,29 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     const lds_u8* rb = rec;
     typedef __attribute__((address_space(3))) const uint32_t lds_u32;
     typedef __attribute__((address_space(3))) const uint16_t lds_u16;
-    uint32_t kw[6];
-    u32x4 sa[2], sb[2], za[2], zb[2];
+    uint32_t kw[6];  // this lane's 64 key codes: token t's pair in bits 6t..6t+5
     {
       const uint32_t ak = r0 + 24 * l;
       u32x2 k0 = dsr8<0>(ak), k1 = dsr8<8>(ak), k2 = dsr8<16>(ak);
-      const uint32_t am = r0 + R::off_km + 32 * g4;
-      sa[0] = dsr16<0>(am);
-      sa[1] = dsr16<16>(am);
-      sb[0] = dsr16<128>(am);
-      sb[1] = dsr16<144>(am);
-      za[0] = dsr16<256>(am);
-      za[1] = dsr16<272>(am);
-      zb[0] = dsr16<384>(am);
-      zb[1] = dsr16<400>(am);
       lds_wait();
       pin(k0);
       pin(k1);
       pin(k2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        pin(sa[e]);
-        pin(sb[e]);
-        pin(za[e]);
-        pin(zb[e]);
-      }
       kw[0] = k0[0]; kw[1] = k0[1]; kw[2] = k1[0]; kw[3] = k1[1]; kw[4] = k2[0]; kw[5] = k2[1];
     }
+    const lds_u16* km = reinterpret_cast<lds_u16*>(rb + R::off_km);
+    const float sa = h2f(km[l]), sb = h2f(km[64 + l]), za = h2f(km[D + l]), zb = h2f(km[D + 64 + l]);
 
-    // ---- key outliers: lane OUTK*t + e computes (x_out - k_dense) * W_t[col]
-    // for entry e of token t; the token's sum is fetched by the score lanes
+    // ---- key outliers: lanes 2t, 2t + 1 compute (x_out - k_dense) * W_t[col]
+    // for the entries of token t (one each, or the same one for a single entry)
     float kcorr = 0.f;
     if constexpr (OUTK > 0) {
-      const int t = OUTK == 2 ? (l >> 1) : l;
-      if (t < count && (OUTK == 2 || l < 32)) {
+      const int t = l >> 1;
+      if (t < count) {
         const uint32_t ent = *reinterpret_cast<lds_u32*>(rb + R::off_ko + 4 * (t * OUTK + (OUTK == 2 ? (l & 1) : 0)));
         const int col = static_cast<int>(ent & 0x7Fu);  // columns are < 128
         const float val = h2f(static_cast<uint16_t>(ent >> 16));
         const int code = k3_lds(rb, t, col);
-        const lds_u16* km = reinterpret_cast<lds_u16*>(rb + R::off_km);
         const float kd = fmaf(h2f(static_cast<uint16_t>(lutk[9 * code])), h2f(km[col]), h2f(km[D + col]));
         const int i = col & 63;
         float w;
@@ -360,8 +357,8 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
           float st_, ct_;
           cs_rev(static_cast<float>(t) * thf[i] * static_cast<float>(kInvTwoPi), ct_, st_);
           const float c = base.x * ct_ - base.y * st_;
-          const float s = base.y * ct_ + base.x * st_;
-          w = col < 64 ? fmaf(qs[i], c, qs[64 + i] * s) : fmaf(qs[64 + i], c, -(qs[i] * s));
+          const float sn = base.y * ct_ + base.x * st_;
+          w = col < 64 ? fmaf(qs[i], c, qs[64 + i] * sn) : fmaf(qs[64 + i], c, -(qs[i] * sn));
         } else {
           w = qs[col];
         }
@@ -370,34 +367,49 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       if constexpr (OUTK == 2) kcorr += dppf<kQuadXor1>(kcorr);
     }
 
-    // ---- key codes -> levels (pairs through lutk), dequantize, dot with W
-    float sc[2];
+    // ---- keys: dequantize this lane's pair for tokens k and 16 + k, dot with
+    // the rotated query, and fold the two tokens across the lane halves
+    uint32_t lk[32];  // level pairs of the 32 tokens, all requested before one wait
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      uint32_t lv[16];
+    for (int t = 0; t < 32; ++t) lk[t] = dsr4<0>(pair_addr(kw, 6 * t, lutk_at));
+    lds_wait();
 #pragma unroll
-      for (int m = 0; m < 16; ++m) lv[m] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lutk) + pair_off(kw, 96 * nt + 6 * m));
-      float acc4[4] = {0.f, 0.f, 0.f, 0.f};  // independent chains
+    for (int t = 0; t < 32; ++t) pin(lk[t]);
+    float e1[16];
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        const half2v lp = __builtin_bit_cast(half2v, lv[m]);
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int el = 2 * m + e;  // 0..15: channel 16g + el; 16..31: 64 + 16g + el - 16
-          const int p = el & 15;
-          const u32x4& sv = el < 16 ? sa[p >> 3] : sb[p >> 3];
-          const u32x4& zv = el < 16 ? za[p >> 3] : zb[p >> 3];
-          const half8 s8 = h8(sv), z8 = h8(zv);
-          const float kd = fmaf(static_cast<float>(lp[e]), static_cast<float>(s8[p & 7]), static_cast<float>(z8[p & 7]));
-          acc4[el & 3] = fmaf(kd, el < 16 ? wa[p] : wb[p], acc4[el & 3]);
-        }
+    for (int k = 0; k < 16; ++k) {
+      const half2v lp1 = __builtin_bit_cast(half2v, lk[k]);
+      const half2v lp2 = __builtin_bit_cast(half2v, lk[16 + k]);
+      const float d1 = fmaf(fmaf(static_cast<float>(lp1[0]), sa, za), w1a, fmaf(static_cast<float>(lp1[1]), sb, zb) * w1b);
+      const float d2 = fmaf(fmaf(static_cast<float>(lp2[0]), sa, za), w2a, fmaf(static_cast<float>(lp2[1]), sb, zb) * w2b);
+      const float2 x = swap32(d1, d2);
+      e1[k] = x.x + x.y;  // token k + 16 (l / 32), lanes l and l ^ 32
+      if constexpr (ROPE) {
+        if (k < 15) rot_by(w1a, w1b, c1, s1);
+        rot_by(w2a, w2b, c1, s1);
       }
-      if constexpr (ROPE) rotate_w();  // to the next token of this lane
-      float acc = lanes4_sum((acc4[0] + acc4[1]) + (acc4[2] + acc4[3]));
-      if constexpr (OUTK > 0)
-        acc += __int_as_float(__builtin_amdgcn_ds_bpermute((OUTK * (16 * nt + n16)) << 2, __float_as_int(kcorr)));
-      sc[nt] = 16 * nt + n16 < count ? acc * kscale : -INFINITY;
     }
+    if constexpr (ROPE) {  // chain 1 restarts 32 positions on, chain 2 16 after it
+      w1a = w2a;
+      w1b = w2b;
+      rot_by(w2a, w2b, c16, s16);
+    }
+    // remaining folds: rows (xor 16), then xor 8, xor 7, xor 2 inside rows;
+    // the lane keeps the token whose index bit matches its own lane bit
+    float e2[8], e3[4], e4[2];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float2 x = swap16(e1[k], e1[k + 8]);
+      e2[k] = x.x + x.y;
+    }
+    const bool b3 = (l & 8) != 0, b2 = (l & 4) != 0, b1 = (l & 2) != 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) e3[k] = (b3 ? e2[k + 4] : e2[k]) + dppf<kRowRor8>(b3 ? e2[k] : e2[k + 4]);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) e4[k] = (b2 ? e3[k + 2] : e3[k]) + dppf<kRowHalfMirror>(b2 ? e3[k] : e3[k + 2]);
+    float dot = (b1 ? e4[1] : e4[0]) + dppf<kQuadXor2>(b1 ? e4[0] : e4[1]);
+    dot += dppf<kQuadXor1>(dot);  // token l / 2, whole sum
+    const float sc = (l >> 1) < count ? (dot + kcorr) * kscale : -INFINITY;
 
     // ---- values: level pairs through lutv as the MFMA B operand
     uint32_t vw[6];
@@ -420,7 +432,13 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       for (int e = 0; e < 5; ++e) pin(vmeta[e]);
       vw[0] = v0[0]; vw[1] = v0[1]; vw[2] = v1[0]; vw[3] = v1[1]; vw[4] = v2[0]; vw[5] = v2[1];
     }
-    const half8 pa = softmax_tile(sc[0], sc[1]);
+    uint32_t vl[32];  // level pairs of the B operands, requested while the softmax runs
+#pragma unroll
+    for (int x = 0; x < 32; ++x) vl[x] = dsr4<0>(pair_addr(vw, 6 * x, lutv_at));
+    const half8 pa = softmax_tile(sc);
+    lds_wait();
+#pragma unroll
+    for (int x = 0; x < 32; ++x) pin(vl[x]);
     zacc = mfma(pa, n16 < 8 ? h8(vmeta[4]) : h8(0u, 0u, 0u, 0u), zacc);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -430,11 +448,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int nt = 2 * g + t2;
-        uint32_t vl[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          vl[m] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(lutv) + pair_off(vw, 24 * nt + 6 * m));
-        const half8 bv = h8(vl[0], vl[1], vl[2], vl[3]);
+        const half8 bv = h8(vl[4 * nt], vl[4 * nt + 1], vl[4 * nt + 2], vl[4 * nt + 3]);
         oacc[nt] = mfma(wh, bv, oacc[nt]);
         oacc[nt] = mfma(wl, bv, oacc[nt]);
       }
@@ -452,7 +466,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
         const int g = col >> 5;
         const float vd = fmaf(h2f(static_cast<uint16_t>(lutv[9 * code])), h2f(vm[g * kBlockTokens + t]),
                               h2f(vm[4 * kBlockTokens + g * kBlockTokens + t]));
-        atomicAdd(&ocorr[col], (val - vd) * static_cast<float>(ptile[0][t]));
+        atomicAdd(&ocorr[col], (val - vd) * static_cast<float>(ptile[t]));
       }
     }
 
@@ -477,7 +491,21 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   {
+    // Wavefronts sharing a SIMD are picked oldest first; each one lowers its
+    // priority as it gets through its blocks so that they finish together.
+    int prio_q = 0;
+    auto age = [&](int i) __attribute__((always_inline)) {
+      const int q = (4 * i) / nmy;
+      if (q != prio_q) {
+        prio_q = q;
+        if (q == 1) __builtin_amdgcn_s_setprio(2);
+        else if (q == 2) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
+    };
+    __builtin_amdgcn_s_setprio(3);
     auto step = [&](int i, lds_u8* cur, lds_u8* ahead) __attribute__((always_inline)) {
+      age(i);
       issue(i + NBUF - 1, ahead);
       wait_vm<(NBUF - 1) * R::loads>();
       const int ch = c_begin + i;
@@ -495,6 +523,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       }
     }
     for (; i < nmy; ++i) {
+      age(i);
       const int ahead = i + NBUF - 1;
       if (ahead < nmy) issue(ahead, slot_at(ahead % NBUF));
       const int newer = min(NBUF - 1, nmy - 1 - i);
@@ -509,13 +538,14 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // ---- partial of this split (row 0): o = O_raw + Z + value-outlier corrections
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * D;
   float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * 2;
-  const float lsum = row16_sum(l_run);
+  const float lsum = wave_sum(l_run);
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const float z = lane_bcast(zacc[0], (l & 48) | (nt >> 1));
@@ -534,9 +564,9 @@ hipError_t launch_lut(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int
   if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm ||
       (OUTK > 0 && (L.off_ko != R::off_ko || L.off_vo != R::off_vo)))
     return hipSuccess;
-  // three slots for records with outliers (LDS allows them at two
-  // wavefronts per SIMD), two otherwise
-  constexpr int NB = OUTK > 0 ? 3 : 2;
+  // two ring slots: with them LDS admits three wavefronts per SIMD, as the
+  // register budget does
+  constexpr int NB = 2;
   static int resident = 0;
   if (resident == 0) {
     int per_cu = 0, dev = 0, cus = 0;

@@ -134,8 +134,7 @@ __device__ __forceinline__ int chunk3_code(const uint8_t* codes, int lane, int e
   return static_cast<int>((pair >> (bit & 31)) & 7u);
 }
 __device__ __forceinline__ int k3_code(const uint8_t* codes, int j, int c) {
-  const int g = (c & 63) >> 4, jj = ((c >> 6) << 1) | ((c & 15) >> 3);
-  return chunk3_code(codes, 16 * g + (j & 15), 32 * (j >> 4) + 8 * jj + (c & 7));
+  return chunk3_code(codes, c & 63, 2 * j + (c >> 6));
 }
 __device__ __forceinline__ int v3_code(const uint8_t* codes, int j, int c) {
   return chunk3_code(codes, 16 * (j >> 3) + (c & 15), 8 * (c >> 4) + (j & 7));

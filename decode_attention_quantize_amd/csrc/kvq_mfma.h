@@ -45,6 +45,7 @@ __device__ __forceinline__ float dppf(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowRor4 = 0x124, kRowRor8 = 0x128;
+constexpr int kRowHalfMirror = 0x141;  // lane i <-> i ^ 7 inside each group of 8
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dppf<kQuadXor1>(v));
   v = fmaxf(v, dppf<kQuadXor2>(v));
@@ -58,6 +59,31 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dppf<kRowRor4>(v);
   v += dppf<kRowRor8>(v);
   return v;
+}
+// Exchanges between 16-lane rows and 32-lane halves (gfx950 permlane swaps).
+// swap32(a, b) = ([a_lo, b_lo], [a_hi, b_hi]) over the halves of 32 lanes;
+// swap16(a, b) = ([a0, b0, a2, b2], [a1, b1, a3, b3]) over the rows of 16.
+__device__ __forceinline__ float2 swap32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float2 swap16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return make_float2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  float2 r = swap16(v, v);
+  v = fmaxf(r.x, r.y);
+  r = swap32(v, v);
+  return fmaxf(r.x, r.y);
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  float2 r = swap16(v, v);
+  v = r.x + r.y;
+  r = swap32(v, v);
+  return r.x + r.y;
 }
 __device__ __forceinline__ float lane_bcast(float v, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
@@ -82,6 +108,12 @@ template <int OFF>
 __device__ __forceinline__ u32x2 dsr8(uint32_t a) {
   u32x2 r;
   asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t dsr4(uint32_t a) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
   return r;
 }
 __device__ __forceinline__ void lds_wait() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

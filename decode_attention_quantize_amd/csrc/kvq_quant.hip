@@ -292,34 +292,18 @@ __device__ __forceinline__ uint32_t bits3_in_word(uint32_t code, int e, int w) {
   return sh >= 0 ? code << sh : code >> -sh;
 }
 
-// Keys: chunk 16g + n holds tokens n (words 0..2) and n + 16 (words 3..5);
-// within a token's 96 bits element 8j + i is channel
-// (j < 2 ? 16g + 8j : 64 + 16g + 8(j-2)) + i.  A token's words hold no other
-// token's codes, so tokens [slot0, slot0 + nrows) are written without a read.
-__device__ void pack_k3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int slot0) {
-  for (int i = threadIdx.x; i < nrows * 12; i += blockDim.x) {
-    const int jr = i / 12, g = (i % 12) / 3, w = i % 3;
-    const int j = slot0 + jr;
-    uint32_t word = 0;
-    for (int e = 0; e < 32; ++e) {
-      const int jj = e >> 3;
-      const int c = (jj < 2 ? 16 * g + 8 * jj : 64 + 16 * g + 8 * (jj - 2)) + (e & 7);
-      word |= bits3_in_word(codes[jr][c], e, w);
-    }
-    reinterpret_cast<uint32_t*>(dst)[6 * (16 * g + (j & 15)) + 3 * (j >> 4) + w] = word;
-  }
-}
-
-// Values: chunk 16g + n, element 8t + i = token 8g + i of channel 16t + n.
-// A fresh block (slot0 == 0) is written whole; otherwise only the bits of
-// tokens [slot0, slot0 + nrows) are replaced.
-__device__ void pack_v3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int slot0) {
+// Pack 3-bit codes into 64 lane chunks of six words; map(lane, e) gives the
+// (token slot, channel) of element e.  A fresh block (slot0 == 0) is written
+// whole (elements of slots >= nrows get code 0); otherwise only the bits of
+// slots [slot0, slot0 + nrows) are replaced.
+template <class Map>
+__device__ void pack3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int slot0, Map map) {
   for (int i = threadIdx.x; i < 64 * 6; i += blockDim.x) {
     const int lane = i / 6, w = i % 6;
     uint32_t word = 0, keep = 0xffffffffu;
     for (int e = (32 * w) / 3; e <= (32 * w + 31) / 3 && e < 64; ++e) {
-      const int j = 8 * (lane >> 4) + (e & 7);
-      const int c = 16 * (e >> 3) + (lane & 15);
+      int j, c;
+      map(lane, e, j, c);
       if (j >= slot0 && j < slot0 + nrows) {
         word |= bits3_in_word(codes[j - slot0][c], e, w);
         keep &= ~bits3_in_word(7u, e, w);
@@ -331,6 +315,21 @@ __device__ void pack_v3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int 
     else if (keep != 0xffffffffu)
       *wp = (*wp & keep) | word;
   }
+}
+// Keys: chunk l holds RoPE pair (l, l + 64); element 2t + e is token t of
+// channel l + 64e, so a token's two codes form one 6-bit field.
+__device__ void pack_k3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int slot0) {
+  pack3(codes, nrows, dst, slot0, [](int lane, int e, int& j, int& c) {
+    j = e >> 1;
+    c = lane + 64 * (e & 1);
+  });
+}
+// Values: chunk 16g + n, element 8t + i = token 8g + i of channel 16t + n.
+__device__ void pack_v3(const uint8_t (*codes)[D], int nrows, uint8_t* dst, int slot0) {
+  pack3(codes, nrows, dst, slot0, [](int lane, int e, int& j, int& c) {
+    j = 8 * (lane >> 4) + (e & 7);
+    c = 16 * (e >> 3) + (lane & 15);
+  });
 }
 
 // Pack values into the lane-chunk layout.  A fresh block (slot0 == 0) is

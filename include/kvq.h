@@ -117,9 +117,9 @@ enum {
  *             16 + bits*j ("pair-split" word).
  *           8 bits: one byte per channel.
  *           3 bits: 64 lane chunks of 24 bytes, each a little-endian bit
- *             stream with element E at bits 3E..3E+2.  Chunk 16g + n holds
- *             element 32*t + 8*j + i = code(token n + 16t, channel
- *             (j < 2 ? 16g + 8j : 64 + 16g + 8(j-2)) + i), t = 0..1, j, i < 4, 8.
+ *             stream with element E at bits 3E..3E+2.  Chunk l holds the
+ *             RoPE pair (l, l + 64): element 2t + e = code(token t, channel
+ *             l + 64e), so token t's two codes are the 6-bit field at 6t.
  *  k_meta   per-channel keys: s[D] fp16 then z[D] fp16 (one group per channel
  *           per block).  Inner keys: [32 tokens][D/k_group] pairs (s, z).
  *           A set sign bit on s marks a symmetric group: value = (code-2^(b-1))*|s|;

@@ -43,17 +43,13 @@ def _chunk3_fields(raw: np.ndarray) -> np.ndarray:
 
 
 def _kchunks3(raw: np.ndarray) -> np.ndarray:
-    """3-bit keys -> [32 tokens][D].  Chunk l = 16*g + n holds tokens n (tile 0)
-    and n + 16 (tile 1); element 32*tile + 8*j + i is channel
-    (j < 2 ? 16g + 8j : 64 + 16g + 8(j-2)) + i."""
+    """3-bit keys -> [32 tokens][D].  Chunk l holds channels l and l + 64;
+    element 2*t + e is token t of channel l + 64*e."""
     el = _chunk3_fields(raw)
     out = np.zeros((BT, D), np.uint8)
     for lane in range(64):
-        n, g = lane % 16, lane // 16
         for e in range(64):
-            tile, j, i = e // 32, (e // 8) % 4, e % 8
-            c = (16 * g + 8 * j if j < 2 else 64 + 16 * g + 8 * (j - 2)) + i
-            out[n + 16 * tile, c] = el[lane, e]
+            out[e // 2, lane + 64 * (e % 2)] = el[lane, e]
     return out
 
 
