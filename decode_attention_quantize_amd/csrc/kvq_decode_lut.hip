@@ -83,12 +83,12 @@ __device__ __forceinline__ void cs_accurate(double a, float& c, float& s) {
 }
 
 // Two 3-bit codes of a lane's chunk (six words) as one 6-bit field at bit
-// offset `bit` of the 192-bit stream: the LDS address of the entry it selects
-// in a table of 32-bit level pairs at `base`.
-__device__ __forceinline__ uint32_t pair_addr(const uint32_t (&w)[6], int bit, uint32_t base) {
+// offset `bit` of the 192-bit stream: the entry it selects in a table of
+// 32-bit level pairs.
+__device__ __forceinline__ uint32_t pair_at(const uint32_t (&w)[6], int bit, const uint32_t* table) {
   const int q = bit >> 5, r = bit & 31;
   const uint32_t f = r <= 26 ? __builtin_amdgcn_ubfe(w[q], r, 6) : (__builtin_amdgcn_alignbit(w[q + 1], w[q], r) & 63u);
-  return (f << 2) + base;
+  return table[f];
 }
 
 // 3-bit code of (token slot j, channel c) in an LDS copy of a record section
@@ -219,7 +219,6 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
   // block's tokens 0 (w1) and 16 (w2); each chain steps one position per token
   float w1a = q_lo, w1b = q_hi, w2a = q_lo, w2b = q_hi;
   float tc = 1.f, ts = 0.f, trc = 1.f, trs = 0.f;  // (cos, sin)(theta_l * block start), step
-  const uint32_t lutv_at = lds_off((lds_u8*)lutv), lutk_at = lds_off((lds_u8*)lutk);
   auto rot_by = [](float& a, float& b, float c, float s) __attribute__((always_inline)) {
     const float a0 = a, b0 = b;
     a = fmaf(c, a0, s * b0);
@@ -369,12 +368,9 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
 
     // ---- keys: dequantize this lane's pair for tokens k and 16 + k, dot with
     // the rotated query, and fold the two tokens across the lane halves
-    uint32_t lk[32];  // level pairs of the 32 tokens, all requested before one wait
+    uint32_t lk[32];  // level pairs of the 32 tokens
 #pragma unroll
-    for (int t = 0; t < 32; ++t) lk[t] = dsr4<0>(pair_addr(kw, 6 * t, lutk_at));
-    lds_wait();
-#pragma unroll
-    for (int t = 0; t < 32; ++t) pin(lk[t]);
+    for (int t = 0; t < 32; ++t) lk[t] = pair_at(kw, 6 * t, lutk);
     float e1[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -432,13 +428,10 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       for (int e = 0; e < 5; ++e) pin(vmeta[e]);
       vw[0] = v0[0]; vw[1] = v0[1]; vw[2] = v1[0]; vw[3] = v1[1]; vw[4] = v2[0]; vw[5] = v2[1];
     }
-    uint32_t vl[32];  // level pairs of the B operands, requested while the softmax runs
+    uint32_t vl[32];  // level pairs of the B operands
 #pragma unroll
-    for (int x = 0; x < 32; ++x) vl[x] = dsr4<0>(pair_addr(vw, 6 * x, lutv_at));
+    for (int x = 0; x < 32; ++x) vl[x] = pair_at(vw, 6 * x, lutv);
     const half8 pa = softmax_tile(sc);
-    lds_wait();
-#pragma unroll
-    for (int x = 0; x < 32; ++x) pin(vl[x]);
     zacc = mfma(pa, n16 < 8 ? h8(vmeta[4]) : h8(0u, 0u, 0u, 0u), zacc);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
