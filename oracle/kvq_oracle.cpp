@@ -23,7 +23,9 @@
 //    (section 3, K/V separation).
 //  * InnerQ (euno.news, 2602.23200): inner-dimension groups (method 1),
 //    per-group symmetric/asymmetric choice from local statistics (method 2),
-//    fp16 recent and sink windows (method 4).
+//    fp16 recent and sink windows (method 4), one-time per-channel key
+//    normalization computed at prefill and folded into the query (method 4;
+//    key contributions list).
 //  * Hadamard 2-bit values (aitrends.kr): rotate values by a Hadamard matrix,
 //    quantize uniformly to 2 bits, undo the rotation after the attention sum
 //    (TL;DR; section details; glossary).
@@ -360,6 +362,49 @@ int32_t oq_state_append(int32_t* n, int32_t* nb, int32_t* r, int32_t W, int32_t 
   return 0;
 }
 
+// ---------------------------------------------------------------- key normalization
+// InnerQ, method 4: a per-channel key scaling computed once over the prefill
+// and folded into the query.  The pages name neither the statistic nor the
+// form of the factor; the readings here:
+//   a_c     = max over the T prefill tokens of |K[t][c]|
+//   e_c     = binary exponent of a_c (a_c = m 2^e_c, 1/2 <= m < 1); a zero
+//             channel takes e_c = E (no scaling)
+//   E       = max_c e_c
+//   shift_c = min(E - e_c, 14)       (an integer >= 0)
+// Normalized keys x_c = K_c * 2^shift_c (every channel scaled toward the
+// range of the largest one), rounded to fp16 with saturation at +-65504
+// (exact unless a later token exceeds its channel's prefill range by 2^shift
+// beyond fp16); the query is folded as q'_c = q_c * 2^-shift_c, so that
+// q' . x = q . K exactly.  Powers of two keep the fold exact.
+void oq_knorm_shifts(const uint16_t* K, int32_t T, int32_t D, int8_t* shift) {
+  std::vector<int> e(D, 0);
+  std::vector<bool> zero(D, true);
+  int E = 0;
+  bool anyc = false;
+  for (int c = 0; c < D; ++c) {
+    double a = 0.0;
+    for (int t = 0; t < T; ++t) a = std::max(a, std::fabs(f16_to_f64(K[static_cast<size_t>(t) * D + c])));
+    if (a > 0.0) {
+      int ex = 0;
+      std::frexp(a, &ex);
+      e[c] = ex;
+      zero[c] = false;
+      E = anyc ? std::max(E, ex) : ex;
+      anyc = true;
+    }
+  }
+  for (int c = 0; c < D; ++c) shift[c] = static_cast<int8_t>(zero[c] ? 0 : std::min(E - e[c], 14));
+}
+// x = fp16(K * 2^shift) per channel for n rows (saturating).
+void oq_knorm_apply(const uint16_t* K, int32_t n, int32_t D, const int8_t* shift, uint16_t* X) {
+  for (int t = 0; t < n; ++t)
+    for (int c = 0; c < D; ++c) {
+      double x = std::ldexp(f16_to_f64(K[static_cast<size_t>(t) * D + c]), shift[c]);
+      x = std::max(-65504.0, std::min(65504.0, x));
+      X[static_cast<size_t>(t) * D + c] = f64_to_f16(x);
+    }
+}
+
 // ---------------------------------------------------------------- encoding
 // Encode the quantized body [s_eff, s_eff+nb) of one (batch, kv-head) unit.
 // K, V: fp16 [n][D] (V before any rotation).  Outputs (logical, unpacked):
@@ -463,12 +508,15 @@ int32_t oq_encode_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* V
 // from codes and parameters, sparse outliers overwriting their dense value,
 // then RoPE on every key at its absolute position when keys are pre-RoPE.
 // Khat, Vhat: [n][D]; only rows [t_begin, t_end) are written.
+// kshift (nullable): per-channel key normalization shifts; body keys (codes
+// and outliers, which live in the normalized domain) are scaled back by
+// 2^-shift before RoPE.
 int32_t oq_dequant_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* vrot, int32_t n,
                         int32_t s_eff, int32_t nb, int32_t t_begin, int32_t t_end,
                         const uint8_t* kcodes, const uint16_t* kmeta,
                         const uint8_t* vcodes, const uint16_t* vmeta, const int32_t* kocol,
                         const uint16_t* koval, const int32_t* vocol, const uint16_t* voval,
-                        double* Khat, double* Vhat) {
+                        const int8_t* kshift, double* Khat, double* Vhat) {
   const int D = sc->D, kg = sc->k_group, vg = sc->v_group, ko = sc->outliers;
   const uint16_t* lk = sc->nuq ? sc->levels_k : nullptr;
   const uint16_t* lv = sc->nuq ? sc->levels_v : nullptr;
@@ -490,6 +538,8 @@ int32_t oq_dequant_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* 
         kh[kocol[i * ko + j]] = f16_to_f64(koval[i * ko + j]);
         vh[vocol[i * ko + j]] = f16_to_f64(voval[i * ko + j]);
       }
+      if (kshift)
+        for (int c = 0; c < D; ++c) kh[c] = std::ldexp(kh[c], -kshift[c]);
     } else {
       for (int c = 0; c < D; ++c) {
         kh[c] = f16_to_f64(K[static_cast<size_t>(t) * D + c]);

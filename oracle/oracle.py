@@ -75,8 +75,10 @@ def lib():
             L.oq_encode_unit.restype = C.c_int32
             L.oq_dequant_unit.argtypes = [C.POINTER(OScheme), u16p, u16p, C.c_int32, C.c_int32,
                                           C.c_int32, C.c_int32, C.c_int32, u8p, u16p, u8p, u16p,
-                                          i32p, u16p, i32p, u16p, f64p, f64p]
+                                          i32p, u16p, i32p, u16p, C.POINTER(C.c_int8), f64p, f64p]
             L.oq_dequant_unit.restype = C.c_int32
+            L.oq_knorm_shifts.argtypes = [u16p, C.c_int32, C.c_int32, C.POINTER(C.c_int8)]
+            L.oq_knorm_apply.argtypes = [u16p, C.c_int32, C.c_int32, C.POINTER(C.c_int8), u16p]
             L.oq_attention.argtypes = [f64p, C.c_int32, f64p, f64p, C.c_int32, C.c_int32, C.c_int32, f64p]
             L.oq_attention_split.argtypes = [f64p, C.c_int32, f64p, f64p, C.c_int32, C.c_int32,
                                              C.c_int32, C.c_int32, f64p]
@@ -240,8 +242,29 @@ def encode_unit(sc: OScheme, K16, V16, n, s_eff, nb):
     return e
 
 
-def dequant_unit(sc: OScheme, K16, enc, n, s_eff, nb, t_begin=0, t_end=None, Khat=None, Vhat=None):
-    """binary64 K-hat, V-hat [n][D] (rows t_begin..t_end rebuilt)."""
+def knorm_shifts(K16_prefill) -> np.ndarray:
+    """int8 [D] per-channel key normalization shifts from the prefill rows."""
+    K16 = np.ascontiguousarray(K16_prefill, dtype=np.uint16)
+    T, D = K16.shape
+    out = np.zeros(D, np.int8)
+    lib().oq_knorm_shifts(_p(K16, C.c_uint16), T, D, _p(out, C.c_int8))
+    return out
+
+
+def knorm_apply(K16, shift) -> np.ndarray:
+    """uint16 [n][D] normalized keys fp16(K * 2^shift) (saturating)."""
+    K16 = np.ascontiguousarray(K16, dtype=np.uint16)
+    n, D = K16.shape
+    out = np.empty((n, D), np.uint16)
+    sh = np.ascontiguousarray(shift, dtype=np.int8)
+    lib().oq_knorm_apply(_p(K16, C.c_uint16), n, D, _p(sh, C.c_int8), _p(out, C.c_uint16))
+    return out
+
+
+def dequant_unit(sc: OScheme, K16, enc, n, s_eff, nb, t_begin=0, t_end=None, Khat=None, Vhat=None,
+                 kshift=None):
+    """binary64 K-hat, V-hat [n][D] (rows t_begin..t_end rebuilt).  kshift: key
+    normalization shifts of the unit (body keys are scaled back by 2^-shift)."""
     D = sc.D
     t_end = n if t_end is None else t_end
     K16 = np.ascontiguousarray(K16, dtype=np.uint16).reshape(-1, D)
@@ -258,6 +281,8 @@ def dequant_unit(sc: OScheme, K16, enc, n, s_eff, nb, t_begin=0, t_end=None, Kha
                                _p(enc["kmeta"], C.c_uint16), _p(enc["vcodes"], C.c_uint8),
                                _p(enc["vmeta"], C.c_uint16), _p(kocol, C.c_int32),
                                _p(koval, C.c_uint16), _p(vocol, C.c_int32), _p(voval, C.c_uint16),
+                               _p(None if kshift is None else np.ascontiguousarray(kshift, dtype=np.int8),
+                                  C.c_int8),
                                _p(Khat, C.c_double), _p(Vhat, C.c_double))
     assert rc == 0
     return Khat, Vhat
@@ -314,8 +339,15 @@ def run_unit(wl, layer, b, h, steps=None, only_steps=None):
         states.append((n, nb, r))
     nb_final = states[-1][1] if states else nb
     n_final = states[-1][0] if states else n
-    enc = encode_unit(sc, K, V, n_final, s_eff, nb_final)
-    Kf, Vf = dequant_unit(sc, K, enc, n_final, s_eff, nb_final)
+    kshift = None
+    Kq = K
+    if getattr(wl, "k_norm", False):
+        # InnerQ method 4: shifts from the prefill rows, body keys quantized
+        # in the normalized domain, fp16 sink/window rows kept as given
+        kshift = knorm_shifts(K[:wl.T])
+        Kq = knorm_apply(K, kshift)
+    enc = encode_unit(sc, Kq, V, n_final, s_eff, nb_final)
+    Kf, Vf = dequant_unit(sc, K, enc, n_final, s_eff, nb_final, kshift=kshift)
     gq = wl.gq
     outs = {}
     for i, (n_i, nb_i, r_i) in enumerate(states):
@@ -324,8 +356,8 @@ def run_unit(wl, layer, b, h, steps=None, only_steps=None):
         Kh, Vh = Kf[:n_i].copy(), Vf[:n_i].copy()
         lo = s_eff + nb_i
         if lo < n_i:
-            dequant_unit(sc, K, enc, n_i, s_eff, nb_i, lo, n_i, Kh, Vh)
+            dequant_unit(sc, K, enc, n_i, s_eff, nb_i, lo, n_i, Kh, Vh, kshift=kshift)
         q = wl.q(layer, i, b0=b, b1=b + 1, h0=h * gq, h1=(h + 1) * gq).reshape(gq, wl.D)
         outs[i] = attention(q.double().numpy(), Kh, Vh, unrotate=bool(wl.v_hadamard))
     return dict(states=states, out=outs, enc=enc, s_eff=s_eff, n_final=n_final,
-                nb_final=nb_final, K=K, V=V, scheme=sc)
+                nb_final=nb_final, K=K, V=V, scheme=sc, kshift=kshift)

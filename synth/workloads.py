@@ -50,6 +50,7 @@ class Workload:
     v_hadamard: bool = False
     k_hybrid: bool = False
     sym_ratio: float = 0.1
+    k_norm: bool = False         # per-channel key normalization from the prefill (inner keys)
     pre_rope: bool = False
     rope_base: float = 10000.0
     nuq: bool = False

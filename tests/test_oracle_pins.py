@@ -468,3 +468,99 @@ def test_average_bits_objective():
             pairs = [W.PAIR_SET[i] for i in c["pair_index"]]
             fm = sum(kb + vb for kb, vb in pairs) / (2 * len(pairs))
             assert fm == c["f_m"], c["name"]
+
+
+# ---------------------------------------------------------------- key normalization (InnerQ method 4)
+def test_knorm_shifts_from_binary_exponents():
+    # channel max-abs 1.0, 0.3, 5.0, 0 (zero), 2^-20 (subnormal), 3.99 and a
+    # channel whose max sits in a negative entry; exponents by hand:
+    # 1.0 = 0.5*2^1 -> 1; 0.3 -> -1; 5.0 -> 3; 2^-20 -> -19; 3.99 -> 2; 6 -> 3
+    D = 8
+    K = np.zeros((3, D), np.float64)
+    K[:, 0] = [0.5, -1.0, 0.25]
+    K[:, 1] = [0.3, 0.1, -0.2]
+    K[:, 2] = [5.0, 1.0, 2.0]
+    K[:, 4] = [2.0 ** -20, 0.0, -(2.0 ** -21)]
+    K[:, 5] = [3.99, 0.0, 1.0]
+    K[:, 6] = [1.0, -6.0, 2.0]
+    K[:, 7] = [0.0, 0.0, 0.0]
+    got = O.knorm_shifts(h16(K).reshape(3, D))
+    E = 3
+    want = [E - 1, E + 1, 0, 0, min(E + 19, 14), E - 2, 0, 0]
+    assert got.tolist() == want
+
+
+def test_knorm_fold_is_exact():
+    # q' . x = q . K in exact arithmetic: powers of two move exponents only
+    Kf = rng.normal(size=(64, 128)) * np.exp(rng.normal(size=128) * 2.0)
+    K = h16(Kf).reshape(64, 128)
+    sh = O.knorm_shifts(K)
+    X = O.knorm_apply(K, sh)
+    k = K.view(np.float16).astype(np.float64)
+    x = X.view(np.float16).astype(np.float64)
+    assert np.array_equal(x, k * 2.0 ** sh.astype(np.float64))           # no rounding at all
+    q = h16(rng.normal(size=128)).view(np.float16).astype(np.float64)
+    qn = q * 2.0 ** (-sh.astype(np.float64))
+    for t in range(64):
+        lhs = sum(Fraction(qn[c]) * Fraction(x[t, c]) for c in range(128))
+        rhs = sum(Fraction(q[c]) * Fraction(k[t, c]) for c in range(128))
+        assert lhs == rhs
+    # every channel's prefill range lands in the largest channel's binade
+    amax = np.abs(x).max(axis=0)
+    E = int(np.frexp(np.abs(k).max())[1])
+    assert np.all((amax < 2.0 ** E) & ((amax >= 2.0 ** (E - 1)) | (sh == 14)))
+
+
+def test_knorm_saturates_beyond_fp16():
+    K = h16([[1.0, 60000.0], [0.25, 1.0]])
+    sh = O.knorm_shifts(K)                     # exponents 1 and 16 -> shifts 14 (capped), 0
+    assert sh.tolist() == [14, 0]
+    later = h16([[8.0, 1.0]])                  # 8 * 2^14 overflows fp16: saturates
+    X = O.knorm_apply(later.reshape(1, 2), sh)
+    assert X.view(np.float16).astype(np.float64).tolist() == [[65504.0, 1.0]]
+
+
+def test_knorm_identity_when_channels_share_a_binade():
+    # all channel maxima in [2, 4): shifts are zero and the cache is unchanged
+    wl = W.C5.with_(B=1, Hq=8, T=128, steps=2, k_out_count=0, v_out_count=0, k_norm=True)
+    K, V = O.unit_inputs(wl, 0, 0, 0, 130)
+    k = K.view(np.float16).astype(np.float64)
+    k = np.clip(k, -3.9, 3.9)
+    k[0] = 3.5                                  # every channel reaches [2, 4) in row 0
+    K = h16(k).reshape(130, 128)
+    sh = O.knorm_shifts(K[:128])
+    assert not sh.any()
+    sc = O.scheme_for(wl, 0)
+    a = O.encode_unit(sc, K, V, 128, 0, 96)
+    b = O.encode_unit(sc, O.knorm_apply(K, sh), V, 128, 0, 96)
+    for key in ("kcodes", "kmeta"):
+        assert np.array_equal(a[key], b[key])
+
+
+def test_knorm_reduces_inner_group_error_on_a_loud_channel():
+    # one channel 64x louder than the rest: inner groups of 64 share its range,
+    # so the other 63 channels of its group lose resolution; normalization
+    # scales them up first, and the dequantized keys come out closer to K.
+    wl = W.C5.with_(B=1, Hq=8, T=256, steps=1, k_out_count=0, v_out_count=0)
+    K, V = O.unit_inputs(wl, 0, 0, 0, 256)
+    k = K.view(np.float16).astype(np.float64)
+    k[:, 5] *= 64.0
+    K = h16(k).reshape(256, 128)
+    sc = O.scheme_for(wl, 0)
+    enc = O.encode_unit(sc, K, V, 256, 0, 256)
+    Kh, _ = O.dequant_unit(sc, K, enc, 256, 0, 256)
+    sh = O.knorm_shifts(K)
+    assert sh[5] == 0 and np.all(sh[np.arange(128) != 5] >= 5)
+    encn = O.encode_unit(sc, O.knorm_apply(K, sh), V, 256, 0, 256)
+    Khn, _ = O.dequant_unit(sc, K, encn, 256, 0, 256, kshift=sh)
+    quiet = np.arange(128) != 5
+    err = np.abs(Kh - k)[:, quiet].mean()
+    errn = np.abs(Khn - k)[:, quiet].mean()
+    assert errn < 0.25 * err, (errn, err)
+    # what attention sees, the error of q . k, does not grow: the loud channel
+    # was an exact group end point before and is not now, while 63 channels
+    # gain resolution
+    q = rng.normal(size=(16, 128))
+    rms = np.sqrt(np.mean((q @ (Kh - k).T) ** 2))
+    rmsn = np.sqrt(np.mean((q @ (Khn - k).T) ** 2))
+    assert rmsn < rms, (rmsn, rms)
