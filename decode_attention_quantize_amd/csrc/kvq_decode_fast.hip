@@ -158,22 +158,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       qa[j] = live ? h8(v) : h8(0u, 0u, 0u, 0u);
     }
   }
-  // inner groups: per-row sums of q over each 64-channel group
-  float qsum[2][RI];
-  if constexpr (INNER) {
-#pragma unroll
-    for (int gg = 0; gg < 2; ++gg) {
-      float s = 0.f;
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int kk = 0; kk < 8; ++kk) s += static_cast<float>(qa[2 * gg + jj][kk]);
-      s += xshflf<16>(s);
-      s += __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __float_as_int(s)));
-#pragma unroll
-      for (int i = 0; i < RI; ++i) qsum[gg][i] = lane_bcast(s, 20 * g4 + i);
-    }
-  }
+  float qsum[2][RI];  // inner groups: per-row sums of q over each 64-channel group
 
   const float kscale = kLog2e / sqrtf(static_cast<float>(D));
   float m_run[RI], l_run[RI];
@@ -466,6 +451,36 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) oacc[nt][i] *= 1.0f / viu;
+  }
+
+  if constexpr (INNER) {
+    // body keys normalized per channel at prefill (InnerQ, method 4): the
+    // query takes the inverse powers of two, q'_c = q_c 2^-shift_c (exact
+    // unless q'_c falls below the fp16 normal range)
+    if (L.kshift) {
+      const int8_t* shp = L.kshift + static_cast<int64_t>(u) * D;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 w = ld8(shp + kchan<INNER>(g4, j, 0));
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          const int sh = static_cast<int8_t>((w[kk >> 2] >> (8 * (kk & 3))) & 0xffu);
+          qa[j][kk] = static_cast<_Float16>(ldexpf(static_cast<float>(qa[j][kk]), -sh));
+        }
+      }
+    }
+#pragma unroll
+    for (int gg = 0; gg < 2; ++gg) {
+      float s = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) s += static_cast<float>(qa[2 * gg + jj][kk]);
+      s += xshflf<16>(s);
+      s += __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __float_as_int(s)));
+#pragma unroll
+      for (int i = 0; i < RI; ++i) qsum[gg][i] = lane_bcast(s, 20 * g4 + i);
+    }
   }
 
   // ---------------- quantized body blocks through the LDS ring

@@ -127,11 +127,13 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(LayerDesc L, Decode
       rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + ch) * L.rec_bytes;
       count = min(kBlockTokens, st.nb - ch * kBlockTokens);
     }
-    // keys of the chunk
+    // keys of the chunk (body keys were normalized per channel at prefill:
+    // scale back by 2^-shift, exact in fp32)
+    const int ksh = (rec && L.kshift) ? L.kshift[static_cast<int64_t>(u) * D + t] : 0;
     for (int j = 0; j < count; ++j) {
       float x;
       if (rec) {
-        x = load_k_body(L, rec, j, t);
+        x = ldexpf(load_k_body(L, rec, j, t), -ksh);
       } else {
         int slot, pos;
         fp16_slot(L, st, ch * kBlockTokens + j, slot, pos);

@@ -95,6 +95,12 @@ kvq_status fill_layout(const kvq_cache& c, int kb, int vb, const uint16_t* cb, L
   return KVQ_OK;
 }
 
+// bytes of the fp16 sink/window slots of all units (the key normalization
+// shifts, when enabled, follow them in the same buffer)
+size_t fp16_area_bytes(const kvq_cache& c) {
+  return static_cast<size_t>(c.units) * 2 * (c.sink_cap + c.win_cap) * kD * sizeof(uint16_t);
+}
+
 int max_splits(const kvq_cache& c) {
   return std::min(kvq::kMaxBodySplits, c.nblk_cap) + kvq::kMaxFp16Splits;
 }
@@ -179,6 +185,7 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
   if (g.k_hybrid && (g.sym_ratio_num < 0 || g.sym_ratio_den <= 0)) return KVQ_ERR_ARG;
   if (g.k_pre_rope && !(g.rope_base > 0.f)) return KVQ_ERR_ARG;
   if (g.nuq && !codebooks) return KVQ_ERR_ARG;
+  if (g.k_norm != 0 && g.k_norm != 1) return KVQ_ERR_ARG;
   const int G = g.n_q_heads / g.n_kv_heads;
   if (g.head_dim != kD) return KVQ_ERR_UNSUPPORTED;
   if (!pow2_in(G, 1, kvq::kMaxGroupRows)) return KVQ_ERR_UNSUPPORTED;
@@ -186,6 +193,7 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
   if (g.k_mode == KVQ_K_INNER && !pow2_in(g.k_group, 16, 64)) return KVQ_ERR_UNSUPPORTED;
   if (!pow2_in(g.v_group, 16, 64)) return KVQ_ERR_UNSUPPORTED;
   if (g.nuq && g.k_hybrid) return KVQ_ERR_UNSUPPORTED;
+  if (g.k_norm && g.k_mode != KVQ_K_INNER) return KVQ_ERR_UNSUPPORTED;
   for (int l = 0; l < g.n_layers; ++l) {
     const int kb = layer_bits[l].k_bits, vb = layer_bits[l].v_bits;
     if (g.nuq) {
@@ -230,8 +238,7 @@ kvq_status kvq_layer_buffer_sizes(const kvq_cache* c, int32_t layer, size_t size
   if (!valid_layer(c, layer) || !sizes) return KVQ_ERR_ARG;
   const LayerDesc& d = c->layers[layer].d;
   sizes[KVQ_BUF_BODY] = static_cast<size_t>(c->units) * c->nblk_cap * d.rec_bytes;
-  sizes[KVQ_BUF_FP16] =
-      static_cast<size_t>(c->units) * 2 * (c->sink_cap + c->win_cap) * kD * sizeof(uint16_t);
+  sizes[KVQ_BUF_FP16] = fp16_area_bytes(*c) + (c->cfg.k_norm ? static_cast<size_t>(c->units) * kD : 0);
   return KVQ_OK;
 }
 
@@ -259,6 +266,7 @@ kvq_status kvq_bind_layer(kvq_cache* c, int32_t layer, void* const bufs[KVQ_NBUF
   Layer& L = c->layers[layer];
   L.d.body = static_cast<uint8_t*>(bufs[KVQ_BUF_BODY]);
   L.d.fp16 = static_cast<uint16_t*>(bufs[KVQ_BUF_FP16]);
+  L.d.kshift = c->cfg.k_norm ? static_cast<int8_t*>(bufs[KVQ_BUF_FP16]) + fp16_area_bytes(*c) : nullptr;
   L.bound = true;
   L.filled = false;
   L.n = L.s_eff = L.nb = L.r = 0;
@@ -297,6 +305,12 @@ kvq_status kvq_quantize_prefill(kvq_cache* c, int32_t layer, const void* k, cons
   const int r = T - s_eff - nb;
   const auto* ks = static_cast<const uint16_t*>(k);
   const auto* vs = static_cast<const uint16_t*>(v);
+  if (L.d.kshift) {
+    // shifts from the whole prefill, before any body block is quantized
+    // (read as 16-byte vectors)
+    if (T > 0 && (reinterpret_cast<uintptr_t>(k) & 15)) return KVQ_ERR_ARG;
+    if (kvq::launch_knorm_shifts(L.d, ks, T, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  }
   if (nb > 0) {
     kvq::QuantJob j{};
     j.k_src = ks;

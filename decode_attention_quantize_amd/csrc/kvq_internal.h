@@ -33,6 +33,7 @@ struct LayerDesc {
   // buffers
   uint8_t* body;     // [units][nblk_cap][rec_bytes]
   uint16_t* fp16;    // per unit: K [slots][D], then V [slots / 8][D][8]
+  int8_t* kshift;    // per-channel key normalization shifts [units][D], or null
 };
 
 // Element offset of value (slot, channel) inside a unit's fp16 value area:
@@ -81,6 +82,9 @@ hipError_t launch_copy_fp16(const LayerDesc& L, const CopyJob& job, hipStream_t 
 // Zero a layer's fp16 area (every unit), so that slots never written hold
 // finite values.
 hipError_t launch_zero_fp16(const LayerDesc& L, hipStream_t s);
+// Per-channel key normalization shifts of every unit from its T prefill
+// tokens (k: fp16 [units][T][D]); T == 0 writes zero shifts.
+hipError_t launch_knorm_shifts(const LayerDesc& L, const uint16_t* k, int32_t T, hipStream_t s);
 
 // Decode attention.  grid.x = nsplit wavefront groups per unit.
 // partials: LDS-staged path [units][nsplit][G][D + 2] fp32; matrix-core path

@@ -381,6 +381,12 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
     const int64_t vo = J.v_interleaved ? vslot(tt0 + j, t) : static_cast<int64_t>(tt0 + j) * D + t;
     sm.v[j][t] = j < nrows ? vsrc[vo] : 0;
   }
+  if (L.kshift) {
+    // normalized keys fp16(K * 2^shift), saturating (InnerQ, method 4)
+    const int sh = L.kshift[static_cast<int64_t>(u) * D + t];
+    for (int j = 0; j < nrows; ++j)
+      sm.k[j][t] = f2h(fminf(fmaxf(ldexpf(h2f(sm.k[j][t]), sh), -65504.f), 65504.f));
+  }
   __syncthreads();
   if (J.rotate_v) hadamard_rows(sm, sm.v, nrows, L.had_scale);
 
@@ -483,6 +489,48 @@ __global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) 
   }
 }
 
+// InnerQ, method 4 (one-time per-channel key normalization from the
+// prefill): per unit, shift_c = min(E - e_c, 14) with e_c the binary exponent
+// of max_t |K[t][c]| (a = m 2^e, 1/2 <= m < 1) and E = max_c e_c; an all-zero
+// channel gets 0.  Magnitudes are compared as fp16 bit patterns (exact), the
+// exponent is read from the maximum's bits.  Block: 16 groups of 16 lanes, a
+// group reads whole token rows as 16-byte vectors.
+__global__ void __launch_bounds__(256) knorm_shift_kernel(const uint16_t* k, int32_t T, int8_t* out) {
+  __shared__ uint16_t part[16][D];
+  __shared__ int e_max;
+  const int tid = threadIdx.x, rg = tid >> 4, cl = tid & 15;
+  const int u = blockIdx.x;
+  const uint4* src = reinterpret_cast<const uint4*>(k + static_cast<int64_t>(u) * T * D) + cl;
+  uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int t = rg; t < T; t += 16) {
+    const uint4 v = src[static_cast<int64_t>(t) * (D / 8)];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m[2 * i] = max(m[2 * i], w[i] & 0x7fffu);
+      m[2 * i + 1] = max(m[2 * i + 1], (w[i] >> 16) & 0x7fffu);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[rg][8 * cl + i] = static_cast<uint16_t>(m[i]);
+  if (tid == 0) e_max = -1000;
+  __syncthreads();
+  int e = 0;
+  bool zero = true;
+  if (tid < D) {
+    uint32_t a = 0;
+    for (int r = 0; r < 16; ++r) a = max(a, static_cast<uint32_t>(part[r][tid]));
+    zero = a == 0;
+    if (!zero) {
+      // normal: (1 + f) 2^(E5 - 15) = 0.5 (1 + f) 2^(E5 - 14); subnormal: a 2^-24
+      e = a >= 0x400u ? static_cast<int>(a >> 10) - 14 : (32 - __clz(static_cast<int>(a))) - 24;
+      atomicMax(&e_max, e);
+    }
+  }
+  __syncthreads();
+  if (tid < D) out[static_cast<int64_t>(u) * D + tid] = static_cast<int8_t>(zero ? 0 : min(e_max - e, 14));
+}
+
 __global__ void __launch_bounds__(256) zero_kernel(uint4* p, int64_t n16) {
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n16; i += static_cast<int64_t>(gridDim.x) * 256)
     p[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -495,6 +543,12 @@ hipError_t launch_zero_fp16(const LayerDesc& L, hipStream_t s) {
   const int64_t n16 = bytes / 16;  // slots are a multiple of 32, so bytes is a multiple of 16
   const int grid = static_cast<int>(std::min<int64_t>((n16 + 255) / 256, 4096));
   hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, s, reinterpret_cast<uint4*>(L.fp16), n16);
+  return hipGetLastError();
+}
+
+hipError_t launch_knorm_shifts(const LayerDesc& L, const uint16_t* k, int32_t T, hipStream_t s) {
+  if (!L.kshift) return hipSuccess;
+  hipLaunchKernelGGL(knorm_shift_kernel, dim3(L.units), dim3(256), 0, s, k, T, L.kshift);
   return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ class kvq_config(C.Structure):
         ("k_mode", C.c_int32), ("k_group", C.c_int32), ("v_mode", C.c_int32), ("v_group", C.c_int32),
         ("k_hybrid", C.c_int32), ("sym_ratio_num", C.c_int32), ("sym_ratio_den", C.c_int32),
         ("k_pre_rope", C.c_int32), ("rope_base", C.c_float), ("nuq", C.c_int32),
-        ("outliers_per_vector", C.c_int32),
+        ("outliers_per_vector", C.c_int32), ("k_norm", C.c_int32),
     ]
 
 
@@ -155,13 +155,14 @@ def kvq_layer_state(handle, layer):
 # ---------------------------------------------------------------- configuration helpers
 def make_config(B, Hq, Hkv, L, max_tokens, D=128, sinks=0, window=0, k_mode=KVQ_K_PER_CHANNEL,
                 k_group=32, v_mode=KVQ_V_PER_TOKEN, v_group=32, k_hybrid=0, sym_ratio=(1, 10),
-                k_pre_rope=0, rope_base=10000.0, nuq=0, outliers=0) -> kvq_config:
+                k_pre_rope=0, rope_base=10000.0, nuq=0, outliers=0, k_norm=0) -> kvq_config:
     c = kvq_config()
     c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim = B, Hq, Hkv, D
     c.n_layers, c.max_tokens, c.sink_tokens, c.recent_window = L, max_tokens, sinks, window
     c.k_mode, c.k_group, c.v_mode, c.v_group = k_mode, k_group, v_mode, v_group
     c.k_hybrid, c.sym_ratio_num, c.sym_ratio_den = k_hybrid, sym_ratio[0], sym_ratio[1]
     c.k_pre_rope, c.rope_base, c.nuq, c.outliers_per_vector = k_pre_rope, rope_base, nuq, outliers
+    c.k_norm = k_norm
     return c
 
 
@@ -175,7 +176,8 @@ def config_from_workload(wl, max_tokens=None) -> kvq_config:
         k_mode=KVQ_K_PER_CHANNEL if wl.k_mode == "channel" else KVQ_K_INNER, k_group=wl.k_group,
         v_mode=KVQ_V_HADAMARD if wl.v_hadamard else KVQ_V_PER_TOKEN, v_group=wl.v_group,
         k_hybrid=int(wl.k_hybrid), sym_ratio=(f.numerator, f.denominator),
-        k_pre_rope=int(wl.pre_rope), rope_base=wl.rope_base, nuq=int(wl.nuq), outliers=wl.outliers)
+        k_pre_rope=int(wl.pre_rope), rope_base=wl.rope_base, nuq=int(wl.nuq), outliers=wl.outliers,
+        k_norm=int(getattr(wl, "k_norm", False)))
 
 
 # ---------------------------------------------------------------- torch plumbing

@@ -91,6 +91,17 @@ typedef struct {
   float rope_base;        /* e.g. 10000 (rotate-half pairs (i, i+D/2)) */
   int32_t nuq;            /* 1: 3-bit codebook quantizer for keys and values */
   int32_t outliers_per_vector; /* 0, or k sparse fp16 entries per token row (k <= 8) */
+  int32_t k_norm;         /* 1: one-time per-channel key normalization (InnerQ, method 4;
+                             inner key groups only).  kvq_quantize_prefill takes, per
+                             (batch, kv head) and channel c, the binary exponent e_c of
+                             max_t |K[t][c]| over the prefill (a = m 2^e, 1/2 <= m < 1),
+                             E = max_c e_c and shift_c = min(E - e_c, 14) (0 for an all-zero
+                             channel); body keys are quantized as fp16(K * 2^shift_c)
+                             (saturating at +-65504) and the decode folds 2^-shift_c into
+                             the query for them, so q'.x = q.K.  Sink and window tokens stay
+                             as given.  The shifts live in the KVQ_BUF_FP16 buffer after the
+                             fp16 slots (units * 128 int8).  With k_norm the prefill
+                             keys must be 16-byte aligned (else KVQ_ERR_ARG). */
 } kvq_config;
 
 /* Per-layer device buffers (caller-owned). */

@@ -69,6 +69,14 @@ def unit_fp16(cache, layer, u, scap, wcap):
     return k, v
 
 
+def unit_kshift(cache, layer, u, scap, wcap):
+    """int8 [128] key normalization shifts of one unit (after every unit's
+    fp16 slots in the same buffer)."""
+    units = cache.cfg.batch * cache.cfg.n_kv_heads
+    off = units * 2 * (scap + wcap) * 128 * 2 + u * 128
+    return cache.raw(layer, 1)[off:off + 128].cpu().numpy().view(np.int8)
+
+
 def rel_err(got, ref):
     got = np.asarray(got, np.float64)
     den = np.max(np.abs(ref), axis=-1)
@@ -96,6 +104,8 @@ def check_unit(wl, cache, outs, layer, u, steps=None, check_steps=None, label=""
     n, s_eff, nbody, r = cache.state(layer)
     assert (n, nbody) == (ref["n_final"], nb)
     scap, wcap = lay["sink_cap"], lay["window_cap"]
+    if ref.get("kshift") is not None:
+        assert np.array_equal(unit_kshift(cache, layer, u, scap, wcap), ref["kshift"]), (label, "kshift")
     fk, fv = unit_fp16(cache, layer, u, scap, wcap)
     for p in list(range(s_eff)) + list(range(s_eff + nb, n)):
         slot = p if p < s_eff else scap + (p - s_eff) % wcap

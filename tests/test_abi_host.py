@@ -65,6 +65,8 @@ def _cfg(**kw):
     (dict(k_mode=7), K.KVQ_ERR_ARG),
     (dict(outliers=9), K.KVQ_ERR_ARG),
     (dict(k_pre_rope=1, rope_base=0.0), K.KVQ_ERR_ARG),
+    (dict(k_norm=2, k_mode=1, k_group=64), K.KVQ_ERR_ARG),
+    (dict(k_norm=1), K.KVQ_ERR_UNSUPPORTED),          # normalization is for inner key groups
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(K.KVQError) as e:
@@ -104,9 +106,9 @@ def _expected_record(kb_, vb, k_inner=False, kg=32, vg=32, outk=0):
     return off[:6], (off[6] + 127) // 128 * 128
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5"])
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "C5n"])
 def test_layout_and_sizes_follow_the_spec(name):
-    wl = W.ALL[name]
+    wl = W.ALL[name] if name in W.ALL else W.C5.with_(k_norm=True)
     h = K.kvq_create(K.config_from_workload(wl), wl.bit_pairs(), wl.codebooks())
     try:
         pairs = wl.bit_pairs()
@@ -126,7 +128,7 @@ def test_layout_and_sizes_follow_the_spec(name):
             assert lay["window_cap"] == wcap and lay["sink_cap"] == scap
             sizes = K.kvq_layer_buffer_sizes(h, l)
             assert sizes[0] == units * (-(-max_tokens // 32)) * rec
-            assert sizes[1] == units * 2 * (scap + wcap) * 128 * 2
+            assert sizes[1] == units * 2 * (scap + wcap) * 128 * 2 + (units * 128 if wl.k_norm else 0)
         assert K.kvq_workspace_size(h) > 0
     finally:
         K.kvq_destroy(h)

@@ -17,6 +17,8 @@ REDUCED = {
     "C3r": W.C3.with_(L=5, B=2, Hq=8, Hkv=2, T=512, steps=40, fixed_pairs=W.PAIR_SET),
     "C4r": W.C4.with_(Hq=2, Hkv=2, T=1024, steps=33),             # one flush at step 32
     "C5r": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4),          # ragged last block
+    # InnerQ key normalization on C5's inner groups; one key channel x64
+    "C5rn": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4, k_norm=True, k_out_factor=64.0),
 }
 
 EDGE = {
@@ -27,6 +29,9 @@ EDGE = {
     "uniform-3bit": W.C2.with_(Hq=2, Hkv=2, T=300, steps=3, fixed_pairs=((3, 3),)),
     "gqa2-kv8": W.C3.with_(L=1, B=1, Hq=4, Hkv=2, T=200, steps=2, fixed_pairs=((8, 8),)),
     "gqa16": W.C3.with_(L=1, B=1, Hq=16, Hkv=1, T=300, steps=2, fixed_pairs=((4, 2),)),
+    "knorm-window-only": W.C5.with_(B=1, Hq=8, Hkv=1, T=20, steps=3, k_norm=True),
+    "knorm-sinks-window": W.C5.with_(B=1, Hq=8, Hkv=1, T=300, steps=3, sinks=4, window=32,
+                                     k_norm=True, k_out_factor=64.0),
 }
 
 
@@ -57,7 +62,7 @@ def test_edge_cases(name):
     _check_all(name, EDGE[name])
 
 
-@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C4r", "C5r"])
+@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C4r", "C5r", "C5rn"])
 def test_reduced_configs_general_kernel(name, monkeypatch):
     """The same workloads through the LDS-staged decode kernel (the path every
     scheme the matrix-core kernel does not cover takes)."""
@@ -130,3 +135,7 @@ def test_full_c4_sampled():
 
 def test_full_c5_sampled():
     _full(W.C5, [(0, 0), (0, 255), (0, 511)])
+
+
+def test_full_c5_key_norm_sampled():
+    _full(W.C5.with_(k_norm=True), [(0, 3), (0, 300)])
