@@ -163,6 +163,37 @@ void quant_sym(const uint16_t* x, int n, int bits, uint8_t* codes, uint16_t* s_o
   }
 }
 
+// Ternary values, the Hadamard 2-bit page's first attempt (about 1.58 bits
+// per value; section details, last paragraph), kept as a negative control.
+// Reading: per-token groups, levels {-s, 0, +s} with s = max |x| over the
+// group's non-outlier members (an fp16 value, so exact), code =
+// clamp(rne(fl32(x / s)), -1, 1) + 1 stored as a 2-bit code with z = -s, so
+// that the plain asymmetric dequantization code * s + z yields the level.
+// An all-zero group has s = 0, z = -0 and code 1.
+void quant_tern(const uint16_t* x, const uint8_t* excl, int n, uint8_t* codes, uint16_t* s_out,
+                uint16_t* z_out) {
+  float a = 0.f;
+  for (int i = 0; i < n; ++i) {
+    if (excl && excl[i]) continue;
+    const float v = std::fabs(h2f(x[i]));
+    if (v > a) a = v;
+  }
+  const uint16_t s = f64_to_f16(static_cast<double>(a));
+  *s_out = s;
+  *z_out = static_cast<uint16_t>(s ^ 0x8000);
+  const float sv = h2f(s);
+  for (int i = 0; i < n; ++i) {
+    if (s == 0) {
+      codes[i] = 1;
+      continue;
+    }
+    float r = std::nearbyint(h2f(x[i]) / sv);
+    if (r < -1.f) r = -1.f;
+    if (r > 1.f) r = 1.f;
+    codes[i] = static_cast<uint8_t>(static_cast<int>(r) + 1);
+  }
+}
+
 // Hybrid choice (InnerQ method 2): symmetric when the group is centred on
 // zero.  Reading: |mean| / range <= ratio, evaluated exactly as
 // den*|sum| <= num*g*(max-min) on fp16 values taken as integers in units of
@@ -302,6 +333,7 @@ typedef struct {
   double rope_base;
   uint16_t levels_k[8];
   uint16_t levels_v[8];
+  int32_t v_ternary;   // values as ternary levels {-s, 0, s} in 2-bit codes
 } oq_scheme;
 
 uint16_t oq_f64_to_f16(double x) { return f64_to_f16(x); }
@@ -322,6 +354,9 @@ void oq_quant_sym(const uint16_t* x, int32_t n, int32_t bits, uint8_t* codes, ui
 }
 int32_t oq_hybrid_is_sym(const uint16_t* x, int32_t n, int32_t num, int32_t den) {
   return hybrid_is_sym(x, n, num, den) ? 1 : 0;
+}
+void oq_quant_tern(const uint16_t* x, const uint8_t* excl, int32_t n, uint8_t* codes, uint16_t* meta) {
+  quant_tern(x, excl, n, codes, &meta[0], &meta[1]);
 }
 void oq_quant_nuq(const uint16_t* x, const uint8_t* excl, int32_t n, const uint16_t* levels,
                   uint8_t* codes, uint16_t* meta) {
@@ -425,6 +460,7 @@ int32_t oq_encode_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* V
   if (sc->k_mode == 0 && nb % kg) return -1;
   if (sc->k_mode == 1 && D % kg) return -1;
   if (sc->nuq && sc->k_hybrid) return -1;
+  if (sc->v_ternary && (sc->v_bits != 2 || sc->nuq || sc->v_hadamard)) return -1;
   // values: optional rotation of every token
   for (int t = 0; t < n; ++t) {
     if (sc->v_hadamard)
@@ -496,6 +532,8 @@ int32_t oq_encode_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* V
       uint16_t* m = vmeta + (static_cast<size_t>(i) * (D / vg) + g) * 2;
       if (sc->nuq)
         quant_nuq(src, ex, vg, sc->levels_v, dst, &m[0], &m[1]);
+      else if (sc->v_ternary)
+        quant_tern(src, ex, vg, dst, &m[0], &m[1]);
       else
         quant_asym(src, ex, vg, sc->v_bits, dst, &m[0], &m[1]);
     }

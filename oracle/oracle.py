@@ -36,6 +36,7 @@ class OScheme(C.Structure):
         ("ratio_num", C.c_int32), ("ratio_den", C.c_int32), ("nuq", C.c_int32),
         ("outliers", C.c_int32), ("v_hadamard", C.c_int32), ("pre_rope", C.c_int32),
         ("rope_base", C.c_double), ("levels_k", C.c_uint16 * 8), ("levels_v", C.c_uint16 * 8),
+        ("v_ternary", C.c_int32),
     ]
 
 
@@ -62,6 +63,7 @@ def lib():
             L.oq_hybrid_is_sym.argtypes = [u16p, C.c_int32, C.c_int32, C.c_int32]
             L.oq_hybrid_is_sym.restype = C.c_int32
             L.oq_quant_nuq.argtypes = [u16p, u8p, C.c_int32, u16p, u8p, u16p]
+            L.oq_quant_tern.argtypes = [u16p, u8p, C.c_int32, u8p, u16p]
             L.oq_topk.argtypes = [u16p, C.c_int32, C.c_int32, i32p]
             L.oq_hadamard_fp16.argtypes = [u16p, C.c_int32, u16p]
             L.oq_hadamard_f64.argtypes = [f64p, C.c_int32, f64p]
@@ -128,6 +130,17 @@ def hybrid_is_sym(x16, num=1, den=10) -> bool:
     return bool(lib().oq_hybrid_is_sym(_p(x16, C.c_uint16), x16.size, num, den))
 
 
+def quant_tern(x16, excl=None):
+    """Ternary levels {-s, 0, s} in 2-bit codes: (codes, [s, z])."""
+    x16 = np.ascontiguousarray(x16, dtype=np.uint16)
+    ex = None if excl is None else np.ascontiguousarray(excl, dtype=np.uint8)
+    codes = np.empty(x16.size, np.uint8)
+    meta = np.empty(2, np.uint16)
+    lib().oq_quant_tern(_p(x16, C.c_uint16), _p(ex, C.c_uint8), x16.size, _p(codes, C.c_uint8),
+                        _p(meta, C.c_uint16))
+    return codes, meta
+
+
 def quant_nuq(x16, levels16, excl=None):
     x16 = np.ascontiguousarray(x16, dtype=np.uint16)
     lv = np.ascontiguousarray(levels16, dtype=np.uint16)
@@ -181,13 +194,14 @@ def state_append(n, nb, r, W, F):
 # ---------------------------------------------------------------- unit level
 def make_scheme(D=128, k_mode=0, k_group=32, v_group=32, k_bits=4, v_bits=4, k_hybrid=0,
                 ratio=(1, 10), nuq=0, outliers=0, v_hadamard=0, pre_rope=0, rope_base=10000.0,
-                levels_k=None, levels_v=None) -> OScheme:
+                levels_k=None, levels_v=None, v_ternary=0) -> OScheme:
     s = OScheme()
     s.D, s.k_mode, s.k_group, s.v_group = D, k_mode, k_group, v_group
     s.k_bits, s.v_bits, s.k_hybrid = k_bits, v_bits, k_hybrid
     s.ratio_num, s.ratio_den = ratio
     s.nuq, s.outliers, s.v_hadamard, s.pre_rope = nuq, outliers, v_hadamard, pre_rope
     s.rope_base = rope_base
+    s.v_ternary = v_ternary
     for i in range(8):
         s.levels_k[i] = int(levels_k[i]) if levels_k is not None else 0
         s.levels_v[i] = int(levels_v[i]) if levels_v is not None else 0
@@ -203,7 +217,8 @@ def scheme_for(wl, layer: int) -> OScheme:
         k_bits=kb, v_bits=vb, k_hybrid=int(wl.k_hybrid), ratio=ratio, nuq=int(wl.nuq),
         outliers=wl.outliers, v_hadamard=int(wl.v_hadamard), pre_rope=int(wl.pre_rope),
         rope_base=wl.rope_base,
-        levels_k=None if cb is None else cb[layer, 0], levels_v=None if cb is None else cb[layer, 1])
+        levels_k=None if cb is None else cb[layer, 0], levels_v=None if cb is None else cb[layer, 1],
+        v_ternary=int(getattr(wl, "v_ternary", False)))
 
 
 def _ratio(r: float):

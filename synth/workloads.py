@@ -48,6 +48,7 @@ class Workload:
     k_group: int = 32
     v_group: int = 32
     v_hadamard: bool = False
+    v_ternary: bool = False      # values as ternary levels {-s, 0, s} (2-bit codes)
     k_hybrid: bool = False
     sym_ratio: float = 0.1
     k_norm: bool = False         # per-channel key normalization from the prefill (inner keys)
