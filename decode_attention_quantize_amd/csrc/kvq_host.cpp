@@ -67,6 +67,7 @@ kvq_status fill_layout(const kvq_cache& c, int kb, int vb, const uint16_t* cb, L
   d.nuq = g.nuq != 0;
   d.outk = g.outliers_per_vector;
   d.v_had = g.v_mode == KVQ_V_HADAMARD;
+  d.v_tern = g.v_mode == KVQ_V_TERNARY;
   d.pre_rope = g.k_pre_rope != 0;
   d.rope_base = g.rope_base;
   if (cb) {
@@ -180,7 +181,8 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
   if (g.max_tokens > (1 << 24) || g.sink_tokens > g.max_tokens || g.recent_window > (1 << 20))
     return KVQ_ERR_ARG;
   if (g.k_mode != KVQ_K_PER_CHANNEL && g.k_mode != KVQ_K_INNER) return KVQ_ERR_ARG;
-  if (g.v_mode != KVQ_V_PER_TOKEN && g.v_mode != KVQ_V_HADAMARD) return KVQ_ERR_ARG;
+  if (g.v_mode != KVQ_V_PER_TOKEN && g.v_mode != KVQ_V_HADAMARD && g.v_mode != KVQ_V_TERNARY)
+    return KVQ_ERR_ARG;
   if (g.outliers_per_vector < 0 || g.outliers_per_vector > kvq::kMaxOutliers) return KVQ_ERR_ARG;
   if (g.k_hybrid && (g.sym_ratio_num < 0 || g.sym_ratio_den <= 0)) return KVQ_ERR_ARG;
   if (g.k_pre_rope && !(g.rope_base > 0.f)) return KVQ_ERR_ARG;
@@ -194,6 +196,7 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
   if (!pow2_in(g.v_group, 16, 64)) return KVQ_ERR_UNSUPPORTED;
   if (g.nuq && g.k_hybrid) return KVQ_ERR_UNSUPPORTED;
   if (g.k_norm && g.k_mode != KVQ_K_INNER) return KVQ_ERR_UNSUPPORTED;
+  if (g.v_mode == KVQ_V_TERNARY && g.nuq) return KVQ_ERR_UNSUPPORTED;
   for (int l = 0; l < g.n_layers; ++l) {
     const int kb = layer_bits[l].k_bits, vb = layer_bits[l].v_bits;
     if (g.nuq) {
@@ -208,6 +211,7 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
       if (!ok(kb) || !ok(vb)) return KVQ_ERR_UNSUPPORTED;
     }
     if (g.k_hybrid && kb < 2) return KVQ_ERR_UNSUPPORTED;
+    if (g.v_mode == KVQ_V_TERNARY && vb != 2) return KVQ_ERR_UNSUPPORTED;
   }
   kvq_cache* c = new (std::nothrow) kvq_cache();
   if (!c) return KVQ_ERR_ARG;

@@ -21,6 +21,7 @@ struct LayerDesc {
   int32_t k_inner, k_group, v_group;
   int32_t k_hybrid, ratio_num, ratio_den;
   int32_t nuq, outk, v_had, pre_rope;
+  int32_t v_tern;  // values as ternary levels {-s, 0, s} in 2-bit codes (z = -s)
   float rope_base;
   uint16_t lev_k[8], lev_v[8];
   double had_scale;  // fl64(1/sqrt(D)), computed on the host

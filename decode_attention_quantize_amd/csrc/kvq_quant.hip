@@ -166,8 +166,17 @@ __device__ void mark_outliers(const uint16_t (*rows)[D], uint8_t (*ex)[D], int n
 template <int W>
 __device__ __forceinline__ void token_group(uint16_t xh, bool excluded, int bits, bool nuq,
                                             const uint16_t* lev, bool hybrid, int rnum, int rden,
-                                            int& code, uint16_t& s, uint16_t& z) {
+                                            bool tern, int& code, uint16_t& s, uint16_t& z) {
   const float x = h2f(xh);
+  if (tern) {
+    // ternary levels {-s, 0, s}, s = max |x| over the non-outlier members (an
+    // fp16 value); 2-bit code clamp(rne(x / s), -1, 1) + 1 with z = -s
+    const float a = group_max<W>(excluded ? 0.f : fabsf(x));
+    s = f2h(a);
+    z = static_cast<uint16_t>(s ^ 0x8000u);
+    code = s == 0 ? 1 : static_cast<int>(fminf(fmaxf(rintf(x / h2f(s)), -1.f), 1.f)) + 1;
+    return;
+  }
   float mn = excluded ? __int_as_float(0x7f800000) : x;
   float mx = excluded ? __int_as_float(0xff800000) : x;
   group_minmax<W>(mn, mx);
@@ -206,7 +215,7 @@ __device__ __forceinline__ void token_group(uint16_t xh, bool excluded, int bits
 template <int W>
 __device__ void quant_token_groups(const uint16_t (*rows)[D], const uint8_t (*ex)[D],
                                    uint8_t (*codes)[D], int nrows, int bits, bool nuq,
-                                   const uint16_t* lev, bool hybrid, int rnum, int rden,
+                                   const uint16_t* lev, bool hybrid, int rnum, int rden, bool tern,
                                    uint8_t* meta_base, int meta_kind, int slot0) {
   // meta_kind 0: inner keys [32][D/W] (s,z) pairs; 1: values s[D/W][32], z[D/W][32]
   const int t = threadIdx.x;
@@ -216,7 +225,7 @@ __device__ void quant_token_groups(const uint16_t (*rows)[D], const uint8_t (*ex
   for (int j = 0; j < nrows; ++j) {
     int code;
     uint16_t s, z;
-    token_group<W>(rows[j][t], ex ? ex[j][t] != 0 : false, bits, nuq, lev, hybrid, rnum, rden,
+    token_group<W>(rows[j][t], ex ? ex[j][t] != 0 : false, bits, nuq, lev, hybrid, rnum, rden, tern,
                    code, s, z);
     codes[j][t] = static_cast<uint8_t>(code);
     if ((t % W) == 0) {
@@ -232,33 +241,21 @@ __device__ void quant_token_groups(const uint16_t (*rows)[D], const uint8_t (*ex
   }
 }
 
-template <int W>
-__device__ __forceinline__ void quant_token_groups_dispatch(int w, const uint16_t (*rows)[D],
-                                                            const uint8_t (*ex)[D],
-                                                            uint8_t (*codes)[D], int nrows,
-                                                            int bits, bool nuq,
-                                                            const uint16_t* lev, bool hybrid,
-                                                            int rnum, int rden, uint8_t* meta,
-                                                            int kind, int slot0) {
-  quant_token_groups<W>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta, kind,
-                        slot0);
-}
-
 __device__ void quant_groups_any(int w, const uint16_t (*rows)[D], const uint8_t (*ex)[D],
                                  uint8_t (*codes)[D], int nrows, int bits, bool nuq,
-                                 const uint16_t* lev, bool hybrid, int rnum, int rden,
+                                 const uint16_t* lev, bool hybrid, int rnum, int rden, bool tern,
                                  uint8_t* meta, int kind, int slot0) {
   switch (w) {
     case 16:
-      quant_token_groups<16>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta,
+      quant_token_groups<16>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, tern, meta,
                              kind, slot0);
       break;
     case 32:
-      quant_token_groups<32>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta,
+      quant_token_groups<32>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, tern, meta,
                              kind, slot0);
       break;
     default:
-      quant_token_groups<64>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, meta,
+      quant_token_groups<64>(rows, ex, codes, nrows, bits, nuq, lev, hybrid, rnum, rden, tern, meta,
                              kind, slot0);
       break;
   }
@@ -447,11 +444,12 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
     km[D + t] = z;
   } else {
     quant_groups_any(L.k_group, sm.k, out ? sm.exk : nullptr, sm.ck, nrows, L.kb, L.nuq != 0,
-                     L.lev_k, L.k_hybrid != 0, L.ratio_num, L.ratio_den, rec + L.off_km, 0, slot0);
+                     L.lev_k, L.k_hybrid != 0, L.ratio_num, L.ratio_den, false, rec + L.off_km, 0,
+                     slot0);
   }
   // ---- values: per-token groups
   quant_groups_any(L.v_group, sm.v, out ? sm.exv : nullptr, sm.cv, nrows, L.vb, L.nuq != 0,
-                   L.lev_v, false, 1, 1, rec + L.off_vm, 1, slot0);
+                   L.lev_v, false, 1, 1, L.v_tern != 0, rec + L.off_vm, 1, slot0);
   __syncthreads();
 
   if (L.kb == 3)

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_ARG, KVQ_ERR_CAPACITY, KVQ_ERR_UNSUPPORTED, KVQ_ERR_STATE, KVQ_ERR_DEVICE = range(6)
 KVQ_K_PER_CHANNEL, KVQ_K_INNER = 0, 1
-KVQ_V_PER_TOKEN, KVQ_V_HADAMARD = 0, 1
+KVQ_V_PER_TOKEN, KVQ_V_HADAMARD, KVQ_V_TERNARY = 0, 1, 2
 KVQ_NBUF = 2
 KVQ_BUF_BODY, KVQ_BUF_FP16 = 0, 1
 
@@ -174,7 +174,9 @@ def config_from_workload(wl, max_tokens=None) -> kvq_config:
         max_tokens if max_tokens is not None else wl.T + (wl.steps if wl.append else 0),
         D=wl.D, sinks=wl.sinks, window=wl.window,
         k_mode=KVQ_K_PER_CHANNEL if wl.k_mode == "channel" else KVQ_K_INNER, k_group=wl.k_group,
-        v_mode=KVQ_V_HADAMARD if wl.v_hadamard else KVQ_V_PER_TOKEN, v_group=wl.v_group,
+        v_mode=(KVQ_V_HADAMARD if wl.v_hadamard else
+                KVQ_V_TERNARY if getattr(wl, "v_ternary", False) else KVQ_V_PER_TOKEN),
+        v_group=wl.v_group,
         k_hybrid=int(wl.k_hybrid), sym_ratio=(f.numerator, f.denominator),
         k_pre_rope=int(wl.pre_rope), rope_base=wl.rope_base, nuq=int(wl.nuq), outliers=wl.outliers,
         k_norm=int(getattr(wl, "k_norm", False)))

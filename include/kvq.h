@@ -65,7 +65,13 @@ typedef enum {
 } kvq_status;
 
 enum { KVQ_K_PER_CHANNEL = 0, KVQ_K_INNER = 1 };
-enum { KVQ_V_PER_TOKEN = 0, KVQ_V_HADAMARD = 1 };
+/* Values: per-token groups; KVQ_V_HADAMARD rotates each value row by the
+ * normalized 128x128 Hadamard matrix first (the Hadamard 2-bit page) and the
+ * decode undoes it after the attention sum; KVQ_V_TERNARY quantizes to the
+ * three levels {-s, 0, +s} with s = max |v| over the group, stored as 2-bit
+ * codes with z = -s (that page's failed first attempt at about 1.58 bits,
+ * kept as a negative control; needs v_bits == 2, no codebooks). */
+enum { KVQ_V_PER_TOKEN = 0, KVQ_V_HADAMARD = 1, KVQ_V_TERNARY = 2 };
 
 /* (k_bits, v_bits) of one layer: 2, 3, 4 or 8 each (3 only with nuq). */
 typedef struct {
@@ -83,7 +89,7 @@ typedef struct {
   int32_t recent_window;  /* W: most recent W..W+F-1 positions kept fp16 */
   int32_t k_mode;         /* KVQ_K_PER_CHANNEL (k_group must be 32) | KVQ_K_INNER */
   int32_t k_group;        /* tokens per key group (per channel) or channels (inner: 32|64|128) */
-  int32_t v_mode;         /* KVQ_V_PER_TOKEN | KVQ_V_HADAMARD */
+  int32_t v_mode;         /* KVQ_V_PER_TOKEN | KVQ_V_HADAMARD | KVQ_V_TERNARY */
   int32_t v_group;        /* channels per value group: 16, 32 or 64 */
   int32_t k_hybrid;       /* inner groups: symmetric iff |mean|/range <= num/den */
   int32_t sym_ratio_num, sym_ratio_den;  /* e.g. 1/10 */

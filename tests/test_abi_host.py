@@ -67,6 +67,7 @@ def _cfg(**kw):
     (dict(k_pre_rope=1, rope_base=0.0), K.KVQ_ERR_ARG),
     (dict(k_norm=2, k_mode=1, k_group=64), K.KVQ_ERR_ARG),
     (dict(k_norm=1), K.KVQ_ERR_UNSUPPORTED),          # normalization is for inner key groups
+    (dict(v_mode=3), K.KVQ_ERR_ARG),
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(K.KVQError) as e:
@@ -89,6 +90,12 @@ def test_create_rejects_bits_and_codebooks():
     with pytest.raises(K.KVQError) as e:
         K.kvq_create(_cfg(nuq=1), [(3, 3), (3, 3)], cb)  # infinite level
     assert e.value.status == K.KVQ_ERR_ARG
+    with pytest.raises(K.KVQError) as e:
+        K.kvq_create(_cfg(v_mode=K.KVQ_V_TERNARY), [(4, 2), (4, 4)])  # ternary values are 2-bit codes
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED
+    with pytest.raises(K.KVQError) as e:
+        K.kvq_create(_cfg(v_mode=K.KVQ_V_TERNARY, nuq=1), [(3, 3), (3, 3)], cb)
+    assert e.value.status == K.KVQ_ERR_UNSUPPORTED
     rc = K.lib().kvq_create(None, None, None, None)
     assert rc == K.KVQ_ERR_ARG
 

@@ -19,6 +19,10 @@ REDUCED = {
     "C5r": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4),          # ragged last block
     # InnerQ key normalization on C5's inner groups; one key channel x64
     "C5rn": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4, k_norm=True, k_out_factor=64.0),
+    # the Hadamard 2-bit page's pairing: KIVI int4 keys (per channel) with
+    # rotated 2-bit values, and its ternary-value negative control
+    "P5r": W.C2.with_(Hq=4, Hkv=4, T=1024, steps=8, v_hadamard=True, v_out_count=2),
+    "P5r-ternary": W.C2.with_(Hq=4, Hkv=4, T=1024, steps=8, v_ternary=True, v_out_count=2),
 }
 
 EDGE = {
@@ -62,7 +66,7 @@ def test_edge_cases(name):
     _check_all(name, EDGE[name])
 
 
-@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C4r", "C5r", "C5rn"])
+@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C4r", "C5r", "C5rn", "P5r", "P5r-ternary"])
 def test_reduced_configs_general_kernel(name, monkeypatch):
     """The same workloads through the LDS-staged decode kernel (the path every
     scheme the matrix-core kernel does not cover takes)."""
