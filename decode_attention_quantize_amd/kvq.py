@@ -21,7 +21,8 @@ KVQ_BUF_BODY, KVQ_BUF_FP16 = 0, 1
 
 EXPORTS = ("kvq_create", "kvq_destroy", "kvq_layer_buffer_sizes", "kvq_block_layout",
            "kvq_bind_layer", "kvq_workspace_size", "kvq_quantize_prefill", "kvq_append_token",
-           "kvq_decode_attn", "kvq_layer_state", "kvq_status_str")
+           "kvq_decode_attn", "kvq_layer_state", "kvq_status_str",
+           "kvq_fit_rate_distortion", "kvq_waterfill_bits", "kvq_allocate_bits")
 
 
 class kvq_config(C.Structure):
@@ -77,6 +78,10 @@ def lib():
         L.kvq_append_token.argtypes = [pcache, i32, vp, vp, vp]
         L.kvq_decode_attn.argtypes = [pcache, i32, vp, vp, vp, vp]
         L.kvq_layer_state.argtypes = [pcache, i32] + [C.POINTER(C.c_int32)] * 4
+        dp, ip = C.POINTER(C.c_double), C.POINTER(C.c_int32)
+        L.kvq_fit_rate_distortion.argtypes = [i32, dp, dp, dp, dp]
+        L.kvq_waterfill_bits.argtypes = [i32, dp, dp, dp, C.c_double, dp]
+        L.kvq_allocate_bits.argtypes = [i32, dp, dp, dp, ip, i32, i32, ip]
         for name in EXPORTS:
             if name != "kvq_status_str":
                 getattr(L, name).restype = C.c_int
@@ -150,6 +155,36 @@ def kvq_layer_state(handle, layer):
     v = [C.c_int32() for _ in range(4)]
     _check(lib().kvq_layer_state(handle, layer, *[C.byref(x) for x in v]), "kvq_layer_state")
     return tuple(x.value for x in v)
+
+
+# ---------------------------------------------------------------- offline bit allocation
+def _darr(x):
+    x = [float(v) for v in x]
+    return (C.c_double * len(x))(*x)
+
+
+def kvq_fit_rate_distortion(bits, mse):
+    a, b = C.c_double(), C.c_double()
+    _check(lib().kvq_fit_rate_distortion(len(bits), _darr(bits), _darr(mse), C.byref(a), C.byref(b)),
+           "kvq_fit_rate_distortion")
+    return a.value, b.value
+
+
+def kvq_waterfill_bits(alpha, beta, w, total_bits):
+    n = len(w)
+    out = (C.c_double * n)()
+    _check(lib().kvq_waterfill_bits(n, _darr(alpha), _darr(beta), _darr(w), float(total_bits), out),
+           "kvq_waterfill_bits")
+    return list(out)
+
+
+def kvq_allocate_bits(alpha, beta, w, allowed, total_bits):
+    n = len(w)
+    al = (C.c_int32 * len(allowed))(*[int(a) for a in allowed])
+    out = (C.c_int32 * n)()
+    _check(lib().kvq_allocate_bits(n, _darr(alpha), _darr(beta), _darr(w), al, len(allowed),
+                                   int(total_bits), out), "kvq_allocate_bits")
+    return list(out)
 
 
 # ---------------------------------------------------------------- configuration helpers

@@ -219,6 +219,37 @@ kvq_status kvq_layer_state(const kvq_cache* cache, int32_t layer, int32_t* n, in
 /* Static text for a status code. */
 const char* kvq_status_str(kvq_status s);
 
+/* ---- Offline bit allocation (host only; no device work) --------------------
+ * RateQuant technical summary, methodology: each quantized component i (the
+ * keys or the values of one layer) follows D_i(b) = alpha_i beta_i^-b; the
+ * widths minimise sum_i w_i D_i(b_i) under sum_i b_i = B (w_i: sensitivity).
+ * The integer result is what kvq_create's per-layer (k_bits, v_bits) table
+ * takes.  All arrays are host memory owned by the caller. */
+
+/* Least-squares fit of ln mse = ln alpha - b ln beta over n >= 2 measured
+ * points (bits[i], mse[i] > 0, at least two distinct widths).
+ * Errors: KVQ_ERR_ARG. */
+kvq_status kvq_fit_rate_distortion(int32_t n, const double* bits, const double* mse,
+                                   double* alpha, double* beta);
+
+/* Real-valued optimum (reverse water-filling, methodology step 1): every
+ * component's w_i alpha_i ln(beta_i) beta_i^-b_i is equal and sum b_i =
+ * total_bits; with one common (alpha, beta) this is b_i = mean + (ln w_i -
+ * ln w_geo) / ln beta.  Needs alpha_i > 0, beta_i > 1, w_i > 0.  No range
+ * clipping.  Errors: KVQ_ERR_ARG. */
+kvq_status kvq_waterfill_bits(int32_t n, const double* alpha, const double* beta,
+                              const double* w, double total_bits, double* bits_out);
+
+/* Integer widths from the allowed set (methodology step 3, greedy marginal
+ * gain): all components start at the smallest allowed width; while budget is
+ * left, the component whose next allowed width gives the largest weighted
+ * distortion reduction per bit, and still fits, takes it (ties: lowest
+ * index).  sum bits_out <= total_bits.  Errors: KVQ_ERR_ARG (bad model
+ * values, empty or out-of-range allowed set, budget below n * min width). */
+kvq_status kvq_allocate_bits(int32_t n, const double* alpha, const double* beta,
+                             const double* w, const int32_t* allowed, int32_t n_allowed,
+                             int32_t total_bits, int32_t* bits_out);
+
 #ifdef __cplusplus
 }
 #endif
