@@ -413,7 +413,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
     const int wchunks = L.win_cap / kBlockTokens;
     const int wstart = st.nb % L.win_cap;  // ring index of the oldest window token
-    for (int c = sp; c < J.fp16_chunks; c += nsplit) {
+    for (int c = sp - J.fp16_split0; c >= 0 && c < J.fp16_chunks; c += J.fp16_nsplit) {
       const bool sinkc = c < J.sink_chunks;
       const int slot0 = sinkc ? kBlockTokens * c
                               : L.sinks_cap + kBlockTokens * ((J.win_chunk0 + c - J.sink_chunks) % wchunks);
@@ -582,7 +582,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
 // time.  The groups of a row meet in LDS; values stored Hadamard-rotated are
 // rotated back there (c * H * o, H Sylvester).
 __global__ void __launch_bounds__(256) decode_merge_kernel(LayerDesc L, DecodeJob J) {
-  // the split plan keeps nsplit <= max(kMaxBodySplits, kMaxFp16Splits) = 256
+  // the split plan keeps nsplit (body and fp16 splits) <= kMaxBodySplits = 256
   constexpr int kMaxSplits = 256;
   static_assert(kMaxBodySplits <= kMaxSplits && kMaxFp16Splits <= kMaxSplits, "split bound");
   constexpr int kMaxRows = kMaxGroupRows;
@@ -752,6 +752,7 @@ hipError_t dispatch(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* 
 hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& j, hipStream_t s) {
   // every group of the workgroup runs the same number of row passes
   if (L.G < 1 || L.G > kMaxGroupRows || (L.G & (L.G - 1)) != 0) return hipErrorInvalidValue;
+  if (j.nsplit < 1 || j.nsplit > kMaxBodySplits) return hipErrorInvalidValue;  // LDS tables hold 256
   hipLaunchKernelGGL(decode_merge_kernel, dim3(L.units), dim3(256), 0, s, L, j);
   return hipGetLastError();
 }

@@ -243,7 +243,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
     const int wchunks = L.win_cap / kBlockTokens;
     const int wstart = st.nb % L.win_cap;
-    for (int c = sp; c < J.fp16_chunks; c += nsplit) {
+    for (int c = sp - J.fp16_split0; c >= 0 && c < J.fp16_chunks; c += J.fp16_nsplit) {
       const bool sinkc = c < J.sink_chunks;
       const int s0 = sinkc ? kBlockTokens * c
                            : L.sinks_cap + kBlockTokens * ((J.win_chunk0 + c - J.sink_chunks) % wchunks);

@@ -138,19 +138,35 @@ void plan_splits(const kvq_cache& c, const kvq::TokenState& st, int fast_waves, 
   } else {
     j.fp16_split = st.s_eff + st.r > 0 ? 1 : 0;
   }
+  // matrix-core path: the fp16 chunks get splits of their own after the body
+  // splits, about two chunks per body split's worth of blocks, so that no
+  // split carries both a full body share and fp16 chunks
+  j.fp16_split0 = 0;
+  j.fp16_nsplit = 1;
   if (nblk <= 0) {
     j.nsplit_body = 0;
     j.blocks_per_split = 1;
+    if (fast && j.fp16_chunks > 0) j.fp16_nsplit = std::min(j.fp16_chunks, kvq::kMaxFp16Splits);
   } else {
-    int want = std::max(1, (fast ? fast_waves : 2048) / std::max(1, c.units));
-    want = std::min({want, kvq::kMaxBodySplits, std::max(1, nblk / 4)});
+    const int resident = std::max(1, (fast ? fast_waves : 2048) / std::max(1, c.units));
+    int want = std::min({resident, kvq::kMaxBodySplits, std::max(1, nblk / 4)});
+    if (fast && j.fp16_chunks > 0) {
+      const int bps0 = (nblk + want - 1) / want;
+      j.fp16_nsplit = std::min({kvq::kMaxFp16Splits, j.fp16_chunks,
+                                std::max(1, (2 * j.fp16_chunks + bps0 - 1) / bps0)});
+      // body + fp16 splits within one resident round and the merge's bound
+      want = std::max(1, std::min({want, resident - j.fp16_nsplit, kvq::kMaxBodySplits - j.fp16_nsplit}));
+    }
     j.blocks_per_split = (nblk + want - 1) / want;
     j.nsplit_body = (nblk + j.blocks_per_split - 1) / j.blocks_per_split;
   }
-  if (fast)
-    j.nsplit = std::max(j.nsplit_body, std::min(j.fp16_chunks, kvq::kMaxFp16Splits));
-  else
+  if (fast) {
+    j.fp16_split0 = j.nsplit_body;
+    j.nsplit = j.nsplit_body + (j.fp16_chunks > 0 ? j.fp16_nsplit : 0);
+    if (j.nsplit == 0) j.nsplit = 1;
+  } else {
     j.nsplit = j.nsplit_body + j.fp16_split;
+  }
 }
 
 }  // namespace

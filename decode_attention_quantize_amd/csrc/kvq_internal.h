@@ -104,11 +104,13 @@ struct DecodeJob {
   int32_t blocks_per_split;
   // sink / window tokens.  LDS-staged path: when fp16_split, split
   // nsplit_body walks them in position order.  Matrix-core path: 32-slot
-  // chunk c < fp16_chunks goes to split c % nsplit; chunks below sink_chunks
-  // are sink slots 32c.., the others window ring chunks win_chunk0, +1, ...
-  // (mod win_cap / 32); slots holding no live token are masked.
+  // chunk c < fp16_chunks goes to split fp16_split0 + c % fp16_nsplit;
+  // chunks below sink_chunks are sink slots 32c.., the others window ring
+  // chunks win_chunk0, +1, ... (mod win_cap / 32); slots holding no live
+  // token are masked.
   int32_t fp16_split;
   int32_t fp16_chunks, sink_chunks, win_chunk0;
+  int32_t fp16_split0, fp16_nsplit;
   int64_t ml_off;         // matrix-core path: float offset of the (max, sum) records
 };
 // Log-sum-exp merge of matrix-core split partials into job.out (one
