@@ -20,7 +20,8 @@
 // kv head); the keys and values of a block are read once for all of them.
 // Block records stream HBM -> LDS with global_load_lds_dwordx4 into a ring of
 // NBUF slots, NBUF-1 blocks ahead of the one being computed.  Sink / window
-// tokens (fp16) are read straight into registers.  Each split writes an
+// tokens (fp16) are read straight into registers by splits of their own,
+// after the body splits.  Each split writes an
 // (o, max, sum) partial; decode_merge_kernel combines them by log-sum-exp and
 // undoes the value rotation.
 #include <hip/hip_runtime.h>

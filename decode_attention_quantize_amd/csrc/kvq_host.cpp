@@ -115,8 +115,8 @@ bool valid_layer(const kvq_cache* c, int32_t layer) {
 
 // Split plan.  The matrix-core path runs one wavefront per split and aims at
 // one full round of resident wavefronts (fast_waves, from the kernel's ring
-// depth and register budget); the 32-slot sink / window chunks ride along on
-// the first splits.
+// depth and register budget); the 32-slot sink / window chunks get splits of
+// their own after the body splits, inside the same round.
 // The LDS-staged path walks the sink / window tokens in one extra split.
 void plan_splits(const kvq_cache& c, const kvq::TokenState& st, int fast_waves, kvq::DecodeJob& j) {
   const bool fast = fast_waves > 0;
