@@ -575,34 +575,39 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   }
 }
 
+// groups of 32 threads in a merge workgroup (16: C2's 96 split partials of a
+// unit are all requested in one batch per group)
+constexpr int kMergeGroups = 16;
+
 // Log-sum-exp merge of the split partials of one unit (all its query rows).
-// 256 threads = 8 groups of 32; thread (group, q) owns channels 4q..4q+3.
-// With G rows, 8/G groups share a row (G <= 8) and take its splits in turn;
+// NG groups of 32 threads; thread (group, q) owns channels 4q..4q+3.
+// With G rows, NG/G groups share a row (G <= NG) and take its splits in turn;
 // each group pulls every (max, sum) pair of its row from LDS, so the row
 // maximum needs no extra pass, and requests its partial vectors eight at a
 // time.  The groups of a row meet in LDS; values stored Hadamard-rotated are
 // rotated back there (c * H * o, H Sylvester).
-__global__ void __launch_bounds__(256) decode_merge_kernel(LayerDesc L, DecodeJob J) {
+template <int NG>
+__global__ void __launch_bounds__(32 * NG) decode_merge_kernel(LayerDesc L, DecodeJob J) {
   // the split plan keeps nsplit (body and fp16 splits) <= kMaxBodySplits = 256
   constexpr int kMaxSplits = 256;
   static_assert(kMaxBodySplits <= kMaxSplits && kMaxFp16Splits <= kMaxSplits, "split bound");
   constexpr int kMaxRows = kMaxGroupRows;
   __shared__ float ms[kMaxSplits * kMaxRows], ls[kMaxSplits * kMaxRows];
-  __shared__ float red[8][D];
+  __shared__ float red[NG][D];
   const int tid = threadIdx.x, grp = tid >> 5, cq = tid & 31;
   const int u = blockIdx.x;
   const int G = L.G, nsplit = J.nsplit;
   const int b = u / L.Hkv, h = u % L.Hkv;
   const float* obase = J.partials + static_cast<int64_t>(u) * nsplit * G * D;
   const float* mlbase = J.partials + J.ml_off + static_cast<int64_t>(u) * nsplit * G * 2;
-  for (int i = tid; i < nsplit * G; i += 256) {
+  for (int i = tid; i < nsplit * G; i += 32 * NG) {
     ms[i] = mlbase[2 * i];
     ls[i] = mlbase[2 * i + 1];
   }
   __syncthreads();
-  const int lpr = G >= 8 ? 1 : 8 / G;      // groups per row
+  const int lpr = G >= NG ? 1 : NG / G;    // groups per row
   const int so = grp % lpr;                // this group's first split
-  for (int r = grp / lpr; r < G; r += 8 / lpr) {
+  for (int r = grp / lpr; r < G; r += NG / lpr) {
     // row maximum and sum over all splits (32 lanes, then the group)
     float M = -INFINITY;
     for (int i = cq; i < nsplit; i += 32) M = fmaxf(M, ms[i * G + r]);
@@ -754,7 +759,7 @@ hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& j, hipStream
   // every group of the workgroup runs the same number of row passes
   if (L.G < 1 || L.G > kMaxGroupRows || (L.G & (L.G - 1)) != 0) return hipErrorInvalidValue;
   if (j.nsplit < 1 || j.nsplit > kMaxBodySplits) return hipErrorInvalidValue;  // LDS tables hold 256
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(L.units), dim3(256), 0, s, L, j);
+  hipLaunchKernelGGL(decode_merge_kernel<kMergeGroups>, dim3(L.units), dim3(32 * kMergeGroups), 0, s, L, j);
   return hipGetLastError();
 }
 
