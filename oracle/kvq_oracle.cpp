@@ -25,7 +25,8 @@
 //    per-group symmetric/asymmetric choice from local statistics (method 2),
 //    fp16 recent and sink windows (method 4), one-time per-channel key
 //    normalization computed at prefill and folded into the query (method 4;
-//    key contributions list).
+//    key contributions list); 4-bit and 8-bit groups mixed in one layer
+//    (limitations and future work).
 //  * Hadamard 2-bit values (aitrends.kr): rotate values by a Hadamard matrix,
 //    quantize uniformly to 2 bits, undo the rotation after the attention sum
 //    (TL;DR; section details; glossary).
@@ -334,6 +335,7 @@ typedef struct {
   uint16_t levels_k[8];
   uint16_t levels_v[8];
   int32_t v_ternary;   // values as ternary levels {-s, 0, s} in 2-bit codes
+  int32_t k_hi_groups; // inner 4-bit keys: groups per token quantized at 8 bits instead
 } oq_scheme;
 
 uint16_t oq_f64_to_f16(double x) { return f64_to_f16(x); }
@@ -449,11 +451,12 @@ void oq_knorm_apply(const uint16_t* K, int32_t n, int32_t D, const int8_t* shift
 //   vcodes  [nb][D]             u8
 //   vmeta   [nb][D/vg][2]
 //   kocol/koval, vocol/voval  [nb][outliers]  (int32 column, fp16 value)
+//   kwidth  inner keys: [nb][D/kg] code width of each key group (nullable)
 // Returns 0, or -1 on an unsupported scheme.
 int32_t oq_encode_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* V, int32_t n,
                        int32_t s_eff, int32_t nb, uint16_t* vrot, uint8_t* kcodes,
                        uint16_t* kmeta, uint8_t* vcodes, uint16_t* vmeta, int32_t* kocol,
-                       uint16_t* koval, int32_t* vocol, uint16_t* voval) {
+                       uint16_t* koval, int32_t* vocol, uint16_t* voval, uint8_t* kwidth) {
   const int D = sc->D;
   const int kg = sc->k_group, vg = sc->v_group, ko = sc->outliers;
   if (D <= 0 || kg <= 0 || vg <= 0 || D % vg) return -1;
@@ -461,6 +464,8 @@ int32_t oq_encode_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* V
   if (sc->k_mode == 1 && D % kg) return -1;
   if (sc->nuq && sc->k_hybrid) return -1;
   if (sc->v_ternary && (sc->v_bits != 2 || sc->nuq || sc->v_hadamard)) return -1;
+  if (sc->k_hi_groups < 0 || (sc->k_mode == 1 && sc->k_hi_groups > D / kg)) return -1;
+  if (sc->k_hi_groups && (sc->k_mode != 1 || sc->k_bits != 4 || sc->nuq || ko)) return -1;
   // values: optional rotation of every token
   for (int t = 0; t < n; ++t) {
     if (sc->v_hadamard)
@@ -509,19 +514,43 @@ int32_t oq_encode_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* V
         for (int j = 0; j < kg; ++j) kcodes[static_cast<size_t>(blk * kg + j) * D + c] = gcode[j];
       }
   } else {
-    for (int i = 0; i < nb; ++i)
-      for (int g = 0; g < D / kg; ++g) {
+    // InnerQ, limitations and future work: a layer may mix 4-bit and 8-bit
+    // groups.  Reading: per token, the k_hi_groups groups whose 4-bit
+    // quantizer has the largest step (fp16 scale magnitude; on equal steps the
+    // lower group first) are quantized again at 8 bits, with the same
+    // symmetric / asymmetric choice.
+    const int ng = D / kg;
+    std::vector<uint16_t> step(ng);
+    std::vector<uint8_t> hi(ng);
+    for (int i = 0; i < nb; ++i) {
+      auto quant_group = [&](int g, int bits) {
         const uint16_t* src = K + static_cast<size_t>(s_eff + i) * D + g * kg;
         const uint8_t* ex = kex.data() + static_cast<size_t>(i) * D + g * kg;
         uint8_t* dst = kcodes + static_cast<size_t>(i) * D + g * kg;
-        uint16_t* m = kmeta + (static_cast<size_t>(i) * (D / kg) + g) * 2;
+        uint16_t* m = kmeta + (static_cast<size_t>(i) * ng + g) * 2;
         if (sc->nuq)
           quant_nuq(src, ex, kg, sc->levels_k, dst, &m[0], &m[1]);
         else if (sc->k_hybrid && hybrid_is_sym(src, kg, sc->ratio_num, sc->ratio_den))
-          quant_sym(src, kg, sc->k_bits, dst, &m[0], &m[1]);
+          quant_sym(src, kg, bits, dst, &m[0], &m[1]);
         else
-          quant_asym(src, ex, kg, sc->k_bits, dst, &m[0], &m[1]);
+          quant_asym(src, ex, kg, bits, dst, &m[0], &m[1]);
+        return static_cast<uint16_t>(m[0] & 0x7fff);
+      };
+      for (int g = 0; g < ng; ++g) {
+        step[g] = quant_group(g, sc->k_bits);
+        hi[g] = 0;
       }
+      for (int k = 0; k < sc->k_hi_groups; ++k) {
+        int best = -1;
+        for (int g = 0; g < ng; ++g)
+          if (!hi[g] && (best < 0 || step[g] > step[best])) best = g;
+        hi[best] = 1;
+      }
+      for (int g = 0; g < ng; ++g) {
+        if (hi[g]) quant_group(g, 8);
+        if (kwidth) kwidth[static_cast<size_t>(i) * ng + g] = static_cast<uint8_t>(hi[g] ? 8 : sc->k_bits);
+      }
+    }
   }
   // values: per-token groups
   for (int i = 0; i < nb; ++i)
@@ -548,13 +577,14 @@ int32_t oq_encode_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* V
 // Khat, Vhat: [n][D]; only rows [t_begin, t_end) are written.
 // kshift (nullable): per-channel key normalization shifts; body keys (codes
 // and outliers, which live in the normalized domain) are scaled back by
-// 2^-shift before RoPE.
+// 2^-shift before RoPE.  kwidth (nullable, inner keys): code width of each
+// key group as returned by oq_encode_unit.
 int32_t oq_dequant_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* vrot, int32_t n,
                         int32_t s_eff, int32_t nb, int32_t t_begin, int32_t t_end,
                         const uint8_t* kcodes, const uint16_t* kmeta,
                         const uint8_t* vcodes, const uint16_t* vmeta, const int32_t* kocol,
                         const uint16_t* koval, const int32_t* vocol, const uint16_t* voval,
-                        const int8_t* kshift, double* Khat, double* Vhat) {
+                        const int8_t* kshift, const uint8_t* kwidth, double* Khat, double* Vhat) {
   const int D = sc->D, kg = sc->k_group, vg = sc->v_group, ko = sc->outliers;
   const uint16_t* lk = sc->nuq ? sc->levels_k : nullptr;
   const uint16_t* lv = sc->nuq ? sc->levels_v : nullptr;
@@ -568,7 +598,9 @@ int32_t oq_dequant_unit(const oq_scheme* sc, const uint16_t* K, const uint16_t* 
         const uint16_t* m = sc->k_mode == 0
                                 ? kmeta + (static_cast<size_t>(i / kg) * D + c) * 2
                                 : kmeta + (static_cast<size_t>(i) * (D / kg) + c / kg) * 2;
-        kh[c] = dequant(kcodes[static_cast<size_t>(i) * D + c], m[0], m[1], sc->k_bits, lk);
+        const int kbits = (kwidth && sc->k_mode == 1) ? kwidth[static_cast<size_t>(i) * (D / kg) + c / kg]
+                                                      : sc->k_bits;
+        kh[c] = dequant(kcodes[static_cast<size_t>(i) * D + c], m[0], m[1], kbits, lk);
         const uint16_t* mv = vmeta + (static_cast<size_t>(i) * (D / vg) + c / vg) * 2;
         vh[c] = dequant(vcodes[static_cast<size_t>(i) * D + c], mv[0], mv[1], sc->v_bits, lv);
       }

@@ -36,7 +36,7 @@ class OScheme(C.Structure):
         ("ratio_num", C.c_int32), ("ratio_den", C.c_int32), ("nuq", C.c_int32),
         ("outliers", C.c_int32), ("v_hadamard", C.c_int32), ("pre_rope", C.c_int32),
         ("rope_base", C.c_double), ("levels_k", C.c_uint16 * 8), ("levels_v", C.c_uint16 * 8),
-        ("v_ternary", C.c_int32),
+        ("v_ternary", C.c_int32), ("k_hi_groups", C.c_int32),
     ]
 
 
@@ -73,11 +73,12 @@ def lib():
             L.oq_state_append.argtypes = [i32p, i32p, i32p, C.c_int32, C.c_int32]
             L.oq_state_append.restype = C.c_int32
             L.oq_encode_unit.argtypes = [C.POINTER(OScheme), u16p, u16p, C.c_int32, C.c_int32,
-                                         C.c_int32, u16p, u8p, u16p, u8p, u16p, i32p, u16p, i32p, u16p]
+                                         C.c_int32, u16p, u8p, u16p, u8p, u16p, i32p, u16p, i32p, u16p,
+                                         u8p]
             L.oq_encode_unit.restype = C.c_int32
             L.oq_dequant_unit.argtypes = [C.POINTER(OScheme), u16p, u16p, C.c_int32, C.c_int32,
                                           C.c_int32, C.c_int32, C.c_int32, u8p, u16p, u8p, u16p,
-                                          i32p, u16p, i32p, u16p, C.POINTER(C.c_int8), f64p, f64p]
+                                          i32p, u16p, i32p, u16p, C.POINTER(C.c_int8), u8p, f64p, f64p]
             L.oq_dequant_unit.restype = C.c_int32
             L.oq_knorm_shifts.argtypes = [u16p, C.c_int32, C.c_int32, C.POINTER(C.c_int8)]
             L.oq_knorm_apply.argtypes = [u16p, C.c_int32, C.c_int32, C.POINTER(C.c_int8), u16p]
@@ -194,7 +195,7 @@ def state_append(n, nb, r, W, F):
 # ---------------------------------------------------------------- unit level
 def make_scheme(D=128, k_mode=0, k_group=32, v_group=32, k_bits=4, v_bits=4, k_hybrid=0,
                 ratio=(1, 10), nuq=0, outliers=0, v_hadamard=0, pre_rope=0, rope_base=10000.0,
-                levels_k=None, levels_v=None, v_ternary=0) -> OScheme:
+                levels_k=None, levels_v=None, v_ternary=0, k_hi_groups=0) -> OScheme:
     s = OScheme()
     s.D, s.k_mode, s.k_group, s.v_group = D, k_mode, k_group, v_group
     s.k_bits, s.v_bits, s.k_hybrid = k_bits, v_bits, k_hybrid
@@ -202,6 +203,7 @@ def make_scheme(D=128, k_mode=0, k_group=32, v_group=32, k_bits=4, v_bits=4, k_h
     s.nuq, s.outliers, s.v_hadamard, s.pre_rope = nuq, outliers, v_hadamard, pre_rope
     s.rope_base = rope_base
     s.v_ternary = v_ternary
+    s.k_hi_groups = k_hi_groups
     for i in range(8):
         s.levels_k[i] = int(levels_k[i]) if levels_k is not None else 0
         s.levels_v[i] = int(levels_v[i]) if levels_v is not None else 0
@@ -218,7 +220,8 @@ def scheme_for(wl, layer: int) -> OScheme:
         outliers=wl.outliers, v_hadamard=int(wl.v_hadamard), pre_rope=int(wl.pre_rope),
         rope_base=wl.rope_base,
         levels_k=None if cb is None else cb[layer, 0], levels_v=None if cb is None else cb[layer, 1],
-        v_ternary=int(getattr(wl, "v_ternary", False)))
+        v_ternary=int(getattr(wl, "v_ternary", False)),
+        k_hi_groups=getattr(wl, "k_hi_groups", 0) if (wl.k_mode == "inner" and kb == 4) else 0)
 
 
 def _ratio(r: float):
@@ -243,12 +246,14 @@ def encode_unit(sc: OScheme, K16, V16, n, s_eff, nb):
         kocol=np.zeros((nb, ko), np.int32), koval=np.zeros((nb, ko), np.uint16),
         vocol=np.zeros((nb, ko), np.int32), voval=np.zeros((nb, ko), np.uint16),
     )
+    if sc.k_mode == 1:
+        e["kwidth"] = np.zeros((nb, D // sc.k_group), np.uint8)
     rc = lib().oq_encode_unit(C.byref(sc), _p(K16, C.c_uint16), _p(V16, C.c_uint16), n, s_eff, nb,
                               _p(e["vrot"], C.c_uint16), _p(e["kcodes"], C.c_uint8),
                               _p(e["kmeta"], C.c_uint16), _p(e["vcodes"], C.c_uint8),
                               _p(e["vmeta"], C.c_uint16), _p(e["kocol"], C.c_int32),
                               _p(e["koval"], C.c_uint16), _p(e["vocol"], C.c_int32),
-                              _p(e["voval"], C.c_uint16))
+                              _p(e["voval"], C.c_uint16), _p(e.get("kwidth"), C.c_uint8))
     if rc != 0:
         raise ValueError("oracle: unsupported scheme")
     if sc.outliers == 0:
@@ -298,6 +303,7 @@ def dequant_unit(sc: OScheme, K16, enc, n, s_eff, nb, t_begin=0, t_end=None, Kha
                                _p(koval, C.c_uint16), _p(vocol, C.c_int32), _p(voval, C.c_uint16),
                                _p(None if kshift is None else np.ascontiguousarray(kshift, dtype=np.int8),
                                   C.c_int8),
+                               _p(enc.get("kwidth"), C.c_uint8),
                                _p(Khat, C.c_double), _p(Vhat, C.c_double))
     assert rc == 0
     return Khat, Vhat

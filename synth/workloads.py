@@ -52,6 +52,7 @@ class Workload:
     k_hybrid: bool = False
     sym_ratio: float = 0.1
     k_norm: bool = False         # per-channel key normalization from the prefill (inner keys)
+    k_hi_groups: int = 0         # inner 4-bit keys: groups per token kept at 8 bits (mixed 4/8)
     pre_rope: bool = False
     rope_base: float = 10000.0
     nuq: bool = False
