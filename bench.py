@@ -36,7 +36,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=64)
     p.add_argument("--warmup", type=int, default=8)
-    p.add_argument("--workload", default="C2")
+    p.add_argument("--workload", default="C2",
+                   help="C1..C5, or a scheme variant: C5n (key normalization), C5m (mixed 4/8-bit "
+                        "key groups), P5 (Hadamard 2-bit values on C2's layer), P5t (ternary values)")
     p.add_argument("--layers", type=int, default=None, help="layer caches in the stack")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -47,7 +49,7 @@ def parse():
 
 def workload(name, layers):
     from synth import workloads as W
-    wl = W.ALL[name]
+    wl = W.get(name)
     if name == "C2":
         wl = wl.with_(L=layers or 8, fixed_pairs=((4, 2),) * (layers or 8))
     elif layers:
@@ -67,6 +69,8 @@ def decode_bytes(wl, layer, n, s_eff, nb, r):
     else:
         per_unit += nb * (D // wl.k_group) * 4
     per_unit += nb * (D // wl.v_group) * 4
+    if wl.k_mode == "inner" and kb == 4 and wl.k_hi_groups:
+        per_unit += nb * (wl.k_hi_groups * wl.k_group // 2 + 1)   # low nibbles + group mask
     per_unit += nb * wl.outliers * 4 * 2
     per_unit += (s_eff + r) * D * 2 * 2
     total = per_unit * wl.units + wl.B * wl.Hq * D * (2 + 4)
@@ -281,7 +285,7 @@ def main():
 
 def W_for_cpu(name):
     from synth import workloads as W
-    return W.ALL[name]
+    return W.get(name)
 
 
 if __name__ == "__main__":

@@ -9,7 +9,9 @@
 //           pair, and the offset and the zero points enter through one more
 //           MFMA against the block's (z, s) columns.  For InnerQ inner-dimension
 //           groups (per-token scales) A = q and the group sums are scaled
-//           afterwards.
+//           afterwards; an 8-bit group of a mixed 4/8-bit layer enters the
+//           same 4-bit operand with its low nibble in the next four mantissa
+//           bits (1 + c/256 instead of 1 + c/16) and takes its own scale.
 //   values  O[r][c] += sum_t (p[r][t] * s[t][g]) code[t][c]: per-token value
 //           scales (KIVI layout) fold into P as an exact hi + lo pair; the zero
 //           points and the code offset are one more MFMA against the block's
@@ -27,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -51,13 +54,19 @@ template <> struct CodeEnc<8> { static constexpr float base = 1024.f, inv_unit =
 // no literal operands) and made opaque once, so that the and-or pairs are
 // selected as single v_and_or_b32 and the constants are not rematerialised.
 struct Unpack {
-  uint32_t m4, m2, e8;  // VGPRs
-  uint32_t one2;        // SGPR: fp16 1.0 in both halves
+  uint32_t m4, m2, e8, m4lo;  // VGPRs
+  uint32_t one2;              // SGPR: fp16 1.0 in both halves
 };
 __device__ __forceinline__ uint32_t andor(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
 __device__ __forceinline__ half8 ex4(const Unpack& k, uint32_t x) {
   return h8(andor(x << 6, k.m4, k.one2), andor(x << 2, k.m4, k.one2), andor(x >> 2, k.m4, k.one2),
             andor(x >> 6, k.m4, k.one2));
+}
+// 4-bit fields x with low nibbles y below them (8-bit codes c = 16 x + y of
+// mixed-width key groups): 1 + x/16 + y/256 = 1 + c/256; y = 0 gives ex4.
+__device__ __forceinline__ half8 ex4lo(const Unpack& k, uint32_t x, uint32_t y) {
+  return h8(andor(y << 2, k.m4lo, andor(x << 6, k.m4, k.one2)), andor(y >> 2, k.m4lo, andor(x << 2, k.m4, k.one2)),
+            andor(y >> 6, k.m4lo, andor(x >> 2, k.m4, k.one2)), andor(y >> 10, k.m4lo, andor(x >> 6, k.m4, k.one2)));
 }
 template <int E>
 __device__ __forceinline__ half8 ex2(const Unpack& k, uint32_t x) {
@@ -100,23 +109,29 @@ __device__ __forceinline__ int kchan(int g4, int j, int kk) {
 
 
 // Compile-time record layout of a block (D = 128, value groups of 32, no
-// sparse outliers); the launcher checks it against the layer's layout.
-template <int KB, int VB, bool INNER>
+// sparse outliers; MIX: inner groups of 64 with one 8-bit group per token);
+// the launcher checks it against the layer's layout.
+template <int KB, int VB, bool INNER, bool MIX = false>
 struct Rec {
   static constexpr int kc = 32 * 16 * KB;
   static constexpr int km = INNER ? 32 * 2 * 4 : 2 * D * 2;
   static constexpr int vc = 32 * 16 * VB;
   static constexpr int vm = 2 * 4 * 32 * 2;
+  static constexpr int kx = MIX ? 32 * 32 : 0;  // low nibbles: 32 tokens x 64 channels
+  static constexpr int ks = MIX ? 32 : 0;       // group masks
   static constexpr int off_km = kc;
   static constexpr int off_vc = off_km + km;
   static constexpr int off_vm = off_vc + vc;
-  static constexpr int bytes = off_vm + vm;
+  static constexpr int off_kx = off_vm + vm;
+  static constexpr int off_ks = off_kx + kx;
+  static constexpr int bytes = off_ks + ks;
   static constexpr int loads = (bytes + 1023) / 1024;  // 1 KiB per wave-wide load
 };
 
-template <int KB, int VB, int G, bool INNER, int NBUF>
+template <int KB, int VB, int G, bool INNER, bool MIX, int NBUF>
 __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob J) {
-  using R = Rec<KB, VB, INNER>;
+  using R = Rec<KB, VB, INNER, MIX>;
+  static_assert(!MIX || (INNER && KB == 4), "mixed groups: 4-bit inner keys");
   // one LDS object per ring slot: the compiler then tells the slots apart and
   // keeps the partial vmcnt waits instead of draining every in-flight load
   static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 slots");
@@ -142,10 +157,11 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   constexpr int RI = G < 4 ? G : 4;           // output rows per lane (registers)
   const bool rows_here = 4 * g4 < G;           // lane holds real query rows
   constexpr int ngv = D / 32;                  // value groups of 32 channels
-  Unpack unp{0x03C003C0u, 0x03000300u, 0x64646464u, 0x3C003C00u};
+  Unpack unp{0x03C003C0u, 0x03000300u, 0x64646464u, 0x003C003Cu, 0x3C003C00u};
   pin(unp.m4);
   pin(unp.m2);
   pin(unp.e8);
+  if constexpr (MIX) pin(unp.m4lo);
   asm volatile("" : "+s"(unp.one2));
 
   // ---- query operand (natural channel order per K-step)
@@ -228,6 +244,8 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     uint32_t kw[2][KB];
     u32x4 kmeta[8];
     u32x2 imeta[2];
+    u32x2 xlo[2];     // mixed groups: low nibbles of the token's 8-bit group
+    uint32_t selw[2]; // mixed groups: group masks of tokens 16 nt + (n16 & 12) ..
     {
       if constexpr (INNER) {
         const uint32_t a = r0 + n16 * 64 + 8 * g4;
@@ -235,6 +253,14 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
         const uint32_t am = r0 + R::off_km + 8 * n16;
         imeta[0] = dsr8<0>(am);
         imeta[1] = dsr8<128>(am);
+        if constexpr (MIX) {
+          const uint32_t ax = r0 + R::off_kx + n16 * 32 + 8 * g4;
+          const uint32_t as = r0 + R::off_ks + (n16 & 12);
+          xlo[0] = dsr8<0>(ax);
+          xlo[1] = dsr8<512>(ax);
+          selw[0] = dsr4<0>(as);
+          selw[1] = dsr4<16>(as);
+        }
         kw[0][0] = x0[0]; kw[0][1] = x0[1]; kw[0][2] = x1[0]; kw[0][3] = x1[1];
         kw[1][0] = y0[0]; kw[1][1] = y0[1]; kw[1][2] = y1[0]; kw[1][3] = y1[1];
       } else {
@@ -268,6 +294,12 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       if constexpr (INNER) {
         pin(imeta[0]);
         pin(imeta[1]);
+        if constexpr (MIX) {
+          pin(xlo[0]);
+          pin(xlo[1]);
+          pin(selw[0]);
+          pin(selw[1]);
+        }
       } else {
 #pragma unroll
         for (int e = 0; e < 8; ++e) pin(kmeta[e]);
@@ -313,14 +345,28 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     } else {
       // per-token groups of 64 channels: group sums sum_c q_c B_ct, offset
       // removed with the group sums of q, then scaled per token
+      // (mixed layers: the token's 8-bit group, marked in its mask, reads
+      // 1 + c/256 operands, so its sums take 256 s and the symmetric offset 128)
       constexpr float base = CodeEnc<KB>::base, iu = CodeEnc<KB>::inv_unit;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
+        uint32_t sel = 0, lo[4] = {0u, 0u, 0u, 0u};
+        if constexpr (MIX) {
+          sel = (selw[nt] >> (8 * (n16 & 3))) & 3u;
+          lo[0] = (sel & 1u) ? xlo[nt][0] : 0u;
+          lo[1] = (sel & 1u) ? xlo[nt][1] : 0u;
+          lo[2] = (sel & 2u) ? xlo[nt][0] : 0u;
+          lo[3] = (sel & 2u) ? xlo[nt][1] : 0u;
+        }
+        auto bk = [&](int j) __attribute__((always_inline)) {
+          if constexpr (MIX) return ex4lo(unp, kw[nt][j], lo[j]);
+          else return kstep<KB>(unp, kw[nt], j);
+        };
         f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
-        p0 = mfma(qa[0], kstep<KB>(unp, kw[nt], 0), p0);
-        p0 = mfma(qa[1], kstep<KB>(unp, kw[nt], 1), p0);
-        p1 = mfma(qa[2], kstep<KB>(unp, kw[nt], 2), p1);
-        p1 = mfma(qa[3], kstep<KB>(unp, kw[nt], 3), p1);
+        p0 = mfma(qa[0], bk(0), p0);
+        p0 = mfma(qa[1], bk(1), p0);
+        p1 = mfma(qa[2], bk(2), p1);
+        p1 = mfma(qa[3], bk(3), p1);
         const u32x2 mm = imeta[nt];  // (s0, z0), (s1, z1) of token 16 nt + n16
         float sg[2], zg[2];
 #pragma unroll
@@ -329,8 +375,9 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
           const uint16_t z16 = static_cast<uint16_t>(mm[gg] >> 16);
           const float sv = h2f(s16 & 0x7fff);
           const bool sym = (s16 & 0x8000) != 0;
-          sg[gg] = sv * iu;
-          zg[gg] = sym ? -static_cast<float>(1 << (KB - 1)) * sv : h2f(z16);
+          const bool wide = MIX && ((sel >> gg) & 1u) != 0;
+          sg[gg] = sv * (wide ? 256.f : iu);
+          zg[gg] = sym ? -(wide ? 128.f : static_cast<float>(1 << (KB - 1))) * sv : h2f(z16);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -693,24 +740,25 @@ __global__ void __launch_bounds__(32 * NG) decode_merge_kernel(LayerDesc L, Deco
 // wavefronts allows: deeper rings keep more blocks in flight behind the
 // VALU / MFMA work of the block being computed.
 constexpr int kLdsPerCu = 160 * 1024;
-template <int KB, int VB, int G, bool INNER>
+template <int KB, int VB, int G, bool INNER, bool MIX>
 constexpr int ring_slots() {
   constexpr int waves = G == 1 ? 12 : 8;
   constexpr int budget = kLdsPerCu / waves - 16 * 32 * 2 - 512;
-  constexpr int n = budget / (Rec<KB, VB, INNER>::loads * 1024);
+  constexpr int n = budget / (Rec<KB, VB, INNER, MIX>::loads * 1024);
   return n < 2 ? 2 : (n > 4 ? 4 : n);
 }
-template <int KB, int VB, int G, bool INNER>
+template <int KB, int VB, int G, bool INNER, bool MIX>
 hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
-  using R = Rec<KB, VB, INNER>;
+  using R = Rec<KB, VB, INNER, MIX>;
   if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm) return hipSuccess;
-  constexpr int NB = ring_slots<KB, VB, G, INNER>();
+  if (MIX && (L.off_kx != R::off_kx || L.off_ks != R::off_ks)) return hipSuccess;
+  constexpr int NB = ring_slots<KB, VB, G, INNER, MIX>();
   // one full round of resident wavefronts, from the runtime's occupancy of
   // this instance (registers and LDS as compiled) and the device's CU count
   static int resident = 0;
   if (resident == 0) {
     int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<KB, VB, G, INNER, NB>, 64, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<KB, VB, G, INNER, MIX, NB>, 64, 0) !=
             hipSuccess ||
         hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -719,17 +767,19 @@ hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* 
   }
   *waves = resident;
   if (!j.q) return hipSuccess;  // query only
-  hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, NB>), dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
+  hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, MIX, NB>), dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   return launch_decode_merge(L, j, s);
 }
 
-template <int G, bool INNER>
+template <int G, bool INNER, bool MIX>
 hipError_t by_bits(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
   const int k = L.kb, v = L.vb;
 #define KVQ_CASE(KB, VB) \
-  if (k == KB && v == VB) return launch_t<KB, VB, G, INNER>(L, j, s, waves);
-  if constexpr (INNER) {
+  if (k == KB && v == VB) return launch_t<KB, VB, G, INNER, MIX>(L, j, s, waves);
+  if constexpr (MIX) {
+    KVQ_CASE(4, 2) KVQ_CASE(4, 4)
+  } else if constexpr (INNER) {
     KVQ_CASE(4, 2) KVQ_CASE(4, 4)
   } else {
     KVQ_CASE(2, 2) KVQ_CASE(2, 4) KVQ_CASE(2, 8)
@@ -744,11 +794,17 @@ hipError_t dispatch(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* 
   *waves = 0;
   if (L.nuq || L.outk || L.pre_rope || (L.k_hybrid && !L.k_inner)) return hipSuccess;
   if (L.k_inner && L.k_group != 64) return hipSuccess;
+  if (L.k_hi && (L.k_hi != 1 || L.kb != 4)) return hipSuccess;  // one 8-bit group of two
   if (L.v_group != 32) return hipSuccess;
+  auto pick = [&](auto g) {
+    constexpr int GG = decltype(g)::value;
+    if (L.k_hi) return by_bits<GG, true, true>(L, j, s, waves);
+    return L.k_inner ? by_bits<GG, true, false>(L, j, s, waves) : by_bits<GG, false, false>(L, j, s, waves);
+  };
   switch (L.G) {
-    case 1: return L.k_inner ? by_bits<1, true>(L, j, s, waves) : by_bits<1, false>(L, j, s, waves);
-    case 4: return L.k_inner ? by_bits<4, true>(L, j, s, waves) : by_bits<4, false>(L, j, s, waves);
-    case 8: return L.k_inner ? by_bits<8, true>(L, j, s, waves) : by_bits<8, false>(L, j, s, waves);
+    case 1: return pick(std::integral_constant<int, 1>{});
+    case 4: return pick(std::integral_constant<int, 4>{});
+    case 8: return pick(std::integral_constant<int, 8>{});
     default: return hipSuccess;
   }
 }

@@ -47,7 +47,8 @@ __device__ __forceinline__ void fp16_slot(const LayerDesc& L, const TokenState& 
 }
 
 __device__ __forceinline__ float load_k_body(const LayerDesc& L, const uint8_t* rec, int j, int c) {
-  const int code = L.kb == 3 ? k3_code(rec + L.off_kc, j, c) : row_code(rec + L.off_kc + j * L.k_row_bytes, L.kb, c);
+  int code = L.kb == 3 ? k3_code(rec + L.off_kc, j, c) : row_code(rec + L.off_kc + j * L.k_row_bytes, L.kb, c);
+  int bits = L.kb;
   const uint16_t* km = reinterpret_cast<const uint16_t*>(rec + L.off_km);
   uint16_t s, z;
   if (!L.k_inner) {
@@ -55,10 +56,24 @@ __device__ __forceinline__ float load_k_body(const LayerDesc& L, const uint8_t* 
     z = km[D + c];
   } else {
     const int ng = D / L.k_group;
-    s = km[(j * ng + c / L.k_group) * 2];
-    z = km[(j * ng + c / L.k_group) * 2 + 1];
+    const int g = c / L.k_group;
+    s = km[(j * ng + g) * 2];
+    z = km[(j * ng + g) * 2 + 1];
+    if (L.k_hi) {
+      // 8-bit group of a mixed layer: high nibble from the code plane, low
+      // nibble from the token's slot for this group in k_ext
+      const uint32_t sel = rec[L.off_ks + j];
+      if ((sel >> g) & 1u) {
+        const int slot = __popc(sel & ((1u << g) - 1u));
+        const int cc = c % L.k_group;
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(rec + L.off_kx) +
+                            (j * L.k_hi + slot) * (L.k_group / 8);
+        code = (code << 4) | static_cast<int>((w[cc >> 3] >> pair_split_pos(4, cc & 7)) & 15u);
+        bits = 8;
+      }
+    }
   }
-  float x = dequant(code, s, z, L.kb, L.nuq ? L.lev_k : nullptr);
+  float x = dequant(code, s, z, bits, L.nuq ? L.lev_k : nullptr);
   if (L.outk) {
     const uint32_t* o = reinterpret_cast<const uint32_t*>(rec + L.off_ko) + j * L.outk;
     for (int i = 0; i < L.outk; ++i)

@@ -68,6 +68,7 @@ kvq_status fill_layout(const kvq_cache& c, int kb, int vb, const uint16_t* cb, L
   d.outk = g.outliers_per_vector;
   d.v_had = g.v_mode == KVQ_V_HADAMARD;
   d.v_tern = g.v_mode == KVQ_V_TERNARY;
+  d.k_hi = (g.k_mode == KVQ_K_INNER && kb == 4) ? g.k_hi_groups : 0;
   d.pre_rope = g.k_pre_rope != 0;
   d.rope_base = g.rope_base;
   if (cb) {
@@ -89,6 +90,10 @@ kvq_status fill_layout(const kvq_cache& c, int kb, int vb, const uint16_t* cb, L
   off = align_up(off + kvq::kBlockTokens * d.outk * 4, 16);
   d.off_vo = static_cast<int32_t>(off);
   off = align_up(off + kvq::kBlockTokens * d.outk * 4, 16);
+  d.off_kx = static_cast<int32_t>(off);
+  off = align_up(off + static_cast<int64_t>(kvq::kBlockTokens) * d.k_hi * (d.k_group / 2), 16);
+  d.off_ks = static_cast<int32_t>(off);
+  off = align_up(off + (d.k_hi ? kvq::kBlockTokens : 0), 16);
   d.rec_bytes = align_up(off, 128);
   d.nblk_cap = c.nblk_cap;
   d.sinks_cap = c.sink_cap;
@@ -213,6 +218,11 @@ kvq_status kvq_create(const kvq_config* cfg, const kvq_bitpair* layer_bits, cons
   if (g.nuq && g.k_hybrid) return KVQ_ERR_UNSUPPORTED;
   if (g.k_norm && g.k_mode != KVQ_K_INNER) return KVQ_ERR_UNSUPPORTED;
   if (g.v_mode == KVQ_V_TERNARY && g.nuq) return KVQ_ERR_UNSUPPORTED;
+  if (g.k_hi_groups < 0) return KVQ_ERR_ARG;
+  if (g.k_hi_groups > 0) {
+    if (g.k_mode != KVQ_K_INNER || g.nuq || g.outliers_per_vector) return KVQ_ERR_UNSUPPORTED;
+    if (g.k_hi_groups > kD / g.k_group) return KVQ_ERR_ARG;
+  }
   for (int l = 0; l < g.n_layers; ++l) {
     const int kb = layer_bits[l].k_bits, vb = layer_bits[l].v_bits;
     if (g.nuq) {
@@ -276,6 +286,8 @@ kvq_status kvq_block_layout(const kvq_cache* c, int32_t layer, kvq_block_layout_
   o->sink_cap = c->sink_cap;
   o->window_cap = c->win_cap;
   o->flush_tokens = c->F;
+  o->k_ext = d.off_kx;
+  o->k_sel = d.off_ks;
   return KVQ_OK;
 }
 
@@ -296,6 +308,21 @@ kvq_status kvq_bind_layer(kvq_cache* c, int32_t layer, void* const bufs[KVQ_NBUF
 kvq_status kvq_workspace_size(const kvq_cache* c, size_t* bytes) {
   if (!c || !bytes) return KVQ_ERR_ARG;
   *bytes = (partials_bytes(*c) + 255) / 256 * 256 + static_cast<size_t>(c->units) * sizeof(uint32_t);
+  return KVQ_OK;
+}
+
+kvq_status kvq_average_bits(const kvq_cache* c, double* code_bits, double* stored_bits) {
+  if (!c) return KVQ_ERR_ARG;
+  double code = 0.0, stored = 0.0;
+  for (const Layer& L : c->layers) {
+    const LayerDesc& d = L.d;
+    const double kbits = d.kb + (d.k_hi ? (8.0 - d.kb) * d.k_hi / (kD / d.k_group) : 0.0);
+    code += kbits + d.vb;
+    stored += 8.0 * d.rec_bytes / (2.0 * kvq::kBlockTokens * kD);
+  }
+  const double nl = static_cast<double>(c->layers.size());
+  if (code_bits) *code_bits = code / (2.0 * nl);
+  if (stored_bits) *stored_bits = stored / nl;
   return KVQ_OK;
 }
 

@@ -22,12 +22,14 @@ struct LayerDesc {
   int32_t k_hybrid, ratio_num, ratio_den;
   int32_t nuq, outk, v_had, pre_rope;
   int32_t v_tern;  // values as ternary levels {-s, 0, s} in 2-bit codes (z = -s)
+  int32_t k_hi;    // mixed 4/8-bit inner key groups: 8-bit groups per token (0: none)
   float rope_base;
   uint16_t lev_k[8], lev_v[8];
   double had_scale;  // fl64(1/sqrt(D)), computed on the host
   // record layout
   int32_t rec_bytes, k_row_bytes;
   int32_t off_kc, off_km, off_vc, off_vm, off_ko, off_vo;
+  int32_t off_kx, off_ks;  // mixed key groups: low code nibbles, per-token group mask
   int32_t nblk_cap;  // blocks per unit
   // fp16 area
   int32_t sinks_cap, win_cap;  // slots per unit, both multiples of 32

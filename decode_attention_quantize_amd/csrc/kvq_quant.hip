@@ -14,6 +14,9 @@
 //     first on ties, excluded from the group statistics
 //   Hadamard values (aitrends.kr page): v' = fp16(fl64(H v) * 1/sqrt(D)) with
 //     exact binary64 butterflies
+//   mixed 4/8-bit inner key groups (InnerQ, limitations and future work): per
+//     token, the k_hi groups with the largest 4-bit step (fp16 scale
+//     magnitude, the lower group first on ties) keep an 8-bit quantization
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -39,6 +42,11 @@ struct QuantSmem {
       uint8_t cv[kBlockTokens][D];
       uint8_t exk[kBlockTokens][D];
       uint8_t exv[kBlockTokens][D];
+      // mixed 4/8-bit key groups: 8-bit codes, then their low nibbles; the
+      // (s4, z4, s8, z8) of every (token, group); the per-token group masks
+      uint8_t lok[kBlockTokens][D];
+      uint16_t gm[kBlockTokens][D / 16][4];
+      uint8_t sel[kBlockTokens];
     };
   };
 };
@@ -261,6 +269,76 @@ __device__ void quant_groups_any(int w, const uint16_t (*rows)[D], const uint8_t
   }
 }
 
+// Mixed 4/8-bit inner key groups.  Every group of a row is quantized at 4 and
+// at 8 bits; the k_hi groups whose 4-bit step ranks highest (ties: lower
+// group first) keep the 8-bit result: its high nibble goes to the 4-bit code
+// plane (ck), its low nibble to lok, its parameters to k_meta, and the
+// token's group mask to k_sel.
+template <int W>
+__device__ void quant_mixed_groups(QuantSmem& sm, int nrows, const LayerDesc& L, uint8_t* rec, int slot0) {
+  constexpr int ng = D / W;
+  const int t = threadIdx.x, g = t / W;
+  const bool hyb = L.k_hybrid != 0;
+  for (int j = 0; j < nrows; ++j) {
+    int c4, c8;
+    uint16_t s4, z4, s8, z8;
+    token_group<W>(sm.k[j][t], false, 4, false, nullptr, hyb, L.ratio_num, L.ratio_den, false, c4, s4, z4);
+    token_group<W>(sm.k[j][t], false, 8, false, nullptr, hyb, L.ratio_num, L.ratio_den, false, c8, s8, z8);
+    sm.ck[j][t] = static_cast<uint8_t>(c4);
+    sm.lok[j][t] = static_cast<uint8_t>(c8);
+    if (t % W == 0) {
+      sm.gm[j][g][0] = s4;
+      sm.gm[j][g][1] = z4;
+      sm.gm[j][g][2] = s8;
+      sm.gm[j][g][3] = z8;
+    }
+  }
+  __syncthreads();
+  uint16_t* m16 = reinterpret_cast<uint16_t*>(rec + L.off_km);
+  for (int j = 0; j < nrows; ++j) {
+    uint32_t sel = 0;
+    for (int a = 0; a < ng; ++a) {
+      const uint16_t sa = sm.gm[j][a][0] & 0x7fff;
+      int rank = 0;
+      for (int b = 0; b < ng; ++b) {
+        const uint16_t sb = sm.gm[j][b][0] & 0x7fff;
+        rank += (sb > sa || (sb == sa && b < a)) ? 1 : 0;
+      }
+      if (rank < L.k_hi) sel |= 1u << a;
+    }
+    const bool hi = ((sel >> g) & 1u) != 0;
+    const int c8 = sm.lok[j][t];
+    if (hi) sm.ck[j][t] = static_cast<uint8_t>(c8 >> 4);
+    sm.lok[j][t] = hi ? static_cast<uint8_t>(c8 & 15) : 0;
+    if (t % W == 0) {
+      m16[((slot0 + j) * ng + g) * 2 + 0] = sm.gm[j][g][hi ? 2 : 0];
+      m16[((slot0 + j) * ng + g) * 2 + 1] = sm.gm[j][g][hi ? 3 : 1];
+    }
+    if (t == 0) {
+      sm.sel[j] = static_cast<uint8_t>(sel);
+      rec[L.off_ks + slot0 + j] = static_cast<uint8_t>(sel);
+    }
+  }
+}
+
+// Low nibbles of each row's 8-bit key groups into k_ext: slot i of a token is
+// its i-th 8-bit group in ascending order, k_group/8 pair-split words.
+__device__ void pack_mixed_ext(const QuantSmem& sm, int nrows, const LayerDesc& L, uint8_t* rec, int slot0) {
+  const int wps = L.k_group / 8;
+  const int per_row = L.k_hi * wps;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(rec + L.off_kx);
+  for (int i = threadIdx.x; i < nrows * per_row; i += blockDim.x) {
+    const int j = i / per_row, r = i % per_row, k = r / wps, w = r % wps;
+    uint32_t sel = sm.sel[j];
+    for (int d = 0; d < k; ++d) sel &= sel - 1u;  // drop the k lowest groups
+    const int g = __ffs(static_cast<int>(sel)) - 1;
+    uint32_t word = 0;
+    for (int e = 0; e < 8; ++e)
+      word |= static_cast<uint32_t>(sm.lok[j][g * L.k_group + 8 * w + e]) << pair_split_pos(4, e);
+    dst[((slot0 + j) * L.k_hi + k) * wps + w] = word;
+  }
+}
+
 // Pack token-major 2/4/8-bit key rows for slots [slot0, slot0+nrows).
 __device__ void pack_rows(const uint8_t (*codes)[D], int nrows, int bits, uint8_t* dst, int row_bytes,
                           int slot0) {
@@ -442,6 +520,13 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
     uint16_t* km = reinterpret_cast<uint16_t*>(rec + L.off_km);
     km[t] = s;
     km[D + t] = z;
+  } else if (L.k_hi) {
+    if (L.k_group == 16)
+      quant_mixed_groups<16>(sm, nrows, L, rec, slot0);
+    else if (L.k_group == 32)
+      quant_mixed_groups<32>(sm, nrows, L, rec, slot0);
+    else
+      quant_mixed_groups<64>(sm, nrows, L, rec, slot0);
   } else {
     quant_groups_any(L.k_group, sm.k, out ? sm.exk : nullptr, sm.ck, nrows, L.kb, L.nuq != 0,
                      L.lev_k, L.k_hybrid != 0, L.ratio_num, L.ratio_den, false, rec + L.off_km, 0,
@@ -456,6 +541,7 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
     pack_k3(sm.ck, nrows, rec + L.off_kc, slot0);
   else
     pack_rows(sm.ck, nrows, L.kb, rec + L.off_kc, L.k_row_bytes, slot0);
+  if (L.k_hi) pack_mixed_ext(sm, nrows, L, rec, slot0);
   if (L.vb == 3)
     pack_v3(sm.cv, nrows, rec + L.off_vc, slot0);
   else

@@ -21,7 +21,7 @@ KVQ_BUF_BODY, KVQ_BUF_FP16 = 0, 1
 
 EXPORTS = ("kvq_create", "kvq_destroy", "kvq_layer_buffer_sizes", "kvq_block_layout",
            "kvq_bind_layer", "kvq_workspace_size", "kvq_quantize_prefill", "kvq_append_token",
-           "kvq_decode_attn", "kvq_layer_state", "kvq_status_str",
+           "kvq_decode_attn", "kvq_layer_state", "kvq_average_bits", "kvq_status_str",
            "kvq_fit_rate_distortion", "kvq_waterfill_bits", "kvq_allocate_bits")
 
 
@@ -33,7 +33,7 @@ class kvq_config(C.Structure):
         ("k_mode", C.c_int32), ("k_group", C.c_int32), ("v_mode", C.c_int32), ("v_group", C.c_int32),
         ("k_hybrid", C.c_int32), ("sym_ratio_num", C.c_int32), ("sym_ratio_den", C.c_int32),
         ("k_pre_rope", C.c_int32), ("rope_base", C.c_float), ("nuq", C.c_int32),
-        ("outliers_per_vector", C.c_int32), ("k_norm", C.c_int32),
+        ("outliers_per_vector", C.c_int32), ("k_norm", C.c_int32), ("k_hi_groups", C.c_int32),
     ]
 
 
@@ -44,7 +44,7 @@ class kvq_bitpair(C.Structure):
 class kvq_block_layout_t(C.Structure):
     _fields_ = [(n, C.c_int32) for n in (
         "record_bytes", "k_codes", "k_meta", "v_codes", "v_meta", "k_out", "v_out",
-        "k_row_bytes", "sink_cap", "window_cap", "flush_tokens")]
+        "k_row_bytes", "sink_cap", "window_cap", "flush_tokens", "k_ext", "k_sel")]
 
 
 class KVQError(RuntimeError):
@@ -79,6 +79,7 @@ def lib():
         L.kvq_decode_attn.argtypes = [pcache, i32, vp, vp, vp, vp]
         L.kvq_layer_state.argtypes = [pcache, i32] + [C.POINTER(C.c_int32)] * 4
         dp, ip = C.POINTER(C.c_double), C.POINTER(C.c_int32)
+        L.kvq_average_bits.argtypes = [pcache, dp, dp]
         L.kvq_fit_rate_distortion.argtypes = [i32, dp, dp, dp, dp]
         L.kvq_waterfill_bits.argtypes = [i32, dp, dp, dp, C.c_double, dp]
         L.kvq_allocate_bits.argtypes = [i32, dp, dp, dp, ip, i32, i32, ip]
@@ -157,6 +158,13 @@ def kvq_layer_state(handle, layer):
     return tuple(x.value for x in v)
 
 
+def kvq_average_bits(handle):
+    """(code_bits, stored_bits): the memory objective f_m and the stored bits per element."""
+    a, b = C.c_double(), C.c_double()
+    _check(lib().kvq_average_bits(handle, C.byref(a), C.byref(b)), "kvq_average_bits")
+    return a.value, b.value
+
+
 # ---------------------------------------------------------------- offline bit allocation
 def _darr(x):
     x = [float(v) for v in x]
@@ -190,7 +198,8 @@ def kvq_allocate_bits(alpha, beta, w, allowed, total_bits):
 # ---------------------------------------------------------------- configuration helpers
 def make_config(B, Hq, Hkv, L, max_tokens, D=128, sinks=0, window=0, k_mode=KVQ_K_PER_CHANNEL,
                 k_group=32, v_mode=KVQ_V_PER_TOKEN, v_group=32, k_hybrid=0, sym_ratio=(1, 10),
-                k_pre_rope=0, rope_base=10000.0, nuq=0, outliers=0, k_norm=0) -> kvq_config:
+                k_pre_rope=0, rope_base=10000.0, nuq=0, outliers=0, k_norm=0,
+                k_hi_groups=0) -> kvq_config:
     c = kvq_config()
     c.batch, c.n_q_heads, c.n_kv_heads, c.head_dim = B, Hq, Hkv, D
     c.n_layers, c.max_tokens, c.sink_tokens, c.recent_window = L, max_tokens, sinks, window
@@ -198,6 +207,7 @@ def make_config(B, Hq, Hkv, L, max_tokens, D=128, sinks=0, window=0, k_mode=KVQ_
     c.k_hybrid, c.sym_ratio_num, c.sym_ratio_den = k_hybrid, sym_ratio[0], sym_ratio[1]
     c.k_pre_rope, c.rope_base, c.nuq, c.outliers_per_vector = k_pre_rope, rope_base, nuq, outliers
     c.k_norm = k_norm
+    c.k_hi_groups = k_hi_groups
     return c
 
 
@@ -214,7 +224,7 @@ def config_from_workload(wl, max_tokens=None) -> kvq_config:
         v_group=wl.v_group,
         k_hybrid=int(wl.k_hybrid), sym_ratio=(f.numerator, f.denominator),
         k_pre_rope=int(wl.pre_rope), rope_base=wl.rope_base, nuq=int(wl.nuq), outliers=wl.outliers,
-        k_norm=int(getattr(wl, "k_norm", False)))
+        k_norm=int(getattr(wl, "k_norm", False)), k_hi_groups=int(getattr(wl, "k_hi_groups", 0)))
 
 
 # ---------------------------------------------------------------- torch plumbing

@@ -24,6 +24,8 @@
  *   values rotated by a normalised Hadamard matrix before 2-bit quantization,
  *       rotation undone after the attention sum -- Hadamard page, TL;DR
  *   fp16 sink tokens and recent window -- InnerQ, methodology 4
+ *   4-bit and 8-bit key groups mixed inside a layer -- InnerQ, limitations
+ *       and future work
  *   per-layer (k_bits, v_bits) pair chosen offline from
  *       {KV8, K8V4, KV4, K4V2, KV2} -- KVTuner review, method steps 1 and 4
  *
@@ -108,6 +110,14 @@ typedef struct {
                              as given.  The shifts live in the KVQ_BUF_FP16 buffer after the
                              fp16 slots (units * 128 int8).  With k_norm the prefill
                              keys must be 16-byte aligned (else KVQ_ERR_ARG). */
+  int32_t k_hi_groups;    /* m >= 0: mixed 4/8-bit key groups (InnerQ, limitations and future
+                             work; inner key groups only, no codebooks, no sparse outliers).
+                             In every layer whose k_bits is 4, each quantized token's m inner
+                             groups with the largest 4-bit step (the magnitude of the fp16
+                             scale its 4-bit quantizer gets; the lower group first on equal
+                             steps) are quantized at 8 bits instead, with the same
+                             symmetric / asymmetric choice.  m <= head_dim / k_group.  Layers
+                             with other key widths ignore it.  0 disables. */
 } kvq_config;
 
 /* Per-layer device buffers (caller-owned). */
@@ -152,6 +162,15 @@ enum {
  *  k_out,   outliers_per_vector entries per token: {uint16 column, fp16
  *  v_out    value}, columns ascending; the fp16 value replaces the dequantized
  *           element.
+ *  k_ext    mixed 4/8-bit key groups only (else empty): [32 tokens][m slots]
+ *           [k_group/2 bytes]; slot i of a token holds the low four bits of
+ *           the 8-bit codes of its i-th 8-bit group (ascending group order),
+ *           channels of the group in pair-split words of 4-bit fields.  The
+ *           high four bits sit in k_codes at the group's own channels, so
+ *           code = (k_codes field << 4) | k_ext field for an 8-bit group, whose
+ *           k_meta pair is its 8-bit (s, z) (symmetric: (code - 128) * |s|).
+ *  k_sel    mixed 4/8-bit key groups only: [32 tokens] uint8, bit g set iff
+ *           inner group g of the token is an 8-bit group.
  */
 typedef struct {
   int32_t record_bytes;
@@ -160,6 +179,7 @@ typedef struct {
   int32_t sink_cap;       /* Scap: sink slots per unit */
   int32_t window_cap;     /* Wcap: window ring slots per unit */
   int32_t flush_tokens;   /* F: 32 for per-channel keys, 1 for inner keys */
+  int32_t k_ext, k_sel;   /* mixed 4/8-bit key group sections (offsets; equal when unused) */
 } kvq_block_layout_t;
 
 /* Create a cache handle.  layer_bits[n_layers]; codebooks: NULL or
@@ -215,6 +235,16 @@ kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, float
  * quantized body tokens and fp16 window tokens (n = sinks + body + window). */
 kvq_status kvq_layer_state(const kvq_cache* cache, int32_t layer, int32_t* n, int32_t* sinks,
                            int32_t* body, int32_t* window);
+
+/* Average bits of the cache's quantized tensors.  code_bits is the
+ * KVTuner review's memory objective f_m = sum(P) / 2L (method step 0): the
+ * mean over the 2L key and value tensors of their code width, where a layer
+ * with mixed 4/8-bit key groups counts 4 + 4 m / (head_dim / k_group) for
+ * its keys.  stored_bits adds everything a body block stores per element
+ * (parameters, outliers, mixed-group sections and the record's alignment
+ * padding): 8 * record_bytes / (2 * 32 * head_dim), averaged over layers.
+ * Either pointer may be NULL.  Errors: KVQ_ERR_ARG. */
+kvq_status kvq_average_bits(const kvq_cache* cache, double* code_bits, double* stored_bits);
 
 /* Static text for a status code. */
 const char* kvq_status_str(kvq_status s);

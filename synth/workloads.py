@@ -195,3 +195,19 @@ C5 = Workload(
     notes="K 4-bit inner groups of 64 hybrid sym/asym; V Hadamard-rotated 2-bit per-token G32")
 
 ALL = {"C1": C1, "C2": C2, "C3": C3, "C4": C4, "C5": C5}
+
+# Scheme variants on the same shapes, measured beside the workloads above:
+# InnerQ's per-channel key normalization and its mixed 4/8-bit key groups on
+# C5; the Hadamard 2-bit page's pairing (int4 keys per channel, rotated 2-bit
+# values) and its ternary-value control on C2's layer.
+VARIANTS = {
+    "C5n": C5.with_(name="C5n-70b-gqa-innerq-keynorm", k_norm=True),
+    "C5m": C5.with_(name="C5m-70b-gqa-innerq-mixed48", k_hi_groups=1),
+    "P5": C2.with_(name="P5-llama7b-mha-k4-hadamard-v2", v_hadamard=True),
+    "P5t": C2.with_(name="P5t-llama7b-mha-k4-ternary-v", v_ternary=True),
+}
+
+
+def get(name: str) -> Workload:
+    """A workload or a scheme variant by its short name."""
+    return ALL[name] if name in ALL else VARIANTS[name]

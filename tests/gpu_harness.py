@@ -90,8 +90,10 @@ def check_unit(wl, cache, outs, layer, u, steps=None, check_steps=None, label=""
     enc, nb = ref["enc"], ref["nb_final"]
     body, lay = unit_body(cache, layer, u)
     kb, vb = wl.bit_pairs()[layer]
-    got = unpack_unit(body, lay, kb, vb, nb, wl.k_mode == "inner", wl.k_group, wl.v_group, wl.outliers)
-    for key in ("kcodes", "kmeta", "vcodes", "vmeta"):
+    k_hi = wl.k_hi_groups if (wl.k_mode == "inner" and kb == 4) else 0
+    got = unpack_unit(body, lay, kb, vb, nb, wl.k_mode == "inner", wl.k_group, wl.v_group, wl.outliers,
+                      k_hi)
+    for key in ("kcodes", "kmeta", "vcodes", "vmeta") + (("kwidth",) if k_hi else ()):
         g, r = got[key], enc[key]
         assert g.shape == r.shape, (label, key, g.shape, r.shape)
         bad = np.argwhere(g != r)

@@ -82,18 +82,39 @@ def _vchunks(raw: np.ndarray, bits: int) -> np.ndarray:
     return out
 
 
+def _mixed_keys(r: np.ndarray, lay: dict, codes: np.ndarray, k_group: int, k_hi: int):
+    """Mixed 4/8-bit key groups of one block: the 8-bit groups named by each
+    token's k_sel mask take (code plane field << 4) | low nibble from the
+    token's k_ext slots (ascending group order).  Returns (codes, widths)."""
+    ng = D // k_group
+    sel = r[lay["k_sel"]: lay["k_sel"] + BT]
+    wps = k_group // 8
+    ext = r[lay["k_ext"]: lay["k_ext"] + BT * k_hi * wps * 4].view(np.uint32).reshape(BT, k_hi, wps)
+    lo = _pair_split_fields(ext, 4)                       # [32][k_hi][k_group]
+    codes = codes.astype(np.uint8).copy()
+    width = np.full((BT, ng), 4, np.uint8)
+    for t in range(BT):
+        groups = [g for g in range(ng) if (sel[t] >> g) & 1]
+        for slot, g in enumerate(groups[:k_hi]):
+            cs = slice(g * k_group, (g + 1) * k_group)
+            codes[t, cs] = (codes[t, cs] << 4) | lo[t, slot]
+            width[t, g] = 8
+    return codes, width
+
+
 def unpack_unit(body_unit: np.ndarray, lay: dict, kb: int, vb: int, nb: int, k_inner: bool,
-                k_group: int, v_group: int, outk: int) -> dict:
+                k_group: int, v_group: int, outk: int, k_hi: int = 0) -> dict:
     """Logical arrays of the first nb body tokens of one unit.
 
     body_unit: uint8 [nblk_cap * record_bytes] for that unit.
     Returns kcodes [nb][D], kmeta (per-channel [nb/32][D][2] or inner [nb][D/kg][2]),
-    vcodes [nb][D], vmeta [nb][D/vg][2], kocol/koval/vocol/voval [nb][outk].
+    vcodes [nb][D], vmeta [nb][D/vg][2], kocol/koval/vocol/voval [nb][outk], and
+    with mixed 4/8-bit key groups (k_hi > 0) kwidth [nb][D/kg].
     """
     R = lay["record_bytes"]
     nblk = (nb + BT - 1) // BT
     recs = body_unit[: nblk * R].reshape(nblk, R)
-    kc, vc, km, vm = [], [], [], []
+    kc, vc, km, vm, kw = [], [], [], [], []
     ko_c, ko_v, vo_c, vo_v = [], [], [], []
     ngv = D // v_group
     for i in range(nblk):
@@ -101,6 +122,10 @@ def unpack_unit(body_unit: np.ndarray, lay: dict, kb: int, vb: int, nb: int, k_i
         cnt = min(BT, nb - BT * i)
         if kb == 3:
             kc.append(_kchunks3(r[lay["k_codes"]:])[:cnt])
+        elif k_hi:
+            codes, width = _mixed_keys(r, lay, _rows(r[lay["k_codes"]:], kb, BT), k_group, k_hi)
+            kc.append(codes[:cnt])
+            kw.append(width[:cnt])
         else:
             kc.append(_rows(r[lay["k_codes"]:], kb, BT)[:cnt])
         if vb == 3:
@@ -129,6 +154,8 @@ def unpack_unit(body_unit: np.ndarray, lay: dict, kb: int, vb: int, nb: int, k_i
         kcodes=cat(kc, (0, D), np.uint8), vcodes=cat(vc, (0, D), np.uint8),
         kmeta=cat(km, (0, D, 2), np.uint16), vmeta=cat(vm, (0, ngv, 2), np.uint16),
     )
+    if k_hi:
+        out["kwidth"] = cat(kw, (0, D // k_group), np.uint8)
     if outk:
         out.update(kocol=cat(ko_c, (0, outk), np.int32), koval=cat(ko_v, (0, outk), np.uint16),
                    vocol=cat(vo_c, (0, outk), np.int32), voval=cat(vo_v, (0, outk), np.uint16))

@@ -33,7 +33,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     L = C.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -68,6 +68,10 @@ def _cfg(**kw):
     (dict(k_norm=2, k_mode=1, k_group=64), K.KVQ_ERR_ARG),
     (dict(k_norm=1), K.KVQ_ERR_UNSUPPORTED),          # normalization is for inner key groups
     (dict(v_mode=3), K.KVQ_ERR_ARG),
+    (dict(k_hi_groups=-1, k_mode=1, k_group=64), K.KVQ_ERR_ARG),
+    (dict(k_hi_groups=1), K.KVQ_ERR_UNSUPPORTED),     # mixed widths are for inner key groups
+    (dict(k_hi_groups=3, k_mode=1, k_group=64), K.KVQ_ERR_ARG),  # a token has two groups of 64
+    (dict(k_hi_groups=1, k_mode=1, k_group=64, outliers=2), K.KVQ_ERR_UNSUPPORTED),
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(K.KVQError) as e:
@@ -100,22 +104,29 @@ def test_create_rejects_bits_and_codebooks():
     assert rc == K.KVQ_ERR_ARG
 
 
-def _expected_record(kb_, vb, k_inner=False, kg=32, vg=32, outk=0):
+def _expected_record(kb_, vb, k_inner=False, kg=32, vg=32, outk=0, k_hi=0):
     a16 = lambda x: (x + 15) // 16 * 16
     kc = 32 * 128 * kb_ // 8
     km = 32 * (128 // kg) * 4 if k_inner else 512
     vc = 32 * 128 * vb // 8
     vm = 2 * (128 // vg) * 32 * 2
     ko = 32 * outk * 4
+    m = k_hi if (k_inner and kb_ == 4) else 0
+    kx = 32 * m * kg // 2                     # low nibbles of the 8-bit groups
+    ks = 32 if m else 0                       # per-token group masks
     off = [0]
-    for sz in (kc, km, vc, vm, ko, ko):
+    for sz in (kc, km, vc, vm, ko, ko, kx, ks):
         off.append(a16(off[-1] + sz))
-    return off[:6], (off[6] + 127) // 128 * 128
+    return off[:8], (off[8] + 127) // 128 * 128
 
 
-@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "C5n"])
+VARIANTS = {"C5n": dict(k_norm=True), "C5m": dict(k_hi_groups=1),
+            "C5m32": dict(k_group=32, k_hi_groups=2, fixed_pairs=((4, 2),))}
+
+
+@pytest.mark.parametrize("name", ["C1", "C2", "C3", "C4", "C5", "C5n", "C5m", "C5m32"])
 def test_layout_and_sizes_follow_the_spec(name):
-    wl = W.ALL[name] if name in W.ALL else W.C5.with_(k_norm=True)
+    wl = W.ALL[name] if name in W.ALL else W.C5.with_(**VARIANTS[name])
     h = K.kvq_create(K.config_from_workload(wl), wl.bit_pairs(), wl.codebooks())
     try:
         pairs = wl.bit_pairs()
@@ -124,8 +135,10 @@ def test_layout_and_sizes_follow_the_spec(name):
         for l in range(min(wl.L, 6)):
             kb_, vb = pairs[l]
             lay = K.kvq_block_layout(h, l)
-            offs, rec = _expected_record(kb_, vb, wl.k_mode == "inner", wl.k_group, wl.v_group, wl.outliers)
-            assert [lay[k] for k in ("k_codes", "k_meta", "v_codes", "v_meta", "k_out", "v_out")] == offs
+            offs, rec = _expected_record(kb_, vb, wl.k_mode == "inner", wl.k_group, wl.v_group, wl.outliers,
+                                         wl.k_hi_groups)
+            assert [lay[k] for k in ("k_codes", "k_meta", "v_codes", "v_meta", "k_out", "v_out",
+                                     "k_ext", "k_sel")] == offs
             assert lay["record_bytes"] == rec
             assert lay["k_row_bytes"] == 128 * kb_ // 8
             F = 32 if wl.k_mode == "channel" else 1
@@ -157,6 +170,27 @@ def test_average_bits_from_code_bytes():
         f_m = sum(kb_ + vb for kb_, vb in pairs) / (2 * wl.L)
         assert np.mean(bits) == f_m
         assert set(pairs) <= set(W.PAIR_SET) and len(set(pairs)) == 5
+        code, stored = K.kvq_average_bits(h)
+        assert code == f_m
+        recs = [K.kvq_block_layout(h, l)["record_bytes"] for l in range(wl.L)]
+        assert stored == np.mean([8 * r / (2 * 32 * 128) for r in recs]) and stored > code
+    finally:
+        K.kvq_destroy(h)
+
+
+@pytest.mark.parametrize("kg,m,pairs,f_m", [
+    (64, 1, [(4, 2), (8, 8)], (6 + 2 + 8 + 8) / 4),    # one of two groups at 8 bits: keys 6 bits
+    (32, 1, [(4, 4)], (5 + 4) / 2),                    # one of four: 5 bits
+    (32, 3, [(4, 2), (2, 2)], (7 + 2 + 2 + 2) / 4),    # three of four: 7; the 2-bit layer unchanged
+    (64, 0, [(4, 2)], 3.0),
+])
+def test_average_bits_counts_mixed_groups(kg, m, pairs, f_m):
+    # f_m = sum(P)/2L with a mixed layer's key width averaged over its groups
+    cfg = K.make_config(1, 8, 8, len(pairs), 64, k_mode=K.KVQ_K_INNER, k_group=kg, k_hybrid=1,
+                        k_hi_groups=m)
+    h = K.kvq_create(cfg, pairs)
+    try:
+        assert K.kvq_average_bits(h)[0] == f_m
     finally:
         K.kvq_destroy(h)
 

@@ -23,6 +23,10 @@ REDUCED = {
     # rotated 2-bit values, and its ternary-value negative control
     "P5r": W.C2.with_(Hq=4, Hkv=4, T=1024, steps=8, v_hadamard=True, v_out_count=2),
     "P5r-ternary": W.C2.with_(Hq=4, Hkv=4, T=1024, steps=8, v_ternary=True, v_out_count=2),
+    # InnerQ's mixed 4/8-bit groups: one of each token's two key groups at 8
+    # bits (matrix-core kernel), and two of four groups of 32 (LDS-staged)
+    "C5rm": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4, k_hi_groups=1, k_out_count=2),
+    "C5rm32": W.C5.with_(B=2, Hq=16, Hkv=2, T=300, steps=3, k_group=32, k_hi_groups=2),
 }
 
 EDGE = {
@@ -36,6 +40,12 @@ EDGE = {
     "knorm-window-only": W.C5.with_(B=1, Hq=8, Hkv=1, T=20, steps=3, k_norm=True),
     "knorm-sinks-window": W.C5.with_(B=1, Hq=8, Hkv=1, T=300, steps=3, sinks=4, window=32,
                                      k_norm=True, k_out_factor=64.0),
+    "mixed-single-token": W.C5.with_(B=1, Hq=8, Hkv=1, T=1, steps=3, k_hi_groups=1),
+    "mixed-all-8bit": W.C5.with_(B=1, Hq=8, Hkv=1, T=100, steps=2, k_hi_groups=2),
+    "mixed-mha-v4": W.C5.with_(B=1, Hq=4, Hkv=4, T=200, steps=2, k_hi_groups=1, v_hadamard=False,
+                               fixed_pairs=((4, 4),)),
+    "mixed-gqa4-knorm-window": W.C5.with_(B=1, Hq=8, Hkv=2, T=300, steps=3, sinks=4, window=32,
+                                          k_norm=True, k_hi_groups=1, k_out_factor=64.0),
 }
 
 
@@ -66,7 +76,7 @@ def test_edge_cases(name):
     _check_all(name, EDGE[name])
 
 
-@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C4r", "C5r", "C5rn", "P5r", "P5r-ternary"])
+@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C4r", "C5r", "C5rn", "P5r", "P5r-ternary", "C5rm"])
 def test_reduced_configs_general_kernel(name, monkeypatch):
     """The same workloads through the LDS-staged decode kernel (the path every
     scheme the matrix-core kernel does not cover takes)."""
@@ -143,3 +153,7 @@ def test_full_c5_sampled():
 
 def test_full_c5_key_norm_sampled():
     _full(W.C5.with_(k_norm=True), [(0, 3), (0, 300)])
+
+
+def test_full_c5_mixed_groups_sampled():
+    _full(W.C5.with_(k_hi_groups=1), [(0, 5), (0, 401)])
