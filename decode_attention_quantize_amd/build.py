@@ -32,10 +32,15 @@ def sources() -> list[str]:
 # Per-source additions.  The matrix-core decodes keep their MFMA accumulators
 # in ordinary VGPRs: they rescale and read them on the VALU every block, and
 # accumulation registers would cost a copy each way (and count against the
-# same per-lane register budget that sets occupancy).
+# same per-lane register budget that sets occupancy).  They are also built
+# without NaN semantics: scores, running maxima and sums there are never NaN
+# (masked tokens are assigned -inf), and in the kernels' IEEE mode every
+# fmaxf would otherwise quiet both inputs first (two extra VALU operations,
+# and a DPP row move that cannot fold into the max).  Non-NaN results are
+# identical.
 EXTRA = {
-    "kvq_decode_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
-    "kvq_decode_lut.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "kvq_decode_fast.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
+    "kvq_decode_lut.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1", "-fno-honor-nans"],
 }
 
 

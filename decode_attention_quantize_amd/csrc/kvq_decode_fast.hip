@@ -367,8 +367,11 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
         p0 = mfma(qa[1], bk(1), p0);
         p1 = mfma(qa[2], bk(2), p1);
         p1 = mfma(qa[3], bk(3), p1);
+        // score of group g: sg (p_g - base qsum_g) + zg qsum_g
+        //                  = sg p_g + (zg - base sg) qsum_g, times kscale,
+        // with the per-token factors formed once per lane
         const u32x2 mm = imeta[nt];  // (s0, z0), (s1, z1) of token 16 nt + n16
-        float sg[2], zg[2];
+        float sk[2], zk[2];
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
           const uint16_t s16 = static_cast<uint16_t>(mm[gg] & 0xffff);
@@ -376,18 +379,15 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
           const float sv = h2f(s16 & 0x7fff);
           const bool sym = (s16 & 0x8000) != 0;
           const bool wide = MIX && ((sel >> gg) & 1u) != 0;
-          sg[gg] = sv * (wide ? 256.f : iu);
-          zg[gg] = sym ? -(wide ? 128.f : static_cast<float>(1 << (KB - 1))) * sv : h2f(z16);
+          const float sg = sv * (wide ? 256.f : iu);
+          const float zg = sym ? -(wide ? 128.f : static_cast<float>(1 << (KB - 1))) * sv : h2f(z16);
+          sk[gg] = sg * kscale;
+          zk[gg] = fmaf(-base, sg, zg) * kscale;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float sc = 0.f;
-          if (i < RI) {
-            sc = fmaf(sg[0], fmaf(-base, qsum[0][i], p0[i]), zg[0] * qsum[0][i]);
-            sc = fmaf(sg[1], fmaf(-base, qsum[1][i], p1[i]), fmaf(zg[1], qsum[1][i], sc));
-          }
-          sacc[nt][i] = sc * kscale;
-        }
+        for (int i = 0; i < 4; ++i)
+          sacc[nt][i] = i < RI ? fmaf(sk[0], p0[i], fmaf(sk[1], p1[i], fmaf(zk[0], qsum[0][i], zk[1] * qsum[1][i])))
+                               : 0.f;
       }
     }
     // ---------------- values: one batch of LDS reads (issued before the softmax)
