@@ -128,6 +128,28 @@ struct Rec {
   static constexpr int loads = (bytes + 1023) / 1024;  // 1 KiB per wave-wide load
 };
 
+// Ring depth and residency.  Every instance is sized for three wavefronts
+// per SIMD (twelve per CU): the ring takes as many slots (2..4) as a twelfth
+// of the CU's LDS allows (deeper rings keep more blocks in flight behind the
+// VALU / MFMA work of the block being computed).  Residency must come out as
+// a multiple of four wavefronts per CU, or the SIMDs get unequal shares of
+// the split plan's equal splits: an instance whose LDS would admit 9..11
+// workgroups per CU pads its first ring slot (static LDS) to admit eight.
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kLdsShare3 = kLdsPerCu / 12;       // three wavefronts per SIMD
+constexpr int kLdsShare2 = kLdsPerCu / 9 + 512;  // at most eight per CU
+template <int KB, int VB, int G, bool INNER, bool MIX>
+constexpr int ring_slots() {
+  constexpr int budget = kLdsShare3 - 512 - 16 * 32 * 2 - 512;
+  constexpr int n = budget / (Rec<KB, VB, INNER, MIX>::loads * 1024);
+  return n < 2 ? 2 : (n > 4 ? 4 : n);
+}
+template <int KB, int VB, bool INNER, bool MIX, int NBUF>
+constexpr int ring_pad() {
+  constexpr int slot = Rec<KB, VB, INNER, MIX>::loads * 1024;
+  constexpr int used = NBUF * slot + 16 * 32 * 2 + (NBUF < 3 ? 16 : 0) + (NBUF < 4 ? 16 : 0);
+  return (used > kLdsShare3 && used < kLdsShare2) ? kLdsShare2 - used : 0;
+}
 template <int KB, int VB, int G, bool INNER, bool MIX, int NBUF>
 __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   using R = Rec<KB, VB, INNER, MIX>;
@@ -135,7 +157,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   // one LDS object per ring slot: the compiler then tells the slots apart and
   // keeps the partial vmcnt waits instead of draining every in-flight load
   static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 slots");
-  __shared__ __attribute__((aligned(16))) uint8_t ring0[R::loads * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[R::loads * 1024 + ring_pad<KB, VB, INNER, MIX, NBUF>()];
   __shared__ __attribute__((aligned(16))) uint8_t ring1[R::loads * 1024];
   __shared__ __attribute__((aligned(16))) uint8_t ring2[NBUF >= 3 ? R::loads * 1024 : 16];
   __shared__ __attribute__((aligned(16))) uint8_t ring3[NBUF >= 4 ? R::loads * 1024 : 16];
@@ -178,14 +200,16 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   float qsum[2][RI];  // inner groups: per-row sums of q over each 64-channel group
 
   const float kscale = kLog2e / sqrtf(static_cast<float>(D));
-  float m_run[RI], l_run[RI];
+  float m_run[RI];
 #pragma unroll
-  for (int i = 0; i < RI; ++i) {
-    m_run[i] = -INFINITY;
-    l_run[i] = 0.f;
-  }
+  for (int i = 0; i < RI; ++i) m_run[i] = -INFINITY;
   f32x4 oacc[8];
+  // zacc: per query row, columns 0-3 sum_t p_t z_tg, 4-7 sum_t p_t s_tg
+  // (value groups g) and column 8 sum_t p_t, the softmax denominator: P is
+  // used as fp16 in every product and the denominator sums the same rounded
+  // weights, through the same matrix-core product (a column of ones)
   f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
+  constexpr uint32_t kOnes = 0x3C003C00u;
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) oacc[nt] = {0.f, 0.f, 0.f, 0.f};
 
@@ -206,16 +230,12 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       const float mn = fmaxf(m_run[i], bm);
       const float mr = mn == -INFINITY ? 0.f : mn;  // nothing live yet: weights 0
       alpha[i] = fexp2(m_run[i] - mr);
-      // P is used as fp16 in every product; the denominator sums the same
-      // rounded weights so numerator and denominator stay consistent
       const _Float16 p0 = static_cast<_Float16>(fexp2(sacc[0][i] - mr));
       const _Float16 p1 = static_cast<_Float16>(fexp2(sacc[1][i] - mr));
-      l_run[i] = fmaf(l_run[i], alpha[i], static_cast<float>(p0) + static_cast<float>(p1));
       m_run[i] = mn;
-      if (rows_here) {
-        ptile[4 * g4 + i][n16] = p0;
-        ptile[4 * g4 + i][16 + n16] = p1;
-      }
+      // every lane writes its rows; rows past the query group are never read
+      ptile[4 * g4 + i][n16] = p0;
+      ptile[4 * g4 + i][16 + n16] = p1;
     }
     // the running max moves rarely once a few tiles are in: the (exact)
     // rescale by alpha = 1 is skipped unless some row of the wave moved
@@ -415,8 +435,10 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     }
     const half8 pa = softmax_tile(sacc, count);
     // one MFMA of P against the block's value parameters: column g < 4 holds
-    // z_g (zero points), column 4 + g holds s_g (removes the code offset)
-    zacc = mfma(pa, n16 < 2 * ngv ? h8(vmeta[4]) : h8(0u, 0u, 0u, 0u), zacc);
+    // z_g (zero points), column 4 + g holds s_g (removes the code offset),
+    // column 8 ones (the denominator)
+    zacc = mfma(pa, n16 < 2 * ngv ? h8(vmeta[4]) : (n16 == 8 ? h8(kOnes, kOnes, kOnes, kOnes) : h8(0u, 0u, 0u, 0u)),
+                zacc);
     // weights w = p * s per (token, value group) as an exact hi + lo pair
 #pragma unroll
     for (int g = 0; g < ngv; ++g) {
@@ -494,6 +516,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       const half8 pa = softmax_tile(sacc, kBlockTokens);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
+      zacc = mfma(pa, n16 == 8 ? h8(kOnes, kOnes, kOnes, kOnes) : h8(0u, 0u, 0u, 0u), zacc);
     }
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
@@ -606,7 +629,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * G * 2;
 #pragma unroll
   for (int i = 0; i < RI; ++i) {
-    const float lsum = row16_sum(l_run[i]);
+    const float lsum = lane_bcast(zacc[i], (l & 48) | 8);
     const int row = 4 * g4 + i;
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
@@ -734,32 +757,19 @@ __global__ void __launch_bounds__(32 * NG) decode_merge_kernel(LayerDesc L, Deco
   }
 }
 
-// Ring depth and residency.  MHA layers (one query row per kv head) carry
-// the fewest registers and can run three wavefronts per SIMD, GQA layers two.
-// The ring takes as many slots (2..4) as the LDS share of that many
-// wavefronts allows: deeper rings keep more blocks in flight behind the
-// VALU / MFMA work of the block being computed.
-constexpr int kLdsPerCu = 160 * 1024;
-template <int KB, int VB, int G, bool INNER, bool MIX>
-constexpr int ring_slots() {
-  constexpr int waves = G == 1 ? 12 : 8;
-  constexpr int budget = kLdsPerCu / waves - 16 * 32 * 2 - 512;
-  constexpr int n = budget / (Rec<KB, VB, INNER, MIX>::loads * 1024);
-  return n < 2 ? 2 : (n > 4 ? 4 : n);
-}
 template <int KB, int VB, int G, bool INNER, bool MIX>
 hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
   using R = Rec<KB, VB, INNER, MIX>;
   if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm) return hipSuccess;
   if (MIX && (L.off_kx != R::off_kx || L.off_ks != R::off_ks)) return hipSuccess;
   constexpr int NB = ring_slots<KB, VB, G, INNER, MIX>();
+  auto kern = decode_mfma_kernel<KB, VB, G, INNER, MIX, NB>;
   // one full round of resident wavefronts, from the runtime's occupancy of
   // this instance (registers and LDS as compiled) and the device's CU count
   static int resident = 0;
   if (resident == 0) {
     int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_mfma_kernel<KB, VB, G, INNER, MIX, NB>, 64, 0) !=
-            hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64, 0) != hipSuccess ||
         hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return hipErrorInvalidValue;
@@ -767,7 +777,7 @@ hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* 
   }
   *waves = resident;
   if (!j.q) return hipSuccess;  // query only
-  hipLaunchKernelGGL((decode_mfma_kernel<KB, VB, G, INNER, MIX, NB>), dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
+  hipLaunchKernelGGL(kern, dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   return launch_decode_merge(L, j, s);
 }
