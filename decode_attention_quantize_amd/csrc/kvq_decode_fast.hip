@@ -223,26 +223,30 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
 #pragma unroll
           for (int i = 0; i < 4; ++i) sacc[nt][i] = -INFINITY;
     }
-    float alpha[RI];
+    float m_old[RI], m_ref[RI];
+    bool moved = false;
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       const float bm = row16_max(fmaxf(sacc[0][i], sacc[1][i]));
       const float mn = fmaxf(m_run[i], bm);
       const float mr = mn == -INFINITY ? 0.f : mn;  // nothing live yet: weights 0
-      alpha[i] = fexp2(m_run[i] - mr);
       const _Float16 p0 = static_cast<_Float16>(fexp2(sacc[0][i] - mr));
       const _Float16 p1 = static_cast<_Float16>(fexp2(sacc[1][i] - mr));
+      moved |= mn > m_run[i];
+      m_old[i] = m_run[i];
+      m_ref[i] = mr;
       m_run[i] = mn;
       // every lane writes its rows; rows past the query group are never read
       ptile[4 * g4 + i][n16] = p0;
       ptile[4 * g4 + i][16 + n16] = p1;
     }
-    // the running max moves rarely once a few tiles are in: the (exact)
-    // rescale by alpha = 1 is skipped unless some row of the wave moved
-    bool moved = false;
-#pragma unroll
-    for (int i = 0; i < RI; ++i) moved |= alpha[i] != 1.f;
+    // the running max moves rarely once a few tiles are in: the rescale
+    // factors 2^(m_old - m_new), exactly 1 for a row whose max stayed, are
+    // only formed (and applied) when some row of the wave moved
     if (__builtin_amdgcn_ballot_w64(moved)) {
+      float alpha[RI];
+#pragma unroll
+      for (int i = 0; i < RI; ++i) alpha[i] = fexp2(m_old[i] - m_ref[i]);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
