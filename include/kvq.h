@@ -227,6 +227,11 @@ kvq_status kvq_append_token(kvq_cache* cache, int32_t layer, const void* k_new,
  * head h / (Hq/Hkv).  out: device fp32 [B][Hq][D] =
  * softmax(q.K^T / sqrt(D)) V, with keys/values dequantized (outliers merged,
  * RoPE applied to pre-RoPE keys, Hadamard rotation undone).
+ * Numerical domain: with per-channel key groups (2/4/8-bit codes) the
+ * product of each query element and its channel's key scale, q_c * s_c, is
+ * formed in binary16 (as an exact hi + lo pair), so |q_c * s_c| must stay
+ * below 65504 for every body block; beyond it the output is not finite.
+ * Every other product on the path is exact or formed in fp32.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (empty cache / unbound), KVQ_ERR_DEVICE. */
 kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, float* out,
                            void* workspace, void* stream);
