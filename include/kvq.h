@@ -90,7 +90,7 @@ typedef struct {
   int32_t sink_tokens;    /* S: first S positions kept fp16 */
   int32_t recent_window;  /* W: most recent W..W+F-1 positions kept fp16 */
   int32_t k_mode;         /* KVQ_K_PER_CHANNEL (k_group must be 32) | KVQ_K_INNER */
-  int32_t k_group;        /* tokens per key group (per channel) or channels (inner: 32|64|128) */
+  int32_t k_group;        /* tokens per key group (per channel) or channels (inner: 16, 32 or 64) */
   int32_t v_mode;         /* KVQ_V_PER_TOKEN | KVQ_V_HADAMARD | KVQ_V_TERNARY */
   int32_t v_group;        /* channels per value group: 16, 32 or 64 */
   int32_t k_hybrid;       /* inner groups: symmetric iff |mean|/range <= num/den */
