@@ -46,6 +46,10 @@ EDGE = {
                                fixed_pairs=((4, 4),)),
     "mixed-gqa4-knorm-window": W.C5.with_(B=1, Hq=8, Hkv=2, T=300, steps=3, sinks=4, window=32,
                                           k_norm=True, k_hi_groups=1, k_out_factor=64.0),
+    # eight groups of 16 per token, three of them at 8 bits (LDS-staged kernel)
+    "mixed-g16": W.C5.with_(B=1, Hq=8, Hkv=1, T=100, steps=2, k_group=16, k_hi_groups=3),
+    # a 2-bit-key layer ignores the setting (plain inner 2-bit keys)
+    "mixed-ignored-k2": W.C5.with_(B=1, Hq=8, Hkv=1, T=100, steps=2, k_hi_groups=1, fixed_pairs=((2, 2),)),
 }
 
 
