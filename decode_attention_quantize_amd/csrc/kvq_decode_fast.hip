@@ -54,8 +54,8 @@ template <> struct CodeEnc<8> { static constexpr float base = 1024.f, inv_unit =
 // no literal operands) and made opaque once, so that the and-or pairs are
 // selected as single v_and_or_b32 and the constants are not rematerialised.
 struct Unpack {
-  uint32_t m4, m2, e8, m4lo;  // VGPRs
-  uint32_t one2;              // SGPR: fp16 1.0 in both halves
+  uint32_t m4, m2, e8, m4lo, m4a, m4b;  // VGPRs
+  uint32_t one2, e64, e4;               // SGPRs: fp16 1.0, 64.0, 4.0 in both halves
 };
 __device__ __forceinline__ uint32_t andor(uint32_t x, uint32_t m, uint32_t o) { return (x & m) | o; }
 __device__ __forceinline__ half8 ex4(const Unpack& k, uint32_t x) {
@@ -67,6 +67,14 @@ __device__ __forceinline__ half8 ex4(const Unpack& k, uint32_t x) {
 __device__ __forceinline__ half8 ex4lo(const Unpack& k, uint32_t x, uint32_t y) {
   return h8(andor(y << 2, k.m4lo, andor(x << 6, k.m4, k.one2)), andor(y >> 2, k.m4lo, andor(x << 2, k.m4, k.one2)),
             andor(y >> 6, k.m4lo, andor(x >> 2, k.m4, k.one2)), andor(y >> 10, k.m4lo, andor(x >> 6, k.m4, k.one2)));
+}
+// Inner-group 4-bit operands, two of four words without a shift: each field
+// takes the exponent under which its code weighs c/16 -- bits 0-3 of a half
+// read as 64 + c/16, bits 4-7 as 4 + c/16 -- so the constant part depends on
+// the position (64 for elements 0-1 of an eight-element K chunk, 4 for 2-7)
+// and the group-sum MFMA starts from minus the matching weighted sum of q.
+__device__ __forceinline__ half8 ex4w(const Unpack& k, uint32_t x) {
+  return h8(andor(x, k.m4a, k.e64), andor(x, k.m4b, k.e4), andor(x >> 4, k.m4b, k.e4), andor(x >> 8, k.m4b, k.e4));
 }
 template <int E>
 __device__ __forceinline__ half8 ex2(const Unpack& k, uint32_t x) {
@@ -179,11 +187,19 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   constexpr int RI = G < 4 ? G : 4;           // output rows per lane (registers)
   const bool rows_here = 4 * g4 < G;           // lane holds real query rows
   constexpr int ngv = D / 32;                  // value groups of 32 channels
-  Unpack unp{0x03C003C0u, 0x03000300u, 0x64646464u, 0x003C003Cu, 0x3C003C00u};
+  Unpack unp{0x03C003C0u, 0x03000300u, 0x64646464u, 0x003C003Cu, 0x000F000Fu, 0x00F000F0u,
+             0x3C003C00u, 0x54005400u, 0x44004400u};
+  constexpr bool kWeighted = INNER && !MIX;  // inner 4-bit keys read through ex4w
   pin(unp.m4);
   pin(unp.m2);
   pin(unp.e8);
   if constexpr (MIX) pin(unp.m4lo);
+  if constexpr (kWeighted) {
+    pin(unp.m4a);
+    pin(unp.m4b);
+    asm volatile("" : "+s"(unp.e64));
+    asm volatile("" : "+s"(unp.e4));
+  }
   asm volatile("" : "+s"(unp.one2));
 
   // ---- query operand (natural channel order per K-step)
@@ -198,6 +214,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     }
   }
   float qsum[2][RI];  // inner groups: per-row sums of q over each 64-channel group
+  f32x4 qinit[2];     // inner 4-bit keys: minus the position-weighted sums (group-sum start)
 
   const float kscale = kLog2e / sqrtf(static_cast<float>(D));
   float m_run[RI];
@@ -384,16 +401,19 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
         }
         auto bk = [&](int j) __attribute__((always_inline)) {
           if constexpr (MIX) return ex4lo(unp, kw[nt][j], lo[j]);
-          else return kstep<KB>(unp, kw[nt], j);
+          else return ex4w(unp, kw[nt][j]);
         };
-        f32x4 p0 = {0.f, 0.f, 0.f, 0.f}, p1 = {0.f, 0.f, 0.f, 0.f};
+        // group sums of q_c B_ct; 4-bit groups start from minus the weighted
+        // sums of q, so they come out as sum_c q_c c_ct / 16 directly
+        f32x4 p0 = MIX ? f32x4{0.f, 0.f, 0.f, 0.f} : qinit[0];
+        f32x4 p1 = MIX ? f32x4{0.f, 0.f, 0.f, 0.f} : qinit[1];
         p0 = mfma(qa[0], bk(0), p0);
         p0 = mfma(qa[1], bk(1), p0);
         p1 = mfma(qa[2], bk(2), p1);
         p1 = mfma(qa[3], bk(3), p1);
-        // score of group g: sg (p_g - base qsum_g) + zg qsum_g
-        //                  = sg p_g + (zg - base sg) qsum_g, times kscale,
-        // with the per-token factors formed once per lane
+        // score of group g: sg (code sum) + zg qsum_g, times kscale, with the
+        // per-token factors formed once per lane; mixed layers remove the
+        // offset here: sg (p_g - qsum_g) + zg qsum_g = sg p_g + (zg - sg) qsum_g
         const u32x2 mm = imeta[nt];  // (s0, z0), (s1, z1) of token 16 nt + n16
         float sk[2], zk[2];
 #pragma unroll
@@ -406,7 +426,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
           const float sg = sv * (wide ? 256.f : iu);
           const float zg = sym ? -(wide ? 128.f : static_cast<float>(1 << (KB - 1))) * sv : h2f(z16);
           sk[gg] = sg * kscale;
-          zk[gg] = fmaf(-base, sg, zg) * kscale;
+          zk[gg] = (MIX ? fmaf(-base, sg, zg) : zg) * kscale;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -546,15 +566,25 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     }
 #pragma unroll
     for (int gg = 0; gg < 2; ++gg) {
-      float s = 0.f;
+      float s = 0.f, sw = 0.f;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int kk = 0; kk < 8; ++kk) s += static_cast<float>(qa[2 * gg + jj][kk]);
+        for (int kk = 0; kk < 8; ++kk) {
+          const float v = static_cast<float>(qa[2 * gg + jj][kk]);
+          s += v;
+          sw = fmaf(v, kk < 2 ? 64.f : 4.f, sw);  // constant parts of the ex4w operands
+        }
       s += xshflf<16>(s);
       s += __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __float_as_int(s)));
+      sw += xshflf<16>(sw);
+      sw += __int_as_float(__builtin_amdgcn_ds_bpermute((l ^ 32) << 2, __float_as_int(sw)));
+      qinit[gg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < RI; ++i) qsum[gg][i] = lane_bcast(s, 20 * g4 + i);
+      for (int i = 0; i < RI; ++i) {
+        qsum[gg][i] = lane_bcast(s, 20 * g4 + i);
+        qinit[gg][i] = -lane_bcast(sw, 20 * g4 + i);
+      }
     }
   }
 
