@@ -158,8 +158,16 @@ constexpr int ring_pad() {
   constexpr int used = NBUF * slot + 16 * 32 * 2 + (NBUF < 3 ? 16 : 0) + (NBUF < 4 ? 16 : 0);
   return (used > kLdsShare3 && used < kLdsShare2) ? kLdsShare2 - used : 0;
 }
+// Wavefronts per SIMD the register allocation is held to: three for the
+// GQA instances whose registers fit 168 with at most a spill outside the
+// block loop, else what they need.
+template <int KB, int VB, int G, bool INNER, bool MIX>
+constexpr int waves_per_simd() {
+  return (G >= 4 && (VB == 2 || (VB == 4 && !INNER && KB != 8))) ? 3 : 1;
+}
 template <int KB, int VB, int G, bool INNER, bool MIX, int NBUF>
-__global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob J) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KB, VB, G, INNER, MIX>())))
+decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   using R = Rec<KB, VB, INNER, MIX>;
   static_assert(!MIX || (INNER && KB == 4), "mixed groups: 4-bit inner keys");
   // one LDS object per ring slot: the compiler then tells the slots apart and
@@ -187,6 +195,19 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   constexpr int RI = G < 4 ? G : 4;           // output rows per lane (registers)
   const bool rows_here = 4 * g4 < G;           // lane holds real query rows
   constexpr int ngv = D / 32;                  // value groups of 32 channels
+  // Query groups of 8 (or 4) rows fill only lanes 0-31 (or 0-15) of a score
+  // tile's accumulators.  The two 16-token tiles of a block are folded into
+  // one register set with a permlane swap: tile 1's live lanes move into
+  // tile 0's empty half (row of 16), so the per-token score factors and the
+  // softmax run once per lane for the whole block instead of once per tile.
+  // Folded, lane (n16, g4) holds rows frow..frow+3 of token ftok.
+  constexpr int kFold = G == 8 ? 32 : (G == 4 ? 16 : 0);
+  const int ftile = kFold == 32 ? g4 >> 1 : g4 & 1;
+  const int ftok = n16 + 16 * ftile;
+  const int frow = kFold == 32 ? 4 * (g4 & 1) : 8 * (g4 >> 1);
+  auto fold = [&](float a, float b) __attribute__((always_inline)) {
+    return kFold == 32 ? swap32(a, b).x : swap16(a, b).x;
+  };
   Unpack unp{0x03C003C0u, 0x03000300u, 0x64646464u, 0x003C003Cu, 0x000F000Fu, 0x00F000F0u,
              0x3C003C00u, 0x54005400u, 0x44004400u};
   constexpr bool kWeighted = INNER && !MIX;  // inner 4-bit keys read through ex4w
@@ -217,9 +238,12 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
   f32x4 qinit[2];     // inner 4-bit keys: minus the position-weighted sums (group-sum start)
 
   const float kscale = kLog2e / sqrtf(static_cast<float>(D));
+  // running row maxima (folded blocks: row ceilings, starting from a finite
+  // value below every score so that masked -inf scores weigh 2^-inf = 0)
+  constexpr float kNoScore = -3.0e38f;
   float m_run[RI];
 #pragma unroll
-  for (int i = 0; i < RI; ++i) m_run[i] = -INFINITY;
+  for (int i = 0; i < RI; ++i) m_run[i] = kFold ? kNoScore : -INFINITY;
   f32x4 oacc[8];
   // zacc: per query row, columns 0-3 sum_t p_t z_tg, 4-7 sum_t p_t s_tg
   // (value groups g) and column 8 sum_t p_t, the softmax denominator: P is
@@ -277,10 +301,64 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
     return n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
   };
 
+  // the same on a folded block (kFold): s[i] is the score of row frow + i
+  // and token ftok.  The row reference m_run is a ceiling rather than the
+  // running maximum: weights are 2^(s - m_run) <= 1 as long as no score
+  // passes it, and only a block with such a score (the first one, and
+  // rarely later) pays for the row maxima (a 16-lane row reduction joined
+  // with the partner lane that holds the other tile's tokens) and the
+  // rescale.  The new ceiling sits kPad above the block's maximum, so that
+  // slowly rising maxima do not trigger it block after block.  The weights
+  // are lifted by 2^kLift (the partial's maximum is lowered to match): with
+  // the small value scales of 4- and 8-bit groups, p * s would otherwise fall
+  // into the fp16 subnormals for tokens a few binades below the ceiling, and
+  // the hi + lo pair would lose its precision.  The lift keeps p * s within
+  // fp16 for any fp16 value range (s <= 131008 / (2^VB - 1)).
+  constexpr float kPad = 2.f;
+  constexpr float kLift = VB == 8 ? 6.f : (VB == 4 ? 2.f : 0.f);
+  auto softmax_fold = [&](f32x4 s, int count) __attribute__((always_inline)) -> half8 {
+    if (count < kBlockTokens) {  // wave-uniform: only a partial last block
+      if (ftok >= count)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = -INFINITY;
+    }
+    bool over = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) over |= s[i] > m_run[i];
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      float alpha[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float bm = row16_max(s[i]);
+        const float2 pr = kFold == 32 ? swap32(bm, bm) : swap16(bm, bm);
+        const float mx = fmaxf(pr.x, pr.y);
+        const float mn = mx > m_run[i] ? mx + kPad : m_run[i];
+        alpha[i] = fexp2(m_run[i] - mn);  // 1 where the ceiling stays, 0 from the start value
+        m_run[i] = mn;
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) oacc[nt][i] *= alpha[i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zacc[i] *= alpha[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // rows past the query group (fold by 16: rows 8-11) are never read
+      ptile[frow + i][ftok] = static_cast<_Float16>(fexp2(s[i] - (m_run[i] - kLift)));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    return n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
+  };
+
   // one quantized block whose record sits in LDS at rec
   auto body_block = [&](const lds_u8* rec, int count) __attribute__((always_inline)) {
     const uint32_t r0 = lds_off(rec);
     f32x4 sacc[2];
+    f32x4 sf;  // folded block scores (kFold)
     // ---------------- keys: one batch of LDS reads
     uint32_t kw[2][KB];
     u32x4 kmeta[8];
@@ -291,9 +369,11 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       if constexpr (INNER) {
         const uint32_t a = r0 + n16 * 64 + 8 * g4;
         const u32x2 x0 = dsr8<0>(a), x1 = dsr8<32>(a), y0 = dsr8<1024>(a), y1 = dsr8<1024 + 32>(a);
-        const uint32_t am = r0 + R::off_km + 8 * n16;
+        // (s, z) pairs of token 16 nt + n16, or of the lane's one token ftok
+        // when the block is folded
+        const uint32_t am = r0 + R::off_km + 8 * (kFold ? ftok : n16);
         imeta[0] = dsr8<0>(am);
-        imeta[1] = dsr8<128>(am);
+        if constexpr (!kFold) imeta[1] = dsr8<128>(am);
         if constexpr (MIX) {
           const uint32_t ax = r0 + R::off_kx + n16 * 32 + 8 * g4;
           const uint32_t as = r0 + R::off_ks + (n16 & 12);
@@ -334,7 +414,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
         for (int e = 0; e < KB; ++e) pin(kw[nt][e]);
       if constexpr (INNER) {
         pin(imeta[0]);
-        pin(imeta[1]);
+        if constexpr (!kFold) pin(imeta[1]);
         if constexpr (MIX) {
           pin(xlo[0]);
           pin(xlo[1]);
@@ -379,16 +459,39 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
           sacc[nt] = mfma(ql, bk, sacc[nt]);
         }
       }
+      if constexpr (kFold) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+        for (int i = 0; i < 4; ++i) sf[i] = fold(sacc[0][i], sacc[1][i]) * (iu * kscale);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sacc[nt][i] *= iu * kscale;
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sacc[nt][i] *= iu * kscale;
+      }
     } else {
       // per-token groups of 64 channels: group sums sum_c q_c B_ct, offset
       // removed with the group sums of q, then scaled per token
       // (mixed layers: the token's 8-bit group, marked in its mask, reads
       // 1 + c/256 operands, so its sums take 256 s and the symmetric offset 128)
       constexpr float base = CodeEnc<KB>::base, iu = CodeEnc<KB>::inv_unit;
+      // score of group g: sg (code sum) + zg qsum_g, times kscale, with the
+      // per-token factors formed once per lane; mixed layers remove the
+      // offset here: sg (p_g - qsum_g) + zg qsum_g = sg p_g + (zg - sg) qsum_g
+      auto factors = [&](u32x2 mm, uint32_t sel, float (&sk)[2], float (&zk)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const uint16_t s16 = static_cast<uint16_t>(mm[gg] & 0xffff);
+          const uint16_t z16 = static_cast<uint16_t>(mm[gg] >> 16);
+          const float sv = h2f(s16 & 0x7fff);
+          const bool sym = (s16 & 0x8000) != 0;
+          const bool wide = MIX && ((sel >> gg) & 1u) != 0;
+          const float sg = sv * (wide ? 256.f : iu);
+          const float zg = sym ? -(wide ? 128.f : static_cast<float>(1 << (KB - 1))) * sv : h2f(z16);
+          sk[gg] = sg * kscale;
+          zk[gg] = (MIX ? fmaf(-base, sg, zg) : zg) * kscale;
+        }
+      };
+      f32x4 pg[2][2];  // folded blocks: group sums [tile][group] before the fold
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         uint32_t sel = 0, lo[4] = {0u, 0u, 0u, 0u};
@@ -411,27 +514,31 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
         p0 = mfma(qa[1], bk(1), p0);
         p1 = mfma(qa[2], bk(2), p1);
         p1 = mfma(qa[3], bk(3), p1);
-        // score of group g: sg (code sum) + zg qsum_g, times kscale, with the
-        // per-token factors formed once per lane; mixed layers remove the
-        // offset here: sg (p_g - qsum_g) + zg qsum_g = sg p_g + (zg - sg) qsum_g
-        const u32x2 mm = imeta[nt];  // (s0, z0), (s1, z1) of token 16 nt + n16
-        float sk[2], zk[2];
+        if constexpr (kFold) {
+          pg[nt][0] = p0;
+          pg[nt][1] = p1;
+        } else {
+          float sk[2], zk[2];
+          factors(imeta[nt], sel, sk, zk);  // (s0, z0), (s1, z1) of token 16 nt + n16
 #pragma unroll
-        for (int gg = 0; gg < 2; ++gg) {
-          const uint16_t s16 = static_cast<uint16_t>(mm[gg] & 0xffff);
-          const uint16_t z16 = static_cast<uint16_t>(mm[gg] >> 16);
-          const float sv = h2f(s16 & 0x7fff);
-          const bool sym = (s16 & 0x8000) != 0;
-          const bool wide = MIX && ((sel >> gg) & 1u) != 0;
-          const float sg = sv * (wide ? 256.f : iu);
-          const float zg = sym ? -(wide ? 128.f : static_cast<float>(1 << (KB - 1))) * sv : h2f(z16);
-          sk[gg] = sg * kscale;
-          zk[gg] = (MIX ? fmaf(-base, sg, zg) : zg) * kscale;
+          for (int i = 0; i < 4; ++i)
+            sacc[nt][i] = i < RI ? fmaf(sk[0], p0[i], fmaf(sk[1], p1[i], fmaf(zk[0], qsum[0][i], zk[1] * qsum[1][i])))
+                                 : 0.f;
         }
+      }
+      if constexpr (kFold) {
+        // the group sums of both tiles in one register set, then the factors
+        // of the lane's one token
+        uint32_t sel = 0;
+        if constexpr (MIX) sel = ((ftile ? selw[1] : selw[0]) >> (8 * (n16 & 3))) & 3u;
+        float sk[2], zk[2];
+        factors(imeta[0], sel, sk, zk);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sacc[nt][i] = i < RI ? fmaf(sk[0], p0[i], fmaf(sk[1], p1[i], fmaf(zk[0], qsum[0][i], zk[1] * qsum[1][i])))
-                               : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          const float g0 = fold(pg[0][0][i], pg[1][0][i]);
+          const float g1 = fold(pg[0][1][i], pg[1][1][i]);
+          sf[i] = fmaf(sk[0], g0, fmaf(sk[1], g1, fmaf(zk[0], qsum[0][i], zk[1] * qsum[1][i])));
+        }
       }
     }
     // ---------------- values: one batch of LDS reads (issued before the softmax)
@@ -457,7 +564,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
 #pragma unroll
       for (int e = 0; e < 5; ++e) pin(vmeta[e]);
     }
-    const half8 pa = softmax_tile(sacc, count);
+    const half8 pa = kFold ? softmax_fold(sf, count) : softmax_tile(sacc, count);
     // one MFMA of P against the block's value parameters: column g < 4 holds
     // z_g (zero points), column 4 + g holds s_g (removes the code offset),
     // column 8 ones (the denominator)
@@ -537,7 +644,11 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
 #pragma unroll
         for (int i = 0; i < 4; ++i) sacc[nt][i] = live ? sacc[nt][i] * kscale : -INFINITY;
       }
-      const half8 pa = softmax_tile(sacc, kBlockTokens);
+      f32x4 sf;
+      if constexpr (kFold)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sf[i] = fold(sacc[0][i], sacc[1][i]);
+      const half8 pa = kFold ? softmax_fold(sf, kBlockTokens) : softmax_tile(sacc, kBlockTokens);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
       zacc = mfma(pa, n16 == 8 ? h8(kOnes, kOnes, kOnes, kOnes) : h8(0u, 0u, 0u, 0u), zacc);
@@ -582,7 +693,7 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       qinit[gg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
-        qsum[gg][i] = lane_bcast(s, 20 * g4 + i);
+        qsum[gg][i] = lane_bcast(s, kFold ? frow + i : 20 * g4 + i);  // lane n16 = row holds its sum
         qinit[gg][i] = -lane_bcast(sw, 20 * g4 + i);
       }
     }
@@ -673,7 +784,9 @@ __global__ void __launch_bounds__(64) decode_mfma_kernel(LayerDesc L, DecodeJob 
       if (rows_here && row < G) opart[row * D + 16 * nt + n16] = o;
     }
     if (rows_here && row < G && n16 == 0) {
-      mlpart[row * 2] = m_run[i];
+      // folded blocks: the weights' reference is the ceiling minus the lift;
+      // a split that saw no live token reports -inf
+      mlpart[row * 2] = m_run[i] == kNoScore ? -INFINITY : (kFold ? m_run[i] - kLift : m_run[i]);
       mlpart[row * 2 + 1] = lsum;
     }
   }
