@@ -238,12 +238,12 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   f32x4 qinit[2];     // inner 4-bit keys: minus the position-weighted sums (group-sum start)
 
   const float kscale = kLog2e / sqrtf(static_cast<float>(D));
-  // running row maxima (folded blocks: row ceilings, starting from a finite
-  // value below every score so that masked -inf scores weigh 2^-inf = 0)
+  // row ceilings, starting from a finite value below every score so that
+  // masked -inf scores weigh 2^-inf = 0
   constexpr float kNoScore = -3.0e38f;
   float m_run[RI];
 #pragma unroll
-  for (int i = 0; i < RI; ++i) m_run[i] = kFold ? kNoScore : -INFINITY;
+  for (int i = 0; i < RI; ++i) m_run[i] = kNoScore;
   f32x4 oacc[8];
   // zacc: per query row, columns 0-3 sum_t p_t z_tg, 4-7 sum_t p_t s_tg
   // (value groups g) and column 8 sum_t p_t, the softmax denominator: P is
@@ -254,8 +254,13 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) oacc[nt] = {0.f, 0.f, 0.f, 0.f};
 
-  // online softmax of one 32-token tile; P (fp16) lands in ptile, the
-  // accumulators are rescaled; returns nothing, reads sacc
+  // Online softmax of one 32-token block in the two-tile layout (lane holds
+  // rows 4 g4 + i of tokens n16 and 16 + n16); P (fp16) lands in ptile and
+  // the accumulators are rescaled when a row's reference moves.  The row
+  // reference m_run is a ceiling rather than the running maximum (see the
+  // folded variant below for the reasons and the weight lift).
+  constexpr float kPad = 2.f;
+  constexpr float kLift = VB == 8 ? 6.f : (VB == 4 ? 2.f : 0.f);
   auto softmax_tile = [&](f32x4 (&sacc)[2], int count) __attribute__((always_inline)) -> half8 {
     if (count < kBlockTokens) {  // wave-uniform: only a partial last block
 #pragma unroll
@@ -264,36 +269,30 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) sacc[nt][i] = -INFINITY;
     }
-    float m_old[RI], m_ref[RI];
-    bool moved = false;
+    bool over = false;
 #pragma unroll
-    for (int i = 0; i < RI; ++i) {
-      const float bm = row16_max(fmaxf(sacc[0][i], sacc[1][i]));
-      const float mn = fmaxf(m_run[i], bm);
-      const float mr = mn == -INFINITY ? 0.f : mn;  // nothing live yet: weights 0
-      const _Float16 p0 = static_cast<_Float16>(fexp2(sacc[0][i] - mr));
-      const _Float16 p1 = static_cast<_Float16>(fexp2(sacc[1][i] - mr));
-      moved |= mn > m_run[i];
-      m_old[i] = m_run[i];
-      m_ref[i] = mr;
-      m_run[i] = mn;
-      // every lane writes its rows; rows past the query group are never read
-      ptile[4 * g4 + i][n16] = p0;
-      ptile[4 * g4 + i][16 + n16] = p1;
-    }
-    // the running max moves rarely once a few tiles are in: the rescale
-    // factors 2^(m_old - m_new), exactly 1 for a row whose max stayed, are
-    // only formed (and applied) when some row of the wave moved
-    if (__builtin_amdgcn_ballot_w64(moved)) {
+    for (int i = 0; i < RI; ++i) over |= fmaxf(sacc[0][i], sacc[1][i]) > m_run[i];
+    if (__builtin_amdgcn_ballot_w64(over)) {
       float alpha[RI];
 #pragma unroll
-      for (int i = 0; i < RI; ++i) alpha[i] = fexp2(m_old[i] - m_ref[i]);
+      for (int i = 0; i < RI; ++i) {
+        const float bm = row16_max(fmaxf(sacc[0][i], sacc[1][i]));
+        const float mn = bm > m_run[i] ? bm + kPad : m_run[i];
+        alpha[i] = fexp2(m_run[i] - mn);  // 1 where the ceiling stays, 0 from the start value
+        m_run[i] = mn;
+      }
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int i = 0; i < RI; ++i) oacc[nt][i] *= alpha[i];
 #pragma unroll
       for (int i = 0; i < RI; ++i) zacc[i] *= alpha[i];
+    }
+#pragma unroll
+    for (int i = 0; i < RI; ++i) {
+      // every lane writes its rows; rows past the query group are never read
+      ptile[4 * g4 + i][n16] = static_cast<_Float16>(fexp2(sacc[0][i] - (m_run[i] - kLift)));
+      ptile[4 * g4 + i][16 + n16] = static_cast<_Float16>(fexp2(sacc[1][i] - (m_run[i] - kLift)));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -314,8 +313,6 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // into the fp16 subnormals for tokens a few binades below the ceiling, and
   // the hi + lo pair would lose its precision.  The lift keeps p * s within
   // fp16 for any fp16 value range (s <= 131008 / (2^VB - 1)).
-  constexpr float kPad = 2.f;
-  constexpr float kLift = VB == 8 ? 6.f : (VB == 4 ? 2.f : 0.f);
   auto softmax_fold = [&](f32x4 s, int count) __attribute__((always_inline)) -> half8 {
     if (count < kBlockTokens) {  // wave-uniform: only a partial last block
       if (ftok >= count)
@@ -478,6 +475,20 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       // per-token factors formed once per lane; mixed layers remove the
       // offset here: sg (p_g - qsum_g) + zg qsum_g = sg p_g + (zg - sg) qsum_g
       auto factors = [&](u32x2 mm, uint32_t sel, float (&sk)[2], float (&zk)[2]) __attribute__((always_inline)) {
+        if constexpr (!MIX) {
+          // a symmetric group stores its zero point as +0 and its flag as the
+          // scale's sign: zg = z - 2^(KB-1) |s| = z + 2^(KB-1) min(s, 0) for
+          // both kinds (products by powers of two are exact, so the factors
+          // equal sv iu kscale and zg kscale as written out below)
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            const float sv = h2f(static_cast<uint16_t>(mm[gg] & 0xffff));
+            const float zv = h2f(static_cast<uint16_t>(mm[gg] >> 16));
+            sk[gg] = fabsf(sv) * (iu * kscale);
+            zk[gg] = fmaf(fminf(sv, 0.f), static_cast<float>(1 << (KB - 1)) * kscale, zv * kscale);
+          }
+          return;
+        }
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
           const uint16_t s16 = static_cast<uint16_t>(mm[gg] & 0xffff);
@@ -784,9 +795,9 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       if (rows_here && row < G) opart[row * D + 16 * nt + n16] = o;
     }
     if (rows_here && row < G && n16 == 0) {
-      // folded blocks: the weights' reference is the ceiling minus the lift;
-      // a split that saw no live token reports -inf
-      mlpart[row * 2] = m_run[i] == kNoScore ? -INFINITY : (kFold ? m_run[i] - kLift : m_run[i]);
+      // the weights' reference is the ceiling minus the lift; a split that
+      // saw no live token reports -inf
+      mlpart[row * 2] = m_run[i] == kNoScore ? -INFINITY : m_run[i] - kLift;
       mlpart[row * 2 + 1] = lsum;
     }
   }
