@@ -50,6 +50,18 @@ EDGE = {
     "mixed-g16": W.C5.with_(B=1, Hq=8, Hkv=1, T=100, steps=2, k_group=16, k_hi_groups=3),
     # a 2-bit-key layer ignores the setting (plain inner 2-bit keys)
     "mixed-ignored-k2": W.C5.with_(B=1, Hq=8, Hkv=1, T=100, steps=2, k_hi_groups=1, fixed_pairs=((2, 2),)),
+    # eight query rows over 8-bit values with loud value channels (x4000): large value
+    # scales against the weights' lift for 8-bit groups
+    "gqa8-kv8-loud-values": W.C3.with_(L=1, B=1, Hq=8, Hkv=1, T=300, steps=2, fixed_pairs=((8, 8),),
+                                       v_out_count=4, v_out_factor=4000.0),
+    # peaked attention (queries x3) over 4-bit values: most weights far below the row
+    # ceiling, the subnormal range the lift for 4-bit groups guards against
+    "gqa4-k4v4-peaky": W.C3.with_(L=1, B=1, Hq=4, Hkv=1, T=600, steps=2, fixed_pairs=((4, 4),),
+                                  q_scale=3.0),
+    # the same over 8-bit values with eight rows, and over MHA 8-bit values
+    "gqa8-kv8-peaky": W.C3.with_(L=1, B=1, Hq=8, Hkv=1, T=600, steps=2, fixed_pairs=((8, 8),),
+                                 q_scale=3.0),
+    "mha-kv8-peaky": W.C2.with_(Hq=2, Hkv=2, T=600, steps=2, fixed_pairs=((8, 8),), q_scale=3.0),
 }
 
 
