@@ -225,10 +225,14 @@ def main():
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     # launch durations: decodes 2..L of each step (the first follows the host's
-    # append calls and can include idle time); every decode when L == 1
+    # append calls and can include idle time).  With one layer, every decode
+    # but the first timed one: the timed loop starts from an idle GPU, so the
+    # first step's start event is passed before the host has launched that
+    # decode; from the second step on the host runs a step ahead.
     first = 1 if wl.L > 1 else 0
-    kern_ms = [e0.elapsed_time(e1) for ev in events for (e0, e1) in ev[first:]]
-    kern_bytes = [nb for k in range(a.steps) for nb in nbytes[k * wl.L + first:(k + 1) * wl.L]]
+    skip = 0 if wl.L > 1 or a.steps < 2 else 1
+    kern_ms = [e0.elapsed_time(e1) for ev in events[skip:] for (e0, e1) in ev[first:]]
+    kern_bytes = [nb for k in range(skip, a.steps) for nb in nbytes[k * wl.L + first:(k + 1) * wl.L]]
     assert all(torch.isfinite(o).all() for o in outs)
 
     total_bytes = sum(nbytes)
