@@ -178,7 +178,10 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
   const float* qb = qs + 64 + 16 * g4;
   const double* th = thd + 16 * g4;
 
-  float m_run = -INFINITY, l_run = 0.f;
+  // row ceiling (no score seen so far exceeds it), starting from a finite
+  // value below every score so that masked -inf scores weigh 2^-inf = 0
+  constexpr float kNoScore = -3.0e38f;
+  float m_run = kNoScore, l_run = 0.f;
   f32x4 oacc[8];
   f32x4 zacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -186,23 +189,25 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
 
   // online softmax of the 32 scores (lanes 2t and 2t + 1 hold token t);
   // P (fp16) of the query row lands in ptile, l_run keeps this lane's share
-  // of the row sum (even lanes)
+  // of the row sum (even lanes).  The weights are 2^(s - m_run) <= 1 under
+  // the row ceiling; only a block with a score above it (the first, rarely
+  // a later one) reduces the block maximum, moves the ceiling 2 binades above
+  // it and rescales the accumulators.
   auto softmax_tile = [&](float sv) __attribute__((always_inline)) -> half8 {
-    const float bm = wave_max(sv);
-    const float mn = fmaxf(m_run, bm);
-    const float mr = mn == -INFINITY ? 0.f : mn;
-    const float alpha = fexp2(m_run - mr);
-    const _Float16 pt = static_cast<_Float16>(fexp2(sv - mr));
-    l_run = fmaf(l_run, alpha, (l & 1) ? 0.f : static_cast<float>(pt));
-    m_run = mn;
-    if (!(l & 1)) ptile[l >> 1] = pt;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+    if (__builtin_amdgcn_ballot_w64(sv > m_run)) {
+      const float mn = wave_max(sv) + 2.f;
+      const float alpha = fexp2(m_run - mn);  // 0 from the start value
+      m_run = mn;
+      l_run *= alpha;
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) oacc[nt][0] *= alpha;
       zacc[0] *= alpha;
       ocorr[l] *= alpha;
       ocorr[64 + l] *= alpha;
     }
+    const _Float16 pt = static_cast<_Float16>(fexp2(sv - m_run));
+    l_run += (l & 1) ? 0.f : static_cast<float>(pt);
+    if (!(l & 1)) ptile[l >> 1] = pt;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -546,7 +551,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     if (g4 == 0) opart[16 * nt + n16] = o;
   }
   if (l == 0) {
-    mlpart[0] = m_run;
+    mlpart[0] = m_run == kNoScore ? -INFINITY : m_run;  // no live token seen: -inf
     mlpart[1] = lsum;
   }
 }
