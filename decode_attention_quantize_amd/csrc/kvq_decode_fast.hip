@@ -205,6 +205,12 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   const int ftile = kFold == 32 ? g4 >> 1 : g4 & 1;
   const int ftok = n16 + 16 * ftile;
   const int frow = kFold == 32 ? 4 * (g4 & 1) : 8 * (g4 >> 1);
+  // Groups of 8 (or 4) query rows: the value products use the next G rows
+  // of the 16-row MFMA too -- rows 0..G-1 take the hi parts of p * s, rows
+  // G..2G-1 the lo parts of the same query rows -- so each value tile needs
+  // one MFMA instead of two; the split's epilogue adds rows G..2G-1 onto
+  // rows 0..G-1 (lanes 32-63 onto 0-31, or 16-31 onto 0-15).
+  constexpr bool kPackLo = G == 8 || G == 4;
   auto fold = [&](float a, float b) __attribute__((always_inline)) {
     return kFold == 32 ? swap32(a, b).x : swap16(a, b).x;
   };
@@ -348,6 +354,8 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (kPackLo)  // rows G..2G-1 read rows 0..G-1 again
+      return n16 < 2 * G ? *reinterpret_cast<const half8*>(&ptile[n16 & (G - 1)][8 * g4]) : h8(0u, 0u, 0u, 0u);
     return n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
   };
 
@@ -586,13 +594,29 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
     for (int g = 0; g < ngv; ++g) {
       const half8 s8 = h8(vmeta[g]);
       const half8 wh = pa * s8;
-      const half8 wl = __builtin_elementwise_fma(pa, s8, -wh);
+      if constexpr (kPackLo) {
+        // lanes of rows G.. replace their hi part by the lo part under an
+        // exec mask (the empty volatile asm keeps the branch from becoming a
+        // select, which would cost one more VALU operation per word)
+        half8 w = wh;
+        if (n16 >= G) {
+          w = __builtin_elementwise_fma(pa, s8, -wh);
+          asm volatile("" : "+v"(w));
+        }
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int nt = 2 * g + t;
-        const half8 bv = vtile<VB>(unp, vw, nt);
-        oacc[nt] = mfma(wh, bv, oacc[nt]);
-        oacc[nt] = mfma(wl, bv, oacc[nt]);
+        for (int t = 0; t < 2; ++t) {
+          const int nt = 2 * g + t;
+          oacc[nt] = mfma(w, vtile<VB>(unp, vw, nt), oacc[nt]);
+        }
+      } else {
+        const half8 wl = __builtin_elementwise_fma(pa, s8, -wh);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int nt = 2 * g + t;
+          const half8 bv = vtile<VB>(unp, vw, nt);
+          oacc[nt] = mfma(wh, bv, oacc[nt]);
+          oacc[nt] = mfma(wl, bv, oacc[nt]);
+        }
       }
     }
   };
@@ -659,7 +683,8 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       if constexpr (kFold)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sf[i] = fold(sacc[0][i], sacc[1][i]);
-      const half8 pa = kFold ? softmax_fold(sf, kBlockTokens) : softmax_tile(sacc, kBlockTokens);
+      half8 pa = kFold ? softmax_fold(sf, kBlockTokens) : softmax_tile(sacc, kBlockTokens);
+      if constexpr (kPackLo) pa = n16 < G ? pa : h8(0u, 0u, 0u, 0u);  // fp16 values take no lo part
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
       zacc = mfma(pa, n16 == 8 ? h8(kOnes, kOnes, kOnes, kOnes) : h8(0u, 0u, 0u, 0u), zacc);
@@ -781,6 +806,13 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   __builtin_amdgcn_s_setprio(0);
   // ---------------- partial of this split: o = (O_raw - base * W_g) * inv_unit + Z_g,
   // merged by decode_merge_kernel (launched next on the same stream)
+  if constexpr (kPackLo) {
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        oacc[nt][i] += G == 8 ? swap32(oacc[nt][i], oacc[nt][i]).y : swap16(oacc[nt][i], oacc[nt][i]).y;
+  }
   float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * G * D;
   float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * G * 2;
 #pragma unroll
