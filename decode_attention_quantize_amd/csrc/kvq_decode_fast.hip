@@ -116,6 +116,21 @@ __device__ __forceinline__ int kchan(int g4, int j, int kk) {
 }
 
 
+// w <- fma(a, s, -w) per fp16 element, in place: the lo part of a product
+// whose hi part w = fp16(a * s) is already in w.  Written out so that the
+// caller's lane-dependent branch stays an exec-masked branch (an asm
+// statement is not speculated into a select, which would cost one more VALU
+// operation per word) and the negation stays an operand modifier; it is not
+// volatile, so the scheduler may still move it within the block.
+__device__ __forceinline__ void lo_in_place(half8& w, half8 a, half8 s) {
+  u32x4 wv = __builtin_bit_cast(u32x4, w);
+  const u32x4 av = __builtin_bit_cast(u32x4, a), sv = __builtin_bit_cast(u32x4, s);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    asm("v_pk_fma_f16 %0, %1, %2, %0 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "+v"(wv[e]) : "v"(av[e]), "v"(sv[e]));
+  w = __builtin_bit_cast(half8, wv);
+}
+
 // Compile-time record layout of a block (D = 128, value groups of 32, no
 // sparse outliers; MIX: inner groups of 64 with one 8-bit group per token);
 // the launcher checks it against the layer's layout.
@@ -205,12 +220,16 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   const int ftile = kFold == 32 ? g4 >> 1 : g4 & 1;
   const int ftok = n16 + 16 * ftile;
   const int frow = kFold == 32 ? 4 * (g4 & 1) : 8 * (g4 >> 1);
-  // Groups of 8 (or 4) query rows: the value products use the next G rows
+  // Groups of 8, 4 or 1 query rows: the value products use the next G rows
   // of the 16-row MFMA too -- rows 0..G-1 take the hi parts of p * s, rows
   // G..2G-1 the lo parts of the same query rows -- so each value tile needs
   // one MFMA instead of two; the split's epilogue adds rows G..2G-1 onto
-  // rows 0..G-1 (lanes 32-63 onto 0-31, or 16-31 onto 0-15).
-  constexpr bool kPackLo = G == 8 || G == 4;
+  // rows 0..G-1 (lanes 32-63 onto 0-31, 16-31 onto 0-15, or row 1 onto row
+  // 0 in the same lanes).  A single query row with per-channel keys packs
+  // the key products q * s the same way (row 1 of the score tiles, added
+  // to row 0 before the softmax).
+  constexpr bool kPackLo = G == 8 || G == 4 || G == 1;
+  constexpr bool kPackK = G == 1 && !INNER;
   auto fold = [&](float a, float b) __attribute__((always_inline)) {
     return kFold == 32 ? swap32(a, b).x : swap16(a, b).x;
   };
@@ -232,8 +251,8 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // ---- query operand (natural channel order per K-step)
   half8 qa[4];
   {
-    const bool live = n16 < G;
-    const uint16_t* qp = J.q + (static_cast<int64_t>(b) * L.Hq + h * G + (live ? n16 : 0)) * D;
+    const bool live = n16 < (kPackK ? 2 : G);  // packed keys: row 1 holds row 0 again
+    const uint16_t* qp = J.q + (static_cast<int64_t>(b) * L.Hq + h * G + (n16 < G ? n16 : 0)) * D;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4 v = ld16(qp + kchan<INNER>(g4, j, 0));
@@ -291,6 +310,10 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
         for (int i = 0; i < RI; ++i) oacc[nt][i] *= alpha[i];
+      if constexpr (kPackLo && G == 1) {
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) oacc[nt][1] *= alpha[0];  // row 1: lo parts of row 0
+      }
 #pragma unroll
       for (int i = 0; i < RI; ++i) zacc[i] *= alpha[i];
     }
@@ -303,6 +326,8 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (kPackLo)  // rows G..2G-1 read rows 0..G-1 again
+      return n16 < 2 * G ? *reinterpret_cast<const half8*>(&ptile[n16 & (G - 1)][8 * g4]) : h8(0u, 0u, 0u, 0u);
     return n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
   };
 
@@ -450,19 +475,31 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
         const float cs = n16 < 8 ? other : cacc[i];
         init[i] = fmaf(cz, 1.f / iu, -base * cs);
       }
+      if constexpr (kPackK) init[1] = 0.f;  // row 1 accumulates the lo parts only
       sacc[0] = init;
       sacc[1] = init;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const half8 s8 = h8(kmeta[4 + j]);
-        const half8 qh = qa[j] * s8;
-        const half8 ql = __builtin_elementwise_fma(qa[j], s8, -qh);
+        if constexpr (kPackK) {
+          half8 w = qa[j] * s8;
+          if (n16 >= 1) lo_in_place(w, qa[j], s8);  // row 1: the lo part
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const half8 bk = kstep<KB>(unp, kw[nt], j);
-          sacc[nt] = mfma(qh, bk, sacc[nt]);
-          sacc[nt] = mfma(ql, bk, sacc[nt]);
+          for (int nt = 0; nt < 2; ++nt) sacc[nt] = mfma(w, kstep<KB>(unp, kw[nt], j), sacc[nt]);
+        } else {
+          const half8 qh = qa[j] * s8;
+          const half8 ql = __builtin_elementwise_fma(qa[j], s8, -qh);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const half8 bk = kstep<KB>(unp, kw[nt], j);
+            sacc[nt] = mfma(qh, bk, sacc[nt]);
+            sacc[nt] = mfma(ql, bk, sacc[nt]);
+          }
         }
+      }
+      if constexpr (kPackK) {
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) sacc[nt][0] += sacc[nt][1];
       }
       if constexpr (kFold) {
 #pragma unroll
@@ -593,22 +630,17 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
     for (int g = 0; g < ngv; ++g) {
       const half8 s8 = h8(vmeta[g]);
-      const half8 wh = pa * s8;
       if constexpr (kPackLo) {
-        // lanes of rows G.. replace their hi part by the lo part under an
-        // exec mask (the empty volatile asm keeps the branch from becoming a
-        // select, which would cost one more VALU operation per word)
-        half8 w = wh;
-        if (n16 >= G) {
-          w = __builtin_elementwise_fma(pa, s8, -wh);
-          asm volatile("" : "+v"(w));
-        }
+        // lanes of rows G.. replace their hi part by the lo part (exec-masked)
+        half8 w = pa * s8;
+        if (n16 >= G) lo_in_place(w, pa, s8);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int nt = 2 * g + t;
           oacc[nt] = mfma(w, vtile<VB>(unp, vw, nt), oacc[nt]);
         }
       } else {
+        const half8 wh = pa * s8;
         const half8 wl = __builtin_elementwise_fma(pa, s8, -wh);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -810,8 +842,11 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        oacc[nt][i] += G == 8 ? swap32(oacc[nt][i], oacc[nt][i]).y : swap16(oacc[nt][i], oacc[nt][i]).y;
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (G == 8) oacc[nt][i] += swap32(oacc[nt][i], oacc[nt][i]).y;
+        else if constexpr (G == 4) oacc[nt][i] += swap16(oacc[nt][i], oacc[nt][i]).y;
+        else if (i == 0) oacc[nt][0] += oacc[nt][1];
+      }
   }
   float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * G * D;
   float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * G * 2;
