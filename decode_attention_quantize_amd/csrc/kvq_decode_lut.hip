@@ -200,7 +200,10 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       m_run = mn;
       l_run *= alpha;
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) oacc[nt][0] *= alpha;
+      for (int nt = 0; nt < 8; ++nt) {
+        oacc[nt][0] *= alpha;
+        oacc[nt][1] *= alpha;  // row 1: the lo parts of the value products
+      }
       zacc[0] *= alpha;
       ocorr[l] *= alpha;
       ocorr[64 + l] *= alpha;
@@ -211,7 +214,8 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    return n16 == 0 ? *reinterpret_cast<const half8*>(&ptile[8 * g4]) : h8(0u, 0u, 0u, 0u);
+    // row 1 reads row 0 again: it carries the lo parts of the value products
+    return n16 < 2 ? *reinterpret_cast<const half8*>(&ptile[8 * g4]) : h8(0u, 0u, 0u, 0u);
   };
   // sum over the four lanes that hold one token's partial dots
   auto lanes4_sum = [&](float v) __attribute__((always_inline)) {
@@ -290,8 +294,9 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       // token l/2 of the chunk: tile (l/2)/16, lane (l/2)%16 of row 0
       const float sa0 = lane_bcast(sc[0], (l >> 1) & 15), sa1 = lane_bcast(sc[1], (l >> 1) & 15);
       const half8 pa = softmax_tile(l < 32 ? sa0 : sa1);
+      const half8 p0 = n16 == 0 ? pa : h8(0u, 0u, 0u, 0u);  // fp16 values: no lo row
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
+      for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(p0, h8(vv[nt]), oacc[nt]);
     }
   }
 
@@ -440,15 +445,14 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     zacc = mfma(pa, n16 < 8 ? h8(vmeta[4]) : h8(0u, 0u, 0u, 0u), zacc);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const half8 s8 = h8(vmeta[g]);
-      const half8 wh = pa * s8;
-      const half8 wl = __builtin_elementwise_fma(pa, s8, -wh);
+      // row 0: hi parts of p * s, row 1: lo parts (added at the end), one MFMA per tile
+      half8 w = pa * h8(vmeta[g]);
+      if (n16 >= 1) lo_in_place(w, pa, h8(vmeta[g]));
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
         const int nt = 2 * g + t2;
         const half8 bv = h8(vl[4 * nt], vl[4 * nt + 1], vl[4 * nt + 2], vl[4 * nt + 3]);
-        oacc[nt] = mfma(wh, bv, oacc[nt]);
-        oacc[nt] = mfma(wl, bv, oacc[nt]);
+        oacc[nt] = mfma(w, bv, oacc[nt]);
       }
     }
 
@@ -547,7 +551,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) {
     const float z = lane_bcast(zacc[0], (l & 48) | (nt >> 1));
-    const float o = oacc[nt][0] + z + ocorr[16 * nt + n16];
+    const float o = (oacc[nt][0] + oacc[nt][1]) + z + ocorr[16 * nt + n16];
     if (g4 == 0) opart[16 * nt + n16] = o;
   }
   if (l == 0) {

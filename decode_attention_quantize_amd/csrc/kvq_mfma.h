@@ -89,6 +89,21 @@ __device__ __forceinline__ float lane_bcast(float v, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
+// w <- fma(a, s, -w) per fp16 element, in place: the lo part of a product
+// whose hi part w = fp16(a * s) is already in w.  Written out so that the
+// caller's lane-dependent branch stays an exec-masked branch (an asm
+// statement is not speculated into a select, which would cost one more VALU
+// operation per word) and the negation stays an operand modifier; it is not
+// volatile, so the scheduler may still move it within the block.
+__device__ __forceinline__ void lo_in_place(half8& w, half8 a, half8 s) {
+  u32x4 wv = __builtin_bit_cast(u32x4, w);
+  const u32x4 av = __builtin_bit_cast(u32x4, a), sv = __builtin_bit_cast(u32x4, s);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    asm("v_pk_fma_f16 %0, %1, %2, %0 neg_lo:[0,0,1] neg_hi:[0,0,1]" : "+v"(wv[e]) : "v"(av[e]), "v"(sv[e]));
+  w = __builtin_bit_cast(half8, wv);
+}
+
 // Reads of the LDS ring filled by global_load_lds.  They are issued as
 // inline-asm ds_reads: the compiler's wait insertion cannot see through the
 // DMA writes precisely (it would drain every in-flight block), so the ring is
