@@ -452,15 +452,16 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) cacc = mfma(qa[j], h8(kmeta[j]), cacc);
-      f32x4 init;
+      // rows past the lane's query rows start from 0 (with a packed single
+      // row, row 1 accumulates the lo parts only)
+      f32x4 init = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < RI; ++i) {
         const float other = dppf<kRowRor8>(cacc[i]);
         const float cz = n16 < 8 ? cacc[i] : other;
         const float cs = n16 < 8 ? other : cacc[i];
         init[i] = fmaf(cz, 1.f / iu, -base * cs);
       }
-      if constexpr (kPackK) init[1] = 0.f;  // row 1 accumulates the lo parts only
       sacc[0] = init;
       sacc[1] = init;
 #pragma unroll
