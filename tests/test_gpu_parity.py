@@ -62,6 +62,11 @@ EDGE = {
     "gqa8-kv8-peaky": W.C3.with_(L=1, B=1, Hq=8, Hkv=1, T=600, steps=2, fixed_pairs=((8, 8),),
                                  q_scale=3.0),
     "mha-kv8-peaky": W.C2.with_(Hq=2, Hkv=2, T=600, steps=2, fixed_pairs=((8, 8),), q_scale=3.0),
+    # single-row layers with the key and value products packed into rows 0 and 1 of the
+    # matrix-core tiles, at the other key/value widths (2-bit keys with 8-bit values and
+    # the reverse), with sinks, a window and a flush during the decode steps
+    "mha-k2v8": W.C2.with_(Hq=2, Hkv=2, T=700, steps=40, fixed_pairs=((2, 8),)),
+    "mha-k8v2": W.C2.with_(Hq=2, Hkv=2, T=700, steps=40, fixed_pairs=((8, 2),)),
 }
 
 
