@@ -271,10 +271,12 @@ void quant_nuq(const uint16_t* x, const uint8_t* excl, int n, const uint16_t* le
 // ascending column order.
 void topk_cols(const uint16_t* row, int d, int k, int32_t* cols) {
   std::vector<int32_t> idx(d);
-  for (int i = 0; i < d; ++i) idx[i] = i;
-  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
-    return std::fabs(f16_to_f64(row[a])) > std::fabs(f16_to_f64(row[b]));
-  });
+  std::vector<double> mag(d);  // |x| widened once per element
+  for (int i = 0; i < d; ++i) {
+    idx[i] = i;
+    mag[i] = std::fabs(f16_to_f64(row[i]));
+  }
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return mag[a] > mag[b]; });
   std::vector<int32_t> top(idx.begin(), idx.begin() + k);
   std::sort(top.begin(), top.end());
   for (int i = 0; i < k; ++i) cols[i] = top[i];
@@ -288,9 +290,11 @@ inline int had(int i, int j) { return (__builtin_popcount(static_cast<unsigned>(
 // terms is exact) and c = fl64(1/sqrt(d)).
 void hadamard_fp16(const uint16_t* v, int d, uint16_t* out) {
   const double c = 1.0 / std::sqrt(static_cast<double>(d));
+  std::vector<double> x(d);
+  for (int j = 0; j < d; ++j) x[j] = f16_to_f64(v[j]);  // exact widening, once per element
   for (int i = 0; i < d; ++i) {
     double s = 0.0;
-    for (int j = 0; j < d; ++j) s += had(i, j) * f16_to_f64(v[j]);
+    for (int j = 0; j < d; ++j) s += had(i, j) * x[j];
     out[i] = f64_to_f16(s * c);
   }
 }
@@ -386,10 +390,18 @@ void oq_state_prefill(int32_t n, int32_t S, int32_t W, int32_t F, int32_t* s_eff
   *r = n - se - body;
 }
 
-// One appended token: returns 1 when the oldest F window tokens were flushed
-// into the body.
-int32_t oq_state_append(int32_t* n, int32_t* nb, int32_t* r, int32_t W, int32_t F) {
+// One appended token.  The first S positions are the sink tokens, kept in
+// fp16 whatever the prompt length: while fewer than S sinks exist (a prompt
+// shorter than S), the token becomes the next sink.  Otherwise it enters the
+// window; when the window reaches W + F tokens its oldest F are flushed into
+// the body.  Returns 1 on a flush.
+int32_t oq_state_append(int32_t* n, int32_t* s_eff, int32_t* nb, int32_t* r, int32_t S, int32_t W,
+                        int32_t F) {
   *n += 1;
+  if (*s_eff < S) {  // only reachable with an empty body and window
+    *s_eff += 1;
+    return 0;
+  }
   *r += 1;
   if (*r == W + F) {
     *nb += F;

@@ -70,7 +70,7 @@ def lib():
             L.oq_dequant.argtypes = [C.c_uint8, C.c_uint16, C.c_uint16, C.c_int32, u16p]
             L.oq_dequant.restype = C.c_double
             L.oq_state_prefill.argtypes = [C.c_int32] * 4 + [i32p] * 3
-            L.oq_state_append.argtypes = [i32p, i32p, i32p, C.c_int32, C.c_int32]
+            L.oq_state_append.argtypes = [i32p, i32p, i32p, i32p, C.c_int32, C.c_int32, C.c_int32]
             L.oq_state_append.restype = C.c_int32
             L.oq_encode_unit.argtypes = [C.POINTER(OScheme), u16p, u16p, C.c_int32, C.c_int32,
                                          C.c_int32, u16p, u8p, u16p, u8p, u16p, i32p, u16p, i32p, u16p,
@@ -186,10 +186,11 @@ def state_prefill(n, S, W, F):
     return a.value, b.value, c.value
 
 
-def state_append(n, nb, r, W, F):
-    a, b, c = C.c_int32(n), C.c_int32(nb), C.c_int32(r)
-    f = lib().oq_state_append(C.byref(a), C.byref(b), C.byref(c), W, F)
-    return a.value, b.value, c.value, bool(f)
+def state_append(n, s_eff, nb, r, S, W, F):
+    """One appended token: (n, s_eff, nb, r, flushed)."""
+    a, se, b, c = C.c_int32(n), C.c_int32(s_eff), C.c_int32(nb), C.c_int32(r)
+    f = lib().oq_state_append(C.byref(a), C.byref(se), C.byref(b), C.byref(c), S, W, F)
+    return a.value, se.value, b.value, c.value, bool(f)
 
 
 # ---------------------------------------------------------------- unit level
@@ -341,7 +342,7 @@ def unit_inputs(wl, layer, b, h, n_total):
 def run_unit(wl, layer, b, h, steps=None, only_steps=None):
     """Oracle for one unit through prefill and the decode steps.
 
-    Returns dict(states=[(n, nb, r)], out={step: [Gq][D] float64}, enc=final
+    Returns dict(states=[(n, s_eff, nb, r)], out={step: [Gq][D] float64}, enc=final
     encoding, s_eff, n_final, nb_final).  The body encoding at any step is a
     prefix of the final one (blocks are pure functions of their tokens), so the
     cache is encoded once and each step dequantizes its own prefix.
@@ -356,9 +357,9 @@ def run_unit(wl, layer, b, h, steps=None, only_steps=None):
     states = []
     for i in range(steps):
         if wl.append:
-            n, nb, r, _ = state_append(n, nb, r, wl.window, F)
-        states.append((n, nb, r))
-    nb_final = states[-1][1] if states else nb
+            n, s_eff, nb, r, _ = state_append(n, s_eff, nb, r, wl.sinks, wl.window, F)
+        states.append((n, s_eff, nb, r))
+    nb_final = states[-1][2] if states else nb
     n_final = states[-1][0] if states else n
     kshift = None
     Kq = K
@@ -371,13 +372,13 @@ def run_unit(wl, layer, b, h, steps=None, only_steps=None):
     Kf, Vf = dequant_unit(sc, K, enc, n_final, s_eff, nb_final, kshift=kshift)
     gq = wl.gq
     outs = {}
-    for i, (n_i, nb_i, r_i) in enumerate(states):
+    for i, (n_i, se_i, nb_i, r_i) in enumerate(states):
         if only_steps is not None and i not in only_steps:
             continue
         Kh, Vh = Kf[:n_i].copy(), Vf[:n_i].copy()
-        lo = s_eff + nb_i
+        lo = se_i + nb_i
         if lo < n_i:
-            dequant_unit(sc, K, enc, n_i, s_eff, nb_i, lo, n_i, Kh, Vh, kshift=kshift)
+            dequant_unit(sc, K, enc, n_i, se_i, nb_i, lo, n_i, Kh, Vh, kshift=kshift)
         q = wl.q(layer, i, b0=b, b1=b + 1, h0=h * gq, h1=(h + 1) * gq).reshape(gq, wl.D)
         outs[i] = attention(q.double().numpy(), Kh, Vh, unrotate=bool(wl.v_hadamard))
     return dict(states=states, out=outs, enc=enc, s_eff=s_eff, n_final=n_final,

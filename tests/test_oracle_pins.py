@@ -361,22 +361,33 @@ def test_state_machine_closed_forms():
     assert (s, nb, r) == (4, 32608, 156)
     n, flushes = 32768, []
     for step in range(1, 65):
-        n, nb, r, f = O.state_append(n, nb, r, 128, 32)
+        n, s, nb, r, f = O.state_append(n, s, nb, r, 4, 128, 32)
         if f:
             flushes.append(step)
-        assert 128 <= r < 160
+        assert 128 <= r < 160 and s == 4
     assert flushes == [4, 36] and (nb, r) == (32672, 156)
     s, nb, r = O.state_prefill(8192, 0, 0, 32)                         # C3
     flushes = []
     n = 8192
     for step in range(1, 65):
-        n, nb, r, f = O.state_append(n, nb, r, 0, 32)
+        n, s, nb, r, f = O.state_append(n, s, nb, r, 0, 0, 32)
         flushes += [step] if f else []
     assert flushes == [32, 64] and r == 0 and nb == 8256
     s, nb, r = O.state_prefill(16384, 0, 0, 1)                         # C5: every token quantized
     assert (nb, r) == (16384, 0)
-    assert O.state_append(16384, 16384, 0, 0, 1) == (16385, 16385, 0, True)
+    assert O.state_append(16384, 0, 16384, 0, 0, 0, 1) == (16385, 0, 16385, 0, True)
     assert O.state_prefill(3, 4, 128, 32) == (3, 0, 0)                 # short prompt: all sinks
+    # a prompt shorter than S: the next appended tokens complete the sinks
+    # (the first S positions stay fp16), then the window fills and flushes
+    n, s, nb, r = 3, 3, 0, 0
+    n, s, nb, r, f = O.state_append(n, s, nb, r, 4, 32, 32)
+    assert (n, s, nb, r, f) == (4, 4, 0, 0, False)
+    flushes = []
+    for step in range(2, 71):
+        n, s, nb, r, f = O.state_append(n, s, nb, r, 4, 32, 32)
+        flushes += [step] if f else []
+        assert s == 4 and n == s + nb + r
+    assert flushes == [65] and (nb, r) == (32, 37)
     with open(os.path.join(GOLDEN, "state_examples.json")) as f:
         for c in json.load(f)["cases"]:
             got = O.state_prefill(c["n"], c["S"], c["W"], c["F"])
