@@ -1,19 +1,22 @@
 """Benchmark: fused dequant decode attention over the packed KV cache.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C2|C3|C4|C5]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload C3|C2|C4|C5|...]
 
 A step is one pass of the hot path for every layer in the stack: append one
 token (quantizing a flush block when due) and decode attention of one query
-per head over the whole packed cache.  The default workload is the Llama-7B
-shaped MHA layer (32 heads, d=128, 32768-token context, keys 4-bit per
-channel, values 2-bit per token, 4 sink + 128 recent fp16 tokens), run as a
-stack of 8 independent layer caches so that consecutive decodes read HBM
-rather than the 256 MB Infinity Cache.
+per head over the whole packed cache.  The default workload is the largest
+one: the Llama-3-8B shaped GQA stack (32 layers, batch 16, 32 query / 8 KV
+heads, d=128, 8192-token context, each layer's (key, value) bit pair drawn
+by seed from {KV8, K8V4, KV4, K4V2, KV2}); its 32 layer caches (about 6.6 GB
+of packed cache) also keep consecutive decodes reading HBM rather than the
+256 MB Infinity Cache.
 
-The JSON line reports effective KV GB/s (algorithmic bytes of the decode,
-whole-job over the timed steps), decode tokens/s per layer, the decode
-kernel's roofline fraction (bytes per launch / event-timed launch duration,
-against 8 TB/s HBM) and the CPU oracle timed on this host on a bounded sample.
+The JSON line reports effective KV GB/s (algorithmic bytes of the decodes,
+whole-job over the timed steps, appends included in the wall time), decode
+tokens/s per layer, the decode's roofline fraction (algorithmic bytes per
+launch over the HIP-event-timed duration of the decode call: split kernel +
+log-sum-exp merge), the prefill (quantize/pack) throughput, and the CPU
+oracle timed on this host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -36,12 +39,13 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=64)
     p.add_argument("--warmup", type=int, default=8)
-    p.add_argument("--workload", default="C2",
+    p.add_argument("--workload", default="C3",
                    help="C1..C5, or a scheme variant: C5n (key normalization), C5m (mixed 4/8-bit "
                         "key groups), P5 (Hadamard 2-bit values on C2's layer), P5t (ternary values)")
     p.add_argument("--layers", type=int, default=None, help="layer caches in the stack")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="oracle time on all host threads (plus a third of it on one thread)")
     p.add_argument("--copy-calib", type=int, default=0,
                    help="only run a plain device copy of this many bytes (counter calibration)")
     return p.parse_args()
@@ -98,9 +102,29 @@ def traffic_record(name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Threads for the oracle: the host's CPUs available to this process,
+    at most 16 (one GPU's share of the host on the machines this runs on)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def cpu_baseline(wl, seconds):
-    """The oracle (as it stands) decoding sampled units of one step on this host."""
-    import numpy as np
+    """The oracle (as it stands) decoding sampled units of one step on this
+    host: all threads, then one thread."""
     from concurrent.futures import ThreadPoolExecutor
     import oracle as O
 
@@ -109,7 +133,7 @@ def cpu_baseline(wl, seconds):
     F = wl.flush
     s_eff, nb, r = O.state_prefill(wl.T, wl.sinks, wl.window, F)
     n = wl.T
-    cores = max(1, min(os.cpu_count() or 1, 16))
+    cores = host_threads()
     units = list(range(min(wl.units, 2 * cores)))
     prepared = []
     for u in units:
@@ -126,18 +150,39 @@ def cpu_baseline(wl, seconds):
 
     per_unit_bytes = (decode_bytes(wl, layer, n, s_eff, nb, r) - wl.B * wl.Hq * wl.D * 6) / wl.units \
         + wl.gq * wl.D * 6
-    done, t0 = 0, time.perf_counter()
-    with ThreadPoolExecutor(cores) as ex:
-        while True:
-            list(ex.map(one, prepared))
-            done += len(prepared)
-            if time.perf_counter() - t0 >= seconds:
-                break
-    dt = time.perf_counter() - t0
-    return {"value": round(per_unit_bytes * done / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"{done} (batch, kv-head) unit decodes of step 0 of {wl.name} "
-                      f"(dequantize {n} tokens in binary64 + attention), {cores} threads, {dt:.1f} s"}
+
+    def timed(threads, budget, items):
+        done, t0 = 0, time.perf_counter()
+        with ThreadPoolExecutor(threads) as ex:
+            while True:
+                list(ex.map(one, items))
+                done += len(items)
+                if time.perf_counter() - t0 >= budget:
+                    break
+        dt = time.perf_counter() - t0
+        return per_unit_bytes * done / dt / 1e9, done, dt
+
+    gbs, done, dt = timed(cores, seconds, prepared)
+    gbs1, done1, dt1 = timed(1, seconds / 3, prepared[:1])
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "one_core_value": round(gbs1, 4),
+            "sample": f"{done} (batch, kv-head) unit decodes of step 0 of layer 0 of {wl.name} "
+                      f"(dequantize {n} tokens in binary64 + attention), {cores} threads, {dt:.1f} s; "
+                      f"one thread: {done1} unit decodes in {dt1:.1f} s"}
+
+
+def prefill_bytes(wl, layer, T, s_eff, nb, r):
+    """Bytes one prefill of T tokens must move: read fp16 K and V of the
+    prompt, write the nb packed body tokens and the s_eff + r fp16 sink /
+    window tokens."""
+    kb, vb = wl.bit_pairs()[layer]
+    D = wl.D
+    body = nb * D * (kb + vb) / 8
+    body += ((nb // 32) * D * 4) if wl.k_mode == "channel" else nb * (D // wl.k_group) * 4
+    body += nb * (D // wl.v_group) * 4 + nb * wl.outliers * 4 * 2
+    if wl.k_mode == "inner" and kb == 4 and wl.k_hi_groups:
+        body += nb * (wl.k_hi_groups * wl.k_group // 2 + 1)
+    return wl.units * (T * D * 2 * 2 + body + (s_eff + r) * D * 2 * 2)
 
 
 def copy_calibration(nbytes):
@@ -161,7 +206,7 @@ def main():
         return
     import torch
     from decode_attention_quantize_amd import build as kb
-    if not os.path.exists(kb.OUT):
+    if kb.is_stale():
         kb.build()
     from decode_attention_quantize_amd import KVQCache, config_from_workload
 
@@ -174,10 +219,24 @@ def main():
     cfg = config_from_workload(wl, max_tokens=wl.T + total_steps)
     cache = KVQCache(cfg, wl.bit_pairs(), wl.codebooks(), device=dev)
     B, Hkv, T, D = wl.B, wl.Hkv, wl.T, wl.D
+    stream = torch.cuda.current_stream(dev)
+    # prefill: the first layer's prompt is quantized twice (the first pass
+    # loads the kernels), then every layer's prefill is timed with events
+    pre_ms, pre_bytes = [], []
     for l in range(wl.L):
         k = wl.k(l, 0, B, 0, Hkv, 0, T, device=dev).contiguous()
         v = wl.v(l, 0, B, 0, Hkv, 0, T, device=dev).contiguous()
+        if l == 0:
+            cache.prefill(l, k, v)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
         cache.prefill(l, k, v)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pre_ms.append(e0.elapsed_time(e1))
+        _, s_eff0, nb0, r0 = cache.state(l)
+        pre_bytes.append(prefill_bytes(wl, l, T, s_eff0, nb0, r0))
         del k, v
     torch.cuda.synchronize()
     # per-step inputs, generated before timing
@@ -191,7 +250,6 @@ def main():
             row.append((kt, vt, q))
         steps_in.append(row)
     outs = [torch.empty(B, wl.Hq, D, dtype=torch.float32, device=dev) for _ in range(wl.L)]
-    stream = torch.cuda.current_stream(dev)
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(wl.L)] for _ in range(a.steps)]
 
@@ -233,7 +291,19 @@ def main():
     skip = 0 if wl.L > 1 or a.steps < 2 else 1
     kern_ms = [e0.elapsed_time(e1) for ev in events[skip:] for (e0, e1) in ev[first:]]
     kern_bytes = [nb for k in range(skip, a.steps) for nb in nbytes[k * wl.L + first:(k + 1) * wl.L]]
+    kern_layer = [l for k in range(skip, a.steps) for l in range(first, wl.L)]
     assert all(torch.isfinite(o).all() for o in outs)
+    assert cache.nonfinite_rows() == 0
+    # per (key, value) bit pair: mean decode call time and its roofline fraction
+    by_pair = {}
+    for ms, nb_, l in zip(kern_ms, kern_bytes, kern_layer):
+        kb_, vb_ = wl.bit_pairs()[l]
+        key = f"K{kb_}V{vb_}"
+        t_, b_, c_ = by_pair.get(key, (0.0, 0.0, 0))
+        by_pair[key] = (t_ + ms, b_ + nb_, c_ + 1)
+    pairs_line = {k: {"us": round(t_ / c_ * 1e3, 2), "mb": round(b_ / c_ / 1e6, 2),
+                      "frac": round(b_ / (t_ / 1e3) / 1e9 / HBM_PEAK_GBS, 4), "launches": c_}
+                  for k, (t_, b_, c_) in sorted(by_pair.items())}
 
     total_bytes = sum(nbytes)
     value = total_bytes / dt / 1e9
@@ -254,7 +324,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": f"{wl.name}: B={B} Hq={wl.Hq} Hkv={Hkv} D={D} context={T}+steps, "
@@ -264,9 +334,18 @@ def main():
             "batch": B,
             "context": T,
         },
+        "arith": "fp16 matrix-core operands (codes, q and p*s as exact hi+lo pairs), fp32 accumulation "
+                 "and softmax",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "tokens_per_s_per_layer": round(tokens_per_s_layer, 1),
-        "decode_kernel_us": round(avg_kernel_s * 1e6, 2),
+        "decode_call_us": round(avg_kernel_s * 1e6, 2),
+        "decode_by_pair": pairs_line,
+        "prefill": {"gbs": round(sum(pre_bytes) / (sum(pre_ms) / 1e3) / 1e9, 1),
+                    "frac": round(sum(pre_bytes) / (sum(pre_ms) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "ms_per_layer": round(sum(pre_ms) / len(pre_ms), 3),
+                    "mb_per_layer": round(sum(pre_bytes) / len(pre_bytes) / 1e6, 1),
+                    "what": "kvq_quantize_prefill of each layer's prompt: fp16 K/V read + packed cache "
+                            "and fp16 sinks/window written, HIP events"},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -275,7 +354,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "bytes_per_launch": round(bytes_per_launch),
-            "kernel": "kvq_decode_attn (split-context decode + log-sum-exp merge)",
+            "kernel": "kvq_decode_attn call: split-context decode kernel + log-sum-exp merge kernel "
+                      "(HIP events around the call, launch gap included)",
             "timed_launches": len(kern_ms),
         },
     }

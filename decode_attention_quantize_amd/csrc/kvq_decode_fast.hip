@@ -165,7 +165,7 @@ template <int KB, int VB, int G, bool INNER, bool MIX>
 constexpr int waves_per_simd() {
   return (G >= 4 && (VB == 2 || (VB == 4 && !INNER && KB != 8))) ? 3 : 1;
 }
-template <int KB, int VB, int G, bool INNER, bool MIX, int NBUF>
+template <int KB, int VB, int G, bool INNER, bool MIX, int NBUF, bool PLO>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KB, VB, G, INNER, MIX>())))
 decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   using R = Rec<KB, VB, INNER, MIX>;
@@ -185,6 +185,9 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
     return k == 0 ? slot0 : (k == 1 ? slot1 : (k == 2 ? slot2 : slot3));
   };
   __shared__ __attribute__((aligned(16))) _Float16 ptile[16][32];
+  // PLO: the weights' residuals fp16(p - fp16(p)), so that P enters the
+  // value products as a hi + lo pair too (rows G..2G-1 of the value tiles)
+  __shared__ __attribute__((aligned(16))) _Float16 plo[PLO ? 16 : 1][32];
   const int l = threadIdx.x;
   const int n16 = l & 15, g4 = l >> 4;
   const int nsplit = J.nsplit;
@@ -215,6 +218,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // to row 0 before the softmax).
   constexpr bool kPackLo = G == 8 || G == 4 || G == 1;
   constexpr bool kPackK = G == 1 && !INNER;
+  static_assert(!PLO || kPackLo, "the weights' lo parts ride in the packed lo rows");
   auto fold = [&](float a, float b) __attribute__((always_inline)) {
     return kFold == 32 ? swap32(a, b).x : swap16(a, b).x;
   };
@@ -271,7 +275,26 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // folded variant below for the reasons and the weight lift).
   constexpr float kPad = 2.f;
   constexpr float kLift = VB == 8 ? 6.f : (VB == 4 ? 2.f : 0.f);
-  auto softmax_tile = [&](f32x4 (&sacc)[2], int count) __attribute__((always_inline)) -> half8 {
+  // Each softmax returns the block's P operands: pa (rows 0..2G-1 hold the
+  // fp16 weights of rows 0..G-1, twice) and pz (rows 0..G-1 the same weights;
+  // with PLO rows G..2G-1 their residuals, else pa again).
+  struct POps {
+    half8 pa, pz;
+  };
+  // lanes of rows G..2G-1 read the residual tile, the others the weights
+  const _Float16* const pz_row = PLO && n16 >= G && n16 < 2 * G ? &plo[n16 & (G - 1)][8 * g4]
+                                                                 : &ptile[n16 & (G - 1)][8 * g4];
+  auto p_operands = [&]() __attribute__((always_inline)) -> POps {
+    if constexpr (kPackLo) {  // rows G..2G-1 read rows 0..G-1 again
+      const bool live = n16 < 2 * G;
+      const half8 pa = live ? *reinterpret_cast<const half8*>(&ptile[n16 & (G - 1)][8 * g4]) : h8(0u, 0u, 0u, 0u);
+      if constexpr (PLO) return POps{pa, live ? *reinterpret_cast<const half8*>(pz_row) : h8(0u, 0u, 0u, 0u)};
+      return POps{pa, pa};
+    }
+    const half8 pa = n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
+    return POps{pa, pa};
+  };
+  auto softmax_tile = [&](f32x4 (&sacc)[2], int count) __attribute__((always_inline)) -> POps {
     if (count < kBlockTokens) {  // wave-uniform: only a partial last block
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
@@ -298,6 +321,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       if constexpr (kPackLo && G == 1) {
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) oacc[nt][1] *= alpha[0];  // row 1: lo parts of row 0
+        if constexpr (PLO) zacc[1] *= alpha[0];
       }
 #pragma unroll
       for (int i = 0; i < RI; ++i) zacc[i] *= alpha[i];
@@ -305,15 +329,18 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
     for (int i = 0; i < RI; ++i) {
       // every lane writes its rows; rows past the query group are never read
-      ptile[4 * g4 + i][n16] = static_cast<_Float16>(fexp2(sacc[0][i] - (m_run[i] - kLift)));
-      ptile[4 * g4 + i][16 + n16] = static_cast<_Float16>(fexp2(sacc[1][i] - (m_run[i] - kLift)));
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const float p = fexp2(sacc[nt][i] - (m_run[i] - kLift));
+        const _Float16 ph = static_cast<_Float16>(p);
+        ptile[4 * g4 + i][16 * nt + n16] = ph;
+        if constexpr (PLO) plo[4 * g4 + i][16 * nt + n16] = static_cast<_Float16>(p - static_cast<float>(ph));
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if constexpr (kPackLo)  // rows G..2G-1 read rows 0..G-1 again
-      return n16 < 2 * G ? *reinterpret_cast<const half8*>(&ptile[n16 & (G - 1)][8 * g4]) : h8(0u, 0u, 0u, 0u);
-    return n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
+    return p_operands();
   };
 
   // the same on a folded block (kFold): s[i] is the score of row frow + i
@@ -329,7 +356,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // into the fp16 subnormals for tokens a few binades below the ceiling, and
   // the hi + lo pair would lose its precision.  The lift keeps p * s within
   // fp16 for any fp16 value range (s <= 131008 / (2^VB - 1)).
-  auto softmax_fold = [&](f32x4 s, int count) __attribute__((always_inline)) -> half8 {
+  auto softmax_fold = [&](f32x4 s, int count) __attribute__((always_inline)) -> POps {
     if (count < kBlockTokens) {  // wave-uniform: only a partial last block
       if (ftok >= count)
 #pragma unroll
@@ -359,14 +386,15 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // rows past the query group (fold by 16: rows 8-11) are never read
-      ptile[frow + i][ftok] = static_cast<_Float16>(fexp2(s[i] - (m_run[i] - kLift)));
+      const float p = fexp2(s[i] - (m_run[i] - kLift));
+      const _Float16 ph = static_cast<_Float16>(p);
+      ptile[frow + i][ftok] = ph;
+      if constexpr (PLO) plo[frow + i][ftok] = static_cast<_Float16>(p - static_cast<float>(ph));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if constexpr (kPackLo)  // rows G..2G-1 read rows 0..G-1 again
-      return n16 < 2 * G ? *reinterpret_cast<const half8*>(&ptile[n16 & (G - 1)][8 * g4]) : h8(0u, 0u, 0u, 0u);
-    return n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
+    return p_operands();
   };
 
   // one quantized block whose record sits in LDS at rec
@@ -606,20 +634,26 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
       for (int e = 0; e < 5; ++e) pin(vmeta[e]);
     }
-    const half8 pa = kFold ? softmax_fold(sf, count) : softmax_tile(sacc, count);
+    const POps P = kFold ? softmax_fold(sf, count) : softmax_tile(sacc, count);
+    const half8 pa = P.pa;
     // one MFMA of P against the block's value parameters: column g < 4 holds
     // z_g (zero points), column 4 + g holds s_g (removes the code offset),
-    // column 8 ones (the denominator)
-    zacc = mfma(pa, n16 < 2 * ngv ? h8(vmeta[4]) : (n16 == 8 ? h8(kOnes, kOnes, kOnes, kOnes) : h8(0u, 0u, 0u, 0u)),
+    // column 8 ones (the denominator); with PLO rows G..2G-1 add the
+    // residuals' share
+    zacc = mfma(P.pz, n16 < 2 * ngv ? h8(vmeta[4]) : (n16 == 8 ? h8(kOnes, kOnes, kOnes, kOnes) : h8(0u, 0u, 0u, 0u)),
                 zacc);
     // weights w = p * s per (token, value group) as an exact hi + lo pair
 #pragma unroll
     for (int g = 0; g < ngv; ++g) {
       const half8 s8 = h8(vmeta[g]);
       if constexpr (kPackLo) {
-        // lanes of rows G.. replace their hi part by the lo part (exec-masked)
+        // lanes of rows G.. replace their hi part by the lo part (exec-masked),
+        // plus the weight residual's product with PLO
         half8 w = pa * s8;
-        if (n16 >= G) lo_in_place(w, pa, s8);
+        if (n16 >= G) {
+          if constexpr (PLO) lo_plus_in_place(w, pa, s8, P.pz);
+          else lo_in_place(w, pa, s8);
+        }
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int nt = 2 * g + t;
@@ -701,8 +735,12 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       if constexpr (kFold)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sf[i] = fold(sacc[0][i], sacc[1][i]);
-      half8 pa = kFold ? softmax_fold(sf, kBlockTokens) : softmax_tile(sacc, kBlockTokens);
-      if constexpr (kPackLo) pa = n16 < G ? pa : h8(0u, 0u, 0u, 0u);  // fp16 values take no lo part
+      const POps P = kFold ? softmax_fold(sf, kBlockTokens) : softmax_tile(sacc, kBlockTokens);
+      // fp16 values take no lo part of a product: rows G..2G-1 carry the
+      // weights' residuals with PLO, nothing otherwise
+      half8 pa = P.pa;
+      if constexpr (PLO) pa = P.pz;
+      else if constexpr (kPackLo) pa = n16 < G ? pa : h8(0u, 0u, 0u, 0u);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) oacc[nt] = mfma(pa, h8(vv[nt]), oacc[nt]);
       zacc = mfma(pa, n16 == 8 ? h8(kOnes, kOnes, kOnes, kOnes) : h8(0u, 0u, 0u, 0u), zacc);
@@ -834,6 +872,14 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
         else if (i == 0) oacc[nt][0] += oacc[nt][1];
       }
   }
+  if constexpr (PLO) {  // the residuals' sums (rows G..2G-1) onto rows 0..G-1
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (G == 8) zacc[i] += swap32(zacc[i], zacc[i]).y;
+      else if constexpr (G == 4) zacc[i] += swap16(zacc[i], zacc[i]).y;
+      else if (i == 0) zacc[0] += zacc[1];
+    }
+  }
   float* opart = J.partials + (static_cast<int64_t>(u) * nsplit + sp) * G * D;
   float* mlpart = J.partials + J.ml_off + (static_cast<int64_t>(u) * nsplit + sp) * G * 2;
 #pragma unroll
@@ -898,9 +944,15 @@ __global__ void __launch_bounds__(32 * NG) decode_merge_kernel(LayerDesc L, Deco
     M = fmaxf(M, xshflf<8>(M));
     M = fmaxf(M, xshflf<16>(M));
     float Ls = 0.f;
+    bool bad = false;
     for (int i = cq; i < nsplit; i += 32) {
       const float mi = ms[i * G + r];
+      bad |= bad_partial(mi, ls[i * G + r]);
       Ls = fmaf(ls[i * G + r], mi == -INFINITY ? 0.f : exp2f(mi - M), Ls);
+    }
+    {
+      const uint64_t m = __ballot(bad);
+      bad = ((tid & 32) ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m)) != 0u;
     }
     Ls += xshflf<1>(Ls);
     Ls += xshflf<2>(Ls);
@@ -961,43 +1013,52 @@ __global__ void __launch_bounds__(32 * NG) decode_merge_kernel(LayerDesc L, Deco
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e] *= c;
       }
+      if (bad) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = __uint_as_float(0x7fc00000u);
+      }
       float* op = J.out + (static_cast<int64_t>(b) * L.Hq + h * G + r) * D + 4 * cq;
       *reinterpret_cast<f32x4*>(op) = f32x4{y[0], y[1], y[2], y[3]};
+      const bool nf = nonfinite_bits(y[0]) || nonfinite_bits(y[1]) || nonfinite_bits(y[2]) ||
+                      nonfinite_bits(y[3]);
+      const uint64_t m = __ballot(nf);
+      const uint32_t mine = (tid & 32) ? static_cast<uint32_t>(m >> 32) : static_cast<uint32_t>(m);
+      if (cq == 0 && mine != 0u) atomicAdd(J.nonfinite, 1u);
     }
     __syncthreads();
   }
 }
 
-template <int KB, int VB, int G, bool INNER, bool MIX>
+template <int KB, int VB, int G, bool INNER, bool MIX, bool PLO>
 hipError_t launch_t(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
   using R = Rec<KB, VB, INNER, MIX>;
   if (L.off_km != R::off_km || L.off_vc != R::off_vc || L.off_vm != R::off_vm) return hipSuccess;
   if (MIX && (L.off_kx != R::off_kx || L.off_ks != R::off_ks)) return hipSuccess;
   constexpr int NB = ring_slots<KB, VB, G, INNER, MIX>();
-  auto kern = decode_mfma_kernel<KB, VB, G, INNER, MIX, NB>;
+  auto kern = decode_mfma_kernel<KB, VB, G, INNER, MIX, NB, PLO>;
   // one full round of resident wavefronts, from the runtime's occupancy of
   // this instance (registers and LDS as compiled) and the device's CU count
-  static int resident = 0;
-  if (resident == 0) {
-    int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64, 0) != hipSuccess ||
-        hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorInvalidValue;
-    resident = std::max(1, per_cu) * std::max(1, cus);
-  }
-  *waves = resident;
+  static std::atomic<int> resident[kMaxDevices];
+  if (resident_waves(kern, resident, waves) != hipSuccess) return hipErrorInvalidValue;
   if (!j.q) return hipSuccess;  // query only
   hipLaunchKernelGGL(kern, dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   return launch_decode_merge(L, j, s);
 }
 
+// Hadamard-rotated 2-bit values (the Hadamard 2-bit page's scheme) carry the
+// attention weights as a hi + lo pair (PLO): their near-uniform attention
+// over rotated values is where fp16-rounded weights cost the most accuracy.
 template <int G, bool INNER, bool MIX>
 hipError_t by_bits(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int* waves) {
   const int k = L.kb, v = L.vb;
-#define KVQ_CASE(KB, VB) \
-  if (k == KB && v == VB) return launch_t<KB, VB, G, INNER, MIX>(L, j, s, waves);
+  const bool plo = L.v_had != 0;
+#define KVQ_CASE(KB, VB)                                                                   \
+  if (k == KB && v == VB) {                                                                \
+    if constexpr (VB == 2)                                                                 \
+      if (plo) return launch_t<KB, VB, G, INNER, MIX, true>(L, j, s, waves);               \
+    return launch_t<KB, VB, G, INNER, MIX, false>(L, j, s, waves);                         \
+  }
   if constexpr (MIX) {
     KVQ_CASE(4, 2) KVQ_CASE(4, 4)
   } else if constexpr (INNER) {
@@ -1061,14 +1122,17 @@ __global__ void __launch_bounds__(256) decode_merge_rows_kernel(LayerDesc L, Dec
   for (int i = 0; i < MAXS; ++i)
     if (i < nsplit) M = fmaxf(M, ml[i].x);
   float Ls = 0.f, a0 = 0.f, a1 = 0.f;
+  bool bad = false;
 #pragma unroll
   for (int i = 0; i < MAXS; ++i) {
+    if (i < nsplit) bad |= bad_partial(ml[i].x, ml[i].y);
     const float wt = (i >= nsplit || ml[i].x == -INFINITY) ? 0.f : exp2f(ml[i].x - M);
     Ls = fmaf(ml[i].y, wt, Ls);
     a0 = fmaf(oi[i].x, wt, a0);
     a1 = fmaf(oi[i].y, wt, a1);
   }
   float y0 = a0 / Ls, y1 = a1 / Ls;
+  if (bad) y0 = y1 = __uint_as_float(0x7fc00000u);
   if (L.v_had) {
     // o <- c H o, H Sylvester: butterflies over channel bit 0 in-lane, then
     // over bits 1-6 with the lane whose index differs in bit 0-5
@@ -1090,6 +1154,7 @@ __global__ void __launch_bounds__(256) decode_merge_rows_kernel(LayerDesc L, Dec
   const int b = u / L.Hkv, h = u - b * L.Hkv;
   float* op = J.out + (static_cast<int64_t>(b) * L.Hq + h * G + r) * D + 2 * lane;
   *reinterpret_cast<float2*>(op) = make_float2(y0, y1);
+  if (__ballot(nonfinite_bits(y0) || nonfinite_bits(y1)) != 0u && lane == 0) atomicAdd(J.nonfinite, 1u);
 }
 
 }  // namespace
@@ -1112,7 +1177,7 @@ hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& j, hipStream
 int decode_fast_waves(const LayerDesc& L) {
   DecodeJob none{};
   int waves = 0;
-  dispatch(L, none, nullptr, &waves);
+  (void)dispatch(L, none, nullptr, &waves);
   return waves;
 }
 

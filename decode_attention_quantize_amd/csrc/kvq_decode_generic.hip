@@ -244,15 +244,17 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(LayerDesc L, Decode
     float M = -INFINITY;
     for (int i = 0; i < nsplit; ++i) M = fmaxf(M, __builtin_nontemporal_load(base + (i * G + r) * PW + D));
     float Ls = 0.f, acc = 0.f;
+    bool bad = false;
     for (int i = 0; i < nsplit; ++i) {
       const float* pr = base + (i * G + r) * PW;
       const float mi = __builtin_nontemporal_load(pr + D);
+      bad |= bad_partial(mi, __builtin_nontemporal_load(pr + D + 1));
       if (mi == -INFINITY) continue;
       const float w = expf(mi - M);
       Ls = fmaf(__builtin_nontemporal_load(pr + D + 1), w, Ls);
       acc = fmaf(__builtin_nontemporal_load(pr + t), w, acc);
     }
-    float y = acc / Ls;
+    float y = bad ? __uint_as_float(0x7fc00000u) : acc / Ls;
     if (L.v_had) {
       // o <- c H o (values were stored rotated)
       sm.o[t] = y;
@@ -267,6 +269,7 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(LayerDesc L, Decode
       __syncthreads();
     }
     J.out[(static_cast<int64_t>(b) * L.Hq + h * G + r) * D + t] = y;
+    if (__syncthreads_or(nonfinite_bits(y)) && t == 0) atomicAdd(J.nonfinite, 1u);
   }
   if (t == 0) J.counters[u] = 0;
 }

@@ -569,17 +569,9 @@ hipError_t launch_lut(const LayerDesc& L, const DecodeJob& j, hipStream_t s, int
   // two ring slots: with them LDS admits three wavefronts per SIMD, as the
   // register budget does
   constexpr int NB = 2;
-  static int resident = 0;
-  if (resident == 0) {
-    int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_lut_kernel<OUTK, ROPE, NB>, 64, 0) !=
-            hipSuccess ||
-        hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      return hipErrorInvalidValue;
-    resident = std::max(1, per_cu) * std::max(1, cus);
-  }
-  *waves = resident;
+  static std::atomic<int> resident[kMaxDevices];
+  if (resident_waves(decode_lut_kernel<OUTK, ROPE, NB>, resident, waves) != hipSuccess)
+    return hipErrorInvalidValue;
   if (!j.q) return hipSuccess;  // query only
   hipLaunchKernelGGL((decode_lut_kernel<OUTK, ROPE, NB>), dim3(j.nsplit, L.units), dim3(64), 0, s, L, j);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

@@ -114,6 +114,26 @@ size_t partials_bytes(const kvq_cache& c) {
   return static_cast<size_t>(c.units) * max_splits(c) * c.G * (kD + 2) * sizeof(float);
 }
 
+// Workspace: split partials (256-byte aligned), one arrival counter per unit
+// (LDS-staged path), then the non-finite output row count.
+size_t partials_padded(const kvq_cache& c) { return (partials_bytes(c) + 255) / 256 * 256; }
+size_t workspace_bytes(const kvq_cache& c) {
+  return partials_padded(c) + (static_cast<size_t>(c.units) + 1) * sizeof(uint32_t);
+}
+uint32_t* nonfinite_counter(const kvq_cache& c, void* ws) {
+  return reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(ws) + partials_padded(c)) + c.units;
+}
+
+// A failed launch can leave some of a call's kernels queued and others not,
+// so the layer's device contents no longer match any host state: the layer
+// is marked empty and needs a new prefill (its appends and decodes return
+// KVQ_ERR_STATE until then).
+kvq_status device_error(Layer& L) {
+  L.filled = false;
+  L.n = L.s_eff = L.nb = L.r = 0;
+  return KVQ_ERR_DEVICE;
+}
+
 bool valid_layer(const kvq_cache* c, int32_t layer) {
   return c && layer >= 0 && layer < static_cast<int32_t>(c->layers.size());
 }
@@ -172,6 +192,43 @@ void plan_splits(const kvq_cache& c, const kvq::TokenState& st, int fast_waves, 
   } else {
     j.nsplit = j.nsplit_body + j.fp16_split;
   }
+}
+
+enum class DecodeKind { kMatrixCore, kTables, kStaged };
+
+// Kernel family and split plan of a decode over the layer's current tokens
+// (matrix-core kernels first: uniform 2/4/8-bit; then the 3-bit table kernel
+// with outliers and pre-RoPE keys for MHA layers; the LDS-staged kernel
+// otherwise).  Fills j.st and the split fields.
+DecodeKind plan_decode(const kvq_cache& c, const Layer& L, kvq::DecodeJob& j) {
+  j.st = kvq::TokenState{L.n, L.s_eff, L.nb, L.r};
+  if (!c.force_generic) {
+    int waves = kvq::decode_fast_waves(L.d);
+    if (waves > 0) {
+      plan_splits(c, j.st, waves, j);
+      return DecodeKind::kMatrixCore;
+    }
+    waves = kvq::decode_lut_waves(L.d);
+    if (waves > 0) {
+      plan_splits(c, j.st, waves, j);
+      return DecodeKind::kTables;
+    }
+  }
+  plan_splits(c, j.st, 0, j);
+  return DecodeKind::kStaged;
+}
+
+kvq_status launch_decode(const Layer& L, DecodeKind kind, const kvq::DecodeJob& j, hipStream_t s) {
+  bool used = false;
+  hipError_t e = hipSuccess;
+  if (kind == DecodeKind::kMatrixCore)
+    e = kvq::launch_decode_fast(L.d, j, s, &used);
+  else if (kind == DecodeKind::kTables)
+    e = kvq::launch_decode_lut(L.d, j, s, &used);
+  else
+    e = kvq::launch_decode_generic(L.d, j, s), used = true;
+  if (!used) return KVQ_ERR_DEVICE;  // the planned kernel did not take the layer
+  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
 }
 
 }  // namespace
@@ -305,9 +362,36 @@ kvq_status kvq_bind_layer(kvq_cache* c, int32_t layer, void* const bufs[KVQ_NBUF
   return KVQ_OK;
 }
 
+kvq_status kvq_unbind_layer(kvq_cache* c, int32_t layer) {
+  if (!valid_layer(c, layer)) return KVQ_ERR_ARG;
+  Layer& L = c->layers[layer];
+  L.d.body = nullptr;
+  L.d.fp16 = nullptr;
+  L.d.kshift = nullptr;
+  L.bound = false;
+  L.filled = false;
+  L.n = L.s_eff = L.nb = L.r = 0;
+  return KVQ_OK;
+}
+
 kvq_status kvq_workspace_size(const kvq_cache* c, size_t* bytes) {
   if (!c || !bytes) return KVQ_ERR_ARG;
-  *bytes = (partials_bytes(*c) + 255) / 256 * 256 + static_cast<size_t>(c->units) * sizeof(uint32_t);
+  *bytes = workspace_bytes(*c);
+  return KVQ_OK;
+}
+
+kvq_status kvq_decode_nonfinite_rows(const kvq_cache* c, void* workspace, void* stream, uint32_t* rows) {
+  if (!c || !workspace || !rows) return KVQ_ERR_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint32_t* dev = nonfinite_counter(*c, workspace);
+  uint32_t v = 0;
+  if (hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return KVQ_ERR_DEVICE;
+  if (v != 0 && (hipMemsetAsync(dev, 0, sizeof(uint32_t), s) != hipSuccess ||
+                 hipStreamSynchronize(s) != hipSuccess))
+    return KVQ_ERR_DEVICE;
+  *rows = v;
   return KVQ_OK;
 }
 
@@ -356,7 +440,7 @@ kvq_status kvq_quantize_prefill(kvq_cache* c, int32_t layer, const void* k, cons
     // shifts from the whole prefill, before any body block is quantized
     // (read as 16-byte vectors)
     if (T > 0 && (reinterpret_cast<uintptr_t>(k) & 15)) return KVQ_ERR_ARG;
-    if (kvq::launch_knorm_shifts(L.d, ks, T, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_knorm_shifts(L.d, ks, T, s) != hipSuccess) return device_error(L);
   }
   if (nb > 0) {
     kvq::QuantJob j{};
@@ -370,9 +454,9 @@ kvq_status kvq_quantize_prefill(kvq_cache* c, int32_t layer, const void* k, cons
     j.cnt = kvq::kBlockTokens;
     j.last_cnt = nb - kvq::kBlockTokens * (j.nblocks - 1);
     j.rotate_v = L.d.v_had;
-    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return device_error(L);
   }
-  if (kvq::launch_zero_fp16(L.d, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  if (kvq::launch_zero_fp16(L.d, s) != hipSuccess) return device_error(L);
   kvq::CopyJob cj{};
   cj.k_src = ks;
   cj.v_src = vs;
@@ -383,13 +467,13 @@ kvq_status kvq_quantize_prefill(kvq_cache* c, int32_t layer, const void* k, cons
     cj.src_t0 = 0;
     cj.count = s_eff;
     cj.pos0 = 0;
-    if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return device_error(L);
   }
   if (r > 0) {
     cj.src_t0 = s_eff + nb;
     cj.count = r;
     cj.pos0 = s_eff + nb;
-    if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return device_error(L);
   }
   L.filled = true;
   L.n = T;
@@ -406,9 +490,26 @@ kvq_status kvq_append_token(kvq_cache* c, int32_t layer, const void* k_new, cons
   if (!L.bound || !L.filled) return KVQ_ERR_STATE;
   if (L.n + 1 > c->cfg.max_tokens) return KVQ_ERR_CAPACITY;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int W = c->cfg.recent_window, F = c->F;
+  const int S = c->cfg.sink_tokens, W = c->cfg.recent_window, F = c->F;
   const auto* ks = static_cast<const uint16_t*>(k_new);
   const auto* vs = static_cast<const uint16_t*>(v_new);
+  if (L.s_eff < S) {
+    // a prompt shorter than S: the token is the next sink (the body and the
+    // window are still empty, so its position n equals s_eff)
+    kvq::CopyJob cj{};
+    cj.k_src = ks;
+    cj.v_src = vs;
+    cj.src_unit_stride = kD;
+    cj.src_t0 = 0;
+    cj.count = 1;
+    cj.pos0 = L.n;
+    cj.s_eff = L.s_eff + 1;
+    cj.rotate_v = L.d.v_had;
+    if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return device_error(L);
+    L.s_eff += 1;
+    L.n += 1;
+    return KVQ_OK;
+  }
   if (F == 1 && W == 0) {
     // every token goes straight into the body
     kvq::QuantJob j{};
@@ -421,7 +522,7 @@ kvq_status kvq_append_token(kvq_cache* c, int32_t layer, const void* k_new, cons
     j.tok0 = L.nb % kvq::kBlockTokens;
     j.cnt = j.last_cnt = 1;
     j.rotate_v = L.d.v_had;
-    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return device_error(L);
     L.nb += 1;
     L.n += 1;
     return KVQ_OK;
@@ -435,7 +536,7 @@ kvq_status kvq_append_token(kvq_cache* c, int32_t layer, const void* k_new, cons
   cj.pos0 = L.n;
   cj.s_eff = L.s_eff;
   cj.rotate_v = L.d.v_had;
-  if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return KVQ_ERR_DEVICE;
+  if (kvq::launch_copy_fp16(L.d, cj, s) != hipSuccess) return device_error(L);
   int nb = L.nb, r = L.r + 1;
   if (r == W + F) {
     // flush the oldest F window tokens (contiguous ring slots) into the body
@@ -451,7 +552,7 @@ kvq_status kvq_append_token(kvq_cache* c, int32_t layer, const void* k_new, cons
     j.tok0 = nb % kvq::kBlockTokens;
     j.cnt = j.last_cnt = F;
     j.rotate_v = 0;  // ring values are stored rotated already
-    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return KVQ_ERR_DEVICE;
+    if (kvq::launch_quantize(L.d, j, s) != hipSuccess) return device_error(L);
     nb += F;
     r -= F;
   }
@@ -466,32 +567,15 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   if (!valid_layer(c, layer) || !q || !out || !workspace) return KVQ_ERR_ARG;
   Layer& L = c->layers[layer];
   if (!L.bound || !L.filled || L.n == 0) return KVQ_ERR_STATE;
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   kvq::DecodeJob j{};
+  const DecodeKind kind = plan_decode(*c, L, j);
   j.q = static_cast<const uint16_t*>(q);
   j.out = out;
   j.partials = static_cast<float*>(workspace);
-  j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) +
-                                           (partials_bytes(*c) + 255) / 256 * 256);
+  j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + partials_padded(*c));
+  j.nonfinite = nonfinite_counter(*c, workspace);
   j.ml_off = static_cast<int64_t>(c->units) * max_splits(*c) * c->G * kD;
-  j.st = kvq::TokenState{L.n, L.s_eff, L.nb, L.r};
-  bool used = false;
-  hipError_t e = hipSuccess;
-  // matrix-core kernels first (uniform 2/4/8-bit; 3-bit tables with outliers
-  // and pre-RoPE keys for MHA layers), the LDS-staged kernel otherwise
-  int fast_waves = c->force_generic ? 0 : kvq::decode_fast_waves(L.d);
-  if (fast_waves > 0) {
-    plan_splits(*c, j.st, fast_waves, j);
-    e = kvq::launch_decode_fast(L.d, j, s, &used);
-  } else if ((fast_waves = c->force_generic ? 0 : kvq::decode_lut_waves(L.d)) > 0) {
-    plan_splits(*c, j.st, fast_waves, j);
-    e = kvq::launch_decode_lut(L.d, j, s, &used);
-  }
-  if (!used) {
-    plan_splits(*c, j.st, 0, j);
-    e = kvq::launch_decode_generic(L.d, j, s);
-  }
-  return e == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+  return launch_decode(L, kind, j, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

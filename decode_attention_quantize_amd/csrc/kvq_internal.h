@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <cstdint>
 
 namespace kvq {
@@ -114,9 +116,54 @@ struct DecodeJob {
   int32_t fp16_chunks, sink_chunks, win_chunk0;
   int32_t fp16_split0, fp16_nsplit;
   int64_t ml_off;         // matrix-core path: float offset of the (max, sum) records
+  uint32_t* nonfinite;    // count of output rows with a non-finite element (never reset here)
 };
 // Log-sum-exp merge of matrix-core split partials into job.out (one
 // (unit, query row) per workgroup); undoes the value rotation when set.
 hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
+
+// Wavefronts of a 64-thread kernel resident on the current device in one
+// round (runtime occupancy x CU count).  `cache` is the caller's per-kernel
+// table, indexed by device; concurrent first calls store the same value.
+constexpr int kMaxDevices = 64;
+template <class Kernel>
+hipError_t resident_waves(Kernel kern, std::atomic<int>* cache, int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return hipErrorInvalidDevice;
+  if (dev < kMaxDevices) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *out = v;
+      return hipSuccess;
+    }
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidValue;
+  const int v = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
+  if (dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+  *out = v;
+  return hipSuccess;
+}
+
+// Device helpers: tests for non-finite values on the bit pattern.  The bits
+// pass through an empty asm statement, so that no floating-point assumption
+// (the decode files are compiled without NaN semantics, under which a test
+// of a value's bits could be rewritten as a compare that is false for NaN)
+// can reach the test.
+__device__ __forceinline__ uint32_t opaque_bits(float x) {
+  uint32_t b = __float_as_uint(x);
+  asm volatile("" : "+v"(b));
+  return b;
+}
+__device__ __forceinline__ bool nonfinite_bits(float x) { return (opaque_bits(x) & 0x7f800000u) == 0x7f800000u; }
+__device__ __forceinline__ bool nan_bits(float x) { return (opaque_bits(x) & 0x7fffffffu) > 0x7f800000u; }
+// A split partial (max m, sum l) that cannot be trusted: a NaN maximum, or a
+// non-finite sum (scores that came out NaN -- a query / key-scale product
+// beyond binary16 -- leave the split's maximum at its start value and make
+// its sum NaN).  The merge then writes the row as NaN and counts it, instead
+// of dropping the split.
+__device__ __forceinline__ bool bad_partial(float m, float l) { return nan_bits(m) || nonfinite_bits(l); }
 
 }  // namespace kvq

@@ -104,6 +104,21 @@ __device__ __forceinline__ void lo_in_place(half8& w, half8 a, half8 s) {
   w = __builtin_bit_cast(half8, wv);
 }
 
+// w <- fma(z, s, fma(a, s, -w)) per fp16 element, in place: the lo part of
+// a * s plus the product of a's residual z (each step rounds once; used by
+// the lanes of the lo rows, exec-masked like lo_in_place).
+__device__ __forceinline__ void lo_plus_in_place(half8& w, half8 a, half8 s, half8 z) {
+  u32x4 wv = __builtin_bit_cast(u32x4, w);
+  const u32x4 av = __builtin_bit_cast(u32x4, a), sv = __builtin_bit_cast(u32x4, s),
+              zv = __builtin_bit_cast(u32x4, z);
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    asm("v_pk_fma_f16 %0, %1, %2, %0 neg_lo:[0,0,1] neg_hi:[0,0,1]\n\t"
+        "v_pk_fma_f16 %0, %3, %2, %0"
+        : "+v"(wv[e]) : "v"(av[e]), "v"(sv[e]), "v"(zv[e]));
+  w = __builtin_bit_cast(half8, wv);
+}
+
 // Reads of the LDS ring filled by global_load_lds.  They are issued as
 // inline-asm ds_reads: the compiler's wait insertion cannot see through the
 // DMA writes precisely (it would drain every in-flight block), so the ring is

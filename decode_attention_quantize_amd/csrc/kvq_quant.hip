@@ -437,6 +437,45 @@ __device__ void pack_vchunks(const uint8_t (*codes)[D], int nrows, int bits, uin
   }
 }
 
+// A fresh block filled only up to nrows tokens: the per-token sections of the
+// slots past them (key code rows, inner key parameters, value parameters,
+// sparse outliers, mixed-group low nibbles and masks) are zeroed, so that
+// the record holds no bytes the buffer had before.  The decode weighs those
+// slots by exactly 0, and 0 times a stale non-finite parameter would not be 0.
+// Value codes and 3-bit key chunks are written whole for a fresh block.
+__device__ void zero_record_tail(const LayerDesc& L, uint8_t* rec, int nrows) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const int rest = kBlockTokens - nrows;
+  if (L.kb != 3) {
+    uint32_t* w = reinterpret_cast<uint32_t*>(rec + L.off_kc + nrows * L.k_row_bytes);
+    for (int i = t; i < rest * L.k_row_bytes / 4; i += nt) w[i] = 0u;
+  }
+  if (L.k_inner) {
+    const int ng = D / L.k_group;  // one (s, z) pair per group and token
+    uint32_t* w = reinterpret_cast<uint32_t*>(rec + L.off_km) + nrows * ng;
+    for (int i = t; i < rest * ng; i += nt) w[i] = 0u;
+  }
+  {
+    const int rows = 2 * (D / L.v_group);  // s[g][32] then z[g][32]
+    uint16_t* m = reinterpret_cast<uint16_t*>(rec + L.off_vm);
+    for (int i = t; i < rows * rest; i += nt) m[(i / rest) * kBlockTokens + nrows + i % rest] = 0;
+  }
+  if (L.outk) {
+    uint32_t* ko = reinterpret_cast<uint32_t*>(rec + L.off_ko) + nrows * L.outk;
+    uint32_t* vo = reinterpret_cast<uint32_t*>(rec + L.off_vo) + nrows * L.outk;
+    for (int i = t; i < rest * L.outk; i += nt) {
+      ko[i] = 0u;
+      vo[i] = 0u;
+    }
+  }
+  if (L.k_hi) {
+    const int wpt = L.k_hi * (L.k_group / 8);  // low-nibble words per token
+    uint32_t* x = reinterpret_cast<uint32_t*>(rec + L.off_kx) + nrows * wpt;
+    for (int i = t; i < rest * wpt; i += nt) x[i] = 0u;
+    for (int i = t; i < rest; i += nt) rec[L.off_ks + nrows + i] = 0;
+  }
+}
+
 __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   QuantSmem& sm = *reinterpret_cast<QuantSmem*>(smem_raw);
@@ -451,6 +490,7 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
   const int tt0 = J.src_t0 + kBlockTokens * bi;
   const int64_t base = u * J.src_unit_stride + static_cast<int64_t>(tt0) * D;
   const uint16_t* vsrc = J.v_src + u * J.src_unit_stride;
+  if (slot0 == 0 && nrows < kBlockTokens) zero_record_tail(L, rec, nrows);
   for (int j = 0; j < kBlockTokens; ++j) {
     sm.k[j][t] = j < nrows ? J.k_src[base + j * D + t] : 0;
     const int64_t vo = J.v_interleaved ? vslot(tt0 + j, t) : static_cast<int64_t>(tt0 + j) * D + t;
@@ -548,6 +588,432 @@ __global__ void __launch_bounds__(128) quantize_kernel(LayerDesc L, QuantJob J) 
     pack_vchunks(sm.cv, nrows, L.vb, rec + L.off_vc, slot0);
 }
 
+// ===================================================================== fresh blocks
+// prefill_kernel quantizes whole fresh blocks (slot 0 onward: prefill and
+// window flushes) with the same arithmetic as quantize_kernel but organised
+// for bandwidth: every thread issues its 16-byte loads of the block at once;
+// each per-token group (values, inner key groups) is one thread's task with
+// its statistics in registers (no per-row chains of cross-lane reductions);
+// value codes are staged in the lane-chunk order of the record, so each
+// packed word is one wide LDS read.  Mixed 4/8-bit key groups and appends
+// into a partly filled block stay on quantize_kernel.
+
+// binary64 -> binary16, round to nearest even, through binary32: x is first
+// rounded to odd in binary32 (round to nearest, then, if inexact, toward
+// zero with the last bit set), which keeps the information needed for the
+// second rounding because binary32 carries 13 more fraction bits than
+// binary16 (Boldo & Melquiond, "Emulation of FMA and correctly rounded sums:
+// proved algorithms using rounding to odd", IEEE TC 2008).  Equal to d2h.
+__device__ __forceinline__ uint16_t d2h_odd(double x) {
+  const float r = static_cast<float>(x);
+  const double back = static_cast<double>(r);
+  uint32_t rb = __float_as_uint(r);
+  if (back != x) {
+    if (fabs(back) > fabs(x)) rb -= 1u;  // one binary32 step toward zero
+    rb |= 1u;
+  }
+  return f2h(__uint_as_float(rb));
+}
+
+// Shared memory of prefill_kernel (dynamic size, offsets in bytes):
+//   k16, v16 [32][D] fp16 | ck [32][D] key codes | cv value codes: [32][D]
+//   (3-bit) or lane-chunk order [64 chunks][64 elements] | exk, exv [32][D]
+//   outlier masks (layers with outliers) ; the Hadamard pass uses a [16][D]
+//   binary64 buffer over the code area (dead until the codes are written).
+constexpr int kPfK = 0, kPfV = 8192, kPfCk = 16384, kPfCv = 20480, kPfExk = 24576, kPfExv = 28672;
+__host__ __device__ constexpr int prefill_smem(bool outk, bool rot) {
+  return (rot || outk) ? 32768 : 24576;
+}
+
+// Element of lane chunk l = 16 (j / 8) + (c % 16) that holds code (token j,
+// channel c) of the value layout: e = 8 (c / 16) + j % 8.
+__device__ __forceinline__ int vchunk_off(int j, int c) {
+  return (16 * (j >> 3) + (c & 15)) * 64 + 8 * (c >> 4) + (j & 7);
+}
+
+// One per-token group (W channels of one row) with its values in registers:
+// the arithmetic of token_group, written per element instead of per lane.
+template <int W>
+__device__ __forceinline__ void group_in_regs(const uint16_t (&xh)[W], uint64_t exm, int bits, bool nuq,
+                                              const uint16_t* lev, bool hybrid, int rnum, int rden, bool tern,
+                                              uint8_t (&code)[W], uint16_t& s, uint16_t& z) {
+  if (tern) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) a = fmaxf(a, ((exm >> i) & 1u) ? 0.f : fabsf(h2f(xh[i])));
+    s = f2h(a);
+    z = static_cast<uint16_t>(s ^ 0x8000u);
+    const float sv = h2f(s);
+#pragma unroll
+    for (int i = 0; i < W; ++i)
+      code[i] = static_cast<uint8_t>(s == 0 ? 1 : static_cast<int>(fminf(fmaxf(rintf(h2f(xh[i]) / sv), -1.f), 1.f)) + 1);
+    return;
+  }
+  float mn = __int_as_float(0x7f800000), mx = __int_as_float(0xff800000);
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    if ((exm >> i) & 1u) continue;
+    const float x = h2f(xh[i]);
+    mn = fminf(mn, x);
+    mx = fmaxf(mx, x);
+  }
+  const bool any = mn <= mx;
+  bool sym = false;
+  if (hybrid) {
+    // exact sum and extremes over every member, in units of 2^-24
+    int64_t sum = 0;
+    float amn = h2f(xh[0]), amx = amn;
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+      sum += h2fixed(xh[i]);
+      const float x = h2f(xh[i]);
+      amn = fminf(amn, x);
+      amx = fmaxf(amx, x);
+    }
+    const int64_t lhs = static_cast<int64_t>(rden) * (sum < 0 ? -sum : sum);
+    const int64_t rhs = static_cast<int64_t>(rnum) * W * (h2fixed(f2h(amx)) - h2fixed(f2h(amn)));
+    sym = lhs <= rhs;
+  }
+  if (sym) {
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) a = fmaxf(a, fabsf(h2f(xh[i])));
+    const uint16_t sv = sym_scale(a, bits);
+#pragma unroll
+    for (int i = 0; i < W; ++i) code[i] = static_cast<uint8_t>(sym_code(h2f(xh[i]), sv, bits));
+    s = sv | 0x8000;
+    z = 0;
+  } else if (nuq) {
+    nuq_params(mn, mx, any, s, z);
+#pragma unroll
+    for (int i = 0; i < W; ++i) code[i] = static_cast<uint8_t>(nuq_code(h2f(xh[i]), mn, s, lev));
+  } else {
+    const int Q = (1 << bits) - 1;
+    asym_params(mn, mx, any, Q, s, z);
+#pragma unroll
+    for (int i = 0; i < W; ++i) code[i] = static_cast<uint8_t>(asym_code(h2f(xh[i]), mn, s, Q));
+  }
+}
+
+// All per-token group tasks of one tensor of the block: task = (row j,
+// group g), W channels.  Codes go to LDS (keys and 3-bit values row-major,
+// 2/4/8-bit values in lane-chunk order), parameters straight to the record.
+template <int W>
+__device__ void group_tasks(const uint8_t* sm, int src_off, int ex_off, bool has_ex, int code_off, bool chunk_order,
+                            int nrows, int bits, bool nuq, const uint16_t* lev, bool hybrid, int rnum, int rden,
+                            bool tern, uint16_t* meta, int meta_kind) {
+  constexpr int ng = D / W;
+  const uint16_t* x16 = reinterpret_cast<const uint16_t*>(sm + src_off);
+  uint8_t* codes = const_cast<uint8_t*>(sm) + code_off;
+  for (int task = threadIdx.x; task < nrows * ng; task += blockDim.x) {
+    const int j = task / ng, g = task % ng;
+    uint16_t xh[W];
+    const uint4* xs = reinterpret_cast<const uint4*>(x16 + j * D + g * W);
+#pragma unroll
+    for (int q = 0; q < W / 8; ++q) {
+      const uint4 v = xs[q];
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xh[8 * q + 2 * e] = static_cast<uint16_t>(w4[e] & 0xffffu);
+        xh[8 * q + 2 * e + 1] = static_cast<uint16_t>(w4[e] >> 16);
+      }
+    }
+    uint64_t exm = 0;
+    if (has_ex) {
+      const uint8_t* ex = sm + ex_off + j * D + g * W;
+#pragma unroll
+      for (int i = 0; i < W; ++i) exm |= static_cast<uint64_t>(ex[i] != 0) << i;
+    }
+    uint8_t code[W];
+    uint16_t s, z;
+    group_in_regs<W>(xh, exm, bits, nuq, lev, hybrid, rnum, rden, tern, code, s, z);
+    if (chunk_order) {
+#pragma unroll
+      for (int i = 0; i < W; ++i) codes[vchunk_off(j, g * W + i)] = code[i];
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + j * D + g * W);
+#pragma unroll
+      for (int q = 0; q < W / 4; ++q)
+        dst[q] = code[4 * q] | (code[4 * q + 1] << 8) | (code[4 * q + 2] << 16) | (static_cast<uint32_t>(code[4 * q + 3]) << 24);
+    }
+    if (meta_kind == 0) {  // inner keys: [32][ng] (s, z)
+      reinterpret_cast<uint32_t*>(meta)[j * ng + g] = s | (static_cast<uint32_t>(z) << 16);
+    } else {  // values: s[ng][32] then z[ng][32]
+      meta[g * kBlockTokens + j] = s;
+      meta[ng * kBlockTokens + g * kBlockTokens + j] = z;
+    }
+  }
+}
+
+// top-k columns of each token row by |x| (fp16 magnitudes, the lower column
+// on equal magnitude), one thread per (tensor, row), a single pass keeping
+// the k largest keys (magnitude << 7 | 127 - column); columns ascending in
+// the record; the mask bytes mark them for the group statistics.
+__device__ void outliers_tasks(uint8_t* sm, int nrows, int k, uint8_t* kout, uint8_t* vout) {
+  for (int task = threadIdx.x; task < 2 * nrows; task += blockDim.x) {
+    const int tsr = task / nrows, j = task % nrows;
+    const uint16_t* row = reinterpret_cast<const uint16_t*>(sm + (tsr ? kPfV : kPfK)) + j * D;
+    uint32_t top[kMaxOutliers];
+#pragma unroll
+    for (int i = 0; i < kMaxOutliers; ++i) top[i] = 0u;
+    for (int c = 0; c < D; ++c) {
+      uint32_t key = (static_cast<uint32_t>(row[c] & 0x7fffu) << 7) | static_cast<uint32_t>(127 - c);
+      // keep top[0..k) sorted descending: bubble the new key in
+#pragma unroll
+      for (int i = 0; i < kMaxOutliers; ++i) {
+        if (i < k && key > top[i]) {
+          const uint32_t t = top[i];
+          top[i] = key;
+          key = t;
+        }
+      }
+    }
+    int col[kMaxOutliers];
+#pragma unroll
+    for (int i = 0; i < kMaxOutliers; ++i) col[i] = 127 - static_cast<int>(top[i] & 127u);
+    for (int a = 1; a < k; ++a)
+      for (int b = a; b > 0 && col[b] < col[b - 1]; --b) {
+        const int t = col[b];
+        col[b] = col[b - 1];
+        col[b - 1] = t;
+      }
+    uint8_t* ex = sm + (tsr ? kPfExv : kPfExk) + j * D;
+    uint32_t* rec = reinterpret_cast<uint32_t*>(tsr ? vout : kout) + j * k;
+    for (int i = 0; i < k; ++i) {
+      ex[col[i]] = 1;
+      rec[i] = static_cast<uint32_t>(col[i]) | (static_cast<uint32_t>(row[col[i]]) << 16);
+    }
+  }
+}
+
+// Token-major key code rows (2/4/8 bits) from the row-major code tile: one
+// thread per output word, reading its codes as one 4-, 8- or 16-byte word.
+__device__ void pack_rows_fast(const uint8_t* ck, int nrows, int bits, uint8_t* dst, int row_bytes) {
+  const int wpr = row_bytes / 4;
+  for (int i = threadIdx.x; i < nrows * wpr; i += blockDim.x) {
+    const int j = i / wpr, w = i % wpr;
+    const uint8_t* src = ck + j * D;
+    uint32_t word = 0;
+    if (bits == 8) {
+      word = reinterpret_cast<const uint32_t*>(src)[w];
+    } else if (bits == 4) {
+      const uint2 b = reinterpret_cast<const uint2*>(src)[w];  // elements 8w..8w+7
+      const uint32_t bb[2] = {b.x, b.y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) word |= ((bb[e >> 2] >> (8 * (e & 3))) & 15u) << pair_split_pos(4, e);
+    } else {
+      const uint4 b = reinterpret_cast<const uint4*>(src)[w];  // elements 16w..16w+15
+      const uint32_t bb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) word |= ((bb[e >> 2] >> (8 * (e & 3))) & 3u) << pair_split_pos(2, e);
+    }
+    reinterpret_cast<uint32_t*>(dst + j * row_bytes)[w] = word;
+  }
+}
+
+// Value lane chunks (2/4/8 bits) from the chunk-order code tile: word wi of
+// chunk l holds its elements n wi .. n wi + n - 1 (n = 32 / bits), pair-split.
+__device__ void pack_vchunks_fast(const uint8_t* cvc, int bits, uint8_t* dst) {
+  const int wpc = 2 * bits;  // words per chunk
+  for (int i = threadIdx.x; i < 64 * wpc; i += blockDim.x) {
+    const int l = i / wpc, w = i % wpc;
+    const uint8_t* src = cvc + l * 64;
+    uint32_t word = 0;
+    if (bits == 8) {
+      word = reinterpret_cast<const uint32_t*>(src)[w];
+    } else if (bits == 4) {
+      const uint2 b = reinterpret_cast<const uint2*>(src)[w];
+      const uint32_t bb[2] = {b.x, b.y};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) word |= ((bb[e >> 2] >> (8 * (e & 3))) & 15u) << pair_split_pos(4, e);
+    } else {
+      const uint4 b = reinterpret_cast<const uint4*>(src)[w];
+      const uint32_t bb[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) word |= ((bb[e >> 2] >> (8 * (e & 3))) & 3u) << pair_split_pos(2, e);
+    }
+    reinterpret_cast<uint32_t*>(dst)[i] = word;
+  }
+}
+
+// Exact fp64 Walsh-Hadamard transform of the value rows [0, nrows) in place
+// (fp16 in, fp16(fl64(S * c)) out), sixteen rows per pass through a binary64
+// buffer; every butterfly of a stage, then a barrier.
+__device__ void hadamard_rows_fast(uint8_t* sm, int nrows, double c) {
+  uint16_t* v16 = reinterpret_cast<uint16_t*>(sm + kPfV);
+  double(*had)[D] = reinterpret_cast<double(*)[D]>(sm + kPfCk);  // over the code area
+  const int t = threadIdx.x;
+  for (int r0 = 0; r0 < nrows; r0 += 16) {
+    const int rows = min(16, nrows - r0);
+    for (int i = t; i < rows * D; i += blockDim.x) had[i / D][i % D] = static_cast<double>(h2f(v16[(r0 + i / D) * D + i % D]));
+    __syncthreads();
+    for (int h = 1; h < D; h <<= 1) {
+      for (int i = t; i < rows * (D / 2); i += blockDim.x) {
+        const int j = i / (D / 2), p = i % (D / 2);
+        const int lo = ((p / h) * 2 * h) + (p % h);
+        const double a = had[j][lo], b = had[j][lo + h];
+        had[j][lo] = a + b;
+        had[j][lo + h] = a - b;
+      }
+      __syncthreads();
+    }
+    for (int i = t; i < rows * D; i += blockDim.x) v16[(r0 + i / D) * D + i % D] = d2h_odd(had[i / D][i % D] * c);
+    __syncthreads();
+  }
+}
+
+__global__ void __launch_bounds__(128) prefill_kernel(LayerDesc L, QuantJob J) {
+  extern __shared__ __align__(16) uint8_t sm[];
+  const int t = threadIdx.x;
+  const int u = blockIdx.y;
+  const int bi = blockIdx.x;
+  const int blk = J.blk0 + bi;
+  const int nrows = (bi == J.nblocks - 1) ? J.last_cnt : J.cnt;
+  uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + blk) * L.rec_bytes;
+  uint16_t* k16 = reinterpret_cast<uint16_t*>(sm + kPfK);
+  uint16_t* v16 = reinterpret_cast<uint16_t*>(sm + kPfV);
+  const bool outk = L.outk > 0;
+  const bool chunk_v = L.vb != 3;
+
+  // ---- loads: 32 rows x 16 chunks of 16 bytes per tensor; thread t takes
+  // chunk t % 16 of rows t / 16 + 8 i, every load issued before the first use
+  const int tt0 = J.src_t0 + kBlockTokens * bi;
+  {
+    const uint16_t* ksrc = J.k_src + u * J.src_unit_stride + static_cast<int64_t>(tt0) * D;
+    uint4 kv[4], vv[4];
+    const int cc = t & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = (t >> 4) + 8 * i;
+      kv[i] = j < nrows ? reinterpret_cast<const uint4*>(ksrc + j * D)[cc] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (!J.v_interleaved) {
+      const uint16_t* vsrc = J.v_src + u * J.src_unit_stride + static_cast<int64_t>(tt0) * D;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = (t >> 4) + 8 * i;
+        vv[i] = j < nrows ? reinterpret_cast<const uint4*>(vsrc + j * D)[cc] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = (t >> 4) + 8 * i;
+      reinterpret_cast<uint4*>(k16 + j * D)[cc] = kv[i];
+      if (!J.v_interleaved) reinterpret_cast<uint4*>(v16 + j * D)[cc] = vv[i];
+    }
+    if (J.v_interleaved) {  // a window flush: values in the fp16 ring's 8-slot interleaved layout
+      const uint16_t* vsrc = J.v_src + u * J.src_unit_stride;
+      for (int j = 0; j < kBlockTokens; ++j) v16[j * D + t] = j < nrows ? vsrc[vslot(tt0 + j, t)] : 0;
+    }
+  }
+  if (nrows < kBlockTokens) zero_record_tail(L, rec, nrows);
+  __syncthreads();
+  if (L.kshift) {
+    // normalized keys fp16(K * 2^shift), saturating (InnerQ, method 4)
+    const int sh = L.kshift[static_cast<int64_t>(u) * D + t];
+    for (int j = 0; j < nrows; ++j)
+      k16[j * D + t] = f2h(fminf(fmaxf(ldexpf(h2f(k16[j * D + t]), sh), -65504.f), 65504.f));
+    __syncthreads();
+  }
+  if (J.rotate_v) hadamard_rows_fast(sm, nrows, L.had_scale);
+
+  // ---- code tiles start at zero (rows past nrows pack as code 0)
+  {
+    uint4* z = reinterpret_cast<uint4*>(sm + kPfCk);
+    const int n16 = (outk ? 16384 : 8192) / 16;
+    for (int i = t; i < n16; i += blockDim.x) z[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  __syncthreads();
+  if (outk) {
+    outliers_tasks(sm, nrows, L.outk, rec + L.off_ko, rec + L.off_vo);
+    __syncthreads();
+  }
+
+  // ---- keys
+  if (!L.k_inner) {
+    // one group per channel over the block's tokens: thread t owns channel t
+    const uint8_t* exk = sm + kPfExk;
+    uint8_t* ck = sm + kPfCk;
+    bool any = false;
+    float mn = 0.f, mx = 0.f;
+    for (int j = 0; j < nrows; ++j) {
+      if (outk && exk[j * D + t]) continue;
+      const float x = h2f(k16[j * D + t]);
+      if (!any) {
+        mn = mx = x;
+        any = true;
+      } else {
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+    }
+    uint16_t s, z;
+    bool sym = false;
+    if (L.k_hybrid) {
+      int64_t sum = 0, fmn = 0, fmx = 0;
+      for (int j = 0; j < nrows; ++j) {
+        const int64_t f = h2fixed(k16[j * D + t]);
+        sum += f;
+        if (j == 0 || f < fmn) fmn = f;
+        if (j == 0 || f > fmx) fmx = f;
+      }
+      sym = static_cast<int64_t>(L.ratio_den) * (sum < 0 ? -sum : sum) <=
+            static_cast<int64_t>(L.ratio_num) * nrows * (fmx - fmn);
+    }
+    if (sym) {
+      float a = 0.f;
+      for (int j = 0; j < nrows; ++j) a = fmaxf(a, fabsf(h2f(k16[j * D + t])));
+      const uint16_t sv = sym_scale(a, L.kb);
+      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(sym_code(h2f(k16[j * D + t]), sv, L.kb));
+      s = sv | 0x8000;
+      z = 0;
+    } else if (L.nuq) {
+      nuq_params(mn, mx, any, s, z);
+      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(nuq_code(h2f(k16[j * D + t]), mn, s, L.lev_k));
+    } else {
+      const int Q = (1 << L.kb) - 1;
+      asym_params(mn, mx, any, Q, s, z);
+      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(asym_code(h2f(k16[j * D + t]), mn, s, Q));
+    }
+    uint16_t* km = reinterpret_cast<uint16_t*>(rec + L.off_km);
+    km[t] = s;
+    km[D + t] = z;
+  } else {
+    uint16_t* km = reinterpret_cast<uint16_t*>(rec + L.off_km);
+    const bool hy = L.k_hybrid != 0;
+    if (L.k_group == 16)
+      group_tasks<16>(sm, kPfK, kPfExk, outk, kPfCk, false, nrows, L.kb, L.nuq != 0, L.lev_k, hy, L.ratio_num, L.ratio_den, false, km, 0);
+    else if (L.k_group == 32)
+      group_tasks<32>(sm, kPfK, kPfExk, outk, kPfCk, false, nrows, L.kb, L.nuq != 0, L.lev_k, hy, L.ratio_num, L.ratio_den, false, km, 0);
+    else
+      group_tasks<64>(sm, kPfK, kPfExk, outk, kPfCk, false, nrows, L.kb, L.nuq != 0, L.lev_k, hy, L.ratio_num, L.ratio_den, false, km, 0);
+  }
+  // ---- values: per-token groups
+  {
+    uint16_t* vm = reinterpret_cast<uint16_t*>(rec + L.off_vm);
+    const bool tern = L.v_tern != 0;
+    if (L.v_group == 16)
+      group_tasks<16>(sm, kPfV, kPfExv, outk, kPfCv, chunk_v, nrows, L.vb, L.nuq != 0, L.lev_v, false, 1, 1, tern, vm, 1);
+    else if (L.v_group == 32)
+      group_tasks<32>(sm, kPfV, kPfExv, outk, kPfCv, chunk_v, nrows, L.vb, L.nuq != 0, L.lev_v, false, 1, 1, tern, vm, 1);
+    else
+      group_tasks<64>(sm, kPfV, kPfExv, outk, kPfCv, chunk_v, nrows, L.vb, L.nuq != 0, L.lev_v, false, 1, 1, tern, vm, 1);
+  }
+  __syncthreads();
+
+  // ---- pack
+  const uint8_t(*ckr)[D] = reinterpret_cast<const uint8_t(*)[D]>(sm + kPfCk);
+  if (L.kb == 3)
+    pack_k3(ckr, nrows, rec + L.off_kc, 0);
+  else
+    pack_rows_fast(sm + kPfCk, nrows, L.kb, rec + L.off_kc, L.k_row_bytes);
+  if (chunk_v)
+    pack_vchunks_fast(sm + kPfCv, L.vb, rec + L.off_vc);
+  else
+    pack_v3(reinterpret_cast<const uint8_t(*)[D]>(sm + kPfCv), nrows, rec + L.off_vc, 0);
+}
+
 __global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   QuantSmem& sm = *reinterpret_cast<QuantSmem*>(smem_raw);
@@ -638,6 +1104,16 @@ hipError_t launch_knorm_shifts(const LayerDesc& L, const uint16_t* k, int32_t T,
 
 hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t s) {
   if (job.nblocks <= 0) return hipSuccess;
+  // whole fresh blocks take the bandwidth kernel; appends into a partly
+  // filled block and mixed 4/8-bit key groups take quantize_kernel
+  // (16-byte loads: the sources must be 16-byte aligned; row strides are
+  // whole 256-byte rows)
+  const bool aligned = ((reinterpret_cast<uintptr_t>(job.k_src) | reinterpret_cast<uintptr_t>(job.v_src)) & 15) == 0;
+  if (job.tok0 == 0 && L.k_hi == 0 && aligned) {
+    const size_t smem = prefill_smem(L.outk > 0, job.rotate_v != 0);
+    hipLaunchKernelGGL(prefill_kernel, dim3(job.nblocks, L.units), dim3(128), smem, s, L, job);
+    return hipGetLastError();
+  }
   const size_t smem = sizeof(QuantSmem);
   hipLaunchKernelGGL(quantize_kernel, dim3(job.nblocks, L.units), dim3(128), smem, s, L, job);
   return hipGetLastError();

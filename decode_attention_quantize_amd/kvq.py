@@ -20,9 +20,10 @@ KVQ_NBUF = 2
 KVQ_BUF_BODY, KVQ_BUF_FP16 = 0, 1
 
 EXPORTS = ("kvq_create", "kvq_destroy", "kvq_layer_buffer_sizes", "kvq_block_layout",
-           "kvq_bind_layer", "kvq_workspace_size", "kvq_quantize_prefill", "kvq_append_token",
-           "kvq_decode_attn", "kvq_layer_state", "kvq_average_bits", "kvq_status_str",
-           "kvq_fit_rate_distortion", "kvq_waterfill_bits", "kvq_allocate_bits")
+           "kvq_bind_layer", "kvq_unbind_layer", "kvq_workspace_size", "kvq_quantize_prefill",
+           "kvq_append_token", "kvq_decode_attn", "kvq_decode_nonfinite_rows", "kvq_layer_state",
+           "kvq_average_bits", "kvq_status_str", "kvq_fit_rate_distortion", "kvq_waterfill_bits",
+           "kvq_allocate_bits")
 
 
 class kvq_config(C.Structure):
@@ -73,6 +74,8 @@ def lib():
         L.kvq_layer_buffer_sizes.argtypes = [pcache, i32, C.POINTER(C.c_size_t)]
         L.kvq_block_layout.argtypes = [pcache, i32, C.POINTER(kvq_block_layout_t)]
         L.kvq_bind_layer.argtypes = [pcache, i32, C.POINTER(C.c_void_p)]
+        L.kvq_unbind_layer.argtypes = [pcache, i32]
+        L.kvq_decode_nonfinite_rows.argtypes = [pcache, vp, vp, C.POINTER(C.c_uint32)]
         L.kvq_workspace_size.argtypes = [pcache, C.POINTER(C.c_size_t)]
         L.kvq_quantize_prefill.argtypes = [pcache, i32, vp, vp, i32, vp, vp]
         L.kvq_append_token.argtypes = [pcache, i32, vp, vp, vp]
@@ -131,6 +134,17 @@ def kvq_block_layout(handle: int, layer: int) -> dict:
 def kvq_bind_layer(handle: int, layer: int, ptrs):
     arr = (C.c_void_p * KVQ_NBUF)(*ptrs)
     _check(lib().kvq_bind_layer(handle, layer, arr), "kvq_bind_layer")
+
+
+def kvq_unbind_layer(handle: int, layer: int):
+    _check(lib().kvq_unbind_layer(handle, layer), "kvq_unbind_layer")
+
+
+def kvq_decode_nonfinite_rows(handle: int, ws_ptr, stream) -> int:
+    n = C.c_uint32()
+    _check(lib().kvq_decode_nonfinite_rows(handle, ws_ptr, stream, C.byref(n)),
+           "kvq_decode_nonfinite_rows")
+    return n.value
 
 
 def kvq_workspace_size(handle: int) -> int:
@@ -229,13 +243,25 @@ def config_from_workload(wl, max_tokens=None) -> kvq_config:
 
 # ---------------------------------------------------------------- torch plumbing
 class KVQCache:
-    """A libkvq cache whose device buffers are torch tensors on one GPU."""
+    """A libkvq cache whose device buffers are torch tensors on one GPU.
 
-    def __init__(self, cfg: kvq_config, layer_bits, codebooks=None, device="cuda", layers=None):
+    Every device call checks that its tensors live on the cache's device and
+    have the dtype and the exact shape the C entry point reads or writes, so
+    a wrong tensor raises here instead of letting a kernel run past it.
+    ``fill`` (tests) fills the layer buffers with that byte instead of zeros.
+    """
+
+    def __init__(self, cfg: kvq_config, layer_bits, codebooks=None, device="cuda", layers=None,
+                 fill=None):
         import torch
         self.torch = torch
         self.device = torch.device(device)
+        if self.device.type != "cuda":
+            raise ValueError(f"KVQCache needs a GPU device, got {self.device}")
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         self.cfg = cfg
+        self.fill = fill
         self.handle = kvq_create(cfg, layer_bits, codebooks)
         self.buffers = {}
         for l in (range(cfg.n_layers) if layers is None else layers):
@@ -246,7 +272,11 @@ class KVQCache:
     def bind(self, layer):
         torch = self.torch
         sizes = kvq_layer_buffer_sizes(self.handle, layer)
-        bufs = [torch.zeros(max(s, 256) + 256, dtype=torch.uint8, device=self.device) for s in sizes]
+        bufs = []
+        for sz in sizes:
+            b = torch.empty(max(sz, 256) + 256, dtype=torch.uint8, device=self.device)
+            b.fill_(0 if self.fill is None else int(self.fill))
+            bufs.append(b)
         ptrs = []
         for b in bufs:
             p = b.data_ptr()
@@ -255,7 +285,12 @@ class KVQCache:
         self.buffers[layer] = (bufs, ptrs, sizes)
 
     def unbind(self, layer):
-        self.buffers.pop(layer, None)
+        """Detach a layer in the C handle, then release its buffers (after
+        the work already queued on the current stream has completed)."""
+        kvq_unbind_layer(self.handle, layer)
+        if layer in self.buffers:
+            self.torch.cuda.current_stream(self.device).synchronize()
+            del self.buffers[layer]
 
     def layout(self, layer):
         return kvq_block_layout(self.handle, layer)
@@ -270,24 +305,55 @@ class KVQCache:
     def _stream(self):
         return self.torch.cuda.current_stream(self.device).cuda_stream
 
+    def _check(self, x, name, dtype, shape):
+        torch = self.torch
+        if not isinstance(x, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch tensor")
+        if x.device != self.device:
+            raise ValueError(f"{name}: tensor on {x.device}, cache on {self.device}")
+        if x.dtype != dtype:
+            raise TypeError(f"{name}: dtype {x.dtype}, expected {dtype}")
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(x.shape)}, expected {tuple(shape)}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name}: tensor must be contiguous")
+
     def prefill(self, layer, k, v):
-        assert k.is_contiguous() and v.is_contiguous() and k.dtype == self.torch.float16
-        T = k.shape[2]
-        kvq_quantize_prefill(self.handle, layer, k.data_ptr(), v.data_ptr(), T,
+        """k, v: fp16 [B][Hkv][T][D] on the cache's device."""
+        c = self.cfg
+        if k.dim() != 4:
+            raise ValueError(f"k: expected [B, Hkv, T, D], got shape {tuple(k.shape)}")
+        shape = (c.batch, c.n_kv_heads, k.shape[2], c.head_dim)
+        self._check(k, "k", self.torch.float16, shape)
+        self._check(v, "v", self.torch.float16, shape)
+        kvq_quantize_prefill(self.handle, layer, k.data_ptr(), v.data_ptr(), shape[2],
                              self.workspace.data_ptr(), self._stream())
 
     def append(self, layer, k, v):
-        assert k.is_contiguous() and v.is_contiguous() and k.dtype == self.torch.float16
+        """k, v: fp16 [B][Hkv][D] (one token per unit)."""
+        c = self.cfg
+        shape = (c.batch, c.n_kv_heads, c.head_dim)
+        self._check(k, "k", self.torch.float16, shape)
+        self._check(v, "v", self.torch.float16, shape)
         kvq_append_token(self.handle, layer, k.data_ptr(), v.data_ptr(), self._stream())
 
     def decode(self, layer, q, out=None):
+        """q: fp16 [B][Hq][D]; out: fp32 [B][Hq][D] (allocated when None)."""
         torch = self.torch
-        assert q.is_contiguous() and q.dtype == torch.float16
+        c = self.cfg
+        shape = (c.batch, c.n_q_heads, c.head_dim)
+        self._check(q, "q", torch.float16, shape)
         if out is None:
-            out = torch.empty(q.shape, dtype=torch.float32, device=self.device)
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        self._check(out, "out", torch.float32, shape)
         kvq_decode_attn(self.handle, layer, q.data_ptr(), out.data_ptr(), self.workspace.data_ptr(),
                         self._stream())
         return out
+
+    def nonfinite_rows(self):
+        """Output rows with a non-finite element since the last call (waits
+        for the current stream; resets the count)."""
+        return kvq_decode_nonfinite_rows(self.handle, self.workspace.data_ptr(), self._stream())
 
     def state(self, layer):
         return kvq_layer_state(self.handle, layer)

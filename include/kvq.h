@@ -39,9 +39,12 @@
  * stream-ordered; the handle has no internal locking.
  *
  * Errors.  Argument, state and capacity checks run on the host before any
- * launch; a failing call returns its status and leaves host state and device
- * buffers untouched.  A failed launch returns KVQ_ERR_DEVICE (the host state
- * of that call is rolled back).  No C++ exception crosses this interface.
+ * launch; a call failing them returns its status and leaves host state and
+ * device buffers untouched.  A failed kernel launch returns KVQ_ERR_DEVICE;
+ * since a call may already have queued some of its kernels, the layer's
+ * device buffers can then hold a partial update, so the layer is marked
+ * empty: its appends and decodes return KVQ_ERR_STATE until the next
+ * kvq_quantize_prefill.  No C++ exception crosses this interface.
  *
  * Data types: fp16 = IEEE binary16 bit patterns in uint16 storage.
  */
@@ -200,9 +203,17 @@ kvq_status kvq_block_layout(const kvq_cache* cache, int32_t layer, kvq_block_lay
 /* Attach caller-owned device buffers to a layer (re-binding resets the layer). */
 kvq_status kvq_bind_layer(kvq_cache* cache, int32_t layer, void* const bufs[KVQ_NBUF]);
 
+/* Detach a layer's buffers (before the caller frees them): the layer becomes
+ * unbound and its device calls return KVQ_ERR_STATE until it is bound again.
+ * Calls already queued on a stream still use the old buffers, so the caller
+ * frees them only after those have completed.  Errors: KVQ_ERR_ARG. */
+kvq_status kvq_unbind_layer(kvq_cache* cache, int32_t layer);
+
 /* Bytes of device workspace kvq_decode_attn needs.  The workspace must be
  * zero-filled once before its first use; each decode call leaves its
- * completion counters at zero again.  One workspace serves one stream. */
+ * completion counters at zero again.  One workspace serves one stream.  Its
+ * last 4 bytes count the output rows that came out non-finite (see
+ * kvq_decode_nonfinite_rows). */
 kvq_status kvq_workspace_size(const kvq_cache* cache, size_t* bytes);
 
 /* Quantize a prompt of T tokens into a layer, replacing its contents.
@@ -214,10 +225,13 @@ kvq_status kvq_workspace_size(const kvq_cache* cache, size_t* bytes);
 kvq_status kvq_quantize_prefill(kvq_cache* cache, int32_t layer, const void* k, const void* v,
                                 int32_t T, void* workspace, void* stream);
 
-/* Append one token per unit.  k_new, v_new: device fp16 [B][Hkv][D].  The
- * token enters the fp16 window; when the window reaches W+F tokens its
- * oldest F tokens are quantized into the next body block (keys and values
- * together).  With inner keys and W = 0 the token is quantized at once.
+/* Append one token per unit.  k_new, v_new: device fp16 [B][Hkv][D].  While
+ * the layer holds fewer than S sink tokens (a prompt shorter than S) the
+ * token becomes the next fp16 sink, so the first S positions are always
+ * sinks.  Otherwise it enters the fp16 window; when the window reaches W+F
+ * tokens its oldest F tokens are quantized into the next body block (keys
+ * and values together).  With inner keys and W = 0 the token is quantized at
+ * once.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (before prefill), KVQ_ERR_CAPACITY. */
 kvq_status kvq_append_token(kvq_cache* cache, int32_t layer, const void* k_new,
                             const void* v_new, void* stream);
@@ -230,11 +244,22 @@ kvq_status kvq_append_token(kvq_cache* cache, int32_t layer, const void* k_new,
  * Numerical domain: with per-channel key groups (2/4/8-bit codes) the
  * product of each query element and its channel's key scale, q_c * s_c, is
  * formed in binary16 (as an exact hi + lo pair), so |q_c * s_c| must stay
- * below 65504 for every body block; beyond it the output is not finite.
- * Every other product on the path is exact or formed in fp32.
+ * below 65504 for every body block; beyond it the output row is not finite.
+ * Every other product on the path is exact or formed in fp32.  Each output
+ * row holding a non-finite element is counted in the workspace (read with
+ * kvq_decode_nonfinite_rows), so a caller can detect such inputs after the
+ * fact without inspecting the output.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (empty cache / unbound), KVQ_ERR_DEVICE. */
 kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, float* out,
                            void* workspace, void* stream);
+
+/* Output rows with a non-finite element written by the decodes that used this
+ * workspace since the last call (counted on the device by the merge step).
+ * Waits for the stream, reads the count into *rows and resets it; not for
+ * use under stream capture.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_DEVICE. */
+kvq_status kvq_decode_nonfinite_rows(const kvq_cache* cache, void* workspace, void* stream,
+                                     uint32_t* rows);
 
 /* Host-side token accounting of a layer: total tokens n, sink tokens,
  * quantized body tokens and fp16 window tokens (n = sinks + body + window). */

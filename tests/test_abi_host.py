@@ -33,7 +33,7 @@ def header_functions():
 
 def test_exports_every_declared_symbol():
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == len(K.EXPORTS), names
     L = C.CDLL(K.LIB_PATH)
     for n in names:
         assert hasattr(L, n), n
@@ -220,6 +220,11 @@ def test_call_order_and_capacity_errors_on_host():
         assert L.kvq_decode_attn(h, 0, None, fake, fake, stream) == K.KVQ_ERR_ARG
         assert K.kvq_layer_state(h, 0) == (0, 0, 0, 0)
         assert L.kvq_layer_state(h, 9, None, None, None, None) == K.KVQ_ERR_ARG
+        # an unbound layer refuses device work again until it is bound
+        assert L.kvq_unbind_layer(h, 0) == K.KVQ_OK
+        assert L.kvq_quantize_prefill(h, 0, fake, fake, 10, None, stream) == K.KVQ_ERR_STATE
+        assert L.kvq_unbind_layer(h, 7) == K.KVQ_ERR_ARG
+        assert L.kvq_decode_nonfinite_rows(h, None, stream, None) == K.KVQ_ERR_ARG
     finally:
         K.kvq_destroy(h)
     assert K.lib().kvq_destroy(None) == K.KVQ_OK
