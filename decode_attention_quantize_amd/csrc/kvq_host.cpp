@@ -381,9 +381,17 @@ kvq_status kvq_workspace_size(const kvq_cache* c, size_t* bytes) {
 }
 
 kvq_status kvq_decode_nonfinite_rows(const kvq_cache* c, void* workspace, void* stream, uint32_t* rows) {
-  if (!c || !workspace || !rows) return KVQ_ERR_ARG;
+  if (!c || !rows) return KVQ_ERR_ARG;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  uint32_t* dev = nonfinite_counter(*c, workspace);
+  uint32_t* dev = nullptr;
+  if (workspace) {
+    dev = nonfinite_counter(*c, workspace);
+  } else {  // the static scratch of the current device (kvq_decode_attn_static)
+    void* base = nullptr;
+    if (kvq::static_scratch(&base) != hipSuccess) return KVQ_ERR_DEVICE;
+    dev = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + kvq::kStaticPartialsBytes) +
+          kvq::kStaticMaxUnits;
+  }
   uint32_t v = 0;
   if (hipMemcpyAsync(&v, dev, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess)
@@ -575,6 +583,28 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + partials_padded(*c));
   j.nonfinite = nonfinite_counter(*c, workspace);
   j.ml_off = static_cast<int64_t>(c->units) * max_splits(*c) * c->G * kD;
+  return launch_decode(L, kind, j, reinterpret_cast<hipStream_t>(stream));
+}
+
+kvq_status kvq_decode_attn_static(kvq_cache* c, int32_t layer, const void* q, float* out, void* stream) {
+  if (!valid_layer(c, layer) || !q || !out) return KVQ_ERR_ARG;
+  Layer& L = c->layers[layer];
+  if (!L.bound || !L.filled || L.n == 0) return KVQ_ERR_STATE;
+  kvq::DecodeJob j{};
+  const DecodeKind kind = plan_decode(*c, L, j);
+  // partials sized by this call's split plan: o [units][nsplit][G][D] then
+  // (max, sum) [units][nsplit][G][2] (the LDS-staged layout [..][D + 2] has
+  // the same size); counters in the array's fixed tail
+  const size_t need = static_cast<size_t>(c->units) * j.nsplit * c->G * (kD + 2) * sizeof(float);
+  if (need > kvq::kStaticPartialsBytes || c->units > kvq::kStaticMaxUnits) return KVQ_ERR_CAPACITY;
+  void* base = nullptr;
+  if (kvq::static_scratch(&base) != hipSuccess) return KVQ_ERR_DEVICE;
+  j.q = static_cast<const uint16_t*>(q);
+  j.out = out;
+  j.partials = static_cast<float*>(base);
+  j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(base) + kvq::kStaticPartialsBytes);
+  j.nonfinite = j.counters + kvq::kStaticMaxUnits;
+  j.ml_off = static_cast<int64_t>(c->units) * j.nsplit * c->G * kD;
   return launch_decode(L, kind, j, reinterpret_cast<hipStream_t>(stream));
 }
 

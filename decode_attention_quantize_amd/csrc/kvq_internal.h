@@ -147,6 +147,16 @@ hipError_t resident_waves(Kernel kern, std::atomic<int>* cache, int* out) {
   return hipSuccess;
 }
 
+// Static decode scratch (kvq_static.hip): a fixed device array per GPU for the
+// decode entry point that allocates nothing.  Partials first, then a fixed
+// tail of per-unit arrival counters whose last word is the non-finite row
+// count.
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr size_t kStaticCounterBytes = size_t(64) << 10;
+constexpr size_t kStaticPartialsBytes = kStaticScratchBytes - kStaticCounterBytes;
+constexpr int kStaticMaxUnits = static_cast<int>(kStaticCounterBytes / 4) - 1;
+hipError_t static_scratch(void** out);
+
 // Device helpers: tests for non-finite values on the bit pattern.  The bits
 // pass through an empty asm statement, so that no floating-point assumption
 // (the decode files are compiled without NaN semantics, under which a test

@@ -21,7 +21,8 @@ KVQ_BUF_BODY, KVQ_BUF_FP16 = 0, 1
 
 EXPORTS = ("kvq_create", "kvq_destroy", "kvq_layer_buffer_sizes", "kvq_block_layout",
            "kvq_bind_layer", "kvq_unbind_layer", "kvq_workspace_size", "kvq_quantize_prefill",
-           "kvq_append_token", "kvq_decode_attn", "kvq_decode_nonfinite_rows", "kvq_layer_state",
+           "kvq_append_token", "kvq_decode_attn", "kvq_decode_attn_static",
+           "kvq_decode_nonfinite_rows", "kvq_layer_state",
            "kvq_average_bits", "kvq_status_str", "kvq_fit_rate_distortion", "kvq_waterfill_bits",
            "kvq_allocate_bits")
 
@@ -80,6 +81,7 @@ def lib():
         L.kvq_quantize_prefill.argtypes = [pcache, i32, vp, vp, i32, vp, vp]
         L.kvq_append_token.argtypes = [pcache, i32, vp, vp, vp]
         L.kvq_decode_attn.argtypes = [pcache, i32, vp, vp, vp, vp]
+        L.kvq_decode_attn_static.argtypes = [pcache, i32, vp, vp, vp]
         L.kvq_layer_state.argtypes = [pcache, i32] + [C.POINTER(C.c_int32)] * 4
         dp, ip = C.POINTER(C.c_double), C.POINTER(C.c_int32)
         L.kvq_average_bits.argtypes = [pcache, dp, dp]
@@ -164,6 +166,10 @@ def kvq_append_token(handle, layer, k_ptr, v_ptr, stream):
 
 def kvq_decode_attn(handle, layer, q_ptr, out_ptr, ws_ptr, stream):
     _check(lib().kvq_decode_attn(handle, layer, q_ptr, out_ptr, ws_ptr, stream), "kvq_decode_attn")
+
+
+def kvq_decode_attn_static(handle, layer, q_ptr, out_ptr, stream):
+    _check(lib().kvq_decode_attn_static(handle, layer, q_ptr, out_ptr, stream), "kvq_decode_attn_static")
 
 
 def kvq_layer_state(handle, layer):
@@ -348,6 +354,16 @@ class KVQCache:
         self._check(out, "out", torch.float32, shape)
         kvq_decode_attn(self.handle, layer, q.data_ptr(), out.data_ptr(), self.workspace.data_ptr(),
                         self._stream())
+        return out
+
+    def decode_static(self, layer, q, out):
+        """kvq_decode_attn_static: the library's static scratch instead of
+        the workspace (out must be given: the call allocates nothing)."""
+        c = self.cfg
+        shape = (c.batch, c.n_q_heads, c.head_dim)
+        self._check(q, "q", self.torch.float16, shape)
+        self._check(out, "out", self.torch.float32, shape)
+        kvq_decode_attn_static(self.handle, layer, q.data_ptr(), out.data_ptr(), self._stream())
         return out
 
     def nonfinite_rows(self):

@@ -253,10 +253,33 @@ kvq_status kvq_append_token(kvq_cache* cache, int32_t layer, const void* k_new,
 kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, float* out,
                            void* workspace, void* stream);
 
+/* kvq_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP stream/graph capture, serving loops
+ * with a fixed memory footprint, harnesses that forbid hipMalloc.  The call
+ * allocates nothing (no hipMalloc, no allocating library routine): the split
+ * partials, the per-unit arrival counters and the non-finite row count live
+ * in a static device array of the library, KVQ_STATIC_SCRATCH_BYTES (32 MiB)
+ * per GPU, held by every GPU the library runs on until the process ends.
+ * Arguments, layouts and results are those of kvq_decode_attn; q and out are
+ * still the caller's.  The first call on a device looks up and clears that
+ * device's array and waits for the device, so make one call before any
+ * stream capture.  Every call on a GPU shares that GPU's array: calls that
+ * may overlap on one GPU (different streams, or several threads) race and
+ * must be serialized by the caller, e.g. issued on one stream.  The non-finite
+ * row count of these calls is read with kvq_decode_nonfinite_rows(cache,
+ * NULL, ...).
+ * Errors: those of kvq_decode_attn, and KVQ_ERR_CAPACITY when the layer's
+ * split plan needs more than the array's 32 MiB - 64 KiB of partials
+ * (units * splits * (Hq/Hkv) * 520 bytes) or more than 16383 units. */
+#define KVQ_STATIC_SCRATCH_BYTES (32u << 20)
+kvq_status kvq_decode_attn_static(kvq_cache* cache, int32_t layer, const void* q, float* out,
+                                  void* stream);
+
 /* Output rows with a non-finite element written by the decodes that used this
- * workspace since the last call (counted on the device by the merge step).
- * Waits for the stream, reads the count into *rows and resets it; not for
- * use under stream capture.
+ * workspace since the last call (counted on the device by the merge step);
+ * workspace NULL reads the count of kvq_decode_attn_static calls on the
+ * current device.  Waits for the stream, reads the count into *rows and
+ * resets it; not for use under stream capture.
  * Errors: KVQ_ERR_ARG, KVQ_ERR_DEVICE. */
 kvq_status kvq_decode_nonfinite_rows(const kvq_cache* cache, void* workspace, void* stream,
                                      uint32_t* rows);
