@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -618,12 +619,9 @@ __device__ __forceinline__ uint16_t d2h_odd(double x) {
 // Shared memory of prefill_kernel (dynamic size, offsets in bytes):
 //   k16, v16 [32][D] fp16 | ck [32][D] key codes | cv value codes: [32][D]
 //   (3-bit) or lane-chunk order [64 chunks][64 elements] | exk, exv [32][D]
-//   outlier masks (layers with outliers) ; the Hadamard pass uses a [16][D]
-//   binary64 buffer over the code area (dead until the codes are written).
+//   outlier masks (layers with outliers).
 constexpr int kPfK = 0, kPfV = 8192, kPfCk = 16384, kPfCv = 20480, kPfExk = 24576, kPfExv = 28672;
-__host__ __device__ constexpr int prefill_smem(bool outk, bool rot) {
-  return (rot || outk) ? 32768 : 24576;
-}
+__host__ __device__ constexpr int prefill_smem(bool outk) { return outk ? 32768 : 24576; }
 
 // Element of lane chunk l = 16 (j / 8) + (c % 16) that holds code (token j,
 // channel c) of the value layout: e = 8 (c / 16) + j % 8.
@@ -631,32 +629,84 @@ __device__ __forceinline__ int vchunk_off(int j, int c) {
   return (16 * (j >> 3) + (c & 15)) * 64 + 8 * (c >> 4) + (j & 7);
 }
 
+// rne(fl32(a / b)) -- the correctly rounded quotient rounded to an integer --
+// from a reciprocal estimate: t = a * rcp(b) lies within 1.5 * 2^-23 |a / b|
+// of the exact quotient (v_rcp_f32 is accurate to 1 ulp), i.e. within 2^-13
+// for the |a / b| <= 512 of every code formula here, while fl32(a / b) lies
+// within 2^-15 of it.  Unless t is within 2^-10 of a rounding boundary
+// k + 1/2, both therefore round to the same integer; near one, the quotient
+// is recomputed with the correctly rounded division.
+__device__ __forceinline__ float rint_quot(float a, float b) {
+  const float t = a * __builtin_amdgcn_rcpf(b);
+  const float r = rintf(t);
+  if (fabsf(fabsf(t - r) - 0.5f) < 0x1p-10f) return rintf(__fdiv_rn(a, b));
+  return r;
+}
+__device__ __forceinline__ int asym_code_fast(float x, float mn, uint16_t s, int Q) {
+  if (s == 0) return 0;
+  return static_cast<int>(fminf(fmaxf(rint_quot(__fsub_rn(x, mn), h2f(s)), 0.f), static_cast<float>(Q)));
+}
+__device__ __forceinline__ int sym_code_fast(float x, uint16_t s, int bits) {
+  if (s == 0) return 0;
+  const int Qs = (1 << (bits - 1)) - 1;
+  const float r = fminf(fmaxf(rint_quot(x, h2f(s)), static_cast<float>(-Qs)), static_cast<float>(Qs));
+  return static_cast<int>(r) + (1 << (bits - 1));
+}
+// Codebook codes: u = fl32((x - mn) / s) in [0, 1] against the seven level
+// midpoints; the reciprocal estimate of u (within 2^-21 of it) decides unless
+// it lies within 2^-18 of a midpoint.
+__device__ __forceinline__ int nuq_code_fast(float x, float mn, uint16_t s, const float (&mid)[7]) {
+  if (s == 0) return 0;
+  const float d = __fsub_rn(x, mn), sv = h2f(s);
+  float u = d * __builtin_amdgcn_rcpf(sv);
+  bool near = false;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) near |= fabsf(u - mid[j]) < 0x1p-18f;
+  if (near) u = __fdiv_rn(d, sv);
+  int c = 0;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) c += u > mid[j] ? 1 : 0;
+  return c;
+}
+__device__ __forceinline__ void nuq_mids(const uint16_t* lev, float (&mid)[7]) {
+#pragma unroll
+  for (int j = 0; j < 7; ++j) mid[j] = __fmul_rn(__fadd_rn(h2f(lev[j]), h2f(lev[j + 1])), 0.5f);
+}
+
 // One per-token group (W channels of one row) with its values in registers:
 // the arithmetic of token_group, written per element instead of per lane.
-template <int W>
-__device__ __forceinline__ void group_in_regs(const uint16_t (&xh)[W], uint64_t exm, int bits, bool nuq,
+// SPLIT lanes (adjacent, 1 or 2) share a group: each holds N = W / SPLIT of
+// its channels and the statistics are joined across the pair.
+template <int N, int SPLIT>
+__device__ __forceinline__ void group_in_regs(const uint16_t (&xh)[N], uint64_t exm, int bits, bool nuq,
                                               const uint16_t* lev, bool hybrid, int rnum, int rden, bool tern,
-                                              uint8_t (&code)[W], uint16_t& s, uint16_t& z) {
+                                              uint8_t (&code)[N], uint16_t& s, uint16_t& z) {
+  constexpr int W = N * SPLIT;  // group size
+  auto join_max = [](float v) __attribute__((always_inline)) { return SPLIT == 2 ? fmaxf(v, xshflf<1>(v)) : v; };
+  auto join_min = [](float v) __attribute__((always_inline)) { return SPLIT == 2 ? fminf(v, xshflf<1>(v)) : v; };
   if (tern) {
     float a = 0.f;
 #pragma unroll
-    for (int i = 0; i < W; ++i) a = fmaxf(a, ((exm >> i) & 1u) ? 0.f : fabsf(h2f(xh[i])));
+    for (int i = 0; i < N; ++i) a = fmaxf(a, ((exm >> i) & 1u) ? 0.f : fabsf(h2f(xh[i])));
+    a = join_max(a);
     s = f2h(a);
     z = static_cast<uint16_t>(s ^ 0x8000u);
     const float sv = h2f(s);
 #pragma unroll
-    for (int i = 0; i < W; ++i)
-      code[i] = static_cast<uint8_t>(s == 0 ? 1 : static_cast<int>(fminf(fmaxf(rintf(h2f(xh[i]) / sv), -1.f), 1.f)) + 1);
+    for (int i = 0; i < N; ++i)
+      code[i] = static_cast<uint8_t>(s == 0 ? 1 : static_cast<int>(fminf(fmaxf(rint_quot(h2f(xh[i]), sv), -1.f), 1.f)) + 1);
     return;
   }
   float mn = __int_as_float(0x7f800000), mx = __int_as_float(0xff800000);
 #pragma unroll
-  for (int i = 0; i < W; ++i) {
+  for (int i = 0; i < N; ++i) {
     if ((exm >> i) & 1u) continue;
     const float x = h2f(xh[i]);
     mn = fminf(mn, x);
     mx = fmaxf(mx, x);
   }
+  mn = join_min(mn);
+  mx = join_max(mx);
   const bool any = mn <= mx;
   bool sym = false;
   if (hybrid) {
@@ -664,12 +714,15 @@ __device__ __forceinline__ void group_in_regs(const uint16_t (&xh)[W], uint64_t 
     int64_t sum = 0;
     float amn = h2f(xh[0]), amx = amn;
 #pragma unroll
-    for (int i = 0; i < W; ++i) {
+    for (int i = 0; i < N; ++i) {
       sum += h2fixed(xh[i]);
       const float x = h2f(xh[i]);
       amn = fminf(amn, x);
       amx = fmaxf(amx, x);
     }
+    if constexpr (SPLIT == 2) sum += xshfl64<1>(sum);
+    amn = join_min(amn);
+    amx = join_max(amx);
     const int64_t lhs = static_cast<int64_t>(rden) * (sum < 0 ? -sum : sum);
     const int64_t rhs = static_cast<int64_t>(rnum) * W * (h2fixed(f2h(amx)) - h2fixed(f2h(amn)));
     sym = lhs <= rhs;
@@ -677,40 +730,53 @@ __device__ __forceinline__ void group_in_regs(const uint16_t (&xh)[W], uint64_t 
   if (sym) {
     float a = 0.f;
 #pragma unroll
-    for (int i = 0; i < W; ++i) a = fmaxf(a, fabsf(h2f(xh[i])));
+    for (int i = 0; i < N; ++i) a = fmaxf(a, fabsf(h2f(xh[i])));
+    a = join_max(a);
     const uint16_t sv = sym_scale(a, bits);
 #pragma unroll
-    for (int i = 0; i < W; ++i) code[i] = static_cast<uint8_t>(sym_code(h2f(xh[i]), sv, bits));
+    for (int i = 0; i < N; ++i) code[i] = static_cast<uint8_t>(sym_code_fast(h2f(xh[i]), sv, bits));
     s = sv | 0x8000;
     z = 0;
   } else if (nuq) {
     nuq_params(mn, mx, any, s, z);
+    float mid[7];
+    nuq_mids(lev, mid);
 #pragma unroll
-    for (int i = 0; i < W; ++i) code[i] = static_cast<uint8_t>(nuq_code(h2f(xh[i]), mn, s, lev));
+    for (int i = 0; i < N; ++i) code[i] = static_cast<uint8_t>(nuq_code_fast(h2f(xh[i]), mn, s, mid));
   } else {
     const int Q = (1 << bits) - 1;
     asym_params(mn, mx, any, Q, s, z);
 #pragma unroll
-    for (int i = 0; i < W; ++i) code[i] = static_cast<uint8_t>(asym_code(h2f(xh[i]), mn, s, Q));
+    for (int i = 0; i < N; ++i) code[i] = static_cast<uint8_t>(asym_code_fast(h2f(xh[i]), mn, s, Q));
   }
 }
 
 // All per-token group tasks of one tensor of the block: task = (row j,
-// group g), W channels.  Codes go to LDS (keys and 3-bit values row-major,
-// 2/4/8-bit values in lane-chunk order), parameters straight to the record.
+// group g, part h), N = W / SPLIT channels of the group; the SPLIT tasks of
+// a group are adjacent lanes.  Codes go to LDS (keys and 3-bit values
+// row-major, 2/4/8-bit values in lane-chunk order), parameters straight to
+// the record.  Every lane of the block runs the same number of loop trips
+// (the pair exchanges need both lanes of a pair active).
 template <int W>
 __device__ void group_tasks(const uint8_t* sm, int src_off, int ex_off, bool has_ex, int code_off, bool chunk_order,
                             int nrows, int bits, bool nuq, const uint16_t* lev, bool hybrid, int rnum, int rden,
                             bool tern, uint16_t* meta, int meta_kind) {
+  constexpr int SPLIT = W == 64 ? 2 : 1;
+  constexpr int N = W / SPLIT;
   constexpr int ng = D / W;
   const uint16_t* x16 = reinterpret_cast<const uint16_t*>(sm + src_off);
   uint8_t* codes = const_cast<uint8_t*>(sm) + code_off;
-  for (int task = threadIdx.x; task < nrows * ng; task += blockDim.x) {
-    const int j = task / ng, g = task % ng;
-    uint16_t xh[W];
-    const uint4* xs = reinterpret_cast<const uint4*>(x16 + j * D + g * W);
+  const int ntask = nrows * ng * SPLIT;
+  for (int t0 = 0; t0 < ntask; t0 += blockDim.x) {
+    const int task = t0 + static_cast<int>(threadIdx.x);
+    const bool live = task < ntask;  // a pair's two lanes are live together (ntask is a multiple of SPLIT)
+    const int gt = live ? task / SPLIT : 0, part = task % SPLIT;
+    const int j = gt / ng, g = gt % ng;
+    const int c0 = g * W + part * N;  // first channel of this lane's part
+    uint16_t xh[N];
+    const uint4* xs = reinterpret_cast<const uint4*>(x16 + j * D + c0);
 #pragma unroll
-    for (int q = 0; q < W / 8; ++q) {
+    for (int q = 0; q < N / 8; ++q) {
       const uint4 v = xs[q];
       const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -721,22 +787,24 @@ __device__ void group_tasks(const uint8_t* sm, int src_off, int ex_off, bool has
     }
     uint64_t exm = 0;
     if (has_ex) {
-      const uint8_t* ex = sm + ex_off + j * D + g * W;
+      const uint8_t* ex = sm + ex_off + j * D + c0;
 #pragma unroll
-      for (int i = 0; i < W; ++i) exm |= static_cast<uint64_t>(ex[i] != 0) << i;
+      for (int i = 0; i < N; ++i) exm |= static_cast<uint64_t>(ex[i] != 0) << i;
     }
-    uint8_t code[W];
+    uint8_t code[N];
     uint16_t s, z;
-    group_in_regs<W>(xh, exm, bits, nuq, lev, hybrid, rnum, rden, tern, code, s, z);
+    group_in_regs<N, SPLIT>(xh, exm, bits, nuq, lev, hybrid, rnum, rden, tern, code, s, z);
+    if (!live) continue;
     if (chunk_order) {
 #pragma unroll
-      for (int i = 0; i < W; ++i) codes[vchunk_off(j, g * W + i)] = code[i];
+      for (int i = 0; i < N; ++i) codes[vchunk_off(j, c0 + i)] = code[i];
     } else {
-      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + j * D + g * W);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(codes + j * D + c0);
 #pragma unroll
-      for (int q = 0; q < W / 4; ++q)
+      for (int q = 0; q < N / 4; ++q)
         dst[q] = code[4 * q] | (code[4 * q + 1] << 8) | (code[4 * q + 2] << 16) | (static_cast<uint32_t>(code[4 * q + 3]) << 24);
     }
+    if (part != 0) continue;
     if (meta_kind == 0) {  // inner keys: [32][ng] (s, z)
       reinterpret_cast<uint32_t*>(meta)[j * ng + g] = s | (static_cast<uint32_t>(z) << 16);
     } else {  // values: s[ng][32] then z[ng][32]
@@ -837,30 +905,57 @@ __device__ void pack_vchunks_fast(const uint8_t* cvc, int bits, uint8_t* dst) {
   }
 }
 
-// Exact fp64 Walsh-Hadamard transform of the value rows [0, nrows) in place
-// (fp16 in, fp16(fl64(S * c)) out), sixteen rows per pass through a binary64
-// buffer; every butterfly of a stage, then a barrier.
-__device__ void hadamard_rows_fast(uint8_t* sm, int nrows, double c) {
+// Exact fp64 Walsh-Hadamard transform of the value rows in place (fp16 in,
+// fp16(fl64(S * c)) out): sixteen lanes per row, eight channels per lane
+// (channel 8 cc + i), eight rows per pass.  Butterflies over channel bits
+// 0-2 stay in the lane, over bits 3-6 they pair lanes cc and cc ^ m through
+// two 32-bit swizzles per binary64 value.  Partial sums of fp16 inputs are
+// exact in binary64, so the order of the stages does not matter.  Rows past
+// the block's tokens hold zeros and stay zero.
+__device__ void hadamard_rows_fast(uint8_t* sm, double c) {
   uint16_t* v16 = reinterpret_cast<uint16_t*>(sm + kPfV);
-  double(*had)[D] = reinterpret_cast<double(*)[D]>(sm + kPfCk);  // over the code area
-  const int t = threadIdx.x;
-  for (int r0 = 0; r0 < nrows; r0 += 16) {
-    const int rows = min(16, nrows - r0);
-    for (int i = t; i < rows * D; i += blockDim.x) had[i / D][i % D] = static_cast<double>(h2f(v16[(r0 + i / D) * D + i % D]));
-    __syncthreads();
-    for (int h = 1; h < D; h <<= 1) {
-      for (int i = t; i < rows * (D / 2); i += blockDim.x) {
-        const int j = i / (D / 2), p = i % (D / 2);
-        const int lo = ((p / h) * 2 * h) + (p % h);
-        const double a = had[j][lo], b = had[j][lo + h];
-        had[j][lo] = a + b;
-        had[j][lo + h] = a - b;
-      }
-      __syncthreads();
+  const int t = threadIdx.x, cc = t & 15;
+  for (int r0 = 0; r0 < kBlockTokens; r0 += 8) {
+    const int j = r0 + (t >> 4);
+    uint4* row = reinterpret_cast<uint4*>(v16 + j * D) + cc;
+    const uint4 w = *row;
+    const uint32_t w4[4] = {w.x, w.y, w.z, w.w};
+    double x[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = static_cast<double>(h2f(static_cast<uint16_t>(w4[e] & 0xffffu)));
+      x[2 * e + 1] = static_cast<double>(h2f(static_cast<uint16_t>(w4[e] >> 16)));
     }
-    for (int i = t; i < rows * D; i += blockDim.x) v16[(r0 + i / D) * D + i % D] = d2h_odd(had[i / D][i % D] * c);
-    __syncthreads();
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (!(i & h)) {
+          const double a = x[i], b = x[i + h];
+          x[i] = a + b;
+          x[i + h] = a - b;
+        }
+    auto xor_lanes = [&](auto mc) __attribute__((always_inline)) {
+      constexpr int M = decltype(mc)::value;
+      const bool hi = (cc & M) != 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int64_t bits = __double_as_longlong(x[i]);
+        const double o = __longlong_as_double(xshfl64<M>(bits));
+        x[i] = hi ? o - x[i] : x[i] + o;
+      }
+    };
+    xor_lanes(std::integral_constant<int, 1>{});
+    xor_lanes(std::integral_constant<int, 2>{});
+    xor_lanes(std::integral_constant<int, 4>{});
+    xor_lanes(std::integral_constant<int, 8>{});
+    uint32_t o4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o4[e] = static_cast<uint32_t>(d2h_odd(x[2 * e] * c)) | (static_cast<uint32_t>(d2h_odd(x[2 * e + 1] * c)) << 16);
+    *row = make_uint4(o4[0], o4[1], o4[2], o4[3]);
   }
+  __syncthreads();
 }
 
 __global__ void __launch_bounds__(128) prefill_kernel(LayerDesc L, QuantJob J) {
@@ -916,7 +1011,7 @@ __global__ void __launch_bounds__(128) prefill_kernel(LayerDesc L, QuantJob J) {
       k16[j * D + t] = f2h(fminf(fmaxf(ldexpf(h2f(k16[j * D + t]), sh), -65504.f), 65504.f));
     __syncthreads();
   }
-  if (J.rotate_v) hadamard_rows_fast(sm, nrows, L.had_scale);
+  if (J.rotate_v) hadamard_rows_fast(sm, L.had_scale);
 
   // ---- code tiles start at zero (rows past nrows pack as code 0)
   {
@@ -965,16 +1060,18 @@ __global__ void __launch_bounds__(128) prefill_kernel(LayerDesc L, QuantJob J) {
       float a = 0.f;
       for (int j = 0; j < nrows; ++j) a = fmaxf(a, fabsf(h2f(k16[j * D + t])));
       const uint16_t sv = sym_scale(a, L.kb);
-      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(sym_code(h2f(k16[j * D + t]), sv, L.kb));
+      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(sym_code_fast(h2f(k16[j * D + t]), sv, L.kb));
       s = sv | 0x8000;
       z = 0;
     } else if (L.nuq) {
       nuq_params(mn, mx, any, s, z);
-      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(nuq_code(h2f(k16[j * D + t]), mn, s, L.lev_k));
+      float mid[7];
+      nuq_mids(L.lev_k, mid);
+      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(nuq_code_fast(h2f(k16[j * D + t]), mn, s, mid));
     } else {
       const int Q = (1 << L.kb) - 1;
       asym_params(mn, mx, any, Q, s, z);
-      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(asym_code(h2f(k16[j * D + t]), mn, s, Q));
+      for (int j = 0; j < nrows; ++j) ck[j * D + t] = static_cast<uint8_t>(asym_code_fast(h2f(k16[j * D + t]), mn, s, Q));
     }
     uint16_t* km = reinterpret_cast<uint16_t*>(rec + L.off_km);
     km[t] = s;
@@ -1110,7 +1207,7 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
   // whole 256-byte rows)
   const bool aligned = ((reinterpret_cast<uintptr_t>(job.k_src) | reinterpret_cast<uintptr_t>(job.v_src)) & 15) == 0;
   if (job.tok0 == 0 && L.k_hi == 0 && aligned) {
-    const size_t smem = prefill_smem(L.outk > 0, job.rotate_v != 0);
+    const size_t smem = prefill_smem(L.outk > 0);
     hipLaunchKernelGGL(prefill_kernel, dim3(job.nblocks, L.units), dim3(128), smem, s, L, job);
     return hipGetLastError();
   }

@@ -1,0 +1,70 @@
+// kvq_stream.hip -- the read ceiling of the decode's access pattern: a kernel
+// that streams a buffer the way the split decode streams body records (one
+// wavefront per split, a contiguous run of 1 KiB wave loads per split,
+// global_load_lds into a two-slot LDS ring with the same vmcnt waits) and
+// does no arithmetic on the data beyond one LDS read per loaded chunk.  Its
+// duration against the bytes read is the bandwidth an HBM-bound decode of
+// that shape can reach on the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "../../include/kvq.h"
+#include "kvq_internal.h"
+#include "kvq_mfma.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kChunk = 4096;  // bytes per ring slot (four 1 KiB wave loads: a C5-sized record)
+
+__global__ void __launch_bounds__(64) stream_read_kernel(const uint8_t* src, int64_t chunks, int64_t per_split,
+                                                         uint32_t* sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t ring0[kChunk];
+  __shared__ __attribute__((aligned(16))) uint8_t ring1[kChunk];
+  const int l = threadIdx.x;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * per_split;
+  const int64_t c1 = c0 + per_split < chunks ? c0 + per_split : chunks;
+  auto issue = [&](int64_t c, lds_u8* dst) __attribute__((always_inline)) {
+    const uint8_t* p = src + c * kChunk;
+#pragma unroll
+    for (int k = 0; k < kChunk / 1024; ++k) __builtin_amdgcn_global_load_lds(p + k * 1024 + l * 16, dst + k * 1024, 16, 0, 0);
+  };
+  lds_u8* const s0 = (lds_u8*)ring0;
+  lds_u8* const s1 = (lds_u8*)ring1;
+  uint32_t acc = 0;
+  if (c0 < c1) issue(c0, s0);
+  for (int64_t c = c0; c < c1; ++c) {
+    lds_u8* cur = ((c - c0) & 1) ? s1 : s0;
+    lds_u8* nxt = ((c - c0) & 1) ? s0 : s1;
+    if (c + 1 < c1) {
+      issue(c + 1, nxt);
+      wait_vm<kChunk / 1024>();
+    } else {
+      wait_vm<0>();
+    }
+    const uint32_t v = dsr4<0>(lds_off(cur) + 4 * l);
+    lds_wait();
+    acc ^= v;
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;  // keeps the reads; (almost) never stores
+}
+
+}  // namespace
+}  // namespace kvq
+
+extern "C" {
+
+kvq_status kvq_stream_read(const void* src, size_t bytes, int32_t splits, uint32_t* sink, void* stream) {
+  if (!src || !sink || splits < 1) return KVQ_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(src) & 255) || bytes % kvq::kChunk != 0) return KVQ_ERR_ARG;
+  const int64_t chunks = static_cast<int64_t>(bytes / kvq::kChunk);
+  if (chunks == 0) return KVQ_OK;
+  const int64_t per = (chunks + splits - 1) / splits;
+  const int64_t grid = (chunks + per - 1) / per;
+  hipLaunchKernelGGL(kvq::stream_read_kernel, dim3(static_cast<uint32_t>(grid)), dim3(64), 0,
+                     reinterpret_cast<hipStream_t>(stream), static_cast<const uint8_t*>(src), chunks, per, sink);
+  return hipGetLastError() == hipSuccess ? KVQ_OK : KVQ_ERR_DEVICE;
+}
+
+}  // extern "C"

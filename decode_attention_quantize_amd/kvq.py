@@ -24,7 +24,7 @@ EXPORTS = ("kvq_create", "kvq_destroy", "kvq_layer_buffer_sizes", "kvq_block_lay
            "kvq_append_token", "kvq_decode_attn", "kvq_decode_attn_static",
            "kvq_decode_nonfinite_rows", "kvq_layer_state",
            "kvq_average_bits", "kvq_status_str", "kvq_fit_rate_distortion", "kvq_waterfill_bits",
-           "kvq_allocate_bits")
+           "kvq_allocate_bits", "kvq_stream_read")
 
 
 class kvq_config(C.Structure):
@@ -88,6 +88,7 @@ def lib():
         L.kvq_fit_rate_distortion.argtypes = [i32, dp, dp, dp, dp]
         L.kvq_waterfill_bits.argtypes = [i32, dp, dp, dp, C.c_double, dp]
         L.kvq_allocate_bits.argtypes = [i32, dp, dp, dp, ip, i32, i32, ip]
+        L.kvq_stream_read.argtypes = [vp, C.c_size_t, i32, vp, vp]
         for name in EXPORTS:
             if name != "kvq_status_str":
                 getattr(L, name).restype = C.c_int
@@ -183,6 +184,11 @@ def kvq_average_bits(handle):
     a, b = C.c_double(), C.c_double()
     _check(lib().kvq_average_bits(handle, C.byref(a), C.byref(b)), "kvq_average_bits")
     return a.value, b.value
+
+
+def kvq_stream_read(src_ptr, nbytes, splits, sink_ptr, stream):
+    """Read-ceiling kernel of the decode's access pattern (measurement helper)."""
+    _check(lib().kvq_stream_read(src_ptr, nbytes, splits, sink_ptr, stream), "kvq_stream_read")
 
 
 # ---------------------------------------------------------------- offline bit allocation

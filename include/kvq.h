@@ -299,6 +299,17 @@ kvq_status kvq_layer_state(const kvq_cache* cache, int32_t layer, int32_t* n, in
  * Either pointer may be NULL.  Errors: KVQ_ERR_ARG. */
 kvq_status kvq_average_bits(const kvq_cache* cache, double* code_bits, double* stored_bits);
 
+/* Read ceiling of the decode's access pattern (measurement helper): streams
+ * `bytes` of device memory at `src` the way kvq_decode_attn streams body
+ * records -- `splits` wavefronts, each reading a contiguous run of 4 KiB
+ * chunks as 1 KiB wave loads into a two-slot LDS ring -- with no arithmetic
+ * on the data.  Its duration against `bytes` is the read bandwidth a decode
+ * of that shape can reach.  src: 256-byte aligned, bytes a multiple of 4096;
+ * sink: device uint32[splits], written only in the (practically never) case
+ * that a split's XOR of sampled words equals 0x9e3779b9.  Asynchronous on
+ * the stream.  Errors: KVQ_ERR_ARG, KVQ_ERR_DEVICE. */
+kvq_status kvq_stream_read(const void* src, size_t bytes, int32_t splits, uint32_t* sink, void* stream);
+
 /* Static text for a status code. */
 const char* kvq_status_str(kvq_status s);
 
