@@ -217,7 +217,12 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // the key products q * s the same way (row 1 of the score tiles, added
   // to row 0 before the softmax).
   constexpr bool kPackLo = G == 8 || G == 4 || G == 1;
-  constexpr bool kPackK = G == 1 && !INNER;
+  // per-channel keys pack the key products the same way: rows G..2G-1 of
+  // the score tiles take the lo parts of q * s (one MFMA per K-step and tile
+  // instead of two, half the accumulation chain); they are added onto rows
+  // 0..G-1 in the same lane (G = 1) or by the permlane swap that folds the
+  // two tiles (G = 4, 8)
+  constexpr bool kPackK = !INNER && (G == 1 || G == 4 || G == 8);
   static_assert(!PLO || kPackLo, "the weights' lo parts ride in the packed lo rows");
   auto fold = [&](float a, float b) __attribute__((always_inline)) {
     return kFold == 32 ? swap32(a, b).x : swap16(a, b).x;
@@ -237,11 +242,33 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   }
   asm volatile("" : "+s"(unp.one2));
 
+  // Key rows of 4- and 8-bit per-channel keys sit in LDS with the 16-byte
+  // chunks of row r XOR-swizzled: chunk k at position k ^ f(r), f(r) =
+  // (r / (16 / chunks per row)) mod (chunks per row).  The 16 rows a K-step
+  // reads (one per lane of a row of 16) then fall in 16 different groups of
+  // four banks instead of two (8-bit) or four (4-bit) groups.  The DMA does
+  // the swizzle for free: each lane picks the global chunk it loads.
+  constexpr bool kSwz = !INNER && (KB == 4 || KB == 8);
+  constexpr int kCpr = KB;                        // 16-byte chunks per key row (16 KB bytes)
+  constexpr int kKeyLoads = kSwz ? 2 * KB / 4 : 0;  // 1 KiB loads covering the key rows
+  // global offset inside a 1 KiB load for this lane (even / odd load index)
+  auto swz_off = [&](int k) __attribute__((always_inline)) {
+    const int p = 64 * k + l;                     // LDS chunk this lane fills
+    return 16 * (p ^ ((p >> 4) & (kCpr - 1))) - 1024 * k;
+  };
+  const int dma_off0 = kSwz ? swz_off(0) : 16 * l;
+  const int dma_off1 = kSwz ? swz_off(1) : 16 * l;
+  // LDS byte offsets of this lane's key chunks (K-steps of tile 0; tile 1
+  // rows are 16 further and share the swizzle)
+  const int kswz = kSwz ? (KB == 8 ? (n16 >> 1) & 7 : (n16 >> 2) & 3) : 0;
+  const uint32_t koff0 = KB == 8 ? n16 * 128 + 16 * ((2 * g4) ^ kswz) : n16 * 16 * KB + 4 * KB * g4 + (kSwz ? 16 * (g4 ^ kswz) - 4 * KB * g4 : 0);
+  const uint32_t koff1 = KB == 8 ? n16 * 128 + 16 * ((2 * g4 + 1) ^ kswz) : koff0;
+
   // ---- query operand (natural channel order per K-step)
   half8 qa[4];
   {
-    const bool live = n16 < (kPackK ? 2 : G);  // packed keys: row 1 holds row 0 again
-    const uint16_t* qp = J.q + (static_cast<int64_t>(b) * L.Hq + h * G + (n16 < G ? n16 : 0)) * D;
+    const bool live = n16 < (kPackK ? 2 * G : G);  // packed keys: rows G..2G-1 hold rows 0..G-1 again
+    const uint16_t* qp = J.q + (static_cast<int64_t>(b) * L.Hq + h * G + (n16 & (G - 1))) * D;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const u32x4 v = ld16(qp + kchan<INNER>(g4, j, 0));
@@ -429,8 +456,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
         kw[1][0] = y0[0]; kw[1][1] = y0[1]; kw[1][2] = y1[0]; kw[1][3] = y1[1];
       } else {
         constexpr int RB = 16 * KB;  // key row bytes
-        constexpr int CB = 4 * KB;   // bytes of one lane's 32-channel chunk
-        const uint32_t a = r0 + n16 * RB + CB * g4;
+        const uint32_t a = r0 + koff0;
         if constexpr (KB == 4) {
           const u32x4 x = dsr16<0>(a), y = dsr16<16 * RB>(a);
 #pragma unroll
@@ -440,7 +466,8 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
           for (int e = 0; e < 2; ++e) { kw[0][e] = x[e]; kw[1][e] = y[e]; }
         } else {
-          const u32x4 x0 = dsr16<0>(a), x1 = dsr16<16>(a), y0 = dsr16<16 * RB>(a), y1 = dsr16<16 * RB + 16>(a);
+          const uint32_t a1 = r0 + koff1;
+          const u32x4 x0 = dsr16<0>(a), x1 = dsr16<0>(a1), y0 = dsr16<16 * RB>(a), y1 = dsr16<16 * RB>(a1);
 #pragma unroll
           for (int e = 0; e < 4; ++e) { kw[0][e] = x0[e]; kw[0][4 + e] = x1[e]; kw[1][e] = y0[e]; kw[1][4 + e] = y1[e]; }
         }
@@ -480,15 +507,15 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) cacc = mfma(qa[j], h8(kmeta[j]), cacc);
-      // rows past the lane's query rows start from 0 (with a packed single
-      // row, row 1 accumulates the lo parts only)
+      // rows past the lane's query rows start from 0 (with packed keys, rows
+      // G..2G-1 accumulate the lo parts only)
       f32x4 init = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < RI; ++i) {
         const float other = dppf<kRowRor8>(cacc[i]);
         const float cz = n16 < 8 ? cacc[i] : other;
         const float cs = n16 < 8 ? other : cacc[i];
-        init[i] = fmaf(cz, 1.f / iu, -base * cs);
+        init[i] = (kPackK && 4 * g4 + i >= G) ? 0.f : fmaf(cz, 1.f / iu, -base * cs);
       }
       sacc[0] = init;
       sacc[1] = init;
@@ -497,7 +524,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
         const half8 s8 = h8(kmeta[4 + j]);
         if constexpr (kPackK) {
           half8 w = qa[j] * s8;
-          if (n16 >= 1) lo_in_place(w, qa[j], s8);  // row 1: the lo part
+          if (n16 >= G) lo_in_place(w, qa[j], s8);  // rows G..2G-1: the lo parts
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) sacc[nt] = mfma(w, kstep<KB>(unp, kw[nt], j), sacc[nt]);
         } else {
@@ -511,11 +538,19 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
           }
         }
       }
-      if constexpr (kPackK) {
+      if constexpr (kPackK && G == 1) {
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) sacc[nt][0] += sacc[nt][1];
       }
-      if constexpr (kFold) {
+      if constexpr (kFold && kPackK) {
+        // the swap that folds tile 1's live lanes into tile 0's empty ones
+        // also brings each tile's lo rows next to its hi rows
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float2 r = kFold == 32 ? swap32(sacc[0][i], sacc[1][i]) : swap16(sacc[0][i], sacc[1][i]);
+          sf[i] = (r.x + r.y) * (iu * kscale);
+        }
+      } else if constexpr (kFold) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sf[i] = fold(sacc[0][i], sacc[1][i]) * (iu * kscale);
       } else {
@@ -684,7 +719,9 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
     for (int k = 0; k < R::loads; ++k) {
       const int off = k * 1024 + l * 16;
-      if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
+      // the key rows' chunks come from their swizzled places (kSwz)
+      const int goff = k < kKeyLoads ? k * 1024 + ((k & 1) ? dma_off1 : dma_off0) : off;
+      if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + goff, dst + k * 1024, 16, 0, 0);
     }
   };
 #pragma unroll
@@ -1165,7 +1202,8 @@ hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& j, hipStream
   if (j.nsplit < 1 || j.nsplit > kMaxBodySplits) return hipErrorInvalidValue;  // LDS tables hold 256
   // up to eight splits per unit: one wavefront per (unit, row) with every
   // split requested at once (512 units x 6 splits of a batch-64 GQA layer:
-  // 3 us faster than a workgroup per unit; with 24 splits, 1.3 us slower)
+  // 3 us faster than a workgroup per unit; with 24 splits, 1.3 us slower, and
+  // a 32-split variant is 5 us slower per call on the 512-unit layers)
   if (j.nsplit <= 8) {
     hipLaunchKernelGGL(decode_merge_rows_kernel<8>, dim3((L.units * L.G + 3) / 4), dim3(256), 0, s, L, j);
     return hipGetLastError();
