@@ -122,12 +122,13 @@ struct DecodeJob {
 // (unit, query row) per workgroup); undoes the value rotation when set.
 hipError_t launch_decode_merge(const LayerDesc& L, const DecodeJob& job, hipStream_t s);
 
-// Wavefronts of a 64-thread kernel resident on the current device in one
-// round (runtime occupancy x CU count).  `cache` is the caller's per-kernel
+// Workgroups of `block` threads and `smem` bytes of dynamic LDS resident on
+// the current device in one round (runtime occupancy x CU count); for a
+// 64-thread kernel, resident wavefronts.  `cache` is the caller's per-kernel
 // table, indexed by device; concurrent first calls store the same value.
 constexpr int kMaxDevices = 64;
 template <class Kernel>
-hipError_t resident_waves(Kernel kern, std::atomic<int>* cache, int* out) {
+hipError_t resident_blocks(Kernel kern, int block, size_t smem, std::atomic<int>* cache, int* out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return hipErrorInvalidDevice;
   if (dev < kMaxDevices) {
@@ -138,13 +139,17 @@ hipError_t resident_waves(Kernel kern, std::atomic<int>* cache, int* out) {
     }
   }
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64, 0) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, block, smem) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidValue;
   const int v = (per_cu > 0 ? per_cu : 1) * (cus > 0 ? cus : 1);
   if (dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
   *out = v;
   return hipSuccess;
+}
+template <class Kernel>
+hipError_t resident_waves(Kernel kern, std::atomic<int>* cache, int* out) {
+  return resident_blocks(kern, 64, 0, cache, out);
 }
 
 // Static decode scratch (kvq_static.hip): a fixed device array per GPU for the

@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "kvq_device.h"
@@ -1111,6 +1112,211 @@ __global__ void __launch_bounds__(128) prefill_kernel(LayerDesc L, QuantJob J) {
     pack_v3(reinterpret_cast<const uint8_t(*)[D]>(sm + kPfCv), nrows, rec + L.off_vc, 0);
 }
 
+// ===================================================================== KIVI-layout prefill
+// prefill_kivi_kernel quantizes the whole prompt blocks of layers with
+// per-channel asymmetric keys and per-token asymmetric values in groups of 32
+// channels (2/4/8-bit codes; no outliers, rotation or key normalization), with
+// the arithmetic of prefill_kernel.  The two wavefronts of a workgroup split a
+// block by tensor, each lane holding whole groups: wavefront 0 the keys (lane
+// l: channels 2l and 2l + 1 of the 32 tokens), wavefront 1 the values (lane l:
+// channels 64 (l % 2) .. + 63 of token l / 2, two groups).  Each loads its
+// tensor straight into registers in that layout, one block ahead: the grid is
+// persistent and a wavefront's next 8 KiB of reads are in flight while it
+// codes the current block.  The codes meet in LDS (key rows, value lane
+// chunks) and both wavefronts pack the record.
+
+// Packed binary16 minimum / maximum of two element pairs, written as asm so
+// that no canonicalizing operation precedes each use (for the fp16 elements
+// here the result is the plain minimum / maximum that fminf / fmaxf give).
+__device__ __forceinline__ uint32_t pk_min_h(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_pk_min_f16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+__device__ __forceinline__ uint32_t pk_max_h(uint32_t a, uint32_t b) {
+  uint32_t d;
+  asm("v_pk_max_f16 %0, %1, %2" : "=v"(d) : "v"(a), "v"(b));
+  return d;
+}
+
+// Asymmetric codes clamp(rne(fl32(a / s)), 0, Q) of a group sharing the scale
+// s (a = fl32(x - min)), as asym_code defines them, from a reciprocal
+// estimate without a branch per element.  t = a * rcp(s) lies within
+// |a / s| 2^-22 of fl32(a / s) (v_rcp_f32 is accurate to 1 ulp; one rounding
+// of the product, one of the exact quotient).  Clamping t to [-1, Q + 1]
+// first leaves the clamped code unchanged and bounds that distance by
+// (Q + 1) 2^-22, so the two round to the same integer unless t lies within
+// (Q + 1) 2^-21 of a half-integer.  quot_fast keeps the running maximum of
+// |t - rne(t)|; a lane whose maximum passes the bound (probability about
+// 2^-20 (Q + 1) per element) recomputes its codes with the
+// correctly rounded division (quot_exact) where quot_near says so.  For
+// 8-bit codes most wavefronts see such an element somewhere, so that pass
+// re-tests each element and divides only the flagged ones.  rc = 0 (s = 0)
+// codes every element 0 and flags nothing.
+__device__ __forceinline__ int quot_fast(float a, float rc, float Q, float& worst) {
+  const float t = __builtin_amdgcn_fmed3f(a * rc, -1.f, Q + 1.f);
+  const float r = rintf(t);
+  worst = fmaxf(worst, fabsf(t - r));
+  return static_cast<int>(__builtin_amdgcn_fmed3f(r, 0.f, Q));
+}
+__device__ __forceinline__ float quot_bound(float Q) { return 0.5f - (Q + 1.f) * 0x1p-21f; }
+__device__ __forceinline__ bool quot_near(float a, float rc, float Q) {
+  const float t = __builtin_amdgcn_fmed3f(a * rc, -1.f, Q + 1.f);
+  return fabsf(t - rintf(t)) > quot_bound(Q);
+}
+__device__ __forceinline__ int quot_exact(float a, uint16_t s, float Q) {
+  if (s == 0) return 0;
+  return static_cast<int>(fminf(fmaxf(rintf(__fdiv_rn(a, h2f(s))), 0.f), Q));
+}
+// A copy the compiler cannot prove equal to its input: the rare exact
+// recomputation reads its operands through it, so that the fast pass does
+// not keep every element's intermediate live across the check.
+__device__ __forceinline__ uint32_t opaque_u32(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// Parameters of an asymmetric group from its packed binary16 extremes
+// (element e of the pairs lo2 / hi2), and the reciprocal of its scale.
+__device__ __forceinline__ void asym_pair_params(uint32_t lo2, uint32_t hi2, int e, int Q, float& mn, uint16_t& s,
+                                                 uint16_t& z, float& rc) {
+  mn = h2f(static_cast<uint16_t>(lo2 >> (16 * e)));
+  asym_params(mn, h2f(static_cast<uint16_t>(hi2 >> (16 * e))), true, Q, s, z);
+  rc = s == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(s));
+}
+
+// Keys of one lane: channels 2l, 2l + 1 (halves of x[j]) of tokens j = 0..31.
+__device__ __forceinline__ void kivi_key_lane(const uint32_t (&x)[kBlockTokens], int bits, int l, uint8_t* ck,
+                                              uint16_t* km) {
+  uint32_t lo2 = x[0], hi2 = x[0];
+#pragma unroll
+  for (int j = 1; j < kBlockTokens; ++j) {
+    lo2 = pk_min_h(lo2, x[j]);
+    hi2 = pk_max_h(hi2, x[j]);
+  }
+  const int Qi = (1 << bits) - 1;
+  const float Q = static_cast<float>(Qi);
+  float mn0, mn1, rc0, rc1;
+  uint16_t s0, z0, s1, z1;
+  asym_pair_params(lo2, hi2, 0, Qi, mn0, s0, z0, rc0);
+  asym_pair_params(lo2, hi2, 1, Qi, mn1, s1, z1, rc1);
+  uint8_t* dst = ck + 2 * l;
+  float worst = 0.f;
+#pragma unroll
+  for (int j = 0; j < kBlockTokens; ++j) {
+    const int c0 = quot_fast(__fsub_rn(h2f(static_cast<uint16_t>(x[j])), mn0), rc0, Q, worst);
+    const int c1 = quot_fast(__fsub_rn(h2f(static_cast<uint16_t>(x[j] >> 16)), mn1), rc1, Q, worst);
+    *reinterpret_cast<uint16_t*>(dst + j * D) = static_cast<uint16_t>(c0 | (c1 << 8));
+  }
+  if (worst > quot_bound(Q)) {
+#pragma unroll
+    for (int j = 0; j < kBlockTokens; ++j) {
+      const uint32_t w = opaque_u32(x[j]);
+      const float a0 = __fsub_rn(h2f(static_cast<uint16_t>(w)), mn0);
+      const float a1 = __fsub_rn(h2f(static_cast<uint16_t>(w >> 16)), mn1);
+      if (quot_near(a0, rc0, Q)) dst[j * D] = static_cast<uint8_t>(quot_exact(a0, s0, Q));
+      if (quot_near(a1, rc1, Q)) dst[j * D + 1] = static_cast<uint8_t>(quot_exact(a1, s1, Q));
+    }
+  }
+  reinterpret_cast<uint32_t*>(km)[l] = s0 | (static_cast<uint32_t>(s1) << 16);
+  reinterpret_cast<uint32_t*>(km + D)[l] = z0 | (static_cast<uint32_t>(z1) << 16);
+}
+
+// Values of one lane: token j = l / 2, groups g = 2 (l % 2) + gi of 32
+// channels (element i of group gi is half i % 2 of x[16 gi + i / 2]).
+__device__ __forceinline__ void kivi_value_lane(const uint32_t (&x)[kBlockTokens], int bits, int l, uint8_t* cvc,
+                                                uint16_t* vm) {
+  const int j = l >> 1;
+  const int Qi = (1 << bits) - 1;
+  const float Q = static_cast<float>(Qi);
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi) {
+    const int g = 2 * (l & 1) + gi;
+    uint32_t lo2 = x[16 * gi], hi2 = x[16 * gi];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) {
+      lo2 = pk_min_h(lo2, x[16 * gi + q]);
+      hi2 = pk_max_h(hi2, x[16 * gi + q]);
+    }
+    // fold the two halves into the low one
+    lo2 = pk_min_h(lo2, lo2 >> 16);
+    hi2 = pk_max_h(hi2, hi2 >> 16);
+    float mn, rc;
+    uint16_t s, z;
+    asym_pair_params(lo2, hi2, 0, Qi, mn, s, z, rc);
+    uint8_t* dst = cvc + vchunk_off(j, 32 * g);
+    float worst = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float a = __fsub_rn(h2f(static_cast<uint16_t>(x[16 * gi + (i >> 1)] >> (16 * (i & 1)))), mn);
+      dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_fast(a, rc, Q, worst));
+    }
+    if (worst > quot_bound(Q)) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t w = opaque_u32(x[16 * gi + (i >> 1)]);
+        const float a = __fsub_rn(h2f(static_cast<uint16_t>(w >> (16 * (i & 1)))), mn);
+        if (quot_near(a, rc, Q)) dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_exact(a, s, Q));
+      }
+    }
+    vm[g * kBlockTokens + j] = s;
+    vm[4 * kBlockTokens + g * kBlockTokens + j] = z;
+  }
+}
+
+__global__ void __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(3)))
+prefill_kivi_kernel(LayerDesc L, QuantJob J) {
+  __shared__ __align__(16) uint8_t ck[kBlockTokens * D];
+  __shared__ __align__(16) uint8_t cvc[64 * 64];
+  const int l = threadIdx.x & 63;
+  const bool keys = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  const uint32_t total = static_cast<uint32_t>(J.nblocks) * static_cast<uint32_t>(L.units);  // below 2^31 (checked at launch)
+  auto load = [&](uint32_t w, uint32_t (&x)[kBlockTokens]) __attribute__((always_inline)) {
+    const uint32_t nbk = static_cast<uint32_t>(J.nblocks);
+    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
+    const int64_t row0 = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + kBlockTokens * bi) * D;
+    if (keys) {
+      const uint16_t* src = J.k_src + row0 + 2 * l;
+#pragma unroll
+      for (int j = 0; j < kBlockTokens; ++j) x[j] = *reinterpret_cast<const uint32_t*>(src + j * D);
+    } else {
+      const uint4* src = reinterpret_cast<const uint4*>(J.v_src + row0 + (l >> 1) * D + 64 * (l & 1));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint4 v = src[q];
+        x[4 * q] = v.x;
+        x[4 * q + 1] = v.y;
+        x[4 * q + 2] = v.z;
+        x[4 * q + 3] = v.w;
+      }
+    }
+  };
+  auto block = [&](uint32_t w, const uint32_t (&x)[kBlockTokens]) __attribute__((always_inline)) {
+    const uint32_t nbk = static_cast<uint32_t>(J.nblocks);
+    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
+    uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + J.blk0 + bi) * L.rec_bytes;
+    if (keys)
+      kivi_key_lane(x, L.kb, l, ck, reinterpret_cast<uint16_t*>(rec + L.off_km));
+    else
+      kivi_value_lane(x, L.vb, l, cvc, reinterpret_cast<uint16_t*>(rec + L.off_vm));
+    __syncthreads();
+    pack_rows_fast(ck, kBlockTokens, L.kb, rec + L.off_kc, L.k_row_bytes);
+    pack_vchunks_fast(cvc, L.vb, rec + L.off_vc);
+    __syncthreads();  // the code tiles are free for the next block
+  };
+  uint32_t xa[kBlockTokens], xb[kBlockTokens];
+  const uint32_t step = gridDim.x;
+  uint32_t w = blockIdx.x;
+  if (w < total) load(w, xa);
+  for (; w < total; w += 2 * step) {
+    if (w + step < total) load(w + step, xb);
+    block(w, xa);
+    if (w + step >= total) break;
+    if (w + 2 * step < total) load(w + 2 * step, xa);
+    block(w + step, xb);
+  }
+}
+
 __global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   QuantSmem& sm = *reinterpret_cast<QuantSmem*>(smem_raw);
@@ -1206,6 +1412,18 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
   // (16-byte loads: the sources must be 16-byte aligned; row strides are
   // whole 256-byte rows)
   const bool aligned = ((reinterpret_cast<uintptr_t>(job.k_src) | reinterpret_cast<uintptr_t>(job.v_src)) & 15) == 0;
+  const bool kivi = job.tok0 == 0 && !job.v_interleaved && !job.rotate_v && job.cnt == kBlockTokens &&
+                    job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid && !L.nuq &&
+                    !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 && L.vb != 3;
+  if (kivi && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31)) {
+    static std::atomic<int> resident[kMaxDevices];
+    int grid = 0;
+    const hipError_t e = resident_blocks(prefill_kivi_kernel, 128, 0, resident, &grid);
+    if (e != hipSuccess) return e;
+    grid = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(job.nblocks) * L.units, grid));
+    hipLaunchKernelGGL(prefill_kivi_kernel, dim3(grid), dim3(128), 0, s, L, job);
+    return hipGetLastError();
+  }
   if (job.tok0 == 0 && L.k_hi == 0 && aligned) {
     const size_t smem = prefill_smem(L.outk > 0);
     hipLaunchKernelGGL(prefill_kernel, dim3(job.nblocks, L.units), dim3(128), smem, s, L, job);
