@@ -1153,21 +1153,28 @@ __device__ __forceinline__ uint32_t pk_max_h(uint32_t a, uint32_t b) {
 // 8-bit codes most wavefronts see such an element somewhere, so that pass
 // re-tests each element and divides only the flagged ones.  rc = 0 (s = 0)
 // codes every element 0 and flags nothing.
-__device__ __forceinline__ int quot_fast(float a, float rc, float Q, float& worst) {
-  const float t = __builtin_amdgcn_fmed3f(a * rc, -1.f, Q + 1.f);
+// The same for symmetric codes (quotient clamped to [-Q, Q]) with lo = -Q;
+// asymmetric ones use lo = 0.  The bound takes Q + 1 >= max(-lo, Q) + 1.
+__device__ __forceinline__ int quot_fast(float a, float rc, float lo, float Q, float& worst) {
+  const float t = __builtin_amdgcn_fmed3f(a * rc, lo - 1.f, Q + 1.f);
   const float r = rintf(t);
   worst = fmaxf(worst, fabsf(t - r));
-  return static_cast<int>(__builtin_amdgcn_fmed3f(r, 0.f, Q));
+  return static_cast<int>(__builtin_amdgcn_fmed3f(r, lo, Q));
+}
+__device__ __forceinline__ int quot_fast(float a, float rc, float Q, float& worst) {
+  return quot_fast(a, rc, 0.f, Q, worst);
 }
 __device__ __forceinline__ float quot_bound(float Q) { return 0.5f - (Q + 1.f) * 0x1p-21f; }
-__device__ __forceinline__ bool quot_near(float a, float rc, float Q) {
-  const float t = __builtin_amdgcn_fmed3f(a * rc, -1.f, Q + 1.f);
+__device__ __forceinline__ bool quot_near(float a, float rc, float lo, float Q) {
+  const float t = __builtin_amdgcn_fmed3f(a * rc, lo - 1.f, Q + 1.f);
   return fabsf(t - rintf(t)) > quot_bound(Q);
 }
-__device__ __forceinline__ int quot_exact(float a, uint16_t s, float Q) {
+__device__ __forceinline__ bool quot_near(float a, float rc, float Q) { return quot_near(a, rc, 0.f, Q); }
+__device__ __forceinline__ int quot_exact(float a, uint16_t s, float lo, float Q) {
   if (s == 0) return 0;
-  return static_cast<int>(fminf(fmaxf(rintf(__fdiv_rn(a, h2f(s))), 0.f), Q));
+  return static_cast<int>(fminf(fmaxf(rintf(__fdiv_rn(a, h2f(s))), lo), Q));
 }
+__device__ __forceinline__ int quot_exact(float a, uint16_t s, float Q) { return quot_exact(a, s, 0.f, Q); }
 // A copy the compiler cannot prove equal to its input: the rare exact
 // recomputation reads its operands through it, so that the fast pass does
 // not keep every element's intermediate live across the check.
@@ -1317,6 +1324,241 @@ prefill_kivi_kernel(LayerDesc L, QuantJob J) {
   }
 }
 
+// ===================================================================== inner-group prefill
+// prefill_inner_kernel quantizes the whole prompt blocks of layers with keys
+// in inner groups of 64 channels (each group symmetric or asymmetric by the
+// hybrid test, or always asymmetric) and per-token asymmetric values in
+// groups of 32, optionally Hadamard-rotated (2/4/8-bit; no outliers, key
+// normalization or mixed widths), with the arithmetic of prefill_kernel.  Its
+// three wavefronts hold whole groups in registers: wavefront 0 the keys (lane
+// l: group l % 2 of token l / 2), wavefronts 1 and 2 the values of tokens
+// 16 (w - 1) .. + 15 (lane l: channels 32 (l % 4) .. + 31 of one token, so that
+// after the rotation a lane holds one value group).  The rotation is the
+// exact binary64 butterfly network of hadamard_rows_fast: five stages inside a
+// lane, two across the lane quad through DPP moves.  Loads run one block
+// ahead on a persistent grid, as in prefill_kivi_kernel.
+
+// 64-bit lane exchange inside a quad (DPP quad_perm: xor 1 or xor 2).
+template <int M>
+__device__ __forceinline__ double quad_xor(double v) {
+  constexpr int ctrl = M == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] / [2,3,0,1]
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(b & 0xffffffff), ctrl, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(b >> 32), ctrl, 0xf, 0xf, false);
+  return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+// Exact binary64 sum of fp16 elements as an int64 count of 2^-24 units (the
+// sum of up to 64 values below 2^16 in those units stays below 2^46, exact in
+// binary64 and in int64).
+__device__ __forceinline__ int64_t units_of(double sum) {
+  const double u = sum * 0x1p24;                    // exact integer, |u| < 2^46
+  const double hi = floor(u * 0x1p-32);             // exact
+  const double lo = u - hi * 0x1p32;                // exact, in [0, 2^32)
+  return (static_cast<int64_t>(static_cast<int32_t>(hi)) << 32) + static_cast<int64_t>(static_cast<uint32_t>(lo));
+}
+
+// Keys of one lane: group g = l % 2 (channels 64 g ..) of token j = l / 2,
+// element i = half i % 2 of x[i / 2].
+__device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const LayerDesc& L, int l, uint8_t* ck,
+                                               uint32_t* kmeta) {
+  const int j = l >> 1, g = l & 1;
+  uint32_t lo2 = x[0], hi2 = x[0];
+#pragma unroll
+  for (int q = 1; q < 32; ++q) {
+    lo2 = pk_min_h(lo2, x[q]);
+    hi2 = pk_max_h(hi2, x[q]);
+  }
+  lo2 = pk_min_h(lo2, lo2 >> 16);
+  hi2 = pk_max_h(hi2, hi2 >> 16);
+  const uint16_t hmn = static_cast<uint16_t>(lo2), hmx = static_cast<uint16_t>(hi2);
+  const float mn = h2f(hmn), mx = h2f(hmx);
+  const int bits = L.kb;
+  bool sym = false;
+  if (L.k_hybrid) {
+    // symmetric iff den |sum x| <= num W (max - min), exactly (units of 2^-24)
+    double sum = 0.0;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) sum += static_cast<double>(h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1)))));
+    int64_t su = units_of(sum);
+    su = su < 0 ? -su : su;
+    sym = static_cast<int64_t>(L.ratio_den) * su <= static_cast<int64_t>(L.ratio_num) * 64 * (h2fixed(hmx) - h2fixed(hmn));
+  }
+  uint16_t s, z;
+  float lo, Q, rc, base;
+  int off;
+  if (sym) {
+    const uint16_t sv = sym_scale(fmaxf(fabsf(mn), fabsf(mx)), bits);
+    s = sv | 0x8000;
+    z = 0;
+    Q = static_cast<float>((1 << (bits - 1)) - 1);
+    lo = -Q;
+    off = sv == 0 ? 0 : 1 << (bits - 1);
+    rc = sv == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(sv));
+    base = 0.f;
+  } else {
+    const int Qi = (1 << bits) - 1;
+    asym_params(mn, mx, true, Qi, s, z);
+    Q = static_cast<float>(Qi);
+    lo = 0.f;
+    off = 0;
+    rc = s == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(s));
+    base = mn;
+  }
+  const uint16_t sdiv = static_cast<uint16_t>(s & 0x7fff);
+  uint32_t* dst = reinterpret_cast<uint32_t*>(ck + j * D + 64 * g);
+  float worst = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * q + e;
+      const float a = __fsub_rn(h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1)))), base);
+      w |= static_cast<uint32_t>(quot_fast(a, rc, lo, Q, worst) + off) << (8 * e);
+    }
+    dst[q] = w;
+  }
+  if (worst > quot_bound(Q)) {
+    uint8_t* db = reinterpret_cast<uint8_t*>(dst);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) {
+      const uint32_t w = opaque_u32(x[i >> 1]);
+      const float a = __fsub_rn(h2f(static_cast<uint16_t>(w >> (16 * (i & 1)))), base);
+      if (quot_near(a, rc, lo, Q)) db[i] = static_cast<uint8_t>(quot_exact(a, sdiv, lo, Q) + off);
+    }
+  }
+  kmeta[j * 2 + g] = s | (static_cast<uint32_t>(z) << 16);
+}
+
+// Values of one lane: channels 32 q .. 32 q + 31 (q = l % 4) of token j,
+// element i = half i % 2 of x[i / 2]; rotated first when `rotate` (the lane
+// quad holds the token's 128 channels), then coded as value group q.
+__device__ __forceinline__ void inner_value_lane(const uint32_t (&x)[16], const LayerDesc& L, bool rotate, int l,
+                                                 int j, uint8_t* cvc, uint16_t* vm) {
+  const int q = l & 3;
+  uint32_t v[16];
+  if (rotate) {
+    double y[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = static_cast<double>(h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1)))));
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; ++i)
+        if (!(i & h)) {
+          const double a = y[i], b = y[i + h];
+          y[i] = a + b;
+          y[i + h] = a - b;
+        }
+    // channel bits 5 and 6 across the quad: x <- x + o (bit clear), o - x (set)
+    const double sg1 = (q & 1) ? -1.0 : 1.0, sg2 = (q & 2) ? -1.0 : 1.0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = fma(y[i], sg1, quad_xor<1>(y[i]));
+#pragma unroll
+    for (int i = 0; i < 32; ++i) y[i] = fma(y[i], sg2, quad_xor<2>(y[i]));
+    const double c = L.had_scale;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      v[i] = static_cast<uint32_t>(d2h_odd(y[2 * i] * c)) | (static_cast<uint32_t>(d2h_odd(y[2 * i + 1] * c)) << 16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = x[i];
+  }
+  uint32_t lo2 = v[0], hi2 = v[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) {
+    lo2 = pk_min_h(lo2, v[k]);
+    hi2 = pk_max_h(hi2, v[k]);
+  }
+  lo2 = pk_min_h(lo2, lo2 >> 16);
+  hi2 = pk_max_h(hi2, hi2 >> 16);
+  const int Qi = (1 << L.vb) - 1;
+  const float Q = static_cast<float>(Qi);
+  float mn, rc;
+  uint16_t s, z;
+  asym_pair_params(lo2, hi2, 0, Qi, mn, s, z, rc);
+  uint8_t* dst = cvc + vchunk_off(j, 32 * q);
+  float worst = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float a = __fsub_rn(h2f(static_cast<uint16_t>(v[i >> 1] >> (16 * (i & 1)))), mn);
+    dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_fast(a, rc, Q, worst));
+  }
+  if (worst > quot_bound(Q)) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t w = opaque_u32(v[i >> 1]);
+      const float a = __fsub_rn(h2f(static_cast<uint16_t>(w >> (16 * (i & 1)))), mn);
+      if (quot_near(a, rc, Q)) dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_exact(a, s, Q));
+    }
+  }
+  vm[q * kBlockTokens + j] = s;
+  vm[4 * kBlockTokens + q * kBlockTokens + j] = z;
+}
+
+// One wavefront's walk over the grid's blocks: ROLE 0 keys (32 words of a
+// lane's key group), ROLE 1 values (16 words of a lane's value quarter); its
+// own double buffer, so the two roles' registers do not add up.  Every
+// wavefront of the workgroup walks the same blocks and meets the same two
+// barriers per block.
+template <int ROLE>
+__device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J, int l, int vj, uint8_t* ck,
+                                           uint8_t* cvc) {
+  constexpr int NW = ROLE == 0 ? 32 : 16;
+  const uint32_t total = static_cast<uint32_t>(J.nblocks) * static_cast<uint32_t>(L.units);  // below 2^31 (checked at launch)
+  const uint32_t nbk = static_cast<uint32_t>(J.nblocks);
+  auto load = [&](uint32_t w, uint32_t (&x)[NW]) __attribute__((always_inline)) {
+    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
+    const int64_t row0 = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + kBlockTokens * bi) * D;
+    const uint4* src = ROLE == 0 ? reinterpret_cast<const uint4*>(J.k_src + row0 + (l >> 1) * D + 64 * (l & 1))
+                                 : reinterpret_cast<const uint4*>(J.v_src + row0 + vj * D + 32 * (l & 3));
+#pragma unroll
+    for (int k = 0; k < NW / 4; ++k) {
+      const uint4 v = src[k];
+      x[4 * k] = v.x;
+      x[4 * k + 1] = v.y;
+      x[4 * k + 2] = v.z;
+      x[4 * k + 3] = v.w;
+    }
+  };
+  auto block = [&](uint32_t w, const uint32_t (&x)[NW]) __attribute__((always_inline)) {
+    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
+    uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + J.blk0 + bi) * L.rec_bytes;
+    if constexpr (ROLE == 0)
+      inner_key_lane(x, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km));
+    else
+      inner_value_lane(x, L, J.rotate_v != 0, l, vj, cvc, reinterpret_cast<uint16_t*>(rec + L.off_vm));
+    __syncthreads();
+    pack_rows_fast(ck, kBlockTokens, L.kb, rec + L.off_kc, L.k_row_bytes);
+    pack_vchunks_fast(cvc, L.vb, rec + L.off_vc);
+    __syncthreads();  // the code tiles are free for the next block
+  };
+  uint32_t xa[NW], xb[NW];
+  const uint32_t step = gridDim.x;
+  uint32_t w = blockIdx.x;
+  if (w < total) load(w, xa);
+  for (; w < total; w += 2 * step) {
+    if (w + step < total) load(w + step, xb);
+    block(w, xa);
+    if (w + step >= total) break;
+    if (w + 2 * step < total) load(w + 2 * step, xa);
+    block(w + step, xb);
+  }
+}
+
+__global__ void __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(3)))
+prefill_inner_kernel(LayerDesc L, QuantJob J) {
+  __shared__ __align__(16) uint8_t ck[kBlockTokens * D];
+  __shared__ __align__(16) uint8_t cvc[64 * 64];
+  const int l = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0 keys, 1 and 2 values
+  if (wv == 0)
+    inner_walk<0>(L, J, l, 0, ck, cvc);
+  else
+    inner_walk<1>(L, J, l, 16 * (wv - 1) + (l >> 2), ck, cvc);
+}
+
 __global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   QuantSmem& sm = *reinterpret_cast<QuantSmem*>(smem_raw);
@@ -1415,6 +1657,19 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
   const bool kivi = job.tok0 == 0 && !job.v_interleaved && !job.rotate_v && job.cnt == kBlockTokens &&
                     job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid && !L.nuq &&
                     !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 && L.vb != 3;
+  const bool inner = job.tok0 == 0 && !job.v_interleaved && job.cnt == kBlockTokens &&
+                     job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && L.k_inner && L.k_group == 64 &&
+                     !L.nuq && !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 &&
+                     L.vb != 3 && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31);
+  if (inner) {
+    static std::atomic<int> resident[kMaxDevices];
+    int grid = 0;
+    const hipError_t e = resident_blocks(prefill_inner_kernel, 192, 0, resident, &grid);
+    if (e != hipSuccess) return e;
+    grid = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(job.nblocks) * L.units, grid));
+    hipLaunchKernelGGL(prefill_inner_kernel, dim3(grid), dim3(192), 0, s, L, job);
+    return hipGetLastError();
+  }
   if (kivi && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31)) {
     static std::atomic<int> resident[kMaxDevices];
     int grid = 0;

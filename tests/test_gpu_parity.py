@@ -17,6 +17,7 @@ REDUCED = {
     "C3r": W.C3.with_(L=5, B=2, Hq=8, Hkv=2, T=512, steps=40, fixed_pairs=W.PAIR_SET),
     "C4r": W.C4.with_(Hq=2, Hkv=2, T=1024, steps=33),             # one flush at step 32
     "C5r": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4),          # ragged last block
+    "C5r-whole-blocks": W.C5.with_(B=2, Hq=16, Hkv=2, T=512, steps=3),
     # InnerQ key normalization on C5's inner groups; one key channel x64
     "C5rn": W.C5.with_(B=2, Hq=16, Hkv=2, T=500, steps=4, k_norm=True, k_out_factor=64.0),
     # the Hadamard 2-bit page's pairing: KIVI int4 keys (per channel) with
@@ -184,17 +185,17 @@ def test_nonfinite_rows_are_counted():
     cache.close()
 
 
-def _ties_tensor(T, D, bits, step, token_groups, nudge):
+def _ties_tensor(T, D, bits, step, token_groups, nudge, glen=32):
     """fp16 [T][D] whose groups (32 tokens of a channel when token_groups, else
-    32 channels of a token) hold their minimum and maximum at positions 0 and
-    1 and elsewhere base + step * m, m a multiple of 1/2 in [0, Q]: with s =
-    step exactly, every quotient (x - min) / s is m, so half the elements sit
-    on a rounding tie; `nudge` moves every fifth of those one ulp up, to a
+    glen channels of a token) hold their minimum and maximum at positions 0
+    and 1 and elsewhere base + step * m, m a multiple of 1/2 in [0, Q]: with
+    s = step exactly, every quotient (x - min) / s is m, so half the elements
+    sit on a rounding tie; `nudge` moves every fifth of those one ulp up, to a
     hair above the tie."""
     Q = (1 << bits) - 1
     t = np.arange(T)[:, None]
     c = np.arange(D)[None, :]
-    pos = (t % 32) if token_groups else (c % 32)
+    pos = (t % 32) if token_groups else (c % glen)
     m = ((t * 7 + c * 3) % (2 * Q + 1)) * 0.5
     m = np.where(pos == 0, 0.0, np.where(pos == 1, float(Q), m))
     base = -1.0 + 0.25 * ((c % 4) if token_groups else (t % 4))
@@ -205,22 +206,30 @@ def _ties_tensor(T, D, bits, step, token_groups, nudge):
     return x
 
 
+@pytest.mark.parametrize("keys", ["channel", "inner"])
 @pytest.mark.parametrize("pair", [(2, 2), (4, 4), (8, 2), (2, 8)])
 @pytest.mark.parametrize("nudge", [False, True])
-def test_prefill_codes_on_rounding_ties(pair, nudge):
+def test_prefill_codes_on_rounding_ties(keys, pair, nudge):
     """Quotients exactly on (or one ulp past) a half-integer, where a
     reciprocal estimate cannot decide the rounding: the library's codes and
-    parameters equal the oracle's correctly rounded ones bit for bit."""
+    parameters equal the oracle's correctly rounded ones bit for bit (keys
+    per channel, or in inner groups of 64 with the symmetric/asymmetric
+    choice)."""
     import oracle as O
     from decode_attention_quantize_amd import KVQCache, config_from_workload
     from gpu_harness import HostLayer, unit_body
     from kvq_unpack import unpack_unit
     kb, vb = pair
-    wl = W.C1.with_(name="ties", window=0, fixed_pairs=(pair,), T=256)
+    if keys == "channel":
+        wl = W.C1.with_(name="ties", window=0, fixed_pairs=(pair,), T=256)
+    else:
+        wl = W.C5.with_(name="ties-inner", B=1, Hq=1, Hkv=1, T=256, steps=1, v_hadamard=False,
+                        fixed_pairs=(pair,))
     T, D = wl.T, wl.D
-    K = _ties_tensor(T, D, kb, 2.0 ** -6 if kb == 8 else 0.125, True, nudge)
+    K = _ties_tensor(T, D, kb, 2.0 ** -6 if kb == 8 else 0.125, keys == "channel", nudge,
+                     glen=wl.k_group if keys == "inner" else 32)
     V = _ties_tensor(T, D, vb, 2.0 ** -6 if vb == 8 else 0.125, False, nudge)
-    say(f"[ties] pair {pair} nudge {nudge}")
+    say(f"[ties] {keys} keys, pair {pair} nudge {nudge}")
     cache = KVQCache(config_from_workload(wl), wl.bit_pairs(), device="cuda")
     k = torch.from_numpy(K).view(1, 1, T, D).cuda()
     v = torch.from_numpy(V).view(1, 1, T, D).cuda()
@@ -229,7 +238,7 @@ def test_prefill_codes_on_rounding_ties(pair, nudge):
     s_eff, nb, _ = O.state_prefill(T, wl.sinks, wl.window, wl.flush)
     enc = O.encode_unit(O.scheme_for(wl, 0), K.view(np.uint16), V.view(np.uint16), T, s_eff, nb)
     body, lay = unit_body(cache, 0, 0, HostLayer(cache, 0))
-    got = unpack_unit(body, lay, kb, vb, nb, False, wl.k_group, wl.v_group, wl.outliers, 0)
+    got = unpack_unit(body, lay, kb, vb, nb, keys == "inner", wl.k_group, wl.v_group, wl.outliers, 0)
     for key in ("kcodes", "kmeta", "vcodes", "vmeta"):
         bad = np.argwhere(got[key] != enc[key])
         assert bad.size == 0, (pair, nudge, key, bad[:5].tolist())
