@@ -1559,6 +1559,331 @@ prefill_inner_kernel(LayerDesc L, QuantJob J) {
     inner_walk<1>(L, J, l, 16 * (wv - 1) + (l >> 2), ck, cvc);
 }
 
+// ===================================================================== codebook prefill
+// prefill_codebook_kernel quantizes the whole prompt blocks of layers with
+// 3-bit codebook keys (per channel) and values (per token, groups of 32) and
+// two sparse fp16 outliers per token row of each tensor (no rotation or key
+// normalization), with the arithmetic of prefill_kernel.  Four wavefronts:
+// 0 and 1 hold key channels l and l + 64 of tokens 16 w .. + 15 (lane l:
+// the channel pair of its own 3-bit record chunk), 2 and 3 hold key and
+// value rows of tokens 16 (w - 2) .. + 15 (lane l: quarter l % 4 of token
+// l / 4, so a lane holds one value group).  Per block: the row wavefronts
+// find each row's two outliers (a top-2 of sortable keys in the lane, then
+// across the lane quad), write the outlier entries, publish the key rows'
+// outlier masks in LDS and code the values; the key wavefronts read the
+// masks, exchange the two halves of each channel's extremes through LDS and
+// write their record chunks straight from registers.  Codebook codes use a
+// three-level search of the sorted level midpoints; the estimate of u =
+// (x - min) / s decides unless it lies within 2^-18 of one of the midpoints
+// the search compared (the two neighbours of u are among them), as in
+// nuq_code_fast.
+
+// code = #{j : u > mid_j} by binary search; `gap` = min distance from u to
+// the midpoints compared (its bracketing midpoints are among them).
+__device__ __forceinline__ int nuq_search(float u, const float (&m)[7], float& gap) {
+  // flat selects (a nested conditional can end up as branches)
+  const bool b2 = u > m[3];
+  const float ma = b2 ? m[5] : m[1];
+  const float mhi = b2 ? m[6] : m[2];
+  const float mlo = b2 ? m[4] : m[0];
+  const bool b1 = u > ma;
+  const float mb = b1 ? mhi : mlo;
+  const bool b0 = u > mb;
+  gap = fminf(fminf(fabsf(u - m[3]), fabsf(u - ma)), fabsf(u - mb));
+  return (b2 ? 4 : 0) + (b1 ? 2 : 0) + (b0 ? 1 : 0);
+}
+// Codebook code of d = fl32(x - min) with scale s (rc its reciprocal, 0 when
+// s == 0: code 0), tracking the smallest gap seen; nuq_exact redoes one with
+// the correctly rounded quotient.
+__device__ __forceinline__ int nuq_fast(float d, float rc, const float (&m)[7], float& worst_gap) {
+  float gap;
+  const int c = nuq_search(d * rc, m, gap);
+  worst_gap = fminf(worst_gap, gap);
+  return c;
+}
+__device__ __forceinline__ bool nuq_near(float d, float rc, const float (&m)[7]) {
+  float gap;
+  nuq_search(d * rc, m, gap);
+  return gap < 0x1p-18f;
+}
+__device__ __forceinline__ int nuq_exact(float d, uint16_t s, const float (&m)[7]) {
+  if (s == 0) return 0;
+  float gap;
+  return nuq_search(__fdiv_rn(d, h2f(s)), m, gap);
+}
+
+// Sortable outlier key of element (x, column c): magnitude, then the lower
+// column, then the sign (so the raw value can be rebuilt).
+__device__ __forceinline__ uint32_t outlier_key(uint32_t x16, int c) {
+  return ((x16 & 0x7fffu) << 8) | (static_cast<uint32_t>(127 - c) << 1) | (x16 >> 15);
+}
+__device__ __forceinline__ int outlier_col(uint32_t key) { return 127 - static_cast<int>((key >> 1) & 127u); }
+__device__ __forceinline__ uint32_t outlier_bits(uint32_t key) { return ((key >> 8) & 0x7fffu) | ((key & 1u) << 15); }
+
+// Top two keys of a row held by a lane quad (lane q: columns 32 q .. + 31,
+// element i = half i % 2 of x[i / 2]); every lane of the quad gets them.
+__device__ __forceinline__ void row_top2(const uint32_t (&x)[16], int q, uint32_t& t0, uint32_t& t1) {
+  t0 = 0u;
+  t1 = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const uint32_t k = outlier_key((x[i >> 1] >> (16 * (i & 1))) & 0xffffu, 32 * q + i);
+    uint32_t m;  // second largest of {t0, t1, k} (t0 >= t1)
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(t0), "v"(t1), "v"(k));
+    t1 = m;
+    t0 = max(t0, k);
+  }
+  auto join = [&](uint32_t o0, uint32_t o1) __attribute__((always_inline)) {
+    t1 = max(min(t0, o0), max(t1, o1));
+    t0 = max(t0, o0);
+  };
+  // across the quad: xor 1, then xor 2 (DPP quad_perm [1,0,3,2], [2,3,0,1])
+  join(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(t0), 0xB1, 0xf, 0xf, false)),
+       static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(t1), 0xB1, 0xf, 0xf, false)));
+  join(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(t0), 0x4E, 0xf, 0xf, false)),
+       static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(t1), 0x4E, 0xf, 0xf, false)));
+}
+
+// The outlier entries of one row ({column, fp16}, columns ascending) and the
+// row's mask word for columns 32 q .. + 31.
+__device__ __forceinline__ uint32_t row_outliers(uint32_t t0, uint32_t t1, int q, uint32_t* entries) {
+  const int c0 = outlier_col(t0), c1 = outlier_col(t1);
+  const uint32_t e0 = static_cast<uint32_t>(c0) | (outlier_bits(t0) << 16);
+  const uint32_t e1 = static_cast<uint32_t>(c1) | (outlier_bits(t1) << 16);
+  if (q == 0) {
+    entries[0] = c0 < c1 ? e0 : e1;
+    entries[1] = c0 < c1 ? e1 : e0;
+  }
+  uint32_t m = 0u;
+  if ((c0 >> 5) == q) m |= 1u << (c0 & 31);
+  if ((c1 >> 5) == q) m |= 1u << (c1 & 31);
+  return m;
+}
+
+// Extremes of the members (elements whose mask bit is clear) of 32 halves.
+__device__ __forceinline__ bool masked_extremes(const uint32_t (&x)[16], uint32_t ex, float& mn, float& mx) {
+  mn = __int_as_float(0x7f800000);
+  mx = __int_as_float(0xff800000);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const float v = h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1))));
+    const bool in = !((ex >> i) & 1u);
+    mn = fminf(mn, in ? v : __int_as_float(0x7f800000));
+    mx = fmaxf(mx, in ? v : __int_as_float(0xff800000));
+  }
+  return mn <= mx;
+}
+
+template <int ROLE>  // 0 keys, 1 rows
+__device__ __forceinline__ void codebook_walk(const LayerDesc& L, const QuantJob& J, int wv, int l, uint32_t* kmask,
+                                              float* kext, uint8_t* cv) {
+  constexpr int NW = ROLE == 0 ? 16 : 32;
+  const uint32_t total = static_cast<uint32_t>(J.nblocks) * static_cast<uint32_t>(L.units);  // below 2^31 (checked at launch)
+  const uint32_t nbk = static_cast<uint32_t>(J.nblocks);
+  const int half = ROLE == 0 ? wv : wv - 2;  // tokens 16 half .. + 15
+  const int q = l & 3, rj = 16 * half + (l >> 2);
+  float mk[7], mv[7];  // level midpoints (read by value: no pointer into the kernel arguments)
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    mk[j] = __fmul_rn(__fadd_rn(h2f(L.lev_k[j]), h2f(L.lev_k[j + 1])), 0.5f);
+    mv[j] = __fmul_rn(__fadd_rn(h2f(L.lev_v[j]), h2f(L.lev_v[j + 1])), 0.5f);
+  }
+  auto load = [&](uint32_t w, uint32_t (&x)[NW]) __attribute__((always_inline)) {
+    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
+    const int64_t row0 = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + kBlockTokens * bi) * D;
+    if constexpr (ROLE == 0) {
+      const uint16_t* src = J.k_src + row0 + static_cast<int64_t>(16 * half) * D + l;
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        x[t] = static_cast<uint32_t>(src[t * D]) | (static_cast<uint32_t>(src[t * D + 64]) << 16);
+    } else {
+      const uint4* ks = reinterpret_cast<const uint4*>(J.k_src + row0 + rj * D + 32 * q);
+      const uint4* vs = reinterpret_cast<const uint4*>(J.v_src + row0 + rj * D + 32 * q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 a = ks[k], b = vs[k];
+        x[4 * k] = a.x;
+        x[4 * k + 1] = a.y;
+        x[4 * k + 2] = a.z;
+        x[4 * k + 3] = a.w;
+        x[16 + 4 * k] = b.x;
+        x[16 + 4 * k + 1] = b.y;
+        x[16 + 4 * k + 2] = b.z;
+        x[16 + 4 * k + 3] = b.w;
+      }
+    }
+  };
+  auto block = [&](uint32_t w, const uint32_t (&x)[NW]) __attribute__((always_inline)) {
+    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
+    uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + J.blk0 + bi) * L.rec_bytes;
+    if constexpr (ROLE == 1) {
+      // ---- outliers of the key and value rows; value codes
+      uint32_t kx[16], vx[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        kx[i] = x[i];
+        vx[i] = x[16 + i];
+      }
+      uint32_t t0, t1;
+      row_top2(kx, q, t0, t1);
+      kmask[rj * 4 + q] = row_outliers(t0, t1, q, reinterpret_cast<uint32_t*>(rec + L.off_ko) + rj * 2);
+      row_top2(vx, q, t0, t1);
+      const uint32_t vex = row_outliers(t0, t1, q, reinterpret_cast<uint32_t*>(rec + L.off_vo) + rj * 2);
+      float mn, mx;
+      const bool any = masked_extremes(vx, vex, mn, mx);
+      uint16_t s, z;
+      nuq_params(mn, mx, any, s, z);
+      const float rc = s == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(s));
+      uint32_t* dst = reinterpret_cast<uint32_t*>(cv + rj * D + 32 * q);
+      float worst = 1.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        uint32_t wd = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * k + e;
+          // converted again rather than kept from the extremes pass (registers)
+          const float d = __fsub_rn(h2f(static_cast<uint16_t>(opaque_u32(vx[i >> 1]) >> (16 * (i & 1)))), mn);
+          wd |= static_cast<uint32_t>(nuq_fast(d, rc, mv, worst)) << (8 * e);
+        }
+        dst[k] = wd;
+        __builtin_amdgcn_sched_barrier(0);  // keep the code words' live ranges short
+      }
+      if (worst < 0x1p-18f) {
+        uint8_t* db = reinterpret_cast<uint8_t*>(dst);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t wv2 = opaque_u32(vx[i >> 1]);
+          const float d = __fsub_rn(h2f(static_cast<uint16_t>(wv2 >> (16 * (i & 1)))), mn);
+          if (nuq_near(d, rc, mv)) db[i] = static_cast<uint8_t>(nuq_exact(d, s, mv));
+        }
+      }
+      uint16_t* vm = reinterpret_cast<uint16_t*>(rec + L.off_vm);
+      vm[q * kBlockTokens + rj] = s;
+      vm[4 * kBlockTokens + q * kBlockTokens + rj] = z;
+    }
+    __syncthreads();  // key outlier masks and value codes complete
+    if constexpr (ROLE == 0) {
+      // ---- value chunks (the key wavefronts wait less than the row ones):
+      // lane l packs elements 32 half .. + 31 of chunk l, i.e. its words
+      // 3 half .. 3 half + 2 (element e of chunk l is code (token 8 (l / 16) +
+      // e % 8, channel 16 (e / 8) + l % 16))
+      {
+        uint32_t wd[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int ep = 0; ep < 32; ++ep) {
+          const int e = 32 * half + ep;
+          const uint32_t code = cv[(8 * (l >> 4) + (e & 7)) * D + 16 * (e >> 3) + (l & 15)];
+          const int b = 3 * ep, wi = b >> 5, sh = b & 31;
+          wd[wi] |= code << sh;
+          if (sh > 29) wd[wi + 1] |= code >> (32 - sh);
+        }
+        uint32_t* chunk = reinterpret_cast<uint32_t*>(rec + L.off_vc) + 6 * l + 3 * half;
+#pragma unroll
+        for (int k = 0; k < 3; ++k) chunk[k] = wd[k];
+      }
+
+      // ---- key channels l (half 0) and l + 64 (half 1) of the wavefront's 16 tokens
+      uint32_t ex0 = 0, ex1 = 0;  // bit t: token 16 half + t is an outlier of the channel
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const uint32_t* m = kmask + (16 * half + t) * 4;
+        ex0 |= ((m[l >> 5] >> (l & 31)) & 1u) << t;
+        ex1 |= ((m[2 + (l >> 5)] >> (l & 31)) & 1u) << t;
+      }
+      float e4[4] = {__int_as_float(0x7f800000), __int_as_float(0xff800000), __int_as_float(0x7f800000),
+                     __int_as_float(0xff800000)};
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float a = h2f(static_cast<uint16_t>(x[t])), b = h2f(static_cast<uint16_t>(x[t] >> 16));
+        const bool ia = !((ex0 >> t) & 1u), ib = !((ex1 >> t) & 1u);
+        e4[0] = fminf(e4[0], ia ? a : __int_as_float(0x7f800000));
+        e4[1] = fmaxf(e4[1], ia ? a : __int_as_float(0xff800000));
+        e4[2] = fminf(e4[2], ib ? b : __int_as_float(0x7f800000));
+        e4[3] = fmaxf(e4[3], ib ? b : __int_as_float(0xff800000));
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) kext[(half * 4 + k) * 64 + l] = e4[k];
+    }
+    __syncthreads();  // both halves' extremes; masks and value codes read
+    if constexpr (ROLE == 0) {
+      float mn[2], rc[2];
+      uint16_t sz[2][2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        mn[e] = fminf(kext[(0 * 4 + 2 * e) * 64 + l], kext[(1 * 4 + 2 * e) * 64 + l]);
+        const float mx = fmaxf(kext[(0 * 4 + 2 * e + 1) * 64 + l], kext[(1 * 4 + 2 * e + 1) * 64 + l]);
+        nuq_params(mn[e], mx, mn[e] <= mx, sz[e][0], sz[e][1]);
+        rc[e] = sz[e][0] == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(sz[e][0]));
+      }
+      // 6-bit fields (c1 << 3 | c0) of tokens t at bit 6 t of the chunk's
+      // 96-bit half 3 half .. 3 half + 2 (words)
+      uint32_t f[16];
+      float worst = 1.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float d0 = __fsub_rn(h2f(static_cast<uint16_t>(x[t])), mn[0]);
+        const float d1 = __fsub_rn(h2f(static_cast<uint16_t>(x[t] >> 16)), mn[1]);
+        f[t] = static_cast<uint32_t>(nuq_fast(d0, rc[0], mk, worst)) |
+               (static_cast<uint32_t>(nuq_fast(d1, rc[1], mk, worst)) << 3);
+        if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // keep the searches' live ranges short
+      }
+      if (worst < 0x1p-18f) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const uint32_t xw = opaque_u32(x[t]);
+          const float d0 = __fsub_rn(h2f(static_cast<uint16_t>(xw)), mn[0]);
+          const float d1 = __fsub_rn(h2f(static_cast<uint16_t>(xw >> 16)), mn[1]);
+          if (nuq_near(d0, rc[0], mk)) f[t] = (f[t] & ~7u) | static_cast<uint32_t>(nuq_exact(d0, sz[0][0], mk));
+          if (nuq_near(d1, rc[1], mk)) f[t] = (f[t] & 7u) | (static_cast<uint32_t>(nuq_exact(d1, sz[1][0], mk)) << 3);
+        }
+      }
+      uint32_t wd[3] = {0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int b = 6 * t, wi = b >> 5, sh = b & 31;
+        wd[wi] |= f[t] << sh;
+        if (sh > 26) wd[wi + 1] |= f[t] >> (32 - sh);
+      }
+      uint32_t* chunk = reinterpret_cast<uint32_t*>(rec + L.off_kc) + 6 * l + 3 * half;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) chunk[k] = wd[k];
+      if (half == 0) {
+        uint16_t* km = reinterpret_cast<uint16_t*>(rec + L.off_km);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          km[l + 64 * e] = sz[e][0];
+          km[D + l + 64 * e] = sz[e][1];
+        }
+      }
+    }
+  };
+  uint32_t xa[NW], xb[NW];
+  const uint32_t step = gridDim.x;
+  uint32_t w = blockIdx.x;
+  if (w < total) load(w, xa);
+  for (; w < total; w += 2 * step) {
+    if (w + step < total) load(w + step, xb);
+    block(w, xa);
+    if (w + step >= total) break;
+    if (w + 2 * step < total) load(w + 2 * step, xa);
+    block(w + step, xb);
+  }
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3)))
+prefill_codebook_kernel(LayerDesc L, QuantJob J) {
+  __shared__ __align__(16) uint32_t kmask[kBlockTokens * 4];   // key-row outlier bits per token
+  __shared__ __align__(16) float kext[2 * 4 * 64];             // [token half][min0, max0, min1, max1][lane]
+  __shared__ __align__(16) uint8_t cv[kBlockTokens * D];       // value codes, row-major
+  const int l = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv < 2)
+    codebook_walk<0>(L, J, wv, l, kmask, kext, cv);
+  else
+    codebook_walk<1>(L, J, wv, l, kmask, kext, cv);
+}
+
 __global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) {
   extern __shared__ __align__(16) uint8_t smem_raw[];
   QuantSmem& sm = *reinterpret_cast<QuantSmem*>(smem_raw);
@@ -1661,6 +1986,19 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
                      job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && L.k_inner && L.k_group == 64 &&
                      !L.nuq && !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 &&
                      L.vb != 3 && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31);
+  const bool codebook = job.tok0 == 0 && !job.v_interleaved && !job.rotate_v && job.cnt == kBlockTokens &&
+                        job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid &&
+                        L.nuq && !L.v_tern && L.outk == 2 && L.kshift == nullptr && L.v_group == 32 && L.kb == 3 &&
+                        L.vb == 3 && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31);
+  if (codebook) {
+    static std::atomic<int> resident[kMaxDevices];
+    int grid = 0;
+    const hipError_t e = resident_blocks(prefill_codebook_kernel, 256, 0, resident, &grid);
+    if (e != hipSuccess) return e;
+    grid = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(job.nblocks) * L.units, grid));
+    hipLaunchKernelGGL(prefill_codebook_kernel, dim3(grid), dim3(256), 0, s, L, job);
+    return hipGetLastError();
+  }
   if (inner) {
     static std::atomic<int> resident[kMaxDevices];
     int grid = 0;
