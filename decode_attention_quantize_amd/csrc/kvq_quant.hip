@@ -1434,14 +1434,16 @@ __device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const La
 // Values of one lane: channels 32 q .. 32 q + 31 (q = l % 4) of token j,
 // element i = half i % 2 of x[i / 2]; rotated first when `rotate` (the lane
 // quad holds the token's 128 channels), then coded as value group q.
-__device__ __forceinline__ void inner_value_lane(const uint32_t (&x)[16], const LayerDesc& L, bool rotate, int l,
-                                                 int j, uint8_t* cvc, uint16_t* vm) {
+template <class Next>
+__device__ __forceinline__ void inner_value_lane(uint32_t (&x)[16], const LayerDesc& L, bool rotate, int l, int j,
+                                                 uint8_t* cvc, uint16_t* vm, Next next) {
   const int q = l & 3;
   uint32_t v[16];
   if (rotate) {
     double y[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) y[i] = static_cast<double>(h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1)))));
+    next(x);  // x is consumed: the next block's loads go in flight now
 #pragma unroll
     for (int h = 1; h < 32; h <<= 1)
 #pragma unroll
@@ -1454,16 +1456,25 @@ __device__ __forceinline__ void inner_value_lane(const uint32_t (&x)[16], const 
     // channel bits 5 and 6 across the quad: x <- x + o (bit clear), o - x (set)
     const double sg1 = (q & 1) ? -1.0 : 1.0, sg2 = (q & 2) ? -1.0 : 1.0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) y[i] = fma(y[i], sg1, quad_xor<1>(y[i]));
+    for (int i = 0; i < 32; ++i) {
+      y[i] = fma(y[i], sg1, quad_xor<1>(y[i]));
+      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // a few partners in flight at a time
+    }
 #pragma unroll
-    for (int i = 0; i < 32; ++i) y[i] = fma(y[i], sg2, quad_xor<2>(y[i]));
+    for (int i = 0; i < 32; ++i) {
+      y[i] = fma(y[i], sg2, quad_xor<2>(y[i]));
+      if ((i & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
     const double c = L.had_scale;
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
+    for (int i = 0; i < 16; ++i) {
       v[i] = static_cast<uint32_t>(d2h_odd(y[2 * i] * c)) | (static_cast<uint32_t>(d2h_odd(y[2 * i + 1] * c)) << 16);
+      if ((i & 1) == 1) __builtin_amdgcn_sched_barrier(0);  // retire the doubles as they are rounded
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = x[i];
+    next(x);
   }
   uint32_t lo2 = v[0], hi2 = v[0];
 #pragma unroll
@@ -1522,28 +1533,46 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
       x[4 * k + 3] = v.w;
     }
   };
-  auto block = [&](uint32_t w, const uint32_t (&x)[NW]) __attribute__((always_inline)) {
-    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
-    uint8_t* rec = L.body + (static_cast<int64_t>(u) * L.nblk_cap + J.blk0 + bi) * L.rec_bytes;
-    if constexpr (ROLE == 0)
-      inner_key_lane(x, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km));
-    else
-      inner_value_lane(x, L, J.rotate_v != 0, l, vj, cvc, reinterpret_cast<uint16_t*>(rec + L.off_vm));
+  auto pack = [&](uint8_t* rec) __attribute__((always_inline)) {
     __syncthreads();
     pack_rows_fast(ck, kBlockTokens, L.kb, rec + L.off_kc, L.k_row_bytes);
     pack_vchunks_fast(cvc, L.vb, rec + L.off_vc);
     __syncthreads();  // the code tiles are free for the next block
   };
-  uint32_t xa[NW], xb[NW];
+  auto record = [&](uint32_t w) __attribute__((always_inline)) {
+    const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
+    return L.body + (static_cast<int64_t>(u) * L.nblk_cap + J.blk0 + bi) * L.rec_bytes;
+  };
   const uint32_t step = gridDim.x;
   uint32_t w = blockIdx.x;
-  if (w < total) load(w, xa);
-  for (; w < total; w += 2 * step) {
-    if (w + step < total) load(w + step, xb);
-    block(w, xa);
-    if (w + step >= total) break;
-    if (w + 2 * step < total) load(w + 2 * step, xa);
-    block(w + step, xb);
+  if constexpr (ROLE == 0) {
+    // keys: two buffers (the group's words are read until its codes are out)
+    uint32_t xa[NW], xb[NW];
+    if (w < total) load(w, xa);
+    for (; w < total; w += 2 * step) {
+      if (w + step < total) load(w + step, xb);
+      uint8_t* rec = record(w);
+      inner_key_lane(xa, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km));
+      pack(rec);
+      if (w + step >= total) break;
+      if (w + 2 * step < total) load(w + 2 * step, xa);
+      rec = record(w + step);
+      inner_key_lane(xb, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km));
+      pack(rec);
+    }
+  } else {
+    // values: one buffer, refilled as soon as the lane has converted it
+    uint32_t x[NW];
+    if (w < total) load(w, x);
+    for (; w < total; w += step) {
+      const uint32_t wn = w + step;
+      uint8_t* rec = record(w);
+      inner_value_lane(x, L, J.rotate_v != 0, l, vj, cvc, reinterpret_cast<uint16_t*>(rec + L.off_vm),
+                       [&](uint32_t (&buf)[NW]) __attribute__((always_inline)) {
+                         if (wn < total) load(wn, buf);
+                       });
+      pack(rec);
+    }
   }
 }
 
