@@ -280,19 +280,18 @@ def main():
                for _ in range(wl.L)] for _ in range(a.steps)]
 
     def step(i, ev=None, nbytes=None):
-        # appends of every layer first, then the layers' decodes back to back:
-        # once the first decode runs, the host stays ahead of the GPU, so the
-        # events around decodes 2..L time the launches themselves
-        if wl.append:
-            for l in range(wl.L):
-                kt, vt, _ = steps_in[i][l]
+        # layer by layer, as a model step runs: append the layer's new token,
+        # then decode over its cache.  Once the first decode runs the host
+        # stays ahead of the GPU (issuing an append and a decode takes less
+        # host time than a decode takes on the device), so the events around
+        # decodes 2..L time the decode launches themselves.
+        for l in range(wl.L):
+            kt, vt, q = steps_in[i][l]
+            if wl.append:
                 cache.append(l, kt, vt)
-        if nbytes is not None:
-            for l in range(wl.L):
+            if nbytes is not None:
                 n, s_eff, nb, r = cache.state(l)
                 nbytes.append(decode_bytes(wl, l, n, s_eff, nb, r))
-        for l in range(wl.L):
-            q = steps_in[i][l][2]
             if ev is not None:
                 ev[l][0].record(stream)
             cache.decode(l, q, outs[l])
