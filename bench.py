@@ -280,23 +280,25 @@ def main():
                for _ in range(wl.L)] for _ in range(a.steps)]
 
     def step(i, ev=None, nbytes=None):
-        # layer by layer, as a model step runs: append the layer's new token,
-        # then decode over its cache.  Once the first decode runs the host
-        # stays ahead of the GPU (issuing an append and a decode takes less
-        # host time than a decode takes on the device), so the events around
-        # decodes 2..L time the decode launches themselves.
+        # layer by layer, as a model step runs: the layer's new token enters
+        # its cache and the query attends over it, in one
+        # kvq_append_decode_attn call (one decode launch and its merge unless
+        # a flush block is due).  Once the first call runs the host stays
+        # ahead of the GPU, so the events around calls 2..L time the launches
+        # themselves.
         for l in range(wl.L):
             kt, vt, q = steps_in[i][l]
+            if ev is not None:
+                ev[l][0].record(stream)
             if wl.append:
-                cache.append(l, kt, vt)
+                cache.append_decode(l, kt, vt, q, outs[l])   # kvq_append_decode_attn
+            else:
+                cache.decode(l, q, outs[l])
+            if ev is not None:
+                ev[l][1].record(stream)
             if nbytes is not None:
                 n, s_eff, nb, r = cache.state(l)
                 nbytes.append(decode_bytes(wl, l, n, s_eff, nb, r))
-            if ev is not None:
-                ev[l][0].record(stream)
-            cache.decode(l, q, outs[l])
-            if ev is not None:
-                ev[l][1].record(stream)
 
     for i in range(a.warmup):
         step(i)
@@ -380,8 +382,11 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "bytes_per_launch": round(bytes_per_launch),
-            "kernel": "kvq_decode_attn call: split-context decode kernel + log-sum-exp merge kernel "
-                      "(HIP events around the call, launch gap included)",
+            "kernel": ("kvq_append_decode_attn call: split-context decode kernel (storing the appended "
+                       "token) + log-sum-exp merge kernel; a flush step adds the block quantization "
+                       "(HIP events around the call, launch gaps included)") if wl.append else
+                      ("kvq_decode_attn call: split-context decode kernel + log-sum-exp merge kernel "
+                       "(HIP events around the call, launch gap included)"),
             "timed_launches": len(kern_ms),
             "frac_of_read_ceiling": round(achieved / ceil_gbs, 4),
         },

@@ -734,8 +734,8 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // rescale (a power of two, exact) restores them.
   {
     const int slots = L.sinks_cap + L.win_cap;
-    const uint16_t* kf = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
-    const uint16_t* vf = kf + static_cast<int64_t>(slots) * D;
+    uint16_t* const kf = L.fp16 + static_cast<int64_t>(u) * 2 * slots * D;
+    uint16_t* const vf = kf + static_cast<int64_t>(slots) * D;
     const int wchunks = L.win_cap / kBlockTokens;
     const int wstart = st.nb % L.win_cap;  // ring index of the oldest window token
     for (int c = sp - J.fp16_split0; c >= 0 && c < J.fp16_chunks; c += J.fp16_nsplit) {
@@ -743,13 +743,40 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       const int slot0 = sinkc ? kBlockTokens * c
                               : L.sinks_cap + kBlockTokens * ((J.win_chunk0 + c - J.sink_chunks) % wchunks);
       u32x4 kv[2][4], vv[8];
+      // an appended token carried by this launch is read from its source
+      // (its slot is written below, and read by no other split)
+      const int xs = J.new_slot - slot0;  // in [0, 32) for the chunk holding it
+      const uint16_t* const nk = J.new_k + static_cast<int64_t>(u) * D;
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) kv[nt][j] = ld16(kf + (slot0 + 16 * nt + n16) * D + kchan<INNER>(g4, j, 0));
+        for (int j = 0; j < 4; ++j)
+          kv[nt][j] = ld16((16 * nt + n16 == xs ? nk : kf + (slot0 + 16 * nt + n16) * D) + kchan<INNER>(g4, j, 0));
       // lane: slots slot0 + 8*g4 .. +7 of channel 16*nt + n16 (16 contiguous bytes)
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) vv[nt] = ld16(vf + (static_cast<int64_t>(slot0 / 8 + g4) * D + 16 * nt + n16) * 8);
+      if (xs >= 0 && xs < kBlockTokens) {  // wave-uniform
+        const uint16_t* const nv = J.new_v + static_cast<int64_t>(u) * D;
+        const int e = xs - 8 * g4;  // element of the lane's eight slots
+        if (e >= 0 && e < 8) {
+#pragma unroll
+          for (int nt = 0; nt < 8; ++nt) {
+            const uint32_t x = nv[16 * nt + n16];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              if (e == 2 * w) vv[nt][w] = (vv[nt][w] & 0xffff0000u) | x;
+              if (e == 2 * w + 1) vv[nt][w] = (vv[nt][w] & 0x0000ffffu) | (x << 16);
+            }
+          }
+        }
+        // store the token: lane l takes channels 2l and 2l + 1
+        const int x = slot0 + xs;
+        const uint32_t kw = *reinterpret_cast<const uint32_t*>(nk + 2 * l);
+        const uint32_t vw = *reinterpret_cast<const uint32_t*>(nv + 2 * l);
+        *reinterpret_cast<uint32_t*>(kf + static_cast<int64_t>(x) * D + 2 * l) = kw;
+        vf[vslot(x, 2 * l)] = static_cast<uint16_t>(vw);
+        vf[vslot(x, 2 * l + 1)] = static_cast<uint16_t>(vw >> 16);
+      }
       f32x4 sacc[2];
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {

@@ -202,6 +202,8 @@ enum class DecodeKind { kMatrixCore, kTables, kStaged };
 // otherwise).  Fills j.st and the split fields.
 DecodeKind plan_decode(const kvq_cache& c, const Layer& L, kvq::DecodeJob& j) {
   j.st = kvq::TokenState{L.n, L.s_eff, L.nb, L.r};
+  j.new_k = j.new_v = nullptr;
+  j.new_slot = -1;
   if (!c.force_generic) {
     int waves = kvq::decode_fast_waves(L.d);
     if (waves > 0) {
@@ -584,6 +586,46 @@ kvq_status kvq_decode_attn(kvq_cache* c, int32_t layer, const void* q, float* ou
   j.nonfinite = nonfinite_counter(*c, workspace);
   j.ml_off = static_cast<int64_t>(c->units) * max_splits(*c) * c->G * kD;
   return launch_decode(L, kind, j, reinterpret_cast<hipStream_t>(stream));
+}
+
+kvq_status kvq_append_decode_attn(kvq_cache* c, int32_t layer, const void* k_new, const void* v_new,
+                                  const void* q, float* out, void* workspace, void* stream) {
+  if (!valid_layer(c, layer) || !k_new || !v_new || !q || !out || !workspace) return KVQ_ERR_ARG;
+  Layer& L = c->layers[layer];
+  if (!L.bound || !L.filled) return KVQ_ERR_STATE;
+  if (L.n + 1 > c->cfg.max_tokens) return KVQ_ERR_CAPACITY;
+  const int S = c->cfg.sink_tokens, W = c->cfg.recent_window, F = c->F;
+  // One launch when the token only needs storing (the next sink, or a window
+  // slot without a flush; values unrotated) and the layer decodes on the
+  // matrix-core kernel: the decode reads the token from k_new / v_new and
+  // stores it.  Otherwise the two calls this one stands for.
+  const bool sink = L.s_eff < S;
+  const bool plain = !L.d.v_had && (sink || (!(F == 1 && W == 0) && L.r + 1 < W + F));
+  if (plain && !c->force_generic && kvq::decode_fast_waves(L.d) > 0) {
+    const int p = L.n;
+    const int slot = sink ? p : c->sink_cap + (p - L.s_eff) % c->win_cap;
+    if (sink)
+      L.s_eff += 1;
+    else
+      L.r += 1;
+    L.n += 1;
+    kvq::DecodeJob j{};
+    const DecodeKind kind = plan_decode(*c, L, j);
+    j.q = static_cast<const uint16_t*>(q);
+    j.out = out;
+    j.partials = static_cast<float*>(workspace);
+    j.counters = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + partials_padded(*c));
+    j.nonfinite = nonfinite_counter(*c, workspace);
+    j.ml_off = static_cast<int64_t>(c->units) * max_splits(*c) * c->G * kD;
+    j.new_k = static_cast<const uint16_t*>(k_new);
+    j.new_v = static_cast<const uint16_t*>(v_new);
+    j.new_slot = slot;
+    const kvq_status e = launch_decode(L, kind, j, reinterpret_cast<hipStream_t>(stream));
+    return e == KVQ_OK ? e : device_error(L);
+  }
+  const kvq_status e = kvq_append_token(c, layer, k_new, v_new, stream);
+  if (e != KVQ_OK) return e;
+  return kvq_decode_attn(c, layer, q, out, workspace, stream);
 }
 
 kvq_status kvq_decode_attn_static(kvq_cache* c, int32_t layer, const void* q, float* out, void* stream) {

@@ -117,6 +117,13 @@ struct DecodeJob {
   int32_t fp16_split0, fp16_nsplit;
   int64_t ml_off;         // matrix-core path: float offset of the (max, sum) records
   uint32_t* nonfinite;    // count of output rows with a non-finite element (never reset here)
+  // Appended token carried by the decode launch (matrix-core path only):
+  // new_slot >= 0 is the fp16 slot of position st.n - 1, whose key and value
+  // ([units][D] fp16) the chunk holding that slot reads from new_k / new_v
+  // and writes into the slot; -1 when the token was stored beforehand.
+  const uint16_t* new_k;
+  const uint16_t* new_v;
+  int32_t new_slot;
 };
 // Log-sum-exp merge of matrix-core split partials into job.out (one
 // (unit, query row) per workgroup); undoes the value rotation when set.

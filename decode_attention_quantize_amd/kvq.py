@@ -21,7 +21,7 @@ KVQ_BUF_BODY, KVQ_BUF_FP16 = 0, 1
 
 EXPORTS = ("kvq_create", "kvq_destroy", "kvq_layer_buffer_sizes", "kvq_block_layout",
            "kvq_bind_layer", "kvq_unbind_layer", "kvq_workspace_size", "kvq_quantize_prefill",
-           "kvq_append_token", "kvq_decode_attn", "kvq_decode_attn_static",
+           "kvq_append_token", "kvq_decode_attn", "kvq_append_decode_attn", "kvq_decode_attn_static",
            "kvq_decode_nonfinite_rows", "kvq_layer_state",
            "kvq_average_bits", "kvq_status_str", "kvq_fit_rate_distortion", "kvq_waterfill_bits",
            "kvq_allocate_bits", "kvq_stream_read")
@@ -81,6 +81,7 @@ def lib():
         L.kvq_quantize_prefill.argtypes = [pcache, i32, vp, vp, i32, vp, vp]
         L.kvq_append_token.argtypes = [pcache, i32, vp, vp, vp]
         L.kvq_decode_attn.argtypes = [pcache, i32, vp, vp, vp, vp]
+        L.kvq_append_decode_attn.argtypes = [pcache, i32, vp, vp, vp, vp, vp, vp]
         L.kvq_decode_attn_static.argtypes = [pcache, i32, vp, vp, vp]
         L.kvq_layer_state.argtypes = [pcache, i32] + [C.POINTER(C.c_int32)] * 4
         dp, ip = C.POINTER(C.c_double), C.POINTER(C.c_int32)
@@ -167,6 +168,11 @@ def kvq_append_token(handle, layer, k_ptr, v_ptr, stream):
 
 def kvq_decode_attn(handle, layer, q_ptr, out_ptr, ws_ptr, stream):
     _check(lib().kvq_decode_attn(handle, layer, q_ptr, out_ptr, ws_ptr, stream), "kvq_decode_attn")
+
+
+def kvq_append_decode_attn(handle, layer, k_ptr, v_ptr, q_ptr, out_ptr, ws_ptr, stream):
+    _check(lib().kvq_append_decode_attn(handle, layer, k_ptr, v_ptr, q_ptr, out_ptr, ws_ptr, stream),
+           "kvq_append_decode_attn")
 
 
 def kvq_decode_attn_static(handle, layer, q_ptr, out_ptr, stream):
@@ -360,6 +366,23 @@ class KVQCache:
         self._check(out, "out", torch.float32, shape)
         kvq_decode_attn(self.handle, layer, q.data_ptr(), out.data_ptr(), self.workspace.data_ptr(),
                         self._stream())
+        return out
+
+    def append_decode(self, layer, k, v, q, out=None):
+        """kvq_append_decode_attn: append(k, v), then decode(q) -- one launch
+        where the library can.  Shapes as for append and decode."""
+        torch = self.torch
+        c = self.cfg
+        kv_shape = (c.batch, c.n_kv_heads, c.head_dim)
+        shape = (c.batch, c.n_q_heads, c.head_dim)
+        self._check(k, "k", torch.float16, kv_shape)
+        self._check(v, "v", torch.float16, kv_shape)
+        self._check(q, "q", torch.float16, shape)
+        if out is None:
+            out = torch.empty(shape, dtype=torch.float32, device=self.device)
+        self._check(out, "out", torch.float32, shape)
+        kvq_append_decode_attn(self.handle, layer, k.data_ptr(), v.data_ptr(), q.data_ptr(), out.data_ptr(),
+                               self.workspace.data_ptr(), self._stream())
         return out
 
     def decode_static(self, layer, q, out):

@@ -10,6 +10,7 @@
  *   kvq_quantize_prefill  quantize a prompt's keys/values into one layer's cache
  *   kvq_append_token      add one decoded token (quantizing a flush block when due)
  *   kvq_decode_attn       attention of one query step over the whole cache
+ *   kvq_append_decode_attn  the two above for one layer, in one launch where it can
  *
  * Schemes (pages as titled):
  *   keys per channel, asymmetric, groups of 32 tokens  -- KVTuner review,
@@ -252,6 +253,22 @@ kvq_status kvq_append_token(kvq_cache* cache, int32_t layer, const void* k_new,
  * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE (empty cache / unbound), KVQ_ERR_DEVICE. */
 kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, float* out,
                            void* workspace, void* stream);
+
+/* kvq_append_token followed by kvq_decode_attn on the same stream, with the
+ * same arguments, state changes, results and errors (the step a decoding
+ * model takes for each layer: the new token enters the cache and the query
+ * attends over it; InnerQ, methodology 4, the fp16 window; KVQuant,
+ * technical approach, the fused dequantize-attend read).  When the token
+ * only needs storing -- the next sink, or a window slot without a flush, with
+ * unrotated values -- and the layer's decode runs on the matrix-core kernel,
+ * both happen in the decode's own launch: it reads the token from k_new /
+ * v_new and stores it into its slot.  Otherwise it makes the two calls.
+ * k_new, v_new: device fp16 [B][Hkv][D]; q, out, workspace as for
+ * kvq_decode_attn.  A failed launch leaves the layer in KVQ_ERR_STATE until
+ * the next prefill, as for the calls it stands for.
+ * Errors: KVQ_ERR_ARG, KVQ_ERR_STATE, KVQ_ERR_CAPACITY, KVQ_ERR_DEVICE. */
+kvq_status kvq_append_decode_attn(kvq_cache* cache, int32_t layer, const void* k_new, const void* v_new,
+                                  const void* q, float* out, void* workspace, void* stream);
 
 /* kvq_decode_attn without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP stream/graph capture, serving loops

@@ -18,12 +18,14 @@ def say(*a):
     sys.stdout.flush()
 
 
-def run_gpu(wl, layers=None, steps=None, keep_units=None, device="cuda", fill=None, keep_steps=None):
+def run_gpu(wl, layers=None, steps=None, keep_units=None, device="cuda", fill=None, keep_steps=None,
+            fused=False):
     """Prefill every layer, then per step: per layer append (when the workload
-    appends) and decode.  Returns outputs [layer][step] -> cpu fp32 [B][Hq][D]
-    (only for the kept units when keep_units is given; only the kept steps
-    when keep_steps is given).  fill: byte the layer buffers hold before the
-    prefill (default zeros)."""
+    appends) and decode -- as one kvq_append_decode_attn call when fused.
+    Returns outputs [layer][step] -> cpu fp32 [B][Hq][D] (only for the kept
+    units when keep_units is given; only the kept steps when keep_steps is
+    given).  fill: byte the layer buffers hold before the prefill (default
+    zeros)."""
     dev = torch.device(device)
     layers = list(range(wl.L)) if layers is None else layers
     steps = wl.steps if steps is None else steps
@@ -38,12 +40,17 @@ def run_gpu(wl, layers=None, steps=None, keep_units=None, device="cuda", fill=No
     outs = {l: {} for l in layers}
     for i in range(steps):
         for l in layers:
+            q = wl.q(l, i, device=dev).contiguous()
             if wl.append:
                 kt = wl.k(l, 0, B, 0, Hkv, T + i, T + i + 1, device=dev).reshape(B, Hkv, wl.D).contiguous()
                 vt = wl.v(l, 0, B, 0, Hkv, T + i, T + i + 1, device=dev).reshape(B, Hkv, wl.D).contiguous()
-                cache.append(l, kt, vt)
-            q = wl.q(l, i, device=dev).contiguous()
-            o = cache.decode(l, q)
+                if fused:
+                    o = cache.append_decode(l, kt, vt, q)
+                else:
+                    cache.append(l, kt, vt)
+                    o = cache.decode(l, q)
+            else:
+                o = cache.decode(l, q)
             if keep_steps is not None and i not in keep_steps:
                 continue
             if keep_units is None:

@@ -207,6 +207,7 @@ def test_call_order_and_capacity_errors_on_host():
         assert L.kvq_quantize_prefill(h, 0, fake, fake, 10, None, stream) == K.KVQ_ERR_STATE   # unbound
         assert L.kvq_decode_attn(h, 0, fake, fake, fake, stream) == K.KVQ_ERR_STATE
         assert L.kvq_append_token(h, 0, fake, fake, stream) == K.KVQ_ERR_STATE
+        assert L.kvq_append_decode_attn(h, 0, fake, fake, fake, fake, fake, stream) == K.KVQ_ERR_STATE
         assert L.kvq_quantize_prefill(h, 5, fake, fake, 10, None, stream) == K.KVQ_ERR_ARG     # layer
         arr = (C.c_void_p * 2)(fake, fake + 1)                                                # misaligned
         assert L.kvq_bind_layer(h, 0, arr) == K.KVQ_ERR_ARG
@@ -218,6 +219,11 @@ def test_call_order_and_capacity_errors_on_host():
         assert L.kvq_append_token(h, 0, fake, fake, stream) == K.KVQ_ERR_STATE               # before prefill
         assert L.kvq_decode_attn(h, 0, fake, fake, fake, stream) == K.KVQ_ERR_STATE
         assert L.kvq_decode_attn(h, 0, None, fake, fake, stream) == K.KVQ_ERR_ARG
+        assert L.kvq_append_decode_attn(h, 0, fake, fake, fake, fake, fake, stream) == K.KVQ_ERR_STATE
+        for i in range(5):                      # every pointer but the stream is required
+            args = [fake] * 5
+            args[i] = None
+            assert L.kvq_append_decode_attn(h, 0, *args, stream) == K.KVQ_ERR_ARG, i
         assert K.kvq_layer_state(h, 0) == (0, 0, 0, 0)
         assert L.kvq_layer_state(h, 9, None, None, None, None) == K.KVQ_ERR_ARG
         # an unbound layer refuses device work again until it is bound

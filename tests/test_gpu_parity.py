@@ -247,6 +247,31 @@ def test_prefill_codes_on_rounding_ties(keys, pair, nudge):
     cache.close()
 
 
+@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C5r", "C4r", "short-prompt-sinks-then-flush"])
+def test_fused_append_decode_matches_the_two_calls(name):
+    """kvq_append_decode_attn stands for kvq_append_token + kvq_decode_attn:
+    at every step the outputs and the layers' buffers are bit-identical to
+    the two calls' (the fused launch where the token only needs storing and
+    the layer runs the matrix-core kernel, the two calls otherwise), and the
+    fused run passes the oracle checks."""
+    from gpu_harness import HostLayer
+    wl = REDUCED.get(name) or EDGE[name]
+    c0, o0 = run_gpu(wl)
+    c1, o1 = run_gpu(wl, fused=True)
+    for l in o0:
+        for i in o0[l]:
+            assert torch.equal(o0[l][i], o1[l][i]), (name, l, i)
+        h0, h1 = HostLayer(c0, l), HostLayer(c1, l)
+        assert h0.state == h1.state
+        assert np.array_equal(h0.body, h1.body) and np.array_equal(h0.fp16, h1.fp16), (name, l)
+    worst = 0.0
+    for l in range(wl.L):
+        worst = max(worst, check_units(wl, c1, o1, l, range(wl.units), label=f"{name}/fused")[0])
+    say(f"[fused] {name}: outputs and buffers equal to append + decode; oracle worst {worst:.3e}")
+    c0.close()
+    c1.close()
+
+
 def test_unbound_layer_refuses_device_calls():
     from decode_attention_quantize_amd import KVQCache, KVQError, config_from_workload
     wl = W.C1
