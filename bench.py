@@ -279,6 +279,12 @@ def main():
     events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(wl.L)] for _ in range(a.steps)]
 
+    # kvq_append_decode_attn carries the append inside the decode launch for
+    # layers with unrotated values that decode on the matrix-core kernel (no
+    # 3-bit codes); other layers take the two calls, and the events then
+    # bracket the decode call alone
+    fused = wl.append and not wl.v_hadamard and not wl.nuq and all(3 not in p for p in wl.bit_pairs())
+
     def step(i, ev=None, nbytes=None):
         # layer by layer, as a model step runs: the layer's new token enters
         # its cache and the query attends over it, in one
@@ -288,9 +294,11 @@ def main():
         # themselves.
         for l in range(wl.L):
             kt, vt, q = steps_in[i][l]
+            if wl.append and not fused:
+                cache.append(l, kt, vt)
             if ev is not None:
                 ev[l][0].record(stream)
-            if wl.append:
+            if wl.append and fused:
                 cache.append_decode(l, kt, vt, q, outs[l])   # kvq_append_decode_attn
             else:
                 cache.decode(l, q, outs[l])
@@ -384,7 +392,7 @@ def main():
             "bytes_per_launch": round(bytes_per_launch),
             "kernel": ("kvq_append_decode_attn call: split-context decode kernel (storing the appended "
                        "token) + log-sum-exp merge kernel; a flush step adds the block quantization "
-                       "(HIP events around the call, launch gaps included)") if wl.append else
+                       "(HIP events around the call, launch gaps included)") if fused else
                       ("kvq_decode_attn call: split-context decode kernel + log-sum-exp merge kernel "
                        "(HIP events around the call, launch gap included)"),
             "timed_launches": len(kern_ms),
