@@ -572,6 +572,39 @@ def test_knorm_reduces_inner_group_error_on_a_loud_channel():
     # step of its group: its own error grows while the 63 others shrink)
 
 
+def test_knorm_score_error_follows_the_query_profile():
+    """Score level.  For a query q the score error is q . (k_hat - k); over
+    queries with independent zero-mean unit-variance components its mean
+    square is the key's total squared error (cross terms vanish), a fixed
+    identity checked here on 512 seeded queries.  Normalization moves error
+    from the channels it scales up to the one it leaves alone, so no pin can
+    hold for every query: queries that do not read the loud channel see their
+    score error fall (here more than tenfold), a query reading only the loud
+    channel sees it rise."""
+    wl = W.C5.with_(B=1, Hq=8, T=256, steps=1, k_out_count=0, v_out_count=0)
+    K, V = O.unit_inputs(wl, 0, 0, 0, 256)
+    k = K.view(np.float16).astype(np.float64)
+    k[:, 5] *= 64.0
+    K = h16(k).reshape(256, 128)
+    sc = O.scheme_for(wl, 0)
+    Kh, _ = O.dequant_unit(sc, K, O.encode_unit(sc, K, V, 256, 0, 256), 256, 0, 256)
+    sh = O.knorm_shifts(K)
+    encn = O.encode_unit(sc, O.knorm_apply(K, sh), V, 256, 0, 256)
+    Khn, _ = O.dequant_unit(sc, K, encn, 256, 0, 256, kshift=sh)
+    r = np.random.default_rng(2602)
+    Q = r.normal(size=(512, 128))
+    for E in (Kh - k, Khn - k):
+        mse = np.mean((Q @ E.T) ** 2)
+        assert abs(mse / np.mean(np.sum(E ** 2, axis=1)) - 1) < 0.15   # the isotropic identity
+    Qq = Q.copy()
+    Qq[:, 5] = 0.0                                     # queries that skip the loud channel
+    before, after = np.mean((Qq @ (Kh - k).T) ** 2), np.mean((Qq @ (Khn - k).T) ** 2)
+    assert after < 0.1 * before, (after, before)
+    ql = np.zeros(128)
+    ql[5] = 1.0                                        # a query reading only the loud channel
+    assert np.mean((ql @ (Khn - k).T) ** 2) > np.mean((ql @ (Kh - k).T) ** 2)
+
+
 # ---------------------------------------------------------------- ternary values (negative control)
 def test_ternary_levels_bruteforce():
     # every code is the nearest of {-s, 0, s} (ties to 0, the even level),
