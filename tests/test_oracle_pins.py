@@ -67,22 +67,23 @@ def test_f16_widening_exact():
 
 
 # ---------------------------------------------------------------- uniform quantizers
-def _groups(n, count):
+def _groups(n, count, gen=None):
+    rng_ = gen if gen is not None else rng
     out = []
     for i in range(count):
         kind = i % 6
         if kind == 0:
-            x = rng.standard_normal(n)
+            x = rng_.standard_normal(n)
         elif kind == 1:
-            x = rng.standard_t(3, n) * 5
+            x = rng_.standard_t(3, n) * 5
         elif kind == 2:
-            x = rng.uniform(-1e-4, 1e-4, n)      # subnormal-range scales
+            x = rng_.uniform(-1e-4, 1e-4, n)      # subnormal-range scales
         elif kind == 3:
-            x = np.full(n, rng.standard_normal())  # constant group
+            x = np.full(n, rng_.standard_normal())  # constant group
         elif kind == 4:
-            x = rng.uniform(-60000, 60000, n)    # near the fp16 edge
+            x = rng_.uniform(-60000, 60000, n)    # near the fp16 edge
         else:
-            x = rng.integers(-3, 4, n).astype(np.float64)
+            x = rng_.integers(-3, 4, n).astype(np.float64)
         out.append(h16(x))
     return out
 
@@ -224,8 +225,14 @@ def test_nuq_nearest_level_bruteforce():
 
 
 def test_nuq_uniform_levels_match_3bit_uniform():
+    # levels fp16(j/7) against the uniform 3-bit quantizer: the two can
+    # differ only where t = 7 (x - min) / (max - min) sits near a
+    # half-integer.  In t units the uniform scale fp16(range/7) moves t by up
+    # to 7 * 2^-11 (3.4e-3), the codebook's scale fp16(range) moves u = t/7 by
+    # as much, and the rounded levels move the midpoints by up to 7 * 2^-12
+    # (1.7e-3): elements within 9e-3 of a half-integer are skipped
     lv = h16(np.arange(8) / 7.0)
-    for g in _groups(32, 120):
+    for g in _groups(32, 120, np.random.default_rng(31)):
         c_n, (s_n, z_n) = O.quant_nuq(g, lv)
         c_u, (s_u, z_u) = O.quant_asym(g, 3)
         assert z_n == z_u
@@ -233,7 +240,7 @@ def test_nuq_uniform_levels_match_3bit_uniform():
             continue
         x = g.view(np.float16).astype(np.float64)
         t = (x - x.min()) / (x.max() - x.min()) * 7
-        near_mid = np.abs(t - np.floor(t) - 0.5) < 2e-3
+        near_mid = np.abs(t - np.floor(t) - 0.5) < 9e-3
         assert np.array_equal(c_n[~near_mid], c_u[~near_mid])
 
 
