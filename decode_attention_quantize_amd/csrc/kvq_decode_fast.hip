@@ -242,27 +242,13 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   }
   asm volatile("" : "+s"(unp.one2));
 
-  // Key rows of 4- and 8-bit per-channel keys sit in LDS with the 16-byte
-  // chunks of row r XOR-swizzled: chunk k at position k ^ f(r), f(r) =
-  // (r / (16 / chunks per row)) mod (chunks per row).  The 16 rows a K-step
-  // reads (one per lane of a row of 16) then fall in 16 different groups of
-  // four banks instead of two (8-bit) or four (4-bit) groups.  The DMA does
-  // the swizzle for free: each lane picks the global chunk it loads.
-  constexpr bool kSwz = !INNER && (KB == 4 || KB == 8);
-  constexpr int kCpr = KB;                        // 16-byte chunks per key row (16 KB bytes)
-  constexpr int kKeyLoads = kSwz ? 2 * KB / 4 : 0;  // 1 KiB loads covering the key rows
-  // global offset inside a 1 KiB load for this lane (even / odd load index)
-  auto swz_off = [&](int k) __attribute__((always_inline)) {
-    const int p = 64 * k + l;                     // LDS chunk this lane fills
-    return 16 * (p ^ ((p >> 4) & (kCpr - 1))) - 1024 * k;
-  };
-  const int dma_off0 = kSwz ? swz_off(0) : 16 * l;
-  const int dma_off1 = kSwz ? swz_off(1) : 16 * l;
   // LDS byte offsets of this lane's key chunks (K-steps of tile 0; tile 1
-  // rows are 16 further and share the swizzle)
-  const int kswz = kSwz ? (KB == 8 ? (n16 >> 1) & 7 : (n16 >> 2) & 3) : 0;
-  const uint32_t koff0 = KB == 8 ? n16 * 128 + 16 * ((2 * g4) ^ kswz) : n16 * 16 * KB + 4 * KB * g4 + (kSwz ? 16 * (g4 ^ kswz) - 4 * KB * g4 : 0);
-  const uint32_t koff1 = KB == 8 ? n16 * 128 + 16 * ((2 * g4 + 1) ^ kswz) : koff0;
+  // rows are 16 further).  Key rows stay in their record order: an XOR
+  // swizzle of their 16-byte chunks spreads a K-step's 16 rows over more
+  // banks, but its address registers made the 168-register instances spill
+  // inside the block loop, and it measured slower.
+  const uint32_t koff0 = KB == 8 ? n16 * 128 + 32 * g4 : n16 * 16 * KB + 4 * KB * g4;
+  const uint32_t koff1 = KB == 8 ? koff0 + 16 : koff0;
 
   // ---- query operand (natural channel order per K-step)
   half8 qa[4];
@@ -719,9 +705,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
     for (int k = 0; k < R::loads; ++k) {
       const int off = k * 1024 + l * 16;
-      // the key rows' chunks come from their swizzled places (kSwz)
-      const int goff = k < kKeyLoads ? k * 1024 + ((k & 1) ? dma_off1 : dma_off0) : off;
-      if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + goff, dst + k * 1024, 16, 0, 0);
+      if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
     }
   };
 #pragma unroll
