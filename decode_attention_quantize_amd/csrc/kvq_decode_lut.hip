@@ -311,7 +311,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
 #pragma unroll
     for (int k = 0; k < R::loads; ++k) {
       const int off = k * 1024 + l * 16;
-      if (off < R::bytes) __builtin_amdgcn_global_load_lds(src + off, dst + k * 1024, 16, 0, 0);
+      if (off < R::bytes) ring_load(src + off, dst + k * 1024);
     }
   };
 #pragma unroll

@@ -1,7 +1,8 @@
 // kvq_stream.hip -- the read ceiling of the decode's access pattern: a kernel
 // that streams a buffer the way the split decode streams body records (one
 // wavefront per split, a contiguous run of 1 KiB wave loads per split,
-// global_load_lds into a two-slot LDS ring with the same vmcnt waits) and
+// global_load_lds with the decode's cache policy into a two-slot LDS ring
+// with the same vmcnt waits) and
 // does no arithmetic on the data beyond one LDS read per loaded chunk.  Its
 // duration against the bytes read is the bandwidth an HBM-bound decode of
 // that shape can reach on the device.
@@ -28,7 +29,7 @@ __global__ void __launch_bounds__(64) stream_read_kernel(const uint8_t* src, int
   auto issue = [&](int64_t c, lds_u8* dst) __attribute__((always_inline)) {
     const uint8_t* p = src + c * kChunk;
 #pragma unroll
-    for (int k = 0; k < kChunk / 1024; ++k) __builtin_amdgcn_global_load_lds(p + k * 1024 + l * 16, dst + k * 1024, 16, 0, 0);
+    for (int k = 0; k < kChunk / 1024; ++k) ring_load(p + k * 1024 + l * 16, dst + k * 1024);
   };
   lds_u8* const s0 = (lds_u8*)ring0;
   lds_u8* const s1 = (lds_u8*)ring1;
