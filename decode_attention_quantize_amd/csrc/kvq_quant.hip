@@ -1140,36 +1140,46 @@ __device__ __forceinline__ uint32_t pk_max_h(uint32_t a, uint32_t b) {
 }
 
 // Asymmetric codes clamp(rne(fl32(a / s)), 0, Q) of a group sharing the scale
-// s (a = fl32(x - min)), as asym_code defines them, from a reciprocal
-// estimate without a branch per element.  t = a * rcp(s) lies within
-// |a / s| 2^-22 of fl32(a / s) (v_rcp_f32 is accurate to 1 ulp; one rounding
-// of the product, one of the exact quotient).  Clamping t to [-1, Q + 1]
-// first leaves the clamped code unchanged and bounds that distance by
-// (Q + 1) 2^-22, so the two round to the same integer unless t lies within
-// (Q + 1) 2^-21 of a half-integer.  quot_fast keeps the running maximum of
-// |t - rne(t)|; a lane whose maximum passes the bound (probability about
-// 2^-20 (Q + 1) per element) recomputes its codes with the
-// correctly rounded division (quot_exact) where quot_near says so.  For
-// 8-bit codes most wavefronts see such an element somewhere, so that pass
-// re-tests each element and divides only the flagged ones.  rc = 0 (s = 0)
-// codes every element 0 and flags nothing.
-// The same for symmetric codes (quotient clamped to [-Q, Q]) with lo = -Q;
-// asymmetric ones use lo = 0.  The bound takes Q + 1 >= max(-lo, Q) + 1.
-__device__ __forceinline__ int quot_fast(float a, float rc, float lo, float Q, float& worst) {
-  const float t = __builtin_amdgcn_fmed3f(a * rc, lo - 1.f, Q + 1.f);
+// s (a = fl32(x - base), base = the group minimum), as asym_code defines them,
+// from a reciprocal estimate without a branch per element.  With rc =
+// rcp(s) (v_rcp_f32, accurate to 1 ulp) and nb = fl32(-base * rc), the
+// element's estimate is t = fl32(x * rc + nb), one fused multiply-add that
+// reads the binary16 element directly.  Where the quotient is not clamped
+// (|a / s| <= Q + 1), t lies within (Q + 1) 2.5 * 2^-23 + |base * rc| 2^-24 of
+// fl32(a / s) (the reciprocal's error, the roundings of nb, of t, of a and of
+// the quotient), so the two round to the same integer unless t lies within
+// E = (Q + 1) 2^-21 + |base * rc| 2^-23 of a half-integer.  Clamping t to
+// [lo, Q] first gives the clamped code directly: a t beyond Q (below lo)
+// means a quotient above Q - 0.5 (below lo + 0.5).  quot_fast keeps the
+// running maximum of |t - rne(t)|; a lane whose maximum passes the group's
+// bound 0.5 - E (probability about 2^-19 (Q + 1) per element when base / s
+// is of the order of Q) recomputes its codes with the correctly rounded
+// division (quot_exact) where quot_near says so.  For 8-bit codes most
+// wavefronts see such an element somewhere, so that pass re-tests each
+// element and divides only the flagged ones.  rc = 0 (s = 0) codes every
+// element 0 and flags nothing.  The same for symmetric codes (base 0,
+// quotient clamped to [-Q, Q]) with lo = -Q; asymmetric ones use lo = 0.
+struct QuotGroup {
+  float rc, nb, lo, Q, bound;
+};
+__device__ __forceinline__ QuotGroup quot_group(float base, float rc, float lo, float Q) {
+  const float e = (Q + 1.f) * 0x1p-21f + fabsf(base * rc) * 0x1p-23f;
+  return QuotGroup{rc, -(base * rc), lo, Q, 0.5f - e};
+}
+__device__ __forceinline__ float quot_t(float x, const QuotGroup& g) {
+  return __builtin_amdgcn_fmed3f(fmaf(x, g.rc, g.nb), g.lo, g.Q);
+}
+// x: the element (a binary16 value widened to fp32)
+__device__ __forceinline__ int quot_fast(float x, const QuotGroup& g, float& worst) {
+  const float t = quot_t(x, g);
   const float r = rintf(t);
   worst = fmaxf(worst, fabsf(t - r));
-  return static_cast<int>(__builtin_amdgcn_fmed3f(r, lo, Q));
+  return static_cast<int>(r);
 }
-__device__ __forceinline__ int quot_fast(float a, float rc, float Q, float& worst) {
-  return quot_fast(a, rc, 0.f, Q, worst);
+__device__ __forceinline__ bool quot_near(float x, const QuotGroup& g) {
+  const float t = quot_t(x, g);
+  return fabsf(t - rintf(t)) > g.bound;
 }
-__device__ __forceinline__ float quot_bound(float Q) { return 0.5f - (Q + 1.f) * 0x1p-21f; }
-__device__ __forceinline__ bool quot_near(float a, float rc, float lo, float Q) {
-  const float t = __builtin_amdgcn_fmed3f(a * rc, lo - 1.f, Q + 1.f);
-  return fabsf(t - rintf(t)) > quot_bound(Q);
-}
-__device__ __forceinline__ bool quot_near(float a, float rc, float Q) { return quot_near(a, rc, 0.f, Q); }
 __device__ __forceinline__ int quot_exact(float a, uint16_t s, float lo, float Q) {
   if (s == 0) return 0;
   return static_cast<int>(fminf(fmaxf(rintf(__fdiv_rn(a, h2f(s))), lo), Q));
@@ -1208,21 +1218,21 @@ __device__ __forceinline__ void kivi_key_lane(const uint32_t (&x)[kBlockTokens],
   asym_pair_params(lo2, hi2, 0, Qi, mn0, s0, z0, rc0);
   asym_pair_params(lo2, hi2, 1, Qi, mn1, s1, z1, rc1);
   uint8_t* dst = ck + 2 * l;
+  const QuotGroup g0 = quot_group(mn0, rc0, 0.f, Q), g1 = quot_group(mn1, rc1, 0.f, Q);
   float worst = 0.f;
 #pragma unroll
   for (int j = 0; j < kBlockTokens; ++j) {
-    const int c0 = quot_fast(__fsub_rn(h2f(static_cast<uint16_t>(x[j])), mn0), rc0, Q, worst);
-    const int c1 = quot_fast(__fsub_rn(h2f(static_cast<uint16_t>(x[j] >> 16)), mn1), rc1, Q, worst);
+    const int c0 = quot_fast(h2f(static_cast<uint16_t>(x[j])), g0, worst);
+    const int c1 = quot_fast(h2f(static_cast<uint16_t>(x[j] >> 16)), g1, worst);
     *reinterpret_cast<uint16_t*>(dst + j * D) = static_cast<uint16_t>(c0 | (c1 << 8));
   }
-  if (worst > quot_bound(Q)) {
+  if (worst > fminf(g0.bound, g1.bound)) {
 #pragma unroll
     for (int j = 0; j < kBlockTokens; ++j) {
       const uint32_t w = opaque_u32(x[j]);
-      const float a0 = __fsub_rn(h2f(static_cast<uint16_t>(w)), mn0);
-      const float a1 = __fsub_rn(h2f(static_cast<uint16_t>(w >> 16)), mn1);
-      if (quot_near(a0, rc0, Q)) dst[j * D] = static_cast<uint8_t>(quot_exact(a0, s0, Q));
-      if (quot_near(a1, rc1, Q)) dst[j * D + 1] = static_cast<uint8_t>(quot_exact(a1, s1, Q));
+      const float x0 = h2f(static_cast<uint16_t>(w)), x1 = h2f(static_cast<uint16_t>(w >> 16));
+      if (quot_near(x0, g0)) dst[j * D] = static_cast<uint8_t>(quot_exact(__fsub_rn(x0, mn0), s0, Q));
+      if (quot_near(x1, g1)) dst[j * D + 1] = static_cast<uint8_t>(quot_exact(__fsub_rn(x1, mn1), s1, Q));
     }
   }
   reinterpret_cast<uint32_t*>(km)[l] = s0 | (static_cast<uint32_t>(s1) << 16);
@@ -1252,18 +1262,18 @@ __device__ __forceinline__ void kivi_value_lane(const uint32_t (&x)[kBlockTokens
     uint16_t s, z;
     asym_pair_params(lo2, hi2, 0, Qi, mn, s, z, rc);
     uint8_t* dst = cvc + vchunk_off(j, 32 * g);
+    const QuotGroup qg = quot_group(mn, rc, 0.f, Q);
     float worst = 0.f;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const float a = __fsub_rn(h2f(static_cast<uint16_t>(x[16 * gi + (i >> 1)] >> (16 * (i & 1)))), mn);
-      dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_fast(a, rc, Q, worst));
-    }
-    if (worst > quot_bound(Q)) {
+    for (int i = 0; i < 32; ++i)
+      dst[vchunk_off(0, i)] =
+          static_cast<uint8_t>(quot_fast(h2f(static_cast<uint16_t>(x[16 * gi + (i >> 1)] >> (16 * (i & 1)))), qg, worst));
+    if (worst > qg.bound) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const uint32_t w = opaque_u32(x[16 * gi + (i >> 1)]);
-        const float a = __fsub_rn(h2f(static_cast<uint16_t>(w >> (16 * (i & 1)))), mn);
-        if (quot_near(a, rc, Q)) dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_exact(a, s, Q));
+        const float xe = h2f(static_cast<uint16_t>(w >> (16 * (i & 1))));
+        if (quot_near(xe, qg)) dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_exact(__fsub_rn(xe, mn), s, Q));
       }
     }
     vm[g * kBlockTokens + j] = s;
@@ -1407,6 +1417,7 @@ __device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const La
   }
   const uint16_t sdiv = static_cast<uint16_t>(s & 0x7fff);
   uint32_t* dst = reinterpret_cast<uint32_t*>(ck + j * D + 64 * g);
+  const QuotGroup qg = quot_group(base, rc, lo, Q);
   float worst = 0.f;
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
@@ -1414,18 +1425,18 @@ __device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const La
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 4 * q + e;
-      const float a = __fsub_rn(h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1)))), base);
-      w |= static_cast<uint32_t>(quot_fast(a, rc, lo, Q, worst) + off) << (8 * e);
+      w |= static_cast<uint32_t>(quot_fast(h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1)))), qg, worst) + off)
+           << (8 * e);
     }
     dst[q] = w;
   }
-  if (worst > quot_bound(Q)) {
+  if (worst > qg.bound) {
     uint8_t* db = reinterpret_cast<uint8_t*>(dst);
 #pragma unroll
     for (int i = 0; i < 64; ++i) {
       const uint32_t w = opaque_u32(x[i >> 1]);
-      const float a = __fsub_rn(h2f(static_cast<uint16_t>(w >> (16 * (i & 1)))), base);
-      if (quot_near(a, rc, lo, Q)) db[i] = static_cast<uint8_t>(quot_exact(a, sdiv, lo, Q) + off);
+      const float xe = h2f(static_cast<uint16_t>(w >> (16 * (i & 1))));
+      if (quot_near(xe, qg)) db[i] = static_cast<uint8_t>(quot_exact(__fsub_rn(xe, base), sdiv, lo, Q) + off);
     }
   }
   kmeta[j * 2 + g] = s | (static_cast<uint32_t>(z) << 16);
@@ -1490,18 +1501,17 @@ __device__ __forceinline__ void inner_value_lane(uint32_t (&x)[16], const LayerD
   uint16_t s, z;
   asym_pair_params(lo2, hi2, 0, Qi, mn, s, z, rc);
   uint8_t* dst = cvc + vchunk_off(j, 32 * q);
+  const QuotGroup qg = quot_group(mn, rc, 0.f, Q);
   float worst = 0.f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float a = __fsub_rn(h2f(static_cast<uint16_t>(v[i >> 1] >> (16 * (i & 1)))), mn);
-    dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_fast(a, rc, Q, worst));
-  }
-  if (worst > quot_bound(Q)) {
+  for (int i = 0; i < 32; ++i)
+    dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_fast(h2f(static_cast<uint16_t>(v[i >> 1] >> (16 * (i & 1)))), qg, worst));
+  if (worst > qg.bound) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
       const uint32_t w = opaque_u32(v[i >> 1]);
-      const float a = __fsub_rn(h2f(static_cast<uint16_t>(w >> (16 * (i & 1)))), mn);
-      if (quot_near(a, rc, Q)) dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_exact(a, s, Q));
+      const float xe = h2f(static_cast<uint16_t>(w >> (16 * (i & 1))));
+      if (quot_near(xe, qg)) dst[vchunk_off(0, i)] = static_cast<uint8_t>(quot_exact(__fsub_rn(xe, mn), s, Q));
     }
   }
   vm[q * kBlockTokens + j] = s;
