@@ -1358,6 +1358,17 @@ __device__ __forceinline__ double quad_xor(double v) {
   return __longlong_as_double((static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo));
 }
 
+// acc + (half H of w), the binary16 operand widened inside one fused
+// multiply-add (one rounding)
+template <int H>
+__device__ __forceinline__ float add_half(float acc, uint32_t w) {
+  if constexpr (H == 0)
+    asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w));
+  else
+    asm("v_fma_mix_f32 %0, %1, 1.0, %0 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(acc) : "v"(w));
+  return acc;
+}
+
 // Exact binary64 sum of fp16 elements as an int64 count of 2^-24 units (the
 // sum of up to 64 values below 2^16 in those units stays below 2^46, exact in
 // binary64 and in int64).
@@ -1386,13 +1397,35 @@ __device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const La
   const int bits = L.kb;
   bool sym = false;
   if (L.k_hybrid) {
-    // symmetric iff den |sum x| <= num W (max - min), exactly (units of 2^-24)
-    double sum = 0.0;
+    // symmetric iff den |sum x| <= num W (max - min), exactly.  First an
+    // fp32 estimate of the sum (four chains of 16; each add widens its
+    // binary16 operand exactly): every element passes through at most 17
+    // roundings, so |est - sum| <= 17.1 * 2^-24 * sum |x| <= 2^-13 A with
+    // A = max(|min|, |max|) >= |x|.  Only a group whose test lies within
+    // that margin sums again exactly (binary64, units of 2^-24).
+    float p[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 64; ++i) sum += static_cast<double>(h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1)))));
-    int64_t su = units_of(sum);
-    su = su < 0 ? -su : su;
-    sym = static_cast<int64_t>(L.ratio_den) * su <= static_cast<int64_t>(L.ratio_num) * 64 * (h2fixed(hmx) - h2fixed(hmn));
+    for (int i = 0; i < 32; ++i) {
+      p[(2 * i) & 3] = add_half<0>(p[(2 * i) & 3], x[i]);
+      p[(2 * i + 1) & 3] = add_half<1>(p[(2 * i + 1) & 3], x[i]);
+    }
+    const double den = static_cast<double>(L.ratio_den);
+    const double est = fabs(static_cast<double>((p[0] + p[1]) + (p[2] + p[3])));
+    const double margin = static_cast<double>(fmaxf(fabsf(mn), fabsf(mx))) * 0x1p-13;
+    const double rhs = static_cast<double>(L.ratio_num) * 64.0 * (static_cast<double>(mx) - static_cast<double>(mn));
+    if (den * (est + margin) <= rhs) {
+      sym = true;
+    } else if (den * (est - margin) > rhs) {
+      sym = false;
+    } else {
+      double sum = 0.0;
+#pragma unroll
+      for (int i = 0; i < 64; ++i)
+        sum += static_cast<double>(h2f(static_cast<uint16_t>(opaque_u32(x[i >> 1]) >> (16 * (i & 1)))));
+      int64_t su = units_of(sum);
+      su = su < 0 ? -su : su;
+      sym = static_cast<int64_t>(L.ratio_den) * su <= static_cast<int64_t>(L.ratio_num) * 64 * (h2fixed(hmx) - h2fixed(hmn));
+    }
   }
   uint16_t s, z;
   float lo, Q, rc, base;
@@ -1631,24 +1664,87 @@ __device__ __forceinline__ int nuq_search(float u, const float (&m)[7], float& g
   gap = fminf(fminf(fabsf(u - m[3]), fabsf(u - ma)), fabsf(u - mb));
   return (b2 ? 4 : 0) + (b1 ? 2 : 0) + (b0 ? 1 : 0);
 }
-// Codebook code of d = fl32(x - min) with scale s (rc its reciprocal, 0 when
-// s == 0: code 0), tracking the smallest gap seen; nuq_exact redoes one with
-// the correctly rounded quotient.
-__device__ __forceinline__ int nuq_fast(float d, float rc, const float (&m)[7], float& worst_gap) {
+// Codebook code of element x with group minimum mn and scale s, from the
+// estimate u = fl32(x * rc + nb) (rc = rcp(s), 0 when s == 0: code 0; nb =
+// fl32(-mn * rc)), tracking the smallest gap seen.  Near the midpoints
+// (|u| <= 1 + 2^-18) u lies within 2^-21 + |mn * rc| 2^-24 of the quotient
+// fl32(fl32(x - mn) / s) (the reciprocal and the four roundings), so a gap
+// of at least nuq_thr = 2^-18 + |mn * rc| 2^-22 leaves the code unchanged;
+// a lane whose smallest gap is below it redoes those elements with
+// nuq_exact and the correctly rounded quotient.
+__device__ __forceinline__ float nuq_thr(float mn, float rc) { return 0x1p-18f + fabsf(mn * rc) * 0x1p-22f; }
+__device__ __forceinline__ int nuq_fast(float x, float rc, float nb, const float (&m)[7], float& worst_gap) {
   float gap;
-  const int c = nuq_search(d * rc, m, gap);
+  const int c = nuq_search(fmaf(x, rc, nb), m, gap);
   worst_gap = fminf(worst_gap, gap);
   return c;
 }
-__device__ __forceinline__ bool nuq_near(float d, float rc, const float (&m)[7]) {
+__device__ __forceinline__ bool nuq_near(float x, float rc, float nb, const float (&m)[7], float thr) {
   float gap;
-  nuq_search(d * rc, m, gap);
-  return gap < 0x1p-18f;
+  nuq_search(fmaf(x, rc, nb), m, gap);
+  return gap < thr;
 }
 __device__ __forceinline__ int nuq_exact(float d, uint16_t s, const float (&m)[7]) {
   if (s == 0) return 0;
   float gap;
   return nuq_search(__fdiv_rn(d, h2f(s)), m, gap);
+}
+
+// Cell tables for the codebook search.  The estimate is taken on the grid
+// t' = u * 256 + o (o = k / 64 chosen per layer so that every midpoint sits at
+// least kCellMargin from a cell edge, at most one per cell, all below cell
+// 254).  Entry c of a table is the shifted midpoint fl32(m * 256 + o) inside
+// cell c (1e30 when the cell holds none) with its three lowest mantissa bits
+// replaced by the number of midpoints below the cell; the code of t' in cell
+// c is that count plus (t' > entry).  The entry moves by at most 2^-13
+// (rounding and the count bits); t' lies within 2^-13.6 + |mn * rc| 2^-15 of
+// 256 fl32(fl32(x - mn) / s) + o (the reciprocal, the roundings of nb, of the
+// offset, of t' and of the quotient), so a distance |t' - entry| of at least
+// cell_thr = 2^-11 + |mn * rc| 2^-14 leaves the code unchanged: the cell's
+// other neighbours are at least kCellMargin >= cell_thr away.  A lane that
+// sees a smaller distance (or a group whose cell_thr passes the margin)
+// recodes its elements by the midpoint search and the exact quotient.
+constexpr float kCellMargin = 1.f / 32;
+__device__ __forceinline__ float cell_thr(float mn, float rc) { return 0x1p-11f + fabsf(mn * rc) * 0x1p-14f; }
+__device__ __forceinline__ uint32_t cvt_u32_sat(float x) {
+  uint32_t r;
+  asm("v_cvt_u32_f32 %0, %1" : "=v"(r) : "v"(x));  // negative and NaN give 0
+  return r;
+}
+__device__ __forceinline__ int cell_code(float x, float rc256, float nbo, const float* table, float& worst) {
+  const float tp = fmaf(x, rc256, nbo);
+  const float e = table[min(cvt_u32_sat(tp), 255u)];
+  const float d = tp - e;
+  worst = fminf(worst, fabsf(d));
+  return static_cast<int>(__float_as_uint(e) & 7u) + (d > 0.f ? 1 : 0);
+}
+// Grid offset o for midpoints m (lanes test o = l / 64; the lowest that works
+// wins), or -1 when none does; then thread i of the workgroup fills entry i.
+__device__ __forceinline__ float cell_offset(const float (&m)[7], int l) {
+  const float o = static_cast<float>(l) * (1.f / 64);
+  bool ok = true;
+  int prev = -1;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const float pj = fmaf(m[j], 256.f, o);
+    const float fl = floorf(pj);
+    ok = ok && pj >= 0.f && pj < 254.f && pj - fl >= kCellMargin && fl + 1.f - pj >= kCellMargin &&
+         static_cast<int>(fl) > prev;
+    prev = static_cast<int>(fl);
+  }
+  const uint64_t b = __ballot(ok);
+  return b == 0 ? -1.f : static_cast<float>(__builtin_ctzll(b)) * (1.f / 64);
+}
+__device__ __forceinline__ float cell_entry(const float (&m)[7], float o, int c) {
+  uint32_t below = 0;
+  float e = 1e30f;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    const float pj = fmaf(m[j], 256.f, o);
+    below += pj < static_cast<float>(c) ? 1u : 0u;
+    if (floorf(pj) == static_cast<float>(c)) e = pj;
+  }
+  return __uint_as_float((__float_as_uint(e) & ~7u) | below);
 }
 
 // Sortable outlier key of element (x, column c): magnitude, then the lower
@@ -1715,7 +1811,7 @@ __device__ __forceinline__ bool masked_extremes(const uint32_t (&x)[16], uint32_
 
 template <int ROLE>  // 0 keys, 1 rows
 __device__ __forceinline__ void codebook_walk(const LayerDesc& L, const QuantJob& J, int wv, int l, uint32_t* kmask,
-                                              float* kext, uint8_t* cv) {
+                                              float* kext, uint8_t* cv, const float* cells, float off) {
   constexpr int NW = ROLE == 0 ? 16 : 32;
   const uint32_t total = static_cast<uint32_t>(J.nblocks) * static_cast<uint32_t>(L.units);  // below 2^31 (checked at launch)
   const uint32_t nbk = static_cast<uint32_t>(J.nblocks);
@@ -1773,28 +1869,56 @@ __device__ __forceinline__ void codebook_walk(const LayerDesc& L, const QuantJob
       uint16_t s, z;
       nuq_params(mn, mx, any, s, z);
       const float rc = s == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(s));
+      const float nb = -(mn * rc), thr = nuq_thr(mn, rc);
       uint32_t* dst = reinterpret_cast<uint32_t*>(cv + rj * D + 32 * q);
-      float worst = 1.f;
+      if (off >= 0.f) {
+        // cell tables (cells + 256: the value table)
+        const float rc256 = rc * 256.f, nbo = -(mn * rc256) + off, cthr = cell_thr(mn, rc);
+        float worst = cthr > kCellMargin ? -1.f : 1e30f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        uint32_t wd = 0;
+        for (int k = 0; k < 8; ++k) {
+          uint32_t wd = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * k + e;
-          // converted again rather than kept from the extremes pass (registers)
-          const float d = __fsub_rn(h2f(static_cast<uint16_t>(opaque_u32(vx[i >> 1]) >> (16 * (i & 1)))), mn);
-          wd |= static_cast<uint32_t>(nuq_fast(d, rc, mv, worst)) << (8 * e);
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * k + e;
+            const float xe = h2f(static_cast<uint16_t>(opaque_u32(vx[i >> 1]) >> (16 * (i & 1))));
+            wd |= static_cast<uint32_t>(cell_code(xe, rc256, nbo, cells + 256, worst)) << (8 * e);
+          }
+          dst[k] = wd;
+          __builtin_amdgcn_sched_barrier(0);  // keep the code words' live ranges short
         }
-        dst[k] = wd;
-        __builtin_amdgcn_sched_barrier(0);  // keep the code words' live ranges short
-      }
-      if (worst < 0x1p-18f) {
-        uint8_t* db = reinterpret_cast<uint8_t*>(dst);
+        if (worst < cthr) {
+          uint8_t* db = reinterpret_cast<uint8_t*>(dst);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const uint32_t wv2 = opaque_u32(vx[i >> 1]);
-          const float d = __fsub_rn(h2f(static_cast<uint16_t>(wv2 >> (16 * (i & 1)))), mn);
-          if (nuq_near(d, rc, mv)) db[i] = static_cast<uint8_t>(nuq_exact(d, s, mv));
+          for (int i = 0; i < 32; ++i) {
+            const float xe = h2f(static_cast<uint16_t>(opaque_u32(vx[i >> 1]) >> (16 * (i & 1))));
+            float gap;
+            const int c = nuq_search(fmaf(xe, rc, nb), mv, gap);
+            db[i] = static_cast<uint8_t>(gap < thr ? nuq_exact(__fsub_rn(xe, mn), s, mv) : c);
+          }
+        }
+      } else {
+        float worst = 1.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          uint32_t wd = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * k + e;
+            // converted again rather than kept from the extremes pass (registers)
+            const float xe = h2f(static_cast<uint16_t>(opaque_u32(vx[i >> 1]) >> (16 * (i & 1))));
+            wd |= static_cast<uint32_t>(nuq_fast(xe, rc, nb, mv, worst)) << (8 * e);
+          }
+          dst[k] = wd;
+          __builtin_amdgcn_sched_barrier(0);  // keep the code words' live ranges short
+        }
+        if (worst < thr) {
+          uint8_t* db = reinterpret_cast<uint8_t*>(dst);
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const float xe = h2f(static_cast<uint16_t>(opaque_u32(vx[i >> 1]) >> (16 * (i & 1))));
+            if (nuq_near(xe, rc, nb, mv, thr)) db[i] = static_cast<uint8_t>(nuq_exact(__fsub_rn(xe, mn), s, mv));
+          }
         }
       }
       uint16_t* vm = reinterpret_cast<uint16_t*>(rec + L.off_vm);
@@ -1858,23 +1982,52 @@ __device__ __forceinline__ void codebook_walk(const LayerDesc& L, const QuantJob
       // 6-bit fields (c1 << 3 | c0) of tokens t at bit 6 t of the chunk's
       // 96-bit half 3 half .. 3 half + 2 (words)
       uint32_t f[16];
-      float worst = 1.f;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float d0 = __fsub_rn(h2f(static_cast<uint16_t>(x[t])), mn[0]);
-        const float d1 = __fsub_rn(h2f(static_cast<uint16_t>(x[t] >> 16)), mn[1]);
-        f[t] = static_cast<uint32_t>(nuq_fast(d0, rc[0], mk, worst)) |
-               (static_cast<uint32_t>(nuq_fast(d1, rc[1], mk, worst)) << 3);
-        if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // keep the searches' live ranges short
-      }
-      if (worst < 0x1p-18f) {
+      const float nb0 = -(mn[0] * rc[0]), nb1 = -(mn[1] * rc[1]);
+      const float thr0 = nuq_thr(mn[0], rc[0]), thr1 = nuq_thr(mn[1], rc[1]);
+      if (off >= 0.f) {
+        const float r0 = rc[0] * 256.f, r1 = rc[1] * 256.f;
+        const float o0 = -(mn[0] * r0) + off, o1 = -(mn[1] * r1) + off;
+        const float cthr = fmaxf(cell_thr(mn[0], rc[0]), cell_thr(mn[1], rc[1]));
+        float worst = cthr > kCellMargin ? -1.f : 1e30f;
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
-          const uint32_t xw = opaque_u32(x[t]);
-          const float d0 = __fsub_rn(h2f(static_cast<uint16_t>(xw)), mn[0]);
-          const float d1 = __fsub_rn(h2f(static_cast<uint16_t>(xw >> 16)), mn[1]);
-          if (nuq_near(d0, rc[0], mk)) f[t] = (f[t] & ~7u) | static_cast<uint32_t>(nuq_exact(d0, sz[0][0], mk));
-          if (nuq_near(d1, rc[1], mk)) f[t] = (f[t] & 7u) | (static_cast<uint32_t>(nuq_exact(d1, sz[1][0], mk)) << 3);
+          const float x0 = h2f(static_cast<uint16_t>(x[t])), x1 = h2f(static_cast<uint16_t>(x[t] >> 16));
+          f[t] = static_cast<uint32_t>(cell_code(x0, r0, o0, cells, worst)) |
+                 (static_cast<uint32_t>(cell_code(x1, r1, o1, cells, worst)) << 3);
+          if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // keep the live ranges short
+        }
+        if (worst < cthr) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const uint32_t xw = opaque_u32(x[t]);
+            const float x0 = h2f(static_cast<uint16_t>(xw)), x1 = h2f(static_cast<uint16_t>(xw >> 16));
+            float g0, g1;
+            int c0 = nuq_search(fmaf(x0, rc[0], nb0), mk, g0);
+            int c1 = nuq_search(fmaf(x1, rc[1], nb1), mk, g1);
+            if (g0 < thr0) c0 = nuq_exact(__fsub_rn(x0, mn[0]), sz[0][0], mk);
+            if (g1 < thr1) c1 = nuq_exact(__fsub_rn(x1, mn[1]), sz[1][0], mk);
+            f[t] = static_cast<uint32_t>(c0) | (static_cast<uint32_t>(c1) << 3);
+          }
+        }
+      } else {
+        float worst = 1.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float x0 = h2f(static_cast<uint16_t>(x[t])), x1 = h2f(static_cast<uint16_t>(x[t] >> 16));
+          f[t] = static_cast<uint32_t>(nuq_fast(x0, rc[0], nb0, mk, worst)) |
+                 (static_cast<uint32_t>(nuq_fast(x1, rc[1], nb1, mk, worst)) << 3);
+          if ((t & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // keep the searches' live ranges short
+        }
+        if (worst < fmaxf(thr0, thr1)) {
+#pragma unroll
+          for (int t = 0; t < 16; ++t) {
+            const uint32_t xw = opaque_u32(x[t]);
+            const float x0 = h2f(static_cast<uint16_t>(xw)), x1 = h2f(static_cast<uint16_t>(xw >> 16));
+            if (nuq_near(x0, rc[0], nb0, mk, thr0))
+              f[t] = (f[t] & ~7u) | static_cast<uint32_t>(nuq_exact(__fsub_rn(x0, mn[0]), sz[0][0], mk));
+            if (nuq_near(x1, rc[1], nb1, mk, thr1))
+              f[t] = (f[t] & 7u) | (static_cast<uint32_t>(nuq_exact(__fsub_rn(x1, mn[1]), sz[1][0], mk)) << 3);
+          }
         }
       }
       uint32_t wd[3] = {0u, 0u, 0u};
@@ -1915,12 +2068,39 @@ prefill_codebook_kernel(LayerDesc L, QuantJob J) {
   __shared__ __align__(16) uint32_t kmask[kBlockTokens * 4];   // key-row outlier bits per token
   __shared__ __align__(16) float kext[2 * 4 * 64];             // [token half][min0, max0, min1, max1][lane]
   __shared__ __align__(16) uint8_t cv[kBlockTokens * D];       // value codes, row-major
+  __shared__ float cells[2 * 256];                             // key and value cell tables
+  __shared__ float offs[2];
   const int l = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  {
+    float mk[7], mv[7];
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      mk[j] = __fmul_rn(__fadd_rn(h2f(L.lev_k[j]), h2f(L.lev_k[j + 1])), 0.5f);
+      mv[j] = __fmul_rn(__fadd_rn(h2f(L.lev_v[j]), h2f(L.lev_v[j + 1])), 0.5f);
+    }
+    if (wv == 0) {
+      const float ok = cell_offset(mk, l), ov = cell_offset(mv, l);
+      if (l == 0) {
+        offs[0] = ok < 0.f || ov < 0.f ? -1.f : ok;
+        offs[1] = ov;
+      }
+    }
+    __syncthreads();
+    const float ok = offs[0], ov = offs[1];
+    if (ok >= 0.f) {
+      cells[threadIdx.x] = cell_entry(mk, ok, threadIdx.x);
+      cells[256 + threadIdx.x] = cell_entry(mv, ov, threadIdx.x);
+    }
+    __syncthreads();
+  }
+  // one offset per table: the key walk reads offs[0], the row walk offs[1]
+  // (both are -1 when either table cannot be built)
+  const float off = offs[0] < 0.f ? -1.f : offs[wv < 2 ? 0 : 1];
   if (wv < 2)
-    codebook_walk<0>(L, J, wv, l, kmask, kext, cv);
+    codebook_walk<0>(L, J, wv, l, kmask, kext, cv, cells, off);
   else
-    codebook_walk<1>(L, J, wv, l, kmask, kext, cv);
+    codebook_walk<1>(L, J, wv, l, kmask, kext, cv, cells, off);
 }
 
 __global__ void __launch_bounds__(128) copy_fp16_kernel(LayerDesc L, CopyJob J) {

@@ -247,6 +247,125 @@ def test_prefill_codes_on_rounding_ties(keys, pair, nudge):
     cache.close()
 
 
+def _hybrid_boundary_keys(T, D):
+    """fp16 [T][D] whose inner key groups of 64 channels sit on the hybrid
+    test's boundary for the ratio 1/10: minimum -1, maximum 4, 29 ones and
+    zeros elsewhere give 10 |sum| = 320 = 64 (max - min) exactly (symmetric);
+    one of the ones moved an ulp up (asymmetric) or down (symmetric).  Each
+    group is scaled by a power of two, negated in turn, and its channels are
+    permuted."""
+    rng = np.random.default_rng(7)
+    out = np.zeros((T, D), np.float32)
+    for t in range(T):
+        for g in range(D // 64):
+            x = np.zeros(64, np.float32)
+            x[0], x[1], x[2:31] = -1.0, 4.0, 1.0
+            kind = (2 * t + g) % 3
+            if kind == 1:
+                x[2] = np.nextafter(np.float16(1.0), np.float16(np.inf))
+            elif kind == 2:
+                x[2] = np.nextafter(np.float16(1.0), np.float16(-np.inf))
+            x *= 2.0 ** ((t % 5) - 2) * (-1.0 if (t + g) % 2 else 1.0)
+            out[t, 64 * g:64 * g + 64] = x[rng.permutation(64)]
+    return out.astype(np.float16)
+
+
+def test_prefill_hybrid_choice_on_its_boundary():
+    """Inner key groups whose symmetric/asymmetric test holds with equality,
+    or misses it by one ulp of one element (where an estimate of the group
+    sum cannot decide): the library's codes and parameters equal the
+    oracle's bit for bit, and both choices occur."""
+    import oracle as O
+    from decode_attention_quantize_amd import KVQCache, config_from_workload
+    from gpu_harness import HostLayer, unit_body
+    from kvq_unpack import unpack_unit
+    wl = W.C5.with_(name="hybrid-boundary", B=1, Hq=1, Hkv=1, T=256, steps=1, v_hadamard=False)
+    kb, vb = wl.fixed_pairs[0]
+    T, D = wl.T, wl.D
+    K = _hybrid_boundary_keys(T, D)
+    V = _ties_tensor(T, D, vb, 0.125, False, False)
+    say("[hybrid] boundary groups")
+    cache = KVQCache(config_from_workload(wl), wl.bit_pairs(), device="cuda")
+    cache.prefill(0, torch.from_numpy(K).view(1, 1, T, D).cuda(), torch.from_numpy(V).view(1, 1, T, D).cuda())
+    torch.cuda.synchronize()
+    s_eff, nb, _ = O.state_prefill(T, wl.sinks, wl.window, wl.flush)
+    enc = O.encode_unit(O.scheme_for(wl, 0), K.view(np.uint16), V.view(np.uint16), T, s_eff, nb)
+    body, lay = unit_body(cache, 0, 0, HostLayer(cache, 0))
+    got = unpack_unit(body, lay, kb, vb, nb, True, wl.k_group, wl.v_group, wl.outliers, 0)
+    for key in ("kcodes", "kmeta", "vcodes", "vmeta"):
+        bad = np.argwhere(got[key] != enc[key])
+        assert bad.size == 0, (key, bad[:5].tolist())
+    # symmetric groups carry the scale's sign bit; both kinds are present
+    sym = [O.hybrid_is_sym(K[t, 64 * g:64 * g + 64].view(np.uint16).copy(), 1, 10)
+           for t in range(nb) for g in range(D // 64)]
+    assert any(sym) and not all(sym)
+    cache.close()
+
+
+# Codebook levels on a 2^-10 grid: their midpoints are binary16 values
+_MID_LEVELS = np.array([0, 129, 266, 408, 541, 679, 838, 1024], np.float64) / 1024
+
+
+def _midpoint_tensor(T, D, lv):
+    """fp16 [T][D] = w - 0.5 with w in [0, 1]: every key group (32 tokens of a
+    channel) and value group (32 channels of a token) holds w = 0 and w = 1, so
+    min = -0.5 and s = 1 and the quotient (x - min) / s is w itself; the other
+    elements are the levels, their midpoints and both 2^-12 neighbours of
+    each.  Two columns per row hold +-100, the row's two sparse outliers."""
+    mids = (lv[:-1] + lv[1:]) / 2
+    pool = np.concatenate([lv, mids, mids - 2.0 ** -12, mids + 2.0 ** -12,
+                           np.clip(lv[1:-1] - 2.0 ** -12, 0, 1), np.clip(lv[1:-1] + 2.0 ** -12, 0, 1)])
+    t = np.arange(T)[:, None]
+    c = np.arange(D)[None, :]
+    r = (t + c) % 32
+    w = pool[(t * 5 + c * 3) % pool.size]
+    w = np.where(r == 0, 0.0, np.where(r == 1, 1.0, w))
+    x = w - 0.5
+    tt = np.arange(T)
+    ca = (2 - tt) % 32 + 32 * (tt % 4)
+    cb = (3 - tt) % 32 + 32 * ((tt + 2) % 4)
+    x[tt, ca] = 100.0
+    x[tt, cb] = -100.0
+    assert np.all(x.astype(np.float16).astype(np.float64) == x)
+    return x.astype(np.float16)
+
+
+def test_codebook_codes_next_to_the_midpoints():
+    """3-bit codebook keys and values whose quotients sit exactly on a level
+    midpoint (a tie, decided below it) or 2^-12 to either side: the
+    library's codes, parameters and outliers equal the oracle's bit for bit."""
+    import oracle as O
+    from decode_attention_quantize_amd import KVQCache, config_from_workload
+    from gpu_harness import HostLayer, unit_body
+    from kvq_unpack import unpack_unit
+    wl = W.C4.with_(name="nuq-midpoints", B=1, Hq=1, Hkv=1, T=256, steps=1)
+    T, D = wl.T, wl.D
+    cb = np.zeros((1, 2, 8), np.uint16)
+    cb[0, 0] = _MID_LEVELS.astype(np.float16).view(np.uint16)
+    cb[0, 1] = _MID_LEVELS.astype(np.float16).view(np.uint16)
+    K = _midpoint_tensor(T, D, _MID_LEVELS)
+    V = np.ascontiguousarray(K[::-1])
+    say("[nuq] codes next to the midpoints")
+    cache = KVQCache(config_from_workload(wl), wl.bit_pairs(), cb, device="cuda")
+    cache.prefill(0, torch.from_numpy(K).view(1, 1, T, D).cuda(), torch.from_numpy(V).view(1, 1, T, D).cuda())
+    torch.cuda.synchronize()
+    s_eff, nb, _ = O.state_prefill(T, wl.sinks, wl.window, wl.flush)
+    sc = O.scheme_for(wl, 0)
+    for i in range(8):
+        sc.levels_k[i] = int(cb[0, 0, i])
+        sc.levels_v[i] = int(cb[0, 1, i])
+    enc = O.encode_unit(sc, K.view(np.uint16), V.view(np.uint16), T, s_eff, nb)
+    body, lay = unit_body(cache, 0, 0, HostLayer(cache, 0))
+    got = unpack_unit(body, lay, 3, 3, nb, False, wl.k_group, wl.v_group, wl.outliers, 0)
+    for key in ("kcodes", "kmeta", "vcodes", "vmeta", "kocol", "koval", "vocol", "voval"):
+        bad = np.argwhere(got[key] != enc[key])
+        assert bad.size == 0, (key, bad[:5].tolist())
+    # the construction reaches every code, and the tie elements' quotients are exact
+    assert set(np.unique(enc["kcodes"]).tolist()) == set(range(8))
+    assert np.all(enc["kmeta"][..., 0] == np.float16(1.0).view(np.uint16))
+    cache.close()
+
+
 @pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C5r", "C4r", "short-prompt-sinks-then-flush"])
 def test_fused_append_decode_matches_the_two_calls(name):
     """kvq_append_decode_attn stands for kvq_append_token + kvq_decode_attn:
