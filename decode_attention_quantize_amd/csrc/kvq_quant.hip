@@ -1747,13 +1747,19 @@ __device__ __forceinline__ float cell_entry(const float (&m)[7], float o, int c)
   return __uint_as_float((__float_as_uint(e) & ~7u) | below);
 }
 
-// Sortable outlier key of element (x, column c): magnitude, then the lower
-// column, then the sign (so the raw value can be rebuilt).
-__device__ __forceinline__ uint32_t outlier_key(uint32_t x16, int c) {
-  return ((x16 & 0x7fffu) << 8) | (static_cast<uint32_t>(127 - c) << 1) | (x16 >> 15);
+// Sortable outlier key of an element: its magnitude (bits 16..30), then the
+// lower column (127 - c in bits 8..15), then the high byte of the binary16
+// (bits 0..7, the sign at bit 7, so the raw value can be rebuilt).  In the
+// lane the column byte holds 31 - i for element i of the lane's 32 columns;
+// one byte permute and one mask build the key from the element's half of
+// its word (H = 0 low half, 1 high half).
+template <int H>
+__device__ __forceinline__ uint32_t outlier_key_local(uint32_t w, int i) {
+  constexpr uint32_t sel = H == 0 ? 0x05040005u : 0x07060007u;  // [hi byte, lo byte, column, hi byte]
+  return __builtin_amdgcn_perm(w, static_cast<uint32_t>(31 - i), sel) & 0x7fffffffu;
 }
-__device__ __forceinline__ int outlier_col(uint32_t key) { return 127 - static_cast<int>((key >> 1) & 127u); }
-__device__ __forceinline__ uint32_t outlier_bits(uint32_t key) { return ((key >> 8) & 0x7fffu) | ((key & 1u) << 15); }
+__device__ __forceinline__ int outlier_col(uint32_t key) { return 127 - static_cast<int>((key >> 8) & 127u); }
+__device__ __forceinline__ uint32_t outlier_bits(uint32_t key) { return ((key >> 16) & 0x7fffu) | ((key & 0x80u) << 8); }
 
 // Top two keys of a row held by a lane quad (lane q: columns 32 q .. + 31,
 // element i = half i % 2 of x[i / 2]); every lane of the quad gets them.
@@ -1762,12 +1768,15 @@ __device__ __forceinline__ void row_top2(const uint32_t (&x)[16], int q, uint32_
   t1 = 0u;
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
-    const uint32_t k = outlier_key((x[i >> 1] >> (16 * (i & 1))) & 0xffffu, 32 * q + i);
+    const uint32_t k = (i & 1) ? outlier_key_local<1>(x[i >> 1], i) : outlier_key_local<0>(x[i >> 1], i);
     uint32_t m;  // second largest of {t0, t1, k} (t0 >= t1)
     asm("v_med3_u32 %0, %1, %2, %3" : "=v"(m) : "v"(t0), "v"(t1), "v"(k));
     t1 = m;
     t0 = max(t0, k);
   }
+  // lane-local columns to row columns (127 - c = 32 (3 - q) + 31 - i)
+  t0 += static_cast<uint32_t>(3 - q) << 13;
+  t1 += static_cast<uint32_t>(3 - q) << 13;
   auto join = [&](uint32_t o0, uint32_t o1) __attribute__((always_inline)) {
     t1 = max(min(t0, o0), max(t1, o1));
     t0 = max(t0, o0);
