@@ -1804,17 +1804,31 @@ __device__ __forceinline__ uint32_t row_outliers(uint32_t t0, uint32_t t1, int q
   return m;
 }
 
-// Extremes of the members (elements whose mask bit is clear) of 32 halves.
+// Halves of w whose element is excluded (mask bits lo / hi set) replaced by
+// the binary16 bit pattern `fill` (both halves).
+__device__ __forceinline__ uint32_t mask_halves(uint32_t w, uint32_t ex, int lo_bit, uint32_t ex_hi, int hi_bit,
+                                                uint32_t fill) {
+  const uint32_t ml = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(ex), lo_bit, 1));
+  const uint32_t mh = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(ex_hi), hi_bit, 1));
+  const uint32_t m = __builtin_amdgcn_perm(mh, ml, 0x07060100u);  // low half from ml, high half from mh
+  return (fill & m) | (w & ~m);
+}
+constexpr uint32_t kInf2 = 0x7c007c00u, kNegInf2 = 0xfc00fc00u;
+
+// Extremes of the members (elements whose mask bit is clear) of 32 halves,
+// on the binary16 pairs (excluded elements read as +inf for the minimum and
+// -inf for the maximum).
 __device__ __forceinline__ bool masked_extremes(const uint32_t (&x)[16], uint32_t ex, float& mn, float& mx) {
-  mn = __int_as_float(0x7f800000);
-  mx = __int_as_float(0xff800000);
+  uint32_t lo2 = kInf2, hi2 = kNegInf2;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float v = h2f(static_cast<uint16_t>(x[i >> 1] >> (16 * (i & 1))));
-    const bool in = !((ex >> i) & 1u);
-    mn = fminf(mn, in ? v : __int_as_float(0x7f800000));
-    mx = fmaxf(mx, in ? v : __int_as_float(0xff800000));
+  for (int k = 0; k < 16; ++k) {
+    lo2 = pk_min_h(lo2, mask_halves(x[k], ex, 2 * k, ex, 2 * k + 1, kInf2));
+    hi2 = pk_max_h(hi2, mask_halves(x[k], ex, 2 * k, ex, 2 * k + 1, kNegInf2));
   }
+  lo2 = pk_min_h(lo2, lo2 >> 16);
+  hi2 = pk_max_h(hi2, hi2 >> 16);
+  mn = h2f(static_cast<uint16_t>(lo2));
+  mx = h2f(static_cast<uint16_t>(hi2));
   return mn <= mx;
 }
 
@@ -1963,17 +1977,15 @@ __device__ __forceinline__ void codebook_walk(const LayerDesc& L, const QuantJob
         ex0 |= ((m[l >> 5] >> (l & 31)) & 1u) << t;
         ex1 |= ((m[2 + (l >> 5)] >> (l & 31)) & 1u) << t;
       }
-      float e4[4] = {__int_as_float(0x7f800000), __int_as_float(0xff800000), __int_as_float(0x7f800000),
-                     __int_as_float(0xff800000)};
+      // channel l in the low halves, l + 64 in the high ones
+      uint32_t lo2 = kInf2, hi2 = kNegInf2;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const float a = h2f(static_cast<uint16_t>(x[t])), b = h2f(static_cast<uint16_t>(x[t] >> 16));
-        const bool ia = !((ex0 >> t) & 1u), ib = !((ex1 >> t) & 1u);
-        e4[0] = fminf(e4[0], ia ? a : __int_as_float(0x7f800000));
-        e4[1] = fmaxf(e4[1], ia ? a : __int_as_float(0xff800000));
-        e4[2] = fminf(e4[2], ib ? b : __int_as_float(0x7f800000));
-        e4[3] = fmaxf(e4[3], ib ? b : __int_as_float(0xff800000));
+        lo2 = pk_min_h(lo2, mask_halves(x[t], ex0, t, ex1, t, kInf2));
+        hi2 = pk_max_h(hi2, mask_halves(x[t], ex0, t, ex1, t, kNegInf2));
       }
+      const float e4[4] = {h2f(static_cast<uint16_t>(lo2)), h2f(static_cast<uint16_t>(hi2)),
+                           h2f(static_cast<uint16_t>(lo2 >> 16)), h2f(static_cast<uint16_t>(hi2 >> 16))};
 #pragma unroll
       for (int k = 0; k < 4; ++k) kext[(half * 4 + k) * 64 + l] = e4[k];
     }
