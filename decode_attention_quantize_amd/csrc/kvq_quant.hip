@@ -1338,8 +1338,9 @@ prefill_kivi_kernel(LayerDesc L, QuantJob J) {
 // prefill_inner_kernel quantizes the whole prompt blocks of layers with keys
 // in inner groups of 64 channels (each group symmetric or asymmetric by the
 // hybrid test, or always asymmetric) and per-token asymmetric values in
-// groups of 32, optionally Hadamard-rotated (2/4/8-bit; no outliers, key
-// normalization or mixed widths), with the arithmetic of prefill_kernel.  Its
+// groups of 32, optionally Hadamard-rotated (2/4/8-bit; 4-bit keys may mix
+// in 8-bit groups; no outliers or key normalization), with the arithmetic of
+// prefill_kernel and quant_mixed_groups.  Its
 // three wavefronts hold whole groups in registers: wavefront 0 the keys (lane
 // l: group l % 2 of token l / 2), wavefronts 1 and 2 the values of tokens
 // 16 (w - 1) .. + 15 (lane l: channels 32 (l % 4) .. + 31 of one token, so that
@@ -1381,8 +1382,26 @@ __device__ __forceinline__ int64_t units_of(double sum) {
 
 // Keys of one lane: group g = l % 2 (channels 64 g ..) of token j = l / 2,
 // element i = half i % 2 of x[i / 2].
+// Eight 4-bit codes, the low nibbles of the bytes of a (elements 0..3) and b
+// (4..7), in the pair-split order of the key extension words.
+__device__ __forceinline__ uint32_t nibbles_pair_split(uint32_t a, uint32_t b) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w |= ((a >> (8 * e)) & 15u) << pair_split_pos(4, e);
+    w |= ((b >> (8 * e)) & 15u) << pair_split_pos(4, 4 + e);
+  }
+  return w;
+}
+
+// Keys of one lane: group g = l % 2 (channels 64 g ..) of token j = l / 2,
+// element i = half i % 2 of x[i / 2].  With mixed 4/8-bit groups (k_hi > 0)
+// the token's k_hi groups whose 4-bit step ranks highest (ties: the lower
+// group) take 8-bit codes: the high nibbles stay in the 4-bit code tile, the
+// low nibbles go to the group's k_ext slot and the token's group mask to
+// k_sel.
 __device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const LayerDesc& L, int l, uint8_t* ck,
-                                               uint32_t* kmeta) {
+                                               uint32_t* kmeta, uint32_t* kext, uint8_t* ksel) {
   const int j = l >> 1, g = l & 1;
   uint32_t lo2 = x[0], hi2 = x[0];
 #pragma unroll
@@ -1430,24 +1449,38 @@ __device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const La
   uint16_t s, z;
   float lo, Q, rc, base;
   int off;
-  if (sym) {
-    const uint16_t sv = sym_scale(fmaxf(fabsf(mn), fabsf(mx)), bits);
-    s = sv | 0x8000;
-    z = 0;
-    Q = static_cast<float>((1 << (bits - 1)) - 1);
-    lo = -Q;
-    off = sv == 0 ? 0 : 1 << (bits - 1);
-    rc = sv == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(sv));
-    base = 0.f;
-  } else {
-    const int Qi = (1 << bits) - 1;
-    asym_params(mn, mx, true, Qi, s, z);
-    Q = static_cast<float>(Qi);
-    lo = 0.f;
-    off = 0;
-    rc = s == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(s));
-    base = mn;
+  auto params = [&](int nbits) __attribute__((always_inline)) {
+    if (sym) {
+      const uint16_t sv = sym_scale(fmaxf(fabsf(mn), fabsf(mx)), nbits);
+      s = sv | 0x8000;
+      z = 0;
+      Q = static_cast<float>((1 << (nbits - 1)) - 1);
+      lo = -Q;
+      off = sv == 0 ? 0 : 1 << (nbits - 1);
+      rc = sv == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(sv));
+      base = 0.f;
+    } else {
+      const int Qi = (1 << nbits) - 1;
+      asym_params(mn, mx, true, Qi, s, z);
+      Q = static_cast<float>(Qi);
+      lo = 0.f;
+      off = 0;
+      rc = s == 0 ? 0.f : __builtin_amdgcn_rcpf(h2f(s));
+      base = mn;
+    }
+  };
+  bool wide = false;  // an 8-bit group of a mixed layer
+  if (L.k_hi) {
+    params(4);
+    // rank of the 4-bit steps within the token (the other group is lane l ^ 1)
+    const uint32_t sa = s & 0x7fffu;
+    const uint32_t sb = static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(sa), 0xB1, 0xf, 0xf, false));
+    const bool first = sa > sb || (sa == sb && g == 0);
+    wide = L.k_hi >= 2 || first;
+    const bool other = L.k_hi >= 2 || !first;
+    if (g == 0) ksel[j] = static_cast<uint8_t>((wide ? 1u : 0u) | (other ? 2u : 0u));
   }
+  params(wide ? 8 : bits);
   const uint16_t sdiv = static_cast<uint16_t>(s & 0x7fff);
   uint32_t* dst = reinterpret_cast<uint32_t*>(ck + j * D + 64 * g);
   const QuotGroup qg = quot_group(base, rc, lo, Q);
@@ -1470,6 +1503,18 @@ __device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const La
       const uint32_t w = opaque_u32(x[i >> 1]);
       const float xe = h2f(static_cast<uint16_t>(w >> (16 * (i & 1))));
       if (quot_near(xe, qg)) db[i] = static_cast<uint8_t>(quot_exact(__fsub_rn(xe, base), sdiv, lo, Q) + off);
+    }
+  }
+  if (wide) {
+    // 8-bit codes: high nibbles back to the tile, low nibbles to k_ext slot
+    // k (the group's place among the token's 8-bit groups)
+    uint32_t* ext = kext + (j * L.k_hi + (L.k_hi >= 2 ? g : 0)) * 8;
+#pragma unroll
+    for (int q = 0; q < 16; q += 2) {
+      const uint32_t a = dst[q], b = dst[q + 1];
+      ext[q >> 1] = nibbles_pair_split(a, b);
+      dst[q] = (a >> 4) & 0x0f0f0f0fu;
+      dst[q + 1] = (b >> 4) & 0x0f0f0f0fu;
     }
   }
   kmeta[j * 2 + g] = s | (static_cast<uint32_t>(z) << 16);
@@ -1595,12 +1640,14 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
     for (; w < total; w += 2 * step) {
       if (w + step < total) load(w + step, xb);
       uint8_t* rec = record(w);
-      inner_key_lane(xa, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km));
+      inner_key_lane(xa, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km), reinterpret_cast<uint32_t*>(rec + L.off_kx),
+                     rec + L.off_ks);
       pack(rec);
       if (w + step >= total) break;
       if (w + 2 * step < total) load(w + 2 * step, xa);
       rec = record(w + step);
-      inner_key_lane(xb, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km));
+      inner_key_lane(xb, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km), reinterpret_cast<uint32_t*>(rec + L.off_kx),
+                     rec + L.off_ks);
       pack(rec);
     }
   } else {
@@ -2223,7 +2270,8 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
                     job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid && !L.nuq &&
                     !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 && L.vb != 3;
   const bool inner = job.tok0 == 0 && !job.v_interleaved && job.cnt == kBlockTokens &&
-                     job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && L.k_inner && L.k_group == 64 &&
+                     job.last_cnt == kBlockTokens && aligned && (L.k_hi == 0 || (L.kb == 4 && L.k_hi <= 2)) &&
+                     L.k_inner && L.k_group == 64 &&
                      !L.nuq && !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 &&
                      L.vb != 3 && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31);
   const bool codebook = job.tok0 == 0 && !job.v_interleaved && !job.rotate_v && job.cnt == kBlockTokens &&
