@@ -1120,9 +1120,9 @@ __global__ void __launch_bounds__(128) prefill_kernel(LayerDesc L, QuantJob J) {
 // block by tensor, each lane holding whole groups: wavefront 0 the keys (lane
 // l: channels 2l and 2l + 1 of the 32 tokens), wavefront 1 the values (lane l:
 // channels 64 (l % 2) .. + 63 of token l / 2, two groups).  Each loads its
-// tensor straight into registers in that layout, one block ahead: the grid is
-// persistent and a wavefront's next 8 KiB of reads are in flight while it
-// codes the current block.  The codes meet in LDS (key rows, value lane
+// tensor straight into registers in that layout, one block ahead: each
+// workgroup walks a grid stride of blocks and a wavefront's next 8 KiB of
+// reads are in flight while it codes the current block.  The codes meet in LDS (key rows, value lane
 // chunks) and both wavefronts pack the record.
 
 // Packed binary16 minimum / maximum of two element pairs, written as asm so
@@ -1339,15 +1339,15 @@ prefill_kivi_kernel(LayerDesc L, QuantJob J) {
 // in inner groups of 64 channels (each group symmetric or asymmetric by the
 // hybrid test, or always asymmetric) and per-token asymmetric values in
 // groups of 32, optionally Hadamard-rotated (2/4/8-bit; 4-bit keys may mix
-// in 8-bit groups; no outliers or key normalization), with the arithmetic of
-// prefill_kernel and quant_mixed_groups.  Its
+// in 8-bit groups, keys may be normalized per channel; no outliers), with the
+// arithmetic of prefill_kernel and quant_mixed_groups.  Its
 // three wavefronts hold whole groups in registers: wavefront 0 the keys (lane
 // l: group l % 2 of token l / 2), wavefronts 1 and 2 the values of tokens
 // 16 (w - 1) .. + 15 (lane l: channels 32 (l % 4) .. + 31 of one token, so that
 // after the rotation a lane holds one value group).  The rotation is the
 // exact binary64 butterfly network of hadamard_rows_fast: five stages inside a
 // lane, two across the lane quad through DPP moves.  Loads run one block
-// ahead on a persistent grid, as in prefill_kivi_kernel.
+// ahead along a grid stride of blocks, as in prefill_kivi_kernel.
 
 // 64-bit lane exchange inside a quad (DPP quad_perm: xor 1 or xor 2).
 template <int M>
@@ -1400,9 +1400,21 @@ __device__ __forceinline__ uint32_t nibbles_pair_split(uint32_t a, uint32_t b) {
 // group) take 8-bit codes: the high nibbles stay in the 4-bit code tile, the
 // low nibbles go to the group's k_ext slot and the token's group mask to
 // k_sel.
-__device__ __forceinline__ void inner_key_lane(const uint32_t (&x)[32], const LayerDesc& L, int l, uint8_t* ck,
-                                               uint32_t* kmeta, uint32_t* kext, uint8_t* ksel) {
+__device__ __forceinline__ void inner_key_lane(uint32_t (&x)[32], const uint32_t (&sw)[16], const LayerDesc& L, int l,
+                                               uint8_t* ck, uint32_t* kmeta, uint32_t* kext, uint8_t* ksel) {
   const int j = l >> 1, g = l & 1;
+  if (L.kshift) {
+    // normalized keys fp16(K * 2^shift), saturating (InnerQ, method 4), in
+    // place; sw holds the group's 64 channel shifts (int8)
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      const int s0 = static_cast<int8_t>((sw[k >> 1] >> (16 * (k & 1))) & 0xffu);
+      const int s1 = static_cast<int8_t>((sw[k >> 1] >> (16 * (k & 1) + 8)) & 0xffu);
+      const float a = fminf(fmaxf(ldexpf(h2f(static_cast<uint16_t>(x[k])), s0), -65504.f), 65504.f);
+      const float b = fminf(fmaxf(ldexpf(h2f(static_cast<uint16_t>(x[k] >> 16)), s1), -65504.f), 65504.f);
+      x[k] = static_cast<uint32_t>(f2h(a)) | (static_cast<uint32_t>(f2h(b)) << 16);
+    }
+  }
   uint32_t lo2 = x[0], hi2 = x[0];
 #pragma unroll
   for (int q = 1; q < 32; ++q) {
@@ -1607,7 +1619,9 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
   constexpr int NW = ROLE == 0 ? 32 : 16;
   const uint32_t total = static_cast<uint32_t>(J.nblocks) * static_cast<uint32_t>(L.units);  // below 2^31 (checked at launch)
   const uint32_t nbk = static_cast<uint32_t>(J.nblocks);
-  auto load = [&](uint32_t w, uint32_t (&x)[NW]) __attribute__((always_inline)) {
+  // a block's words of this lane (and, for normalized keys, the group's 64
+  // channel shifts of the block's unit)
+  auto load = [&](uint32_t w, uint32_t (&x)[NW], uint32_t (&sh)[16]) __attribute__((always_inline)) {
     const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
     const int64_t row0 = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + kBlockTokens * bi) * D;
     const uint4* src = ROLE == 0 ? reinterpret_cast<const uint4*>(J.k_src + row0 + (l >> 1) * D + 64 * (l & 1))
@@ -1619,6 +1633,17 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
       x[4 * k + 1] = v.y;
       x[4 * k + 2] = v.z;
       x[4 * k + 3] = v.w;
+    }
+    if (ROLE == 0 && L.kshift) {
+      const uint4* sp = reinterpret_cast<const uint4*>(L.kshift + static_cast<int64_t>(u) * D + 64 * (l & 1));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 v = sp[k];
+        sh[4 * k] = v.x;
+        sh[4 * k + 1] = v.y;
+        sh[4 * k + 2] = v.z;
+        sh[4 * k + 3] = v.w;
+      }
     }
   };
   auto pack = [&](uint8_t* rec) __attribute__((always_inline)) {
@@ -1635,31 +1660,31 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
   uint32_t w = blockIdx.x;
   if constexpr (ROLE == 0) {
     // keys: two buffers (the group's words are read until its codes are out)
-    uint32_t xa[NW], xb[NW];
-    if (w < total) load(w, xa);
+    uint32_t xa[NW], xb[NW], sa[16], sb[16];
+    if (w < total) load(w, xa, sa);
     for (; w < total; w += 2 * step) {
-      if (w + step < total) load(w + step, xb);
+      if (w + step < total) load(w + step, xb, sb);
       uint8_t* rec = record(w);
-      inner_key_lane(xa, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km), reinterpret_cast<uint32_t*>(rec + L.off_kx),
-                     rec + L.off_ks);
+      inner_key_lane(xa, sa, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km),
+                     reinterpret_cast<uint32_t*>(rec + L.off_kx), rec + L.off_ks);
       pack(rec);
       if (w + step >= total) break;
-      if (w + 2 * step < total) load(w + 2 * step, xa);
+      if (w + 2 * step < total) load(w + 2 * step, xa, sa);
       rec = record(w + step);
-      inner_key_lane(xb, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km), reinterpret_cast<uint32_t*>(rec + L.off_kx),
-                     rec + L.off_ks);
+      inner_key_lane(xb, sb, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km),
+                     reinterpret_cast<uint32_t*>(rec + L.off_kx), rec + L.off_ks);
       pack(rec);
     }
   } else {
     // values: one buffer, refilled as soon as the lane has converted it
-    uint32_t x[NW];
-    if (w < total) load(w, x);
+    uint32_t x[NW], unused[16];
+    if (w < total) load(w, x, unused);
     for (; w < total; w += step) {
       const uint32_t wn = w + step;
       uint8_t* rec = record(w);
       inner_value_lane(x, L, J.rotate_v != 0, l, vj, cvc, reinterpret_cast<uint16_t*>(rec + L.off_vm),
                        [&](uint32_t (&buf)[NW]) __attribute__((always_inline)) {
-                         if (wn < total) load(wn, buf);
+                         if (wn < total) load(wn, buf, unused);
                        });
       pack(rec);
     }
@@ -2209,15 +2234,25 @@ __global__ void __launch_bounds__(256) knorm_shift_kernel(const uint16_t* k, int
   const int u = blockIdx.x;
   const uint4* src = reinterpret_cast<const uint4*>(k + static_cast<int64_t>(u) * T * D) + cl;
   uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int t = rg; t < T; t += 16) {
-    const uint4 v = src[static_cast<int64_t>(t) * (D / 8)];
+  auto take = [&](const uint4 v) __attribute__((always_inline)) {
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       m[2 * i] = max(m[2 * i], w[i] & 0x7fffu);
       m[2 * i + 1] = max(m[2 * i + 1], (w[i] >> 16) & 0x7fffu);
     }
+  };
+  // eight rows per group in flight at a time
+  constexpr int kRows = 8;
+  int t = rg;
+  for (; t + 16 * (kRows - 1) < T; t += 16 * kRows) {
+    uint4 v[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) v[r] = src[static_cast<int64_t>(t + 16 * r) * (D / 8)];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) take(v[r]);
   }
+  for (; t < T; t += 16) take(src[static_cast<int64_t>(t) * (D / 8)]);
 #pragma unroll
   for (int i = 0; i < 8; ++i) part[rg][8 * cl + i] = static_cast<uint16_t>(m[i]);
   if (tid == 0) e_max = -1000;
@@ -2259,6 +2294,22 @@ hipError_t launch_knorm_shifts(const LayerDesc& L, const uint16_t* k, int32_t T,
   return hipGetLastError();
 }
 
+// Grid of a block-walking prefill kernel: `rounds` times the workgroups
+// resident at once, capped at one per block.  A grid of exactly one resident
+// round leaves the kernel's length to the most loaded compute unit, and
+// where the hardware places a workgroup depends on what ran before (the
+// same launch measured up to 1.4x slower after one other short kernel);
+// more, shorter workgroups let the dispatcher even the load out, at the cost
+// of one unhidden block load per workgroup.
+template <class Kernel>
+hipError_t walk_grid(Kernel kern, int block, std::atomic<int>* cache, int rounds, int64_t blocks, int* grid) {
+  int resident = 0;
+  const hipError_t e = resident_blocks(kern, block, 0, cache, &resident);
+  if (e != hipSuccess) return e;
+  *grid = static_cast<int>(std::min<int64_t>(blocks, static_cast<int64_t>(resident) * rounds));
+  return hipSuccess;
+}
+
 hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t s) {
   if (job.nblocks <= 0) return hipSuccess;
   // whole fresh blocks take the bandwidth kernel; appends into a partly
@@ -2272,7 +2323,7 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
   const bool inner = job.tok0 == 0 && !job.v_interleaved && job.cnt == kBlockTokens &&
                      job.last_cnt == kBlockTokens && aligned && (L.k_hi == 0 || (L.kb == 4 && L.k_hi <= 2)) &&
                      L.k_inner && L.k_group == 64 &&
-                     !L.nuq && !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 &&
+                     !L.nuq && !L.v_tern && L.outk == 0 && L.v_group == 32 && L.kb != 3 &&
                      L.vb != 3 && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31);
   const bool codebook = job.tok0 == 0 && !job.v_interleaved && !job.rotate_v && job.cnt == kBlockTokens &&
                         job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid &&
@@ -2281,27 +2332,27 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
   if (codebook) {
     static std::atomic<int> resident[kMaxDevices];
     int grid = 0;
-    const hipError_t e = resident_blocks(prefill_codebook_kernel, 256, 0, resident, &grid);
+    const hipError_t e =
+        walk_grid(prefill_codebook_kernel, 256, resident, 8, static_cast<int64_t>(job.nblocks) * L.units, &grid);
     if (e != hipSuccess) return e;
-    grid = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(job.nblocks) * L.units, grid));
     hipLaunchKernelGGL(prefill_codebook_kernel, dim3(grid), dim3(256), 0, s, L, job);
     return hipGetLastError();
   }
   if (inner) {
     static std::atomic<int> resident[kMaxDevices];
     int grid = 0;
-    const hipError_t e = resident_blocks(prefill_inner_kernel, 192, 0, resident, &grid);
+    const hipError_t e =
+        walk_grid(prefill_inner_kernel, 192, resident, 32, static_cast<int64_t>(job.nblocks) * L.units, &grid);
     if (e != hipSuccess) return e;
-    grid = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(job.nblocks) * L.units, grid));
     hipLaunchKernelGGL(prefill_inner_kernel, dim3(grid), dim3(192), 0, s, L, job);
     return hipGetLastError();
   }
   if (kivi && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31)) {
     static std::atomic<int> resident[kMaxDevices];
     int grid = 0;
-    const hipError_t e = resident_blocks(prefill_kivi_kernel, 128, 0, resident, &grid);
+    const hipError_t e =
+        walk_grid(prefill_kivi_kernel, 128, resident, 32, static_cast<int64_t>(job.nblocks) * L.units, &grid);
     if (e != hipSuccess) return e;
-    grid = static_cast<int>(std::min<int64_t>(static_cast<int64_t>(job.nblocks) * L.units, grid));
     hipLaunchKernelGGL(prefill_kivi_kernel, dim3(grid), dim3(128), 0, s, L, job);
     return hipGetLastError();
   }
