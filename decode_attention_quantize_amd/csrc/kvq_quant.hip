@@ -1347,7 +1347,10 @@ prefill_kivi_kernel(LayerDesc L, QuantJob J) {
 // after the rotation a lane holds one value group).  The rotation is the
 // exact binary64 butterfly network of hadamard_rows_fast: five stages inside a
 // lane, two across the lane quad through DPP moves.  Loads run one block
-// ahead along a grid stride of blocks, as in prefill_kivi_kernel.
+// ahead along a grid stride of blocks, as in prefill_kivi_kernel.  The
+// CHAN instance takes per-channel asymmetric keys with rotated values
+// instead: its key wavefront is prefill_kivi_kernel's (lane l: channels 2l,
+// 2l + 1 of the 32 tokens).
 
 // 64-bit lane exchange inside a quad (DPP quad_perm: xor 1 or xor 2).
 template <int M>
@@ -1613,7 +1616,7 @@ __device__ __forceinline__ void inner_value_lane(uint32_t (&x)[16], const LayerD
 // own double buffer, so the two roles' registers do not add up.  Every
 // wavefront of the workgroup walks the same blocks and meets the same two
 // barriers per block.
-template <int ROLE>
+template <bool CHAN, int ROLE>
 __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J, int l, int vj, uint8_t* ck,
                                            uint8_t* cvc) {
   constexpr int NW = ROLE == 0 ? 32 : 16;
@@ -1624,17 +1627,24 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
   auto load = [&](uint32_t w, uint32_t (&x)[NW], uint32_t (&sh)[16]) __attribute__((always_inline)) {
     const int u = static_cast<int>(w / nbk), bi = static_cast<int>(w % nbk);
     const int64_t row0 = u * J.src_unit_stride + static_cast<int64_t>(J.src_t0 + kBlockTokens * bi) * D;
-    const uint4* src = ROLE == 0 ? reinterpret_cast<const uint4*>(J.k_src + row0 + (l >> 1) * D + 64 * (l & 1))
-                                 : reinterpret_cast<const uint4*>(J.v_src + row0 + vj * D + 32 * (l & 3));
+    if constexpr (ROLE == 0 && CHAN) {
+      // per-channel keys: channels 2l, 2l + 1 of each token
+      const uint16_t* src = J.k_src + row0 + 2 * l;
 #pragma unroll
-    for (int k = 0; k < NW / 4; ++k) {
-      const uint4 v = src[k];
-      x[4 * k] = v.x;
-      x[4 * k + 1] = v.y;
-      x[4 * k + 2] = v.z;
-      x[4 * k + 3] = v.w;
+      for (int j = 0; j < kBlockTokens; ++j) x[j] = *reinterpret_cast<const uint32_t*>(src + j * D);
+    } else {
+      const uint4* src = ROLE == 0 ? reinterpret_cast<const uint4*>(J.k_src + row0 + (l >> 1) * D + 64 * (l & 1))
+                                   : reinterpret_cast<const uint4*>(J.v_src + row0 + vj * D + 32 * (l & 3));
+#pragma unroll
+      for (int k = 0; k < NW / 4; ++k) {
+        const uint4 v = src[k];
+        x[4 * k] = v.x;
+        x[4 * k + 1] = v.y;
+        x[4 * k + 2] = v.z;
+        x[4 * k + 3] = v.w;
+      }
     }
-    if (ROLE == 0 && L.kshift) {
+    if (ROLE == 0 && !CHAN && L.kshift) {
       const uint4* sp = reinterpret_cast<const uint4*>(L.kshift + static_cast<int64_t>(u) * D + 64 * (l & 1));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -1659,20 +1669,25 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
   const uint32_t step = gridDim.x;
   uint32_t w = blockIdx.x;
   if constexpr (ROLE == 0) {
+    auto keys = [&](uint32_t (&x)[NW], const uint32_t (&sh)[16], uint8_t* rec) __attribute__((always_inline)) {
+      if constexpr (CHAN)
+        kivi_key_lane(x, L.kb, l, ck, reinterpret_cast<uint16_t*>(rec + L.off_km));
+      else
+        inner_key_lane(x, sh, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km),
+                       reinterpret_cast<uint32_t*>(rec + L.off_kx), rec + L.off_ks);
+    };
     // keys: two buffers (the group's words are read until its codes are out)
     uint32_t xa[NW], xb[NW], sa[16], sb[16];
     if (w < total) load(w, xa, sa);
     for (; w < total; w += 2 * step) {
       if (w + step < total) load(w + step, xb, sb);
       uint8_t* rec = record(w);
-      inner_key_lane(xa, sa, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km),
-                     reinterpret_cast<uint32_t*>(rec + L.off_kx), rec + L.off_ks);
+      keys(xa, sa, rec);
       pack(rec);
       if (w + step >= total) break;
       if (w + 2 * step < total) load(w + 2 * step, xa, sa);
       rec = record(w + step);
-      inner_key_lane(xb, sb, L, l, ck, reinterpret_cast<uint32_t*>(rec + L.off_km),
-                     reinterpret_cast<uint32_t*>(rec + L.off_kx), rec + L.off_ks);
+      keys(xb, sb, rec);
       pack(rec);
     }
   } else {
@@ -1691,6 +1706,7 @@ __device__ __forceinline__ void inner_walk(const LayerDesc& L, const QuantJob& J
   }
 }
 
+template <bool CHAN>
 __global__ void __launch_bounds__(192) __attribute__((amdgpu_waves_per_eu(3)))
 prefill_inner_kernel(LayerDesc L, QuantJob J) {
   __shared__ __align__(16) uint8_t ck[kBlockTokens * D];
@@ -1698,9 +1714,9 @@ prefill_inner_kernel(LayerDesc L, QuantJob J) {
   const int l = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // 0 keys, 1 and 2 values
   if (wv == 0)
-    inner_walk<0>(L, J, l, 0, ck, cvc);
+    inner_walk<CHAN, 0>(L, J, l, 0, ck, cvc);
   else
-    inner_walk<1>(L, J, l, 16 * (wv - 1) + (l >> 2), ck, cvc);
+    inner_walk<CHAN, 1>(L, J, l, 16 * (wv - 1) + (l >> 2), ck, cvc);
 }
 
 // ===================================================================== codebook prefill
@@ -2312,14 +2328,18 @@ hipError_t walk_grid(Kernel kern, int block, std::atomic<int>* cache, int rounds
 
 hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t s) {
   if (job.nblocks <= 0) return hipSuccess;
-  // whole fresh blocks take the bandwidth kernel; appends into a partly
-  // filled block and mixed 4/8-bit key groups take quantize_kernel
+  // whole fresh blocks of the common schemes take the register kernels
   // (16-byte loads: the sources must be 16-byte aligned; row strides are
-  // whole 256-byte rows)
+  // whole 256-byte rows); the other schemes take prefill_kernel, appends
+  // into a partly filled block quantize_kernel
   const bool aligned = ((reinterpret_cast<uintptr_t>(job.k_src) | reinterpret_cast<uintptr_t>(job.v_src)) & 15) == 0;
-  const bool kivi = job.tok0 == 0 && !job.v_interleaved && !job.rotate_v && job.cnt == kBlockTokens &&
-                    job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid && !L.nuq &&
-                    !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 && L.vb != 3;
+  const bool kivi_layout = job.tok0 == 0 && !job.v_interleaved && job.cnt == kBlockTokens &&
+                           job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid &&
+                           !L.nuq && !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 &&
+                           L.vb != 3;
+  const bool kivi = kivi_layout && !job.rotate_v;
+  const bool kivi_rotated = kivi_layout && job.rotate_v &&
+                            static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31);
   const bool inner = job.tok0 == 0 && !job.v_interleaved && job.cnt == kBlockTokens &&
                      job.last_cnt == kBlockTokens && aligned && (L.k_hi == 0 || (L.kb == 4 && L.k_hi <= 2)) &&
                      L.k_inner && L.k_group == 64 &&
@@ -2342,9 +2362,18 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
     static std::atomic<int> resident[kMaxDevices];
     int grid = 0;
     const hipError_t e =
-        walk_grid(prefill_inner_kernel, 192, resident, 32, static_cast<int64_t>(job.nblocks) * L.units, &grid);
+        walk_grid(prefill_inner_kernel<false>, 192, resident, 32, static_cast<int64_t>(job.nblocks) * L.units, &grid);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prefill_inner_kernel, dim3(grid), dim3(192), 0, s, L, job);
+    hipLaunchKernelGGL(prefill_inner_kernel<false>, dim3(grid), dim3(192), 0, s, L, job);
+    return hipGetLastError();
+  }
+  if (kivi_rotated) {
+    static std::atomic<int> resident[kMaxDevices];
+    int grid = 0;
+    const hipError_t e =
+        walk_grid(prefill_inner_kernel<true>, 192, resident, 32, static_cast<int64_t>(job.nblocks) * L.units, &grid);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prefill_inner_kernel<true>, dim3(grid), dim3(192), 0, s, L, job);
     return hipGetLastError();
   }
   if (kivi && static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31)) {

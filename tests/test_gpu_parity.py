@@ -206,15 +206,16 @@ def _ties_tensor(T, D, bits, step, token_groups, nudge, glen=32):
     return x
 
 
-@pytest.mark.parametrize("keys", ["channel", "inner"])
+@pytest.mark.parametrize("keys", ["channel", "channel-rotated", "inner"])
 @pytest.mark.parametrize("pair", [(2, 2), (4, 4), (8, 2), (2, 8)])
 @pytest.mark.parametrize("nudge", [False, True])
 def test_prefill_codes_on_rounding_ties(keys, pair, nudge):
     """Quotients exactly on (or one ulp past) a half-integer, where a
     reciprocal estimate cannot decide the rounding: the library's codes and
     parameters equal the oracle's correctly rounded ones bit for bit (keys
-    per channel, or in inner groups of 64 with the symmetric/asymmetric
-    choice)."""
+    per channel, also beside Hadamard-rotated values -- the rotation moves
+    the values off their ties, the keys keep them -- or in inner groups of
+    64 with the symmetric/asymmetric choice)."""
     import oracle as O
     from decode_attention_quantize_amd import KVQCache, config_from_workload
     from gpu_harness import HostLayer, unit_body
@@ -222,11 +223,13 @@ def test_prefill_codes_on_rounding_ties(keys, pair, nudge):
     kb, vb = pair
     if keys == "channel":
         wl = W.C1.with_(name="ties", window=0, fixed_pairs=(pair,), T=256)
+    elif keys == "channel-rotated":
+        wl = W.C1.with_(name="ties-rotated", window=0, fixed_pairs=(pair,), T=256, v_hadamard=True)
     else:
         wl = W.C5.with_(name="ties-inner", B=1, Hq=1, Hkv=1, T=256, steps=1, v_hadamard=False,
                         fixed_pairs=(pair,))
     T, D = wl.T, wl.D
-    K = _ties_tensor(T, D, kb, 2.0 ** -6 if kb == 8 else 0.125, keys == "channel", nudge,
+    K = _ties_tensor(T, D, kb, 2.0 ** -6 if kb == 8 else 0.125, keys != "inner", nudge,
                      glen=wl.k_group if keys == "inner" else 32)
     V = _ties_tensor(T, D, vb, 2.0 ** -6 if vb == 8 else 0.125, False, nudge)
     say(f"[ties] {keys} keys, pair {pair} nudge {nudge}")
