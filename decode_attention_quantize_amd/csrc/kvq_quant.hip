@@ -1114,9 +1114,9 @@ __global__ void __launch_bounds__(128) prefill_kernel(LayerDesc L, QuantJob J) {
 
 // ===================================================================== KIVI-layout prefill
 // prefill_kivi_kernel quantizes the whole prompt blocks of layers with
-// per-channel asymmetric keys and per-token asymmetric values in groups of 32
-// channels (2/4/8-bit codes; no outliers, rotation or key normalization), with
-// the arithmetic of prefill_kernel.  The two wavefronts of a workgroup split a
+// per-channel asymmetric keys and per-token asymmetric (or 2-bit ternary)
+// values in groups of 32 channels (2/4/8-bit codes; no outliers, rotation or
+// key normalization), with the arithmetic of prefill_kernel.  The two wavefronts of a workgroup split a
 // block by tensor, each lane holding whole groups: wavefront 0 the keys (lane
 // l: channels 2l and 2l + 1 of the 32 tokens), wavefront 1 the values (lane l:
 // channels 64 (l % 2) .. + 63 of token l / 2, two groups).  Each loads its
@@ -1241,14 +1241,35 @@ __device__ __forceinline__ void kivi_key_lane(const uint32_t (&x)[kBlockTokens],
 
 // Values of one lane: token j = l / 2, groups g = 2 (l % 2) + gi of 32
 // channels (element i of group gi is half i % 2 of x[16 gi + i / 2]).
-__device__ __forceinline__ void kivi_value_lane(const uint32_t (&x)[kBlockTokens], int bits, int l, uint8_t* cvc,
-                                                uint16_t* vm) {
+// Ternary groups (2-bit codes): s = max |x|, z = -s, and the code of
+// clamp(rne(x / s), -1, 1) + 1, which is 1 unless 2 |x| > s exactly (x / s
+// of two binary16 values other than +-1/2 lies at least 2^-12 relative from
+// +-1/2, beyond any rounding of the quotient; +-1/2 itself rounds to 0).
+__device__ __forceinline__ void kivi_value_lane(const uint32_t (&x)[kBlockTokens], int bits, bool tern, int l,
+                                                uint8_t* cvc, uint16_t* vm) {
   const int j = l >> 1;
   const int Qi = (1 << bits) - 1;
   const float Q = static_cast<float>(Qi);
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi) {
     const int g = 2 * (l & 1) + gi;
+    if (tern) {
+      uint32_t a2 = x[16 * gi] & 0x7fff7fffu;
+#pragma unroll
+      for (int q = 1; q < 16; ++q) a2 = pk_max_h(a2, x[16 * gi + q] & 0x7fff7fffu);
+      a2 = pk_max_h(a2, a2 >> 16);
+      const uint16_t s = static_cast<uint16_t>(a2);
+      const float half = 0.5f * h2f(s);  // exact
+      uint8_t* dst = cvc + vchunk_off(j, 32 * g);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float xe = h2f(static_cast<uint16_t>(x[16 * gi + (i >> 1)] >> (16 * (i & 1))));
+        dst[vchunk_off(0, i)] = static_cast<uint8_t>(fabsf(xe) > half ? (xe < 0.f ? 0 : 2) : 1);
+      }
+      vm[g * kBlockTokens + j] = s;
+      vm[4 * kBlockTokens + g * kBlockTokens + j] = static_cast<uint16_t>(s ^ 0x8000u);
+      continue;
+    }
     uint32_t lo2 = x[16 * gi], hi2 = x[16 * gi];
 #pragma unroll
     for (int q = 1; q < 16; ++q) {
@@ -1315,7 +1336,7 @@ prefill_kivi_kernel(LayerDesc L, QuantJob J) {
     if (keys)
       kivi_key_lane(x, L.kb, l, ck, reinterpret_cast<uint16_t*>(rec + L.off_km));
     else
-      kivi_value_lane(x, L.vb, l, cvc, reinterpret_cast<uint16_t*>(rec + L.off_vm));
+      kivi_value_lane(x, L.vb, L.v_tern != 0, l, cvc, reinterpret_cast<uint16_t*>(rec + L.off_vm));
     __syncthreads();
     pack_rows_fast(ck, kBlockTokens, L.kb, rec + L.off_kc, L.k_row_bytes);
     pack_vchunks_fast(cvc, L.vb, rec + L.off_vc);
@@ -2335,10 +2356,9 @@ hipError_t launch_quantize(const LayerDesc& L, const QuantJob& job, hipStream_t 
   const bool aligned = ((reinterpret_cast<uintptr_t>(job.k_src) | reinterpret_cast<uintptr_t>(job.v_src)) & 15) == 0;
   const bool kivi_layout = job.tok0 == 0 && !job.v_interleaved && job.cnt == kBlockTokens &&
                            job.last_cnt == kBlockTokens && aligned && L.k_hi == 0 && !L.k_inner && !L.k_hybrid &&
-                           !L.nuq && !L.v_tern && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 &&
-                           L.vb != 3;
-  const bool kivi = kivi_layout && !job.rotate_v;
-  const bool kivi_rotated = kivi_layout && job.rotate_v &&
+                           !L.nuq && L.outk == 0 && L.kshift == nullptr && L.v_group == 32 && L.kb != 3 && L.vb != 3;
+  const bool kivi = kivi_layout && !job.rotate_v && (!L.v_tern || L.vb == 2);
+  const bool kivi_rotated = kivi_layout && job.rotate_v && !L.v_tern &&
                             static_cast<int64_t>(job.nblocks) * L.units < (int64_t(1) << 31);
   const bool inner = job.tok0 == 0 && !job.v_interleaved && job.cnt == kBlockTokens &&
                      job.last_cnt == kBlockTokens && aligned && (L.k_hi == 0 || (L.kb == 4 && L.k_hi <= 2)) &&

@@ -250,6 +250,56 @@ def test_prefill_codes_on_rounding_ties(keys, pair, nudge):
     cache.close()
 
 
+def _ternary_tie_values(T, D):
+    """fp16 [T][D] whose per-token groups of 32 channels put elements on the
+    ternary threshold |x| = s / 2 (s = the group's max |x|), one ulp either
+    side of it, at +-s and at 0, over scales from 2^-20 (subnormal halves)
+    to 2^4."""
+    rng = np.random.default_rng(11)
+    out = np.zeros((T, D), np.float32)
+    for t in range(T):
+        for g in range(D // 32):
+            sc = np.float16(2.0 ** rng.integers(-20, 5) * (1 + rng.integers(0, 1024) / 1024))
+            half = np.float16(sc / np.float16(2))
+            cand = [sc, half, np.nextafter(half, np.float16(np.inf)), np.nextafter(half, np.float16(0)), np.float16(0)]
+            x = np.array([cand[i] for i in rng.integers(0, len(cand), 32)], np.float16)
+            x[rng.integers(0, 32)] = sc
+            x *= np.where(rng.integers(0, 2, 32) == 1, np.float16(-1), np.float16(1)).astype(np.float16)
+            out[t, 32 * g:32 * g + 32] = x.astype(np.float32)
+    return out.astype(np.float16)
+
+
+def test_prefill_ternary_values_on_their_threshold():
+    """Ternary value groups (levels -s, 0, s) whose elements sit exactly on
+    the rounding threshold |x| = s / 2 (which rounds to 0), one ulp past or
+    short of it: the library's codes and (s, z) equal the oracle's bit for
+    bit."""
+    import oracle as O
+    from decode_attention_quantize_amd import KVQCache, config_from_workload
+    from gpu_harness import HostLayer, unit_body
+    from kvq_unpack import unpack_unit
+    wl = W.C1.with_(name="ternary-threshold", window=0, fixed_pairs=((4, 2),), T=256, v_ternary=True)
+    T, D = wl.T, wl.D
+    K = (np.random.default_rng(3).standard_normal((T, D))).astype(np.float16)
+    V = _ternary_tie_values(T, D)
+    say("[ternary threshold] C1 layout, K4 V2 ternary")
+    cache = KVQCache(config_from_workload(wl), wl.bit_pairs(), device="cuda")
+    k = torch.from_numpy(K).view(1, 1, T, D).cuda()
+    v = torch.from_numpy(V).view(1, 1, T, D).cuda()
+    cache.prefill(0, k, v)
+    torch.cuda.synchronize()
+    s_eff, nb, _ = O.state_prefill(T, wl.sinks, wl.window, wl.flush)
+    enc = O.encode_unit(O.scheme_for(wl, 0), K.view(np.uint16), V.view(np.uint16), T, s_eff, nb)
+    body, lay = unit_body(cache, 0, 0, HostLayer(cache, 0))
+    got = unpack_unit(body, lay, 4, 2, nb, False, wl.k_group, wl.v_group, wl.outliers, 0)
+    for key in ("kcodes", "kmeta", "vcodes", "vmeta"):
+        bad = np.argwhere(got[key] != enc[key])
+        assert bad.size == 0, (key, bad[:5].tolist())
+    # all three levels occur
+    assert all(np.any(enc["vcodes"] == c) for c in (0, 1, 2))
+    cache.close()
+
+
 def _hybrid_boundary_keys(T, D):
     """fp16 [T][D] whose inner key groups of 64 channels sit on the hybrid
     test's boundary for the ratio 1/10: minimum -1, maximum 4, 29 ones and
