@@ -517,6 +517,16 @@ def test_full_c5_mixed_groups_every_unit():
     _full(W.C5.with_(k_hi_groups=1), {3})
 
 
+@pytest.mark.timeout(900)
+def test_full_c2_hadamard_values_every_unit():
+    _full(W.C2.with_(v_hadamard=True), {0, 63})
+
+
+@pytest.mark.timeout(900)
+def test_full_c2_ternary_values_every_unit():
+    _full(W.C2.with_(v_ternary=True), {0, 63})
+
+
 # ---------------------------------------------------------------- calibration on the library's records
 def test_library_quantizer_mse_equals_the_calibration_mse():
     """RateQuant's distortion calibration measured on the library itself: a
