@@ -21,7 +21,9 @@
 // Only the first G rows of the 16-row tiles carry queries (the GQA group of a
 // kv head); the keys and values of a block are read once for all of them.
 // Block records stream HBM -> LDS with global_load_lds_dwordx4 into a ring of
-// NBUF slots, NBUF-1 blocks ahead of the one being computed.  Sink / window
+// NBUF slots; a slot takes its next block as soon as the current one has read
+// its record out, so NBUF - 1 to NBUF blocks are in flight behind the one
+// being computed.  Sink / window
 // tokens (fp16) are read straight into registers by splits of their own,
 // after the body splits.  Each split writes an
 // (o, max, sum) partial; decode_merge_kernel combines them by log-sum-exp and
@@ -294,17 +296,24 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   struct POps {
     half8 pa, pz;
   };
+  // LDS byte offsets of the weight tiles (element (r, t) at 2 (32 r + t))
+  const uint32_t pt_base = lds_off((lds_u8*)ptile);
+  const uint32_t plo_base = lds_off((lds_u8*)plo);
   // lanes of rows G..2G-1 read the residual tile, the others the weights
-  const _Float16* const pz_row = PLO && n16 >= G && n16 < 2 * G ? &plo[n16 & (G - 1)][8 * g4]
-                                                                 : &ptile[n16 & (G - 1)][8 * g4];
+  const uint32_t pz_addr = (PLO && n16 >= G && n16 < 2 * G ? plo_base : pt_base) + 2 * (32 * (n16 & (G - 1)) + 8 * g4);
   auto p_operands = [&]() __attribute__((always_inline)) -> POps {
     if constexpr (kPackLo) {  // rows G..2G-1 read rows 0..G-1 again
       const bool live = n16 < 2 * G;
-      const half8 pa = live ? *reinterpret_cast<const half8*>(&ptile[n16 & (G - 1)][8 * g4]) : h8(0u, 0u, 0u, 0u);
-      if constexpr (PLO) return POps{pa, live ? *reinterpret_cast<const half8*>(pz_row) : h8(0u, 0u, 0u, 0u)};
+      const half8 pr = h8(dsr16_now(pt_base + 2 * (32 * (n16 & (G - 1)) + 8 * g4)));
+      const half8 pa = live ? pr : h8(0u, 0u, 0u, 0u);
+      if constexpr (PLO) {
+        const half8 zr = h8(dsr16_now(pz_addr));
+        return POps{pa, live ? zr : h8(0u, 0u, 0u, 0u)};
+      }
       return POps{pa, pa};
     }
-    const half8 pa = n16 < G ? *reinterpret_cast<const half8*>(&ptile[n16][8 * g4]) : h8(0u, 0u, 0u, 0u);
+    const half8 pr = h8(dsr16_now(pt_base + 2 * (32 * n16 + 8 * g4)));
+    const half8 pa = n16 < G ? pr : h8(0u, 0u, 0u, 0u);
     return POps{pa, pa};
   };
   auto softmax_tile = [&](f32x4 (&sacc)[2], int count) __attribute__((always_inline)) -> POps {
@@ -346,8 +355,9 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       for (int nt = 0; nt < 2; ++nt) {
         const float p = fexp2(sacc[nt][i] - (m_run[i] - kLift));
         const _Float16 ph = static_cast<_Float16>(p);
-        ptile[4 * g4 + i][16 * nt + n16] = ph;
-        if constexpr (PLO) plo[4 * g4 + i][16 * nt + n16] = static_cast<_Float16>(p - static_cast<float>(ph));
+        const uint32_t e = 2 * (32 * (4 * g4 + i) + 16 * nt + n16);
+        dsw_h(pt_base + e, ph);
+        if constexpr (PLO) dsw_h(plo_base + e, static_cast<_Float16>(p - static_cast<float>(ph)));
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -401,8 +411,9 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       // rows past the query group (fold by 16: rows 8-11) are never read
       const float p = fexp2(s[i] - (m_run[i] - kLift));
       const _Float16 ph = static_cast<_Float16>(p);
-      ptile[frow + i][ftok] = ph;
-      if constexpr (PLO) plo[frow + i][ftok] = static_cast<_Float16>(p - static_cast<float>(ph));
+      const uint32_t e = 2 * (32 * (frow + i) + ftok);
+      dsw_h(pt_base + e, ph);
+      if constexpr (PLO) dsw_h(plo_base + e, static_cast<_Float16>(p - static_cast<float>(ph)));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -410,8 +421,9 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
     return p_operands();
   };
 
-  // one quantized block whose record sits in LDS at rec
-  auto body_block = [&](const lds_u8* rec, int count) __attribute__((always_inline)) {
+  // one quantized block whose record sits in LDS at rec; refill() runs once
+  // the block's last read of its record has completed (the slot is free)
+  auto body_block = [&](const lds_u8* rec, int count, auto refill) __attribute__((always_inline)) {
     const uint32_t r0 = lds_off(rec);
     f32x4 sacc[2];
     f32x4 sf;  // folded block scores (kFold)
@@ -655,6 +667,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 #pragma unroll
       for (int e = 0; e < 5; ++e) pin(vmeta[e]);
     }
+    refill();
     const POps P = kFold ? softmax_fold(sf, count) : softmax_tile(sacc, count);
     const half8 pa = P.pa;
     // one MFMA of P against the block's value parameters: column g < 4 holds
@@ -709,7 +722,7 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
     }
   };
 #pragma unroll
-  for (int k = 0; k < NBUF - 1; ++k)
+  for (int k = 0; k < NBUF; ++k)
     if (k < nmy) issue(k, slot_at(k));
 
   // ---------------- sink / window tokens: fp16 operands as stored, one
@@ -841,9 +854,12 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
 
   // ---------------- quantized body blocks through the LDS ring
   {
-    // block i sits in slot i % NBUF.  Steady state: every step issues block
-    // i + NBUF - 1 and waits until only the (NBUF - 1) newer blocks are in
-    // flight, so the waits are the same on every path.  The tail drains.
+    // block i sits in slot i % NBUF.  Steady state: a step waits until only
+    // the (NBUF - 1) newer blocks are in flight, and as soon as the block has
+    // read its record out of LDS (half-way through its work, before the
+    // softmax and the value products) the slot takes block i + NBUF, so
+    // NBUF - 1 to NBUF blocks stay in flight behind the compute.  The waits
+    // are the same on every path.  The tail drains.
     // Wavefronts sharing a SIMD are picked oldest first, so without help the
     // last one dispatched finishes long after the others.  Each wavefront
     // lowers its priority as it gets through its blocks: one that is ahead
@@ -859,38 +875,34 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       }
     };
     __builtin_amdgcn_s_setprio(3);
-    auto step = [&](int i, lds_u8* cur, lds_u8* ahead) __attribute__((always_inline)) {
+    auto step = [&](int i, lds_u8* cur) __attribute__((always_inline)) {
       age(i);
-      issue(i + NBUF - 1, ahead);
       wait_vm<(NBUF - 1) * R::loads>();
       const int ch = c_begin + i;
-      body_block(cur, min(kBlockTokens, st.nb - ch * kBlockTokens));
+      body_block(cur, min(kBlockTokens, st.nb - ch * kBlockTokens),
+                 [&]() __attribute__((always_inline)) { issue(i + NBUF, cur); });
     };
     int i = 0;
-    for (; i + 2 * NBUF - 2 < nmy; i += NBUF) {
+    // every step of an iteration refills its slot: blocks up to i + 2 NBUF - 1
+    for (; i + 2 * NBUF - 1 < nmy; i += NBUF) {
       if constexpr (NBUF == 4) {
-        step(i, slot0, slot3);
-        step(i + 1, slot1, slot0);
-        step(i + 2, slot2, slot1);
-        step(i + 3, slot3, slot2);
+        step(i, slot0);
+        step(i + 1, slot1);
+        step(i + 2, slot2);
+        step(i + 3, slot3);
       } else if constexpr (NBUF == 3) {
-        step(i, slot0, slot2);
-        step(i + 1, slot1, slot0);
-        step(i + 2, slot2, slot1);
+        step(i, slot0);
+        step(i + 1, slot1);
+        step(i + 2, slot2);
       } else {
-        step(i, slot0, slot1);
-        step(i + 1, slot1, slot0);
+        step(i, slot0);
+        step(i + 1, slot1);
       }
     }
     for (; i < nmy; ++i) {
       age(i);
-      // remaining blocks: issue what is still missing, then drain in order
-      const int ahead = i + NBUF - 1;
-      if (ahead < nmy) {
-        const int s_ah = ahead % NBUF;
-        issue(ahead, slot_at(s_ah));
-      }
-      // wait for block i only: the blocks issued after it stay in flight
+      // remaining blocks (every one up to i + NBUF - 1 is issued): wait for
+      // block i only, the blocks issued after it stay in flight
       const int newer = min(NBUF - 1, nmy - 1 - i);
       if (NBUF >= 4 && newer >= 3)
         wait_vm<(NBUF >= 4 ? 3 : 0) * R::loads>();
@@ -902,8 +914,9 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
         wait_vm<0>();
       const int s_cur = i % NBUF;
       const int ch = c_begin + i;
-      body_block(slot_at(s_cur),
-                 min(kBlockTokens, st.nb - ch * kBlockTokens));
+      body_block(slot_at(s_cur), min(kBlockTokens, st.nb - ch * kBlockTokens), [&]() __attribute__((always_inline)) {
+        if (i + NBUF < nmy) issue(i + NBUF, slot_at(s_cur));
+      });
     }
   }
 

@@ -142,6 +142,19 @@ __device__ __forceinline__ u32x4 dsr16(uint32_t a) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "i"(OFF));
   return r;
 }
+// The weights' tile that a wavefront writes and then reads back goes through
+// inline asm as well: a compiler-visible LDS access while ring blocks are in
+// flight gets a wait for all of them.  One binary16 store, and a 16-byte load
+// that waits for its data in the same statement.
+__device__ __forceinline__ void dsw_h(uint32_t a, _Float16 v) {
+  const uint32_t b = __builtin_bit_cast(uint16_t, v);
+  asm volatile("ds_write_b16 %0, %1" : : "v"(a), "v"(b));
+}
+__device__ __forceinline__ u32x4 dsr16_now(uint32_t a) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a));
+  return r;
+}
 template <int OFF>
 __device__ __forceinline__ u32x2 dsr8(uint32_t a) {
   u32x2 r;
