@@ -290,10 +290,10 @@ def main():
     sampled_set = set(sampled)
 
     # kvq_append_decode_attn carries the append inside the decode launch for
-    # layers with unrotated values that decode on the matrix-core kernel (no
-    # 3-bit codes); other layers take the two calls, and the events then
-    # bracket the decode call alone
-    fused = wl.append and not wl.v_hadamard and not wl.nuq and all(3 not in p for p in wl.bit_pairs())
+    # layers that decode on the matrix-core kernel (no 3-bit codes); other
+    # layers take the two calls, and the events then bracket the decode call
+    # alone
+    fused = wl.append and not wl.nuq and all(3 not in p for p in wl.bit_pairs())
 
     def step(i, ev=None, nbytes=None):
         # layer by layer, as a model step runs: the layer's new token enters

@@ -162,13 +162,15 @@ constexpr int ring_pad() {
 }
 // Wavefronts per SIMD the register allocation is held to: three for the
 // GQA instances whose registers fit 168 with at most a spill outside the
-// block loop, else what they need.
-template <int KB, int VB, int G, bool INNER, bool MIX>
+// block loop and for the 2-bit rotated-value instances with per-channel keys
+// (whose appended-token rotation would otherwise set their register count),
+// else what they need.
+template <int KB, int VB, int G, bool INNER, bool MIX, bool PLO = false>
 constexpr int waves_per_simd() {
-  return (G >= 4 && (VB == 2 || (VB == 4 && !INNER && KB != 8))) ? 3 : 1;
+  return ((G >= 4 && (VB == 2 || (VB == 4 && !INNER && KB != 8))) || (PLO && !INNER && VB == 2)) ? 3 : 1;
 }
 template <int KB, int VB, int G, bool INNER, bool MIX, int NBUF, bool PLO>
-__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KB, VB, G, INNER, MIX>())))
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<KB, VB, G, INNER, MIX, PLO>())))
 decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   using R = Rec<KB, VB, INNER, MIX>;
   static_assert(!MIX || (INNER && KB == 4), "mixed groups: 4-bit inner keys");
@@ -744,6 +746,17 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       // (its slot is written below, and read by no other split)
       const int xs = J.new_slot - slot0;  // in [0, 32) for the chunk holding it
       const uint16_t* const nk = J.new_k + static_cast<int64_t>(u) * D;
+      // rotated values (PLO instances serve exactly those layers; the host
+      // fuses the append for per-channel keys only): the token's channels 2l
+      // and 2l + 1 as the window keeps them, c H v, taken before the chunk's
+      // operands are in registers
+      constexpr bool kRotNew = PLO && !INNER;
+      uint32_t vrot = 0;
+      if constexpr (kRotNew) {
+        if (xs >= 0 && xs < kBlockTokens)  // wave-uniform
+          vrot = hadamard_pair_rows(*reinterpret_cast<const uint32_t*>(J.new_v + static_cast<int64_t>(u) * D + 2 * l),
+                                    L.had_scale, l);
+      }
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -755,21 +768,43 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
       if (xs >= 0 && xs < kBlockTokens) {  // wave-uniform
         const uint16_t* const nv = J.new_v + static_cast<int64_t>(u) * D;
         const int e = xs - 8 * g4;  // element of the lane's eight slots
-        if (e >= 0 && e < 8) {
+        uint32_t vw;
+        if constexpr (kRotNew) {
+          vw = vrot;
+          // channel 16 nt + n16 sits in lane 8 nt + n16 / 2 (every lane takes part)
+          uint32_t pw[8];
 #pragma unroll
-          for (int nt = 0; nt < 8; ++nt) {
-            const uint32_t x = nv[16 * nt + n16];
+          for (int nt = 0; nt < 8; ++nt)
+            pw[nt] = static_cast<uint32_t>(
+                __builtin_amdgcn_ds_bpermute((8 * nt + (n16 >> 1)) << 2, static_cast<int>(vw)));
+          if (e >= 0 && e < 8) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              if (e == 2 * w) vv[nt][w] = (vv[nt][w] & 0xffff0000u) | x;
-              if (e == 2 * w + 1) vv[nt][w] = (vv[nt][w] & 0x0000ffffu) | (x << 16);
+            for (int nt = 0; nt < 8; ++nt) {
+              const uint32_t x = (n16 & 1) ? pw[nt] >> 16 : pw[nt] & 0xffffu;
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                if (e == 2 * w) vv[nt][w] = (vv[nt][w] & 0xffff0000u) | x;
+                if (e == 2 * w + 1) vv[nt][w] = (vv[nt][w] & 0x0000ffffu) | (x << 16);
+              }
+            }
+          }
+        } else {
+          vw = *reinterpret_cast<const uint32_t*>(nv + 2 * l);
+          if (e >= 0 && e < 8) {
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+              const uint32_t x = nv[16 * nt + n16];
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                if (e == 2 * w) vv[nt][w] = (vv[nt][w] & 0xffff0000u) | x;
+                if (e == 2 * w + 1) vv[nt][w] = (vv[nt][w] & 0x0000ffffu) | (x << 16);
+              }
             }
           }
         }
         // store the token: lane l takes channels 2l and 2l + 1
         const int x = slot0 + xs;
         const uint32_t kw = *reinterpret_cast<const uint32_t*>(nk + 2 * l);
-        const uint32_t vw = *reinterpret_cast<const uint32_t*>(nv + 2 * l);
         *reinterpret_cast<uint32_t*>(kf + static_cast<int64_t>(x) * D + 2 * l) = kw;
         vf[vslot(x, 2 * l)] = static_cast<uint16_t>(vw);
         vf[vslot(x, 2 * l + 1)] = static_cast<uint16_t>(vw >> 16);

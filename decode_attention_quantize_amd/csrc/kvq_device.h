@@ -81,6 +81,34 @@ __device__ __forceinline__ int64_t xshfl64(int64_t v) {
   return (static_cast<int64_t>(hi) << 32) | static_cast<uint32_t>(lo);
 }
 
+template <int M>
+__device__ __forceinline__ double xshfld(double v) {
+  return __longlong_as_double(xshfl64<M>(__double_as_longlong(v)));
+}
+
+// One 128-channel row rotated by the normalized Hadamard matrix, c H v with
+// c = fl64(1 / sqrt(128)), across a wavefront: lane l holds channels 2l and
+// 2l + 1 as a binary16 pair.  The butterflies run in binary64, where every
+// sum of up to 128 binary16 values is exact; the product with c is the one
+// rounding before the binary16 result (round to nearest even).
+__device__ __forceinline__ uint32_t hadamard_pair_rows(uint32_t w, double c, int lane) {
+  const double a = static_cast<double>(h2f(static_cast<uint16_t>(w)));
+  const double b = static_cast<double>(h2f(static_cast<uint16_t>(w >> 16)));
+  double y0 = a + b, y1 = a - b;  // channel bit 0, inside the lane
+  auto stage = [&](double p0, double p1, bool upper) __attribute__((always_inline)) {
+    y0 = upper ? p0 - y0 : y0 + p0;
+    y1 = upper ? p1 - y1 : y1 + p1;
+  };
+  // channel bits 1..6 are lane bits 0..5
+  stage(xshfld<1>(y0), xshfld<1>(y1), (lane & 1) != 0);
+  stage(xshfld<2>(y0), xshfld<2>(y1), (lane & 2) != 0);
+  stage(xshfld<4>(y0), xshfld<4>(y1), (lane & 4) != 0);
+  stage(xshfld<8>(y0), xshfld<8>(y1), (lane & 8) != 0);
+  stage(xshfld<16>(y0), xshfld<16>(y1), (lane & 16) != 0);
+  stage(xshfld<32>(y0), xshfld<32>(y1), (lane & 32) != 0);
+  return static_cast<uint32_t>(d2h(y0 * c)) | (static_cast<uint32_t>(d2h(y1 * c)) << 16);
+}
+
 // Reductions over aligned groups of W lanes (W a power of two <= 64).
 template <int W>
 __device__ __forceinline__ void group_minmax(float& mn, float& mx) {

@@ -596,11 +596,12 @@ kvq_status kvq_append_decode_attn(kvq_cache* c, int32_t layer, const void* k_new
   if (L.n + 1 > c->cfg.max_tokens) return KVQ_ERR_CAPACITY;
   const int S = c->cfg.sink_tokens, W = c->cfg.recent_window, F = c->F;
   // One launch when the token only needs storing (the next sink, or a window
-  // slot without a flush; values unrotated) and the layer decodes on the
-  // matrix-core kernel: the decode reads the token from k_new / v_new and
-  // stores it.  Otherwise the two calls this one stands for.
+  // slot without a flush) and the layer decodes on the matrix-core kernel:
+  // the decode reads the token from k_new / v_new (rotating its values when
+  // the layer keeps them rotated; per-channel keys only) and stores it.
+  // Otherwise the two calls this one stands for.
   const bool sink = L.s_eff < S;
-  const bool plain = !L.d.v_had && (sink || (!(F == 1 && W == 0) && L.r + 1 < W + F));
+  const bool plain = !(L.d.v_had && L.d.k_inner) && (sink || (!(F == 1 && W == 0) && L.r + 1 < W + F));
   if (plain && !c->force_generic && kvq::decode_fast_waves(L.d) > 0) {
     const int p = L.n;
     const int slot = sink ? p : c->sink_cap + (p - L.s_eff) % c->win_cap;

@@ -259,10 +259,12 @@ kvq_status kvq_decode_attn(kvq_cache* cache, int32_t layer, const void* q, float
  * model takes for each layer: the new token enters the cache and the query
  * attends over it; InnerQ, methodology 4, the fp16 window; KVQuant,
  * technical approach, the fused dequantize-attend read).  When the token
- * only needs storing -- the next sink, or a window slot without a flush, with
- * unrotated values -- and the layer's decode runs on the matrix-core kernel,
- * both happen in the decode's own launch: it reads the token from k_new /
- * v_new and stores it into its slot.  Otherwise it makes the two calls.
+ * only needs storing -- the next sink, or a window slot without a flush --
+ * and the layer's decode runs on the matrix-core kernel, both happen in the
+ * decode's own launch: it reads the token from k_new / v_new, rotates its
+ * values when the layer keeps them rotated (Hadamard page; layers with
+ * per-channel keys), and stores it into its slot.  Otherwise it makes the
+ * two calls.
  * k_new, v_new: device fp16 [B][Hkv][D]; q, out, workspace as for
  * kvq_decode_attn.  A failed launch leaves the layer in KVQ_ERR_STATE until
  * the next prefill, as for the calls it stands for.

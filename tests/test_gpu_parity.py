@@ -419,7 +419,8 @@ def test_codebook_codes_next_to_the_midpoints():
     cache.close()
 
 
-@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C5r", "C4r", "short-prompt-sinks-then-flush"])
+@pytest.mark.parametrize("name", ["C1", "C2r", "C3r", "C5r", "C4r", "P5r", "P5r-ternary",
+                                  "short-prompt-sinks-then-flush"])
 def test_fused_append_decode_matches_the_two_calls(name):
     """kvq_append_decode_attn stands for kvq_append_token + kvq_decode_attn:
     at every step the outputs and the layers' buffers are bit-identical to
