@@ -34,6 +34,25 @@
 namespace kvq {
 namespace {
 
+// Ring copies issued from inline assembly.  Through the builtin, the compiler
+// knows of the copy into LDS and, unable to tell the ring apart from the
+// kernel's tables, waits for every copy in flight (the next block's too)
+// before its first LDS access of each block.  Issued here, the copies are
+// awaited only by ring_wait, at the top of the block that reads them; a
+// slot is refilled one block after its last read, whose results the block
+// has consumed by then.  M0 holds the LDS base (one nop between its write
+// and the copy); each lane's 16 bytes land at M0 + 16 * lane.
+__device__ __forceinline__ void ring_load_opaque(const uint8_t* src, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" : : "v"(src), "s"(lds_dst)
+               : "memory", "m0");
+}
+// wait until at most N ring copies are in flight; also a compiler barrier
+// for the LDS reads that follow
+template <int N>
+__device__ __forceinline__ void ring_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 // Record of a block with 3-bit keys and values, value groups of 32 and K
 // outliers per token vector (the host layout rules, fixed at compile time).
 template <int OUTK>
@@ -311,7 +330,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
 #pragma unroll
     for (int k = 0; k < R::loads; ++k) {
       const int off = k * 1024 + l * 16;
-      if (off < R::bytes) ring_load(src + off, dst + k * 1024);
+      if (off < R::bytes) ring_load_opaque(src + off, lds_off(dst) + k * 1024);
     }
   };
 #pragma unroll
@@ -509,7 +528,7 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
     auto step = [&](int i, lds_u8* cur, lds_u8* ahead) __attribute__((always_inline)) {
       age(i);
       issue(i + NBUF - 1, ahead);
-      wait_vm<(NBUF - 1) * R::loads>();
+      ring_wait<(NBUF - 1) * R::loads>();
       const int ch = c_begin + i;
       body_block(cur, min(kBlockTokens, st.nb - ch * kBlockTokens));
     };
@@ -530,11 +549,11 @@ __global__ void __launch_bounds__(64) decode_lut_kernel(LayerDesc L, DecodeJob J
       if (ahead < nmy) issue(ahead, slot_at(ahead % NBUF));
       const int newer = min(NBUF - 1, nmy - 1 - i);
       if (NBUF >= 3 && newer >= 2)
-        wait_vm<(NBUF >= 3 ? 2 : 0) * R::loads>();
+        ring_wait<(NBUF >= 3 ? 2 : 0) * R::loads>();
       else if (newer >= 1)
-        wait_vm<R::loads>();
+        ring_wait<R::loads>();
       else
-        wait_vm<0>();
+        ring_wait<0>();
       const int ch = c_begin + i;
       body_block(slot_at(i % NBUF), min(kBlockTokens, st.nb - ch * kBlockTokens));
     }
