@@ -426,12 +426,13 @@ decode_mfma_kernel(LayerDesc L, DecodeJob J) {
   // one quantized block whose record sits in LDS at rec; refill() runs once
   // the block's last read of its record has completed (the slot is free)
   auto body_block = [&](const lds_u8* rec, int count, auto refill) __attribute__((always_inline)) {
-    // inner-key instances take the slot's base afresh for every block:
-    // hoisted out of the loop, each slot's lane addresses held registers
-    // of their own, and the spilled ones were reloaded inside the loop,
-    // whose wait on the reload drained the ring
+    // inner-key instances (and the 4-bit GQA one, measured faster with it)
+    // take the slot's base afresh for every block: hoisted out of the loop,
+    // each slot's lane addresses held registers of their own, and the
+    // spilled ones were reloaded inside the loop, whose wait on the reload
+    // drained the ring
     uint32_t r0 = lds_off(rec);
-    if constexpr (INNER) asm volatile("" : "+s"(r0));
+    if constexpr (INNER || (KB == 4 && VB == 4 && G >= 4)) asm volatile("" : "+s"(r0));
     f32x4 sacc[2];
     f32x4 sf;  // folded block scores (kFold)
     // ---------------- keys: one batch of LDS reads
